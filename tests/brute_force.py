@@ -1,0 +1,133 @@
+"""Pure-Python loop versions of both ops, for tiny inputs only.
+
+Written independently of the oracle (no NumPy arithmetic: explicit loops over
+Python floats and ints) so that a transposed operand, a wrong index or a
+dropped term in the vectorised oracle shows up as a mismatch.  Values come in
+as nested Python lists of exact floats (decoded from storage by the test).
+"""
+
+from __future__ import annotations
+
+import math
+
+
+def _dot(a, b):
+    s = 0.0
+    for x, y in zip(a, b):
+        s += x * y
+    return s
+
+
+def _matvec_rows(x_row, W, ncols):
+    # x_row (K) times W (K x ncols), W as a list of rows
+    out = [0.0] * ncols
+    for k, xv in enumerate(x_row):
+        wr = W[k]
+        for j in range(ncols):
+            out[j] += xv * wr[j]
+    return out
+
+
+def _rms_norm(row, gamma, eps):
+    ms = sum(v * v for v in row) / len(row)
+    r = math.sqrt(ms + eps)
+    return [gamma[i] * row[i] / r for i in range(len(row))]
+
+
+def _rope(row, cos_row, sin_row):
+    h = len(row) // 2
+    out = []
+    for i in range(len(row)):
+        partner = -row[i + h] if i < h else row[i - h]
+        out.append(row[i] * cos_row[i] + partner * sin_row[i])
+    return out
+
+
+def _q8(v, scale, offset=0.0):
+    q = v / scale + offset
+    r = round(q)  # Python rounds half to even
+    return max(-128, min(127, int(r)))
+
+
+def mla_prolog_brute(x, Wdq, Wdkvkr, Wuqqr, Wuk, g_cq, g_ckv, cos, sin,
+                     dims, eps_cq, eps_ckv, quant=None):
+    """Per-token loops.  quant: None or dict(smooth, dq, qs_ckv, qs_ckr).
+
+    Returns per-token lists: query[t][n][j], query_rope[t][n][j], kv_row[t],
+    kr_row[t] (codes when qs_ckv is given), and c8/s when quantised.
+    """
+    He, Hcq, N, D, Hckv, Dr = (dims[k] for k in ("He", "Hcq", "N", "D",
+                                                  "Hckv", "Dr"))
+    res = {"query": [], "query_rope": [], "kv_row": [], "kr_row": [],
+           "c8": [], "s": []}
+    for t in range(len(x)):
+        h = _matvec_rows(x[t], Wdq, Hcq)
+        cq = _rms_norm(h, g_cq, eps_cq)
+        if quant is None:
+            y = _matvec_rows(cq, Wuqqr, N * (D + Dr))
+        else:
+            u = [cq[i] * quant["smooth"][i] for i in range(Hcq)]
+            amax = max(abs(v) for v in u)
+            s = amax / 127.0
+            c8 = [max(-127, min(127, int(round(v / s)))) if s > 0 else 0
+                  for v in u]
+            res["c8"].append(c8)
+            res["s"].append(s)
+            y = []
+            for j in range(N * (D + Dr)):
+                acc = 0
+                for k in range(Hcq):
+                    acc += c8[k] * int(Wuqqr[k][j])
+                y.append(acc * s * quant["dq"][j])
+        qn, qr = [], []
+        for n in range(N):
+            qc = y[n * D:(n + 1) * D]
+            row = []
+            for j in range(Hckv):
+                row.append(_dot(qc, [Wuk[n][d][j] for d in range(D)]))
+            qn.append(row)
+            pre = y[N * D + n * Dr: N * D + (n + 1) * Dr]
+            qr.append(_rope(pre, cos[t], sin[t]))
+        res["query"].append(qn)
+        res["query_rope"].append(qr)
+        g = _matvec_rows(x[t], Wdkvkr, Hckv + Dr)
+        ckv = _rms_norm(g[:Hckv], g_ckv, eps_ckv)
+        kr = _rope(g[Hckv:], cos[t], sin[t])
+        if quant is not None and quant.get("qs_ckv") is not None:
+            ckv = [_q8(ckv[j], quant["qs_ckv"][j]) for j in range(Hckv)]
+            kr = [_q8(kr[j], quant["qs_ckr"][j]) for j in range(Dr)]
+        res["kv_row"].append(ckv)
+        res["kr_row"].append(kr)
+    return res
+
+
+def qkv_brute(qkv, gq, gk, cos, sin, dims, eps, scales=None):
+    """qkv[t][head][d].  scales: None or dict(ks, vs[, ko, vo]) per (h, d)."""
+    Nq, Nk, Nv, D = (dims[k] for k in ("Nq", "Nk", "Nv", "D"))
+    q_out, k_rows, v_rows = [], [], []
+    for t in range(len(qkv)):
+        qt, kt, vt = [], [], []
+        for hh in range(Nq + Nk + Nv):
+            row = qkv[t][hh]
+            if hh < Nq:
+                qt.append(_rope(_rms_norm(row, gq, eps), cos[t], sin[t]))
+            elif hh < Nq + Nk:
+                kr = _rope(_rms_norm(row, gk, eps), cos[t], sin[t])
+                if scales is not None:
+                    i = hh - Nq
+                    kr = [_q8(kr[d], scales["ks"][i][d],
+                              scales.get("ko", [[0.0] * D] * Nk)[i][d])
+                          for d in range(D)]
+                kt.append(kr)
+            else:
+                vr = list(row)
+                if scales is not None:
+                    i = hh - Nq - Nk
+                    vr = [_q8(vr[d], scales["vs"][i][d],
+                              scales.get("vo", [[0.0] * D] * Nv)[i][d])
+                          for d in range(D)]
+                vt.append(vr)
+        q_out.append(qt)
+        k_rows.append(kt)
+        v_rows.append(vt)
+    return q_out, k_rows, v_rows
