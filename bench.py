@@ -1,0 +1,332 @@
+"""Benchmark of the MLA prolog hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step = one full mla_prolog_v2 call (down projection, RmsNorms, c^KV /
+k^R cache scatter, up projection with RoPE, per-head W^UK product) over one
+batch of seeded synthetic tokens.  The headline workload is DeepSeek-V3-
+shaped decode, T = 32 tokens (bf16).  Inputs are resident in HBM before the
+timed region; steps rotate over several independent copies of weights,
+activations, caches and outputs so the working set exceeds the 256 MB
+last-level cache and bytes really come from HBM.
+
+Prints ONE JSON line.  Besides the headline value it carries:
+* roofline - the dominant kernel (the c^Q . [W^UQ | W^QR] up projection),
+  its algorithmic bytes over its average duration measured with HIP events
+  recorded by the library on the launch stream during the timed steps;
+* step_roofline - the whole call's algorithmic bytes over the step time;
+* prefill - the same prolog at T = 4096 (bf16 MFMA-bound);
+* qkv_rmsnorm_rope_cache - the fused qkv op on its (B=64, S=128) workload;
+* cpu_baseline - the float64 NumPy oracle timed on this host on a bounded
+  sample of the decode workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = ("MLA-prolog tokens/s at decode T=32 & prefill T=4096; "
+          "%HBM BW / %MFMA peak")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="independent input sets cycled by the decode steps")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-qkv", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (bytes / flops the method must move / do per call)
+# ---------------------------------------------------------------------------
+
+def mla_bytes(c, wb_uq=2, cache_b=2):
+    T = c.T
+    weights = (c.He * c.Hcq + c.He * (c.Hckv + c.Dr)) * 2 \
+        + c.Hcq * c.N * (c.D + c.Dr) * wb_uq + c.N * c.D * c.Hckv * 2
+    gammas = (c.Hcq + c.Hckv) * 2
+    per_tok = (c.He * 2 + 2 * c.Dr * 2 + 8 + c.N * c.Hckv * 2
+               + c.N * c.Dr * 2 + (c.Hckv + c.Dr) * cache_b)
+    return weights + gammas + T * per_tok
+
+
+def mla_flops(c):
+    return 2 * c.T * (c.He * (c.Hcq + c.Hckv + c.Dr)
+                      + c.Hcq * c.N * (c.D + c.Dr) + c.N * c.D * c.Hckv)
+
+
+def uqqr_bytes(c):
+    """Up projection as launched: W^UQ_QR, c^Q in, q^C out (bf16), q^R out,
+    cos/sin rows."""
+    return c.Hcq * c.N * (c.D + c.Dr) * 2 + c.T * (
+        c.Hcq * 2 + c.N * c.D * 2 + c.N * c.Dr * 2 + 2 * c.Dr * 2)
+
+
+def uqqr_flops(c):
+    return 2 * c.T * c.Hcq * c.N * (c.D + c.Dr)
+
+
+def qkv_bytes(c, n_valid):
+    T = c.T
+    return T * ((c.Nq + c.Nk + c.Nv) * c.D * 2 + 2 * c.D * 2 + 8
+                + c.Nq * c.D * 2) + n_valid * (c.Nk + c.Nv) * c.D \
+        + 2 * c.D * 2 + (c.Nk + c.Nv) * c.D * 4
+
+
+# ---------------------------------------------------------------------------
+
+def prepare_mla_sets(w, n_sets, torch, qn, gh):
+    """Upload one seeded workload, pack its weights, and clone it n_sets-1
+    times into distinct allocations."""
+    cfg = w.cfg
+    d = gh.upload(w)
+    base = {
+        "token_x": d["token_x"].view(cfg.B, cfg.S, cfg.He),
+        "weight_dq": qn.mla_pack_weight(d["weight_dq"]),
+        "weight_dkv_kr": qn.mla_pack_weight(d["weight_dkv_kr"]),
+        "weight_uq_qr": qn.mla_pack_weight(d["weight_uq_qr"]),
+        "weight_uk": qn.mla_pack_weight(d["weight_uk"]),
+    }
+    for k in ("rmsnorm_gamma_cq", "rmsnorm_gamma_ckv", "rope_sin", "rope_cos",
+              "cache_index", "kv_cache", "kr_cache"):
+        base[k] = d[k]
+    sets = [base]
+    for _ in range(1, n_sets):
+        sets.append({k: v.clone() for k, v in base.items()})
+    for s in sets:
+        s["query"] = torch.empty((cfg.B, cfg.S, cfg.N, cfg.Hckv),
+                                 dtype=torch.bfloat16, device="cuda")
+        s["query_rope"] = torch.empty((cfg.B, cfg.S, cfg.N, cfg.Dr),
+                                      dtype=torch.bfloat16, device="cuda")
+    return sets
+
+
+def run_mla(cfg, sets, steps, warmup, torch, qn):
+    """Time `steps` calls cycling over the sets; phase events on every step."""
+    ws = None
+    nph = len(qn.MLA_PHASES)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nph)]
+          for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    for row in ev:  # materialise the events on this stream
+        for e in row:
+            e.record(stream)
+
+    def call(s, phase_events=None):
+        nonlocal ws
+        q, qr = qn.mla_prolog_v2(
+            s["token_x"], s["weight_dq"], s["weight_uq_qr"], s["weight_uk"],
+            s["weight_dkv_kr"], s["rmsnorm_gamma_cq"], s["rmsnorm_gamma_ckv"],
+            s["rope_sin"], s["rope_cos"], s["cache_index"], s["kv_cache"],
+            s["kr_cache"], quant_mode=cfg.quant_mode,
+            rmsnorm_epsilon_cq=cfg.eps_cq, rmsnorm_epsilon_ckv=cfg.eps_ckv,
+            query=s["query"], query_rope=s["query_rope"], workspace=ws,
+            phase_events=phase_events)
+        return q
+
+    # one call to size and keep the workspace
+    from qkv_norm_rope_amd import _binding as b
+    s0 = sets[0]
+    a = b.mla_prolog_v2_args(
+        s0["token_x"], s0["weight_dq"], s0["weight_uq_qr"], s0["weight_uk"],
+        s0["weight_dkv_kr"], s0["rmsnorm_gamma_cq"], s0["rmsnorm_gamma_ckv"],
+        s0["rope_sin"], s0["rope_cos"], s0["cache_index"], s0["kv_cache"],
+        s0["kr_cache"], s0["query"], s0["query_rope"],
+        quant_mode=cfg.quant_mode)
+    ws = torch.empty(max(1, b.mla_prolog_v2_workspace_size(a)),
+                     dtype=torch.uint8, device="cuda")
+    for i in range(warmup):
+        call(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        call(sets[i % len(sets)], ev[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    phase_ms = [0.0] * (nph - 1)
+    for row in ev:
+        for p in range(nph - 1):
+            phase_ms[p] += row[p].elapsed_time(row[p + 1]) / steps
+    return ms_step, phase_ms
+
+
+def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
+    w = make_workload(4)
+    cfg = w.cfg
+    sets = []
+    for _ in range(2):
+        d = gh.upload(w)
+        d["q_out"] = torch.empty((cfg.T, cfg.Nq, cfg.D), dtype=torch.float16,
+                                 device="cuda")
+        sets.append(d)
+
+    def call(d):
+        qn.qkv_rmsnorm_rope_cache(
+            d["qkv"], d["gamma_q"], d["gamma_k"], d["cos"], d["sin"],
+            d["index"], d["k_cache"], d["v_cache"], Nq=cfg.Nq, Nk=cfg.Nk,
+            Nv=cfg.Nv, quant_mode=cfg.quant_mode, epsilon=cfg.eps,
+            k_scale=d["k_scale"], v_scale=d["v_scale"], q_out=d["q_out"],
+            B=cfg.B, S=cfg.S)
+
+    for i in range(warmup):
+        call(sets[i % 2])
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(s)
+    for i in range(steps):
+        call(sets[i % 2])
+    t1.record(s)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    n_valid = int((w.arrays["index"] >= 0).sum())
+    nbytes = qkv_bytes(cfg, n_valid)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "tokens_per_s": cfg.T / (ms * 1e-3),
+            "ms_per_step": ms, "algorithmic_bytes": nbytes,
+            "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+
+def cpu_baseline(w, seconds):
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = len(os.sched_getaffinity(0))
+    cfg = w.cfg
+    dims = dict(He=cfg.He, Hcq=cfg.Hcq, N=cfg.N, D=cfg.D, Hckv=cfg.Hckv,
+                Dr=cfg.Dr)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.mla_prolog_v2(w.arrays, w.dtypes, dims, cfg.quant_mode,
+                             cfg.eps_cq, cfg.eps_ckv)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} float64 NumPy oracle calls of the full T={cfg.T} "
+                      f"decode workload ({el:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the prolog shards by token or head with no "
+              "collective in this build)", file=sys.stderr)
+        return 2
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import qkv_norm_rope_amd as qn
+    from workloads import device as gh
+    from workloads import make_workload
+
+    qn.load_library()  # fail loudly without the HIP library
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    # ---- decode, T = 32 -------------------------------------------------
+    w = make_workload(1)
+    cfg = w.cfg
+    sets = prepare_mla_sets(w, args.rotate, torch, qn, gh)
+    ms, phase_ms = run_mla(cfg, sets, args.steps, args.warmup, torch, qn)
+    step_bytes = mla_bytes(cfg)
+    a6_ms = phase_ms[2]
+    a6_bytes = uqqr_bytes(cfg)
+    a6_gbs = a6_bytes / (a6_ms * 1e-3) / 1e9
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, random-init weights of the DeepSeek-V3 "
+                "MLA shapes)",
+        "config": {"workload": cfg.name, "T": cfg.T, "B": cfg.B, "S": cfg.S,
+                   "He": cfg.He, "Hcq": cfg.Hcq, "N": cfg.N, "D": cfg.D,
+                   "Hckv": cfg.Hckv, "Dr": cfg.Dr, "block_num": cfg.block_num,
+                   "block_size": cfg.block_size, "quant_mode": cfg.quant_mode,
+                   "weight_layout": "packed_k16",
+                   "rotating_input_sets": args.rotate},
+        "roofline": {"kernel": "up projection c^Q.[W^UQ|W^QR] + RoPE q^R",
+                     "bound": "hbm", "achieved": a6_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": a6_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": a6_bytes,
+                     "avg_launch_us": a6_ms * 1e3},
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes,
+                          "achieved": step_gbs, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS},
+        "phase_us": dict(zip(("down", "norm_cache", "up_qr", "uk"),
+                             [p * 1e3 for p in phase_ms])),
+    }
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---- prefill, T = 4096 ------------------------------------------------
+    if not args.no_prefill:
+        wp = make_workload(2)
+        pc = wp.cfg
+        psets = prepare_mla_sets(wp, 1, torch, qn, gh)
+        psteps = max(3, args.steps // 20)
+        pms, pph = run_mla(pc, psets, psteps, max(2, args.warmup // 10),
+                           torch, qn)
+        fl = mla_flops(pc)
+        a6f = uqqr_flops(pc)
+        out["prefill"] = {
+            "workload": pc.name, "tokens_per_s": pc.T / (pms * 1e-3),
+            "ms_per_step": pms, "steps": psteps, "algorithmic_flops": fl,
+            "step_TFLOPs": fl / (pms * 1e-3) / 1e12,
+            "mfma_frac": fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "phase_us": dict(zip(("down", "norm_cache", "up_qr", "uk"),
+                                 [p * 1e3 for p in pph])),
+            "roofline": {"kernel": "up projection c^Q.[W^UQ|W^QR] + RoPE q^R",
+                         "bound": "mfma",
+                         "achieved": a6f / (pph[2] * 1e-3) / 1e12,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": a6f / (pph[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "traffic": None},
+        }
+        del psets
+        torch.cuda.empty_cache()
+
+    if not args.no_qkv:
+        out["qkv_rmsnorm_rope_cache"] = bench_qkv(
+            max(10, args.steps // 2), max(3, args.warmup // 2), torch, qn, gh,
+            make_workload)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,280 @@
+/*
+ * qkvnr.h - C ABI of the MI355X (gfx950) MLA-prolog / qkv RmsNorm-RoPE-cache
+ * library.
+ *
+ * Two operations, both from public operator documentation:
+ *
+ *  - MlaPrologV2 ("MlaPrologV2" README, ops-transformer, attention/
+ *    mla_prolog_v2: function description and formulas, parameter table,
+ *    constraints).  It computes, per token t:
+ *        c^Q  = RmsNorm(x . W^DQ)
+ *        q^N  = (c^Q . W^UQ) . W^UK           per head   -> query
+ *        q^R  = RoPE(c^Q . W^QR)                         -> query_rope
+ *        c^KV = RmsNorm(x . W^DKV)     written to kv_cache at cache_index[t]
+ *        k^R  = RoPE(x . W^KR)         written to kr_cache at cache_index[t]
+ *
+ *  - QkvRmsNormRopeCache ("aclnnQkvRmsNormRopeCache", CANN API reference:
+ *    function description and formulas (1)-(4)).  It splits a fused qkv
+ *    tensor into q, k and v (SplitVD), RmsNorms q and k, applies
+ *    half-and-half RoPE to both, quantises k and v, writes q to q_out and
+ *    scatters k and v into paged caches.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer named in an argument struct is a DEVICE pointer into
+ *    memory the caller owns (the struct itself lives in host memory).  The
+ *    library never allocates, frees or synchronises, keeps no state between
+ *    calls, and launches all work on the caller's stream (`stream` is a
+ *    hipStream_t passed as void*; NULL is the default stream).  Calls on one
+ *    stream are ordered by that stream; calls that share output buffers on
+ *    different streams race.
+ *  - Tensors are dense and row-major (C order) with the shapes given below.
+ *    bf16 and fp16 are IEEE-style 16-bit floats; int8 is two's complement.
+ *  - Every entry point validates its arguments on the host first and
+ *    returns a negative QKVNR_ERR_* code without launching anything when a
+ *    check fails.  QKVNR_OK (0) means all work was enqueued; kernel faults
+ *    surface on the stream like any other HIP error.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    and caches (no floating-point atomics; fixed-order reductions).
+ *  - Cache updates: a token whose index is -1 writes nothing.  Indexes must
+ *    lie in [-1, BlockNum*BlockSize) and must not repeat (both operators'
+ *    index restrictions).  The kernels skip any index outside that range
+ *    (memory safety); a repeated slot gets an unspecified winner.
+ */
+#ifndef QKVNR_H
+#define QKVNR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKVNR_VERSION_STRING "0.1.0"
+
+/* ---- status codes ------------------------------------------------------ */
+enum {
+  QKVNR_OK = 0,
+  QKVNR_ERR_NULL_ARG = -1,          /* a required pointer is NULL */
+  QKVNR_ERR_BAD_SHAPE = -2,         /* a dimension is negative or breaks a
+                                       shape rule */
+  QKVNR_ERR_BAD_MODE = -3,          /* unknown quant mode, dtype or layout */
+  QKVNR_ERR_UNSUPPORTED = -4,       /* valid on the pages, not built here
+                                       (full quantisation, PA_NZ caches,
+                                       Nkv != 1, ...) */
+  QKVNR_ERR_RESERVED_NONNULL = -5,  /* a reserved pointer is not NULL */
+  QKVNR_ERR_WORKSPACE_TOO_SMALL = -6,
+  QKVNR_ERR_BAD_EPS = -7,           /* epsilon negative or not finite */
+  QKVNR_ERR_BAD_STRUCT = -8,        /* struct_size does not match */
+  QKVNR_ERR_BAD_ALIGNMENT = -9,     /* a pointer is not 16-byte aligned */
+  QKVNR_ERR_LAUNCH_FAILED = -10,    /* hipGetLastError after a launch */
+  QKVNR_ERR_BAD_INDEX = -11         /* host index check (debug flag) */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* qkvnr_status_string(int status);
+
+/* Library version, QKVNR_VERSION_STRING. */
+const char* qkvnr_version(void);
+
+/* ======================================================================= */
+/* MlaPrologV2                                                              */
+/* ======================================================================= */
+
+/* Quantisation scenarios of the MlaPrologV2 README's scenario table.
+ * NONE: every input and output is bf16.
+ * PARTIAL_KV_BF16: weight_uq_qr is int8 with a per-channel fp32 dequant
+ *   scale (dequant_scale_w_uq_qr); c^Q is quantised per token to int8 after
+ *   multiplying by smooth_scales_cq; caches stay bf16.
+ * PARTIAL_KV_INT8: as PARTIAL_KV_BF16, plus int8 kv_cache / kr_cache
+ *   quantised per channel by quant_scale_ckv / quant_scale_ckr
+ *   (code = saturate(round_half_even(value / scale))).
+ * FULL_KV_BF16, FULL_KV_INT8: the full-quantisation rows; rejected with
+ *   QKVNR_ERR_UNSUPPORTED. */
+enum {
+  MLA_QUANT_NONE = 0,
+  MLA_QUANT_PARTIAL_KV_BF16 = 1,
+  MLA_QUANT_PARTIAL_KV_INT8 = 2,
+  MLA_QUANT_FULL_KV_BF16 = 3,
+  MLA_QUANT_FULL_KV_INT8 = 4
+};
+
+/* Weight layouts for weight_dq, weight_dkv_kr, weight_uq_qr, weight_uk.
+ * ND: the page's unblocked (k, n) row-major layout ((N, D, Hckv) for
+ *   weight_uk).  The library packs ND weights into the workspace on every
+ *   call (convenient, slower).
+ * PACKED_K16: the MFMA-native blocked layout produced once by
+ *   mla_pack_weight(): for a (K, N) matrix with G = 16 / element_bytes
+ *   (8 for bf16, 16 for int8), element (k, n) is stored at
+ *       ((k / G) * N + n) * G + (k % G),
+ *   so the G consecutive-k values of one column form one 16-byte chunk.
+ *   weight_uk packs each head's (D, Hckv) matrix this way, heads in order.
+ *   This plays the role that the pages' FRACTAL_NZ weight format plays for
+ *   their hardware. */
+enum { MLA_WEIGHT_ND = 0, MLA_WEIGHT_PACKED_K16 = 1 };
+
+typedef struct MlaPrologV2Args {
+  uint32_t struct_size;      /* = sizeof(MlaPrologV2Args) */
+  int32_t quant_mode;        /* MLA_QUANT_* */
+  int32_t weight_layout;     /* MLA_WEIGHT_* */
+  int32_t reserved0;         /* must be 0 */
+
+  /* Dimensions (MlaPrologV2 README, constraints).  T = B*S tokens; for the
+   * (T, He) layout pass B = T, S = 1.  Requirements checked here:
+   * He, Hcq, D multiples of 32 (K dims of the MFMA tiles), Hckv a multiple
+   * of 16, Dr in {16, 32, 64} with (N*D) % Dr == 0, Nkv == 1, all > 0
+   * except B, S (either may be 0: nothing is done) and block_num /
+   * block_size (either 0: the caches are left untouched, queries are still
+   * computed). */
+  int64_t B, S, He, Hcq, N, D, Hckv, Dr, Nkv, block_num, block_size;
+
+  double rmsnorm_epsilon_cq;   /* epsilon of c^Q's RmsNorm, >= 0 */
+  double rmsnorm_epsilon_ckv;  /* epsilon of c^KV's RmsNorm, >= 0 */
+  const char* cache_mode;      /* NULL, "" or "PA_ND" (paged, row-major);
+                                  "PA_NZ" -> QKVNR_ERR_UNSUPPORTED */
+
+  /* ---- inputs (device) ---- */
+  const void* token_x;         /* (T, He) bf16 */
+  const void* weight_dq;       /* (He, Hcq) bf16 */
+  const void* weight_uq_qr;    /* (Hcq, N*(D+Dr)): bf16 (NONE) or int8
+                                  (PARTIAL_*).  Columns [0, N*D) are W^UQ,
+                                  head n at n*D; columns [N*D, N*(D+Dr)) are
+                                  W^QR, head n at N*D + n*Dr. */
+  const void* weight_uk;       /* (N, D, Hckv) bf16 */
+  const void* weight_dkv_kr;   /* (He, Hckv+Dr) bf16: [W^DKV | W^KR] */
+  const void* rmsnorm_gamma_cq;   /* (Hcq) bf16 */
+  const void* rmsnorm_gamma_ckv;  /* (Hckv) bf16 */
+  const void* rope_sin;        /* (T, Dr) bf16 */
+  const void* rope_cos;        /* (T, Dr) bf16 */
+  const int64_t* cache_index;  /* (T) flat slot ids, -1 = skip */
+  const float* dequant_scale_x;        /* reserved: must be NULL */
+  const float* dequant_scale_w_dq;     /* reserved: must be NULL */
+  const float* dequant_scale_w_uq_qr;  /* (N*(D+Dr)) fp32, PARTIAL_* only */
+  const float* dequant_scale_w_dkv_kr; /* reserved: must be NULL */
+  const float* quant_scale_ckv;        /* (Hckv) fp32, PARTIAL_KV_INT8 only */
+  const float* quant_scale_ckr;        /* (Dr) fp32, PARTIAL_KV_INT8 only */
+  const float* smooth_scales_cq;       /* (Hcq) fp32, PARTIAL_* only */
+
+  /* ---- in/out (device), updated in place at indexed slots only ---- */
+  void* kv_cache;              /* (BlockNum, BlockSize, Nkv, Hckv): bf16, or
+                                  int8 in PARTIAL_KV_INT8 */
+  void* kr_cache;              /* (BlockNum, BlockSize, Nkv, Dr): same dtype
+                                  rule as kv_cache */
+
+  /* ---- outputs (device), fully overwritten ---- */
+  void* query;                 /* (T, N, Hckv) bf16 */
+  void* query_rope;            /* (T, N, Dr) bf16 */
+  float* dequant_scale_q_nope; /* full quantisation only: must be NULL */
+
+  /* ---- optional diagnostics (device), NULL when not wanted ----
+   * PARTIAL_* only: the int8 codes of c^Q (T, Hcq) and their per-token
+   * scales (T) exactly as the up-projection consumed them. */
+  int8_t* dbg_cq_int8;
+  float* dbg_cq_scale;
+
+  /* ---- optional instrumentation (host array of hipEvent_t handles) ----
+   * When n_phase_events > 0 the library records phase_events[i] on `stream`
+   * at the phase boundaries MLA_PHASE_* below (only the first
+   * n_phase_events of them).  The work is exactly that of a normal call;
+   * ND-layout weight packing happens before MLA_PHASE_START. */
+  void* const* phase_events;
+  int32_t n_phase_events;
+  int32_t reserved1;                /* must be 0 */
+} MlaPrologV2Args;
+
+/* Phase boundaries of one mla_prolog_v2 call, in launch order. */
+enum {
+  MLA_PHASE_START = 0,        /* before the first kernel */
+  MLA_PHASE_AFTER_DOWN = 1,   /* after x . [W^DQ | W^DKV_KR] */
+  MLA_PHASE_AFTER_NORM = 2,   /* after RmsNorms, c^Q quant, RoPE k^R, scatter */
+  MLA_PHASE_AFTER_UQQR = 3,   /* after c^Q . [W^UQ | W^QR] and RoPE q^R */
+  MLA_PHASE_AFTER_UK = 4,     /* after q^C . W^UK per head (end of call) */
+  MLA_PHASE_COUNT = 5
+};
+
+/* Bytes of device workspace mla_prolog_v2() needs for these arguments
+ * (depends on the dims, T, quant mode and weight layout).  Writes *bytes
+ * and returns QKVNR_OK, or a validation error (then *bytes is 0). */
+int mla_prolog_v2_workspace_size(const MlaPrologV2Args* args, size_t* bytes);
+
+/* Host-only validation of args (the checks mla_prolog_v2 runs first).
+ * Makes no HIP call. */
+int mla_prolog_v2_validate(const MlaPrologV2Args* args);
+
+/* Run the prolog.  workspace: device scratch of at least
+ * mla_prolog_v2_workspace_size() bytes, 256-byte aligned, owned by the
+ * caller, contents undefined on entry and exit (may be NULL when the size
+ * is 0).  Enqueues on `stream` and returns without synchronising. */
+int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Pack `batch` row-major (K, N) matrices (each K*N elements of
+ * `elem_bytes` = 2 (bf16/fp16) or 1 (int8), batches contiguous) into the
+ * MLA_WEIGHT_PACKED_K16 layout at dst (same total size, distinct buffer).
+ * K must be a multiple of 16 / elem_bytes.  Device pointers; enqueued on
+ * `stream`. */
+int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K,
+                    int64_t N, int32_t elem_bytes, void* stream);
+
+/* ======================================================================= */
+/* QkvRmsNormRopeCache                                                      */
+/* ======================================================================= */
+
+/* Quant step of formula (4): NONE (caches have the input dtype), SYMMETRIC
+ * (int8 = sat(rne(x / scale))), ASYMMETRIC (int8 = sat(rne(x / scale +
+ * offset))).  Scales and offsets are per channel over (head, dim). */
+enum { QKV_QUANT_NONE = 0, QKV_QUANT_SYMMETRIC = 1, QKV_QUANT_ASYMMETRIC = 2 };
+
+/* Element type of qkv, gamma, cos, sin, q_out and the BeforeQuant outputs
+ * (and of the caches in QKV_QUANT_NONE). */
+enum { QKV_DTYPE_FP16 = 0, QKV_DTYPE_BF16 = 1 };
+
+typedef struct QkvRmsNormRopeCacheArgs {
+  uint32_t struct_size;      /* = sizeof(QkvRmsNormRopeCacheArgs) */
+  int32_t quant_mode;        /* QKV_QUANT_* */
+  int32_t dtype;             /* QKV_DTYPE_* */
+  int32_t reserved0;         /* must be 0 */
+
+  /* Dimensions (aclnnQkvRmsNormRopeCache, input shape restrictions):
+   * D == 128; Nk == Nv; Nq, Nk >= 1; block_num >= ceil(S / block_size) * B
+   * when B*S > 0. */
+  int64_t B, S, Nq, Nk, Nv, D, block_num, block_size;
+  double epsilon;            /* RmsNorm epsilon, >= 0 */
+  const char* cache_mode;    /* NULL, "" or "PA_ND"; "PA_NZ" unsupported */
+
+  /* ---- inputs (device) ---- */
+  const void* qkv;           /* (B*S, Nq+Nk+Nv, D): q heads, then k, then v */
+  const void* gamma_q;       /* (D) */
+  const void* gamma_k;       /* (D) */
+  const void* cos;           /* (B*S, D) */
+  const void* sin;           /* (B*S, D) */
+  const int64_t* index;      /* (B*S) flat slot ids, -1 = skip */
+  const float* k_scale;      /* (Nk*D), nonzero; quantised modes only */
+  const float* v_scale;      /* (Nv*D), nonzero; quantised modes only */
+  const float* k_offset;     /* (Nk*D); ASYMMETRIC only, else NULL */
+  const float* v_offset;     /* (Nv*D); ASYMMETRIC only, else NULL */
+
+  /* ---- in/out (device) ---- */
+  void* k_cache;             /* (block_num, block_size, Nk, D) */
+  void* v_cache;             /* (block_num, block_size, Nv, D) */
+
+  /* ---- outputs (device) ---- */
+  void* q_out;               /* (B*S, Nq, D), the rotated q */
+  void* q_before_quant;      /* optional (B*S, Nq, D): same as q_out */
+  void* k_before_quant;      /* optional (B*S, Nk, D): k after RoPE */
+  void* v_before_quant;      /* optional (B*S, Nv, D): v as split */
+} QkvRmsNormRopeCacheArgs;
+
+/* Host-only validation (makes no HIP call). */
+int qkv_rmsnorm_rope_cache_validate(const QkvRmsNormRopeCacheArgs* args);
+
+/* Run the fused op: one pass over qkv, no workspace.  Enqueues on `stream`
+ * and returns without synchronising. */
+int qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* args, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* QKVNR_H */

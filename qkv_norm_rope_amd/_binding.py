@@ -1,0 +1,396 @@
+"""ctypes binding over libqkvnr.so (argument marshalling only).
+
+Every computation happens in the HIP library; this module checks tensor
+metadata, allocates outputs and workspace through torch (device memory and
+streams only), fills the C argument structs declared in include/qkvnr.h and
+raises on a non-zero status.  There is no fallback: without the built
+library every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libqkvnr.so")
+
+# ---- constants mirrored from include/qkvnr.h --------------------------------
+QKVNR_OK = 0
+STATUS_NAMES = {
+    0: "QKVNR_OK", -1: "QKVNR_ERR_NULL_ARG", -2: "QKVNR_ERR_BAD_SHAPE",
+    -3: "QKVNR_ERR_BAD_MODE", -4: "QKVNR_ERR_UNSUPPORTED",
+    -5: "QKVNR_ERR_RESERVED_NONNULL", -6: "QKVNR_ERR_WORKSPACE_TOO_SMALL",
+    -7: "QKVNR_ERR_BAD_EPS", -8: "QKVNR_ERR_BAD_STRUCT",
+    -9: "QKVNR_ERR_BAD_ALIGNMENT", -10: "QKVNR_ERR_LAUNCH_FAILED",
+    -11: "QKVNR_ERR_BAD_INDEX",
+}
+MLA_QUANT = {"none": 0, "partial_kv_bf16": 1, "partial_kv_int8": 2,
+             "full_kv_bf16": 3, "full_kv_int8": 4}
+MLA_WEIGHT_ND, MLA_WEIGHT_PACKED_K16 = 0, 1
+MLA_PHASES = ("start", "after_down", "after_norm", "after_uqqr", "after_uk")
+QKV_QUANT = {"none": 0, "symmetric": 1, "asymmetric": 2}
+QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
+
+EXPORTS = (
+    "qkvnr_status_string", "qkvnr_version", "mla_prolog_v2_workspace_size",
+    "mla_prolog_v2_validate", "mla_prolog_v2", "mla_pack_weight",
+    "qkv_rmsnorm_rope_cache_validate", "qkv_rmsnorm_rope_cache",
+)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class MlaPrologV2Args(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("quant_mode", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("B", _i64), ("S", _i64), ("He", _i64), ("Hcq", _i64), ("N", _i64),
+        ("D", _i64), ("Hckv", _i64), ("Dr", _i64), ("Nkv", _i64),
+        ("block_num", _i64), ("block_size", _i64),
+        ("rmsnorm_epsilon_cq", ctypes.c_double),
+        ("rmsnorm_epsilon_ckv", ctypes.c_double),
+        ("cache_mode", ctypes.c_char_p),
+        ("token_x", _vp), ("weight_dq", _vp), ("weight_uq_qr", _vp),
+        ("weight_uk", _vp), ("weight_dkv_kr", _vp),
+        ("rmsnorm_gamma_cq", _vp), ("rmsnorm_gamma_ckv", _vp),
+        ("rope_sin", _vp), ("rope_cos", _vp), ("cache_index", _vp),
+        ("dequant_scale_x", _vp), ("dequant_scale_w_dq", _vp),
+        ("dequant_scale_w_uq_qr", _vp), ("dequant_scale_w_dkv_kr", _vp),
+        ("quant_scale_ckv", _vp), ("quant_scale_ckr", _vp),
+        ("smooth_scales_cq", _vp),
+        ("kv_cache", _vp), ("kr_cache", _vp),
+        ("query", _vp), ("query_rope", _vp), ("dequant_scale_q_nope", _vp),
+        ("dbg_cq_int8", _vp), ("dbg_cq_scale", _vp),
+        ("phase_events", ctypes.POINTER(_vp)), ("n_phase_events", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
+    ]
+
+
+class QkvRmsNormRopeCacheArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("quant_mode", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("B", _i64), ("S", _i64), ("Nq", _i64), ("Nk", _i64), ("Nv", _i64),
+        ("D", _i64), ("block_num", _i64), ("block_size", _i64),
+        ("epsilon", ctypes.c_double), ("cache_mode", ctypes.c_char_p),
+        ("qkv", _vp), ("gamma_q", _vp), ("gamma_k", _vp), ("cos", _vp),
+        ("sin", _vp), ("index", _vp), ("k_scale", _vp), ("v_scale", _vp),
+        ("k_offset", _vp), ("v_offset", _vp), ("k_cache", _vp),
+        ("v_cache", _vp), ("q_out", _vp), ("q_before_quant", _vp),
+        ("k_before_quant", _vp), ("v_before_quant", _vp),
+    ]
+
+
+class QkvnrError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} "
+                         f"({status_string(status)})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libqkvnr.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m qkv_norm_rope_amd.build`"
+            " (there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    lib.qkvnr_status_string.restype = ctypes.c_char_p
+    lib.qkvnr_status_string.argtypes = [ctypes.c_int]
+    lib.qkvnr_version.restype = ctypes.c_char_p
+    lib.qkvnr_version.argtypes = []
+    lib.mla_prolog_v2_workspace_size.restype = ctypes.c_int
+    lib.mla_prolog_v2_workspace_size.argtypes = [
+        ctypes.POINTER(MlaPrologV2Args), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prolog_v2_validate.restype = ctypes.c_int
+    lib.mla_prolog_v2_validate.argtypes = [ctypes.POINTER(MlaPrologV2Args)]
+    lib.mla_prolog_v2.restype = ctypes.c_int
+    lib.mla_prolog_v2.argtypes = [ctypes.POINTER(MlaPrologV2Args), _vp,
+                                  ctypes.c_size_t, _vp]
+    lib.mla_pack_weight.restype = ctypes.c_int
+    lib.mla_pack_weight.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_int32,
+                                    _vp]
+    lib.qkv_rmsnorm_rope_cache_validate.restype = ctypes.c_int
+    lib.qkv_rmsnorm_rope_cache_validate.argtypes = [
+        ctypes.POINTER(QkvRmsNormRopeCacheArgs)]
+    lib.qkv_rmsnorm_rope_cache.restype = ctypes.c_int
+    lib.qkv_rmsnorm_rope_cache.argtypes = [
+        ctypes.POINTER(QkvRmsNormRopeCacheArgs), _vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().qkvnr_status_string(status).decode()
+
+
+def version() -> str:
+    return load_library().qkvnr_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != QKVNR_OK:
+        raise QkvnrError(status, what)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# weight packing
+# ---------------------------------------------------------------------------
+
+def mla_pack_weight(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pack a (K, N) or (batch, K, N) weight into the K16 blocked layout.
+
+    The result has w's shape and dtype; only the element order changes (see
+    MLA_WEIGHT_PACKED_K16 in include/qkvnr.h).
+    """
+    lib = load_library()
+    if w.dim() not in (2, 3):
+        raise ValueError("weight must be (K, N) or (batch, K, N)")
+    batch = 1 if w.dim() == 2 else w.shape[0]
+    K, N = w.shape[-2], w.shape[-1]
+    eb = w.element_size()
+    out = torch.empty_like(w)
+    _check(lib.mla_pack_weight(_ptr(w), _ptr(out), batch, K, N, eb,
+                               _stream(stream)), "mla_pack_weight")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# MlaPrologV2
+# ---------------------------------------------------------------------------
+
+def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
+                       weight_dkv_kr, rmsnorm_gamma_cq, rmsnorm_gamma_ckv,
+                       rope_sin, rope_cos, cache_index, kv_cache, kr_cache,
+                       query, query_rope, *, quant_mode="none",
+                       weight_layout=MLA_WEIGHT_PACKED_K16,
+                       rmsnorm_epsilon_cq=1e-5, rmsnorm_epsilon_ckv=1e-5,
+                       dequant_scale_w_uq_qr=None, quant_scale_ckv=None,
+                       quant_scale_ckr=None, smooth_scales_cq=None,
+                       dbg_cq_int8=None, dbg_cq_scale=None, cache_mode=None,
+                       B=None, S=None) -> MlaPrologV2Args:
+    """Fill the C struct from tensors.  Dims come from the tensor shapes:
+    token_x (T, He) or (B, S, He); weight_dq (He, Hcq); weight_uk
+    (N, D, Hckv); rope tables (T, Dr); caches (BlockNum, BlockSize, Nkv, H).
+    """
+    a = MlaPrologV2Args()
+    a.struct_size = ctypes.sizeof(MlaPrologV2Args)
+    a.quant_mode = MLA_QUANT[quant_mode] if isinstance(quant_mode, str) \
+        else int(quant_mode)
+    a.weight_layout = int(weight_layout)
+    He = token_x.shape[-1]
+    T = token_x.numel() // He if He else 0
+    if B is None:
+        B, S = (token_x.shape[0], token_x.shape[1]) if token_x.dim() == 3 \
+            else (T, 1)
+    a.B, a.S = int(B), int(S)
+    a.He = int(He)
+    a.Hcq = int(weight_dq.shape[-1])
+    a.N, a.D, a.Hckv = (int(v) for v in weight_uk.shape)
+    a.Dr = int(rope_sin.shape[-1])
+    a.Nkv = int(kv_cache.shape[2])
+    a.block_num, a.block_size = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    a.rmsnorm_epsilon_cq = float(rmsnorm_epsilon_cq)
+    a.rmsnorm_epsilon_ckv = float(rmsnorm_epsilon_ckv)
+    a.cache_mode = cache_mode.encode() if cache_mode else None
+    if T > 0:
+        a.token_x = _ptr(token_x)
+        a.rope_sin = _ptr(rope_sin)
+        a.rope_cos = _ptr(rope_cos)
+        a.cache_index = _ptr(cache_index)
+        a.query = _ptr(query)
+        a.query_rope = _ptr(query_rope)
+        a.dbg_cq_int8 = _ptr(dbg_cq_int8)
+        a.dbg_cq_scale = _ptr(dbg_cq_scale)
+    a.weight_dq = _ptr(weight_dq)
+    a.weight_uq_qr = _ptr(weight_uq_qr)
+    a.weight_uk = _ptr(weight_uk)
+    a.weight_dkv_kr = _ptr(weight_dkv_kr)
+    a.rmsnorm_gamma_cq = _ptr(rmsnorm_gamma_cq)
+    a.rmsnorm_gamma_ckv = _ptr(rmsnorm_gamma_ckv)
+    if kv_cache.numel():
+        a.kv_cache = _ptr(kv_cache)
+    if kr_cache.numel():
+        a.kr_cache = _ptr(kr_cache)
+    a.dequant_scale_w_uq_qr = _ptr(dequant_scale_w_uq_qr)
+    a.quant_scale_ckv = _ptr(quant_scale_ckv)
+    a.quant_scale_ckr = _ptr(quant_scale_ckr)
+    a.smooth_scales_cq = _ptr(smooth_scales_cq)
+    return a
+
+
+def mla_prolog_v2_workspace_size(args: MlaPrologV2Args) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().mla_prolog_v2_workspace_size(ctypes.byref(args),
+                                                       ctypes.byref(n)),
+           "mla_prolog_v2_workspace_size")
+    return n.value
+
+
+def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
+                  rmsnorm_gamma_cq, rmsnorm_gamma_ckv, rope_sin, rope_cos,
+                  cache_index, kv_cache, kr_cache, *, quant_mode="none",
+                  weight_layout=MLA_WEIGHT_PACKED_K16,
+                  rmsnorm_epsilon_cq=1e-5, rmsnorm_epsilon_ckv=1e-5,
+                  dequant_scale_w_uq_qr=None, quant_scale_ckv=None,
+                  quant_scale_ckr=None, smooth_scales_cq=None,
+                  query=None, query_rope=None, workspace=None,
+                  return_cq_quant=False, cache_mode=None, stream=None,
+                  phase_events=None):
+    """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
+
+    Returns (query, query_rope), plus (cq_int8, cq_scale) when
+    return_cq_quant is set in a partial-quant mode.  phase_events: optional
+    list of recorded torch.cuda.Event(enable_timing=True) objects, recorded
+    again by the library at the MLA_PHASES boundaries.
+    """
+    lib = load_library()
+    He = token_x.shape[-1]
+    lead = tuple(token_x.shape[:-1])
+    T = token_x.numel() // He if He else 0
+    N, D, Hckv = weight_uk.shape
+    Dr = rope_sin.shape[-1]
+    dev = token_x.device
+    if query is None:
+        query = torch.empty(lead + (N, Hckv), dtype=torch.bfloat16, device=dev)
+    if query_rope is None:
+        query_rope = torch.empty(lead + (N, Dr), dtype=torch.bfloat16,
+                                 device=dev)
+    dbg8 = dbgs = None
+    if return_cq_quant:
+        dbg8 = torch.empty((T, weight_dq.shape[-1]), dtype=torch.int8,
+                           device=dev)
+        dbgs = torch.empty((T,), dtype=torch.float32, device=dev)
+    a = mla_prolog_v2_args(
+        token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
+        rmsnorm_gamma_cq, rmsnorm_gamma_ckv, rope_sin, rope_cos, cache_index,
+        kv_cache, kr_cache, query, query_rope, quant_mode=quant_mode,
+        weight_layout=weight_layout, rmsnorm_epsilon_cq=rmsnorm_epsilon_cq,
+        rmsnorm_epsilon_ckv=rmsnorm_epsilon_ckv,
+        dequant_scale_w_uq_qr=dequant_scale_w_uq_qr,
+        quant_scale_ckv=quant_scale_ckv, quant_scale_ckr=quant_scale_ckr,
+        smooth_scales_cq=smooth_scales_cq, dbg_cq_int8=dbg8, dbg_cq_scale=dbgs,
+        cache_mode=cache_mode,
+        B=lead[0] if len(lead) == 2 else None,
+        S=lead[1] if len(lead) == 2 else None)
+    if phase_events:
+        handles = (_vp * len(phase_events))(*[e.cuda_event for e in phase_events])
+        a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
+        a.n_phase_events = len(phase_events)
+    nbytes = mla_prolog_v2_workspace_size(a)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.mla_prolog_v2(ctypes.byref(a), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(),
+                             _stream(stream)), "mla_prolog_v2")
+    if return_cq_quant:
+        return query, query_rope, dbg8, dbgs
+    return query, query_rope
+
+
+# ---------------------------------------------------------------------------
+# QkvRmsNormRopeCache
+# ---------------------------------------------------------------------------
+
+def qkv_rmsnorm_rope_cache_args(qkv, gamma_q, gamma_k, cos, sin, index,
+                                k_cache, v_cache, q_out, *, Nq, Nk, Nv,
+                                quant_mode="symmetric", epsilon=1e-6,
+                                k_scale=None, v_scale=None, k_offset=None,
+                                v_offset=None, q_before_quant=None,
+                                k_before_quant=None, v_before_quant=None,
+                                B=None, S=None, cache_mode=None):
+    a = QkvRmsNormRopeCacheArgs()
+    a.struct_size = ctypes.sizeof(QkvRmsNormRopeCacheArgs)
+    a.quant_mode = QKV_QUANT[quant_mode] if isinstance(quant_mode, str) \
+        else int(quant_mode)
+    a.dtype = QKV_DTYPE.get(qkv.dtype, -1)
+    D = qkv.shape[-1] if qkv.dim() >= 1 else 0
+    T = index.numel()
+    if B is None:
+        B, S = T, 1
+    a.B, a.S = int(B), int(S)
+    a.Nq, a.Nk, a.Nv, a.D = int(Nq), int(Nk), int(Nv), int(D)
+    a.block_num, a.block_size = int(k_cache.shape[0]), int(k_cache.shape[1])
+    a.epsilon = float(epsilon)
+    a.cache_mode = cache_mode.encode() if cache_mode else None
+    if T > 0:
+        a.qkv, a.cos, a.sin, a.index = _ptr(qkv), _ptr(cos), _ptr(sin), \
+            _ptr(index)
+        a.q_out = _ptr(q_out)
+        a.q_before_quant = _ptr(q_before_quant)
+        a.k_before_quant = _ptr(k_before_quant)
+        a.v_before_quant = _ptr(v_before_quant)
+    a.gamma_q, a.gamma_k = _ptr(gamma_q), _ptr(gamma_k)
+    a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.k_offset, a.v_offset = _ptr(k_offset), _ptr(v_offset)
+    return a
+
+
+def qkv_rmsnorm_rope_cache(qkv, gamma_q, gamma_k, cos, sin, index, k_cache,
+                           v_cache, *, Nq, Nk, Nv, quant_mode="symmetric",
+                           epsilon=1e-6, k_scale=None, v_scale=None,
+                           k_offset=None, v_offset=None, q_out=None,
+                           before_quant=False, B=None, S=None,
+                           cache_mode=None, stream=None):
+    """Run QkvRmsNormRopeCache; k_cache and v_cache are updated in place.
+
+    qkv: (T, Nq+Nk+Nv, D) or (B, S, (Nq+Nk+Nv)*D).  Returns q_out (T, Nq, D),
+    plus (q_before_quant, k_before_quant, v_before_quant) when
+    before_quant is set.
+    """
+    lib = load_library()
+    T = index.numel()
+    D = qkv.shape[-1] if qkv.dim() == 3 and qkv.shape[1] == Nq + Nk + Nv \
+        else qkv.shape[-1] // (Nq + Nk + Nv)
+    dev = qkv.device
+    if q_out is None:
+        q_out = torch.empty((T, Nq, D), dtype=qkv.dtype, device=dev)
+    qb = kb = vb = None
+    if before_quant:
+        qb = torch.empty((T, Nq, D), dtype=qkv.dtype, device=dev)
+        kb = torch.empty((T, Nk, D), dtype=qkv.dtype, device=dev)
+        vb = torch.empty((T, Nv, D), dtype=qkv.dtype, device=dev)
+    qkv3 = qkv.reshape(T, Nq + Nk + Nv, D) if T else qkv
+    a = qkv_rmsnorm_rope_cache_args(
+        qkv3, gamma_q, gamma_k, cos, sin, index, k_cache, v_cache, q_out,
+        Nq=Nq, Nk=Nk, Nv=Nv, quant_mode=quant_mode, epsilon=epsilon,
+        k_scale=k_scale, v_scale=v_scale, k_offset=k_offset,
+        v_offset=v_offset, q_before_quant=qb, k_before_quant=kb,
+        v_before_quant=vb, B=B, S=S, cache_mode=cache_mode)
+    a.D = int(D)
+    _check(lib.qkv_rmsnorm_rope_cache(ctypes.byref(a), _stream(stream)),
+           "qkv_rmsnorm_rope_cache")
+    if before_quant:
+        return q_out, qb, kb, vb
+    return q_out

@@ -1,0 +1,993 @@
+// MlaPrologV2 on gfx950 ("MlaPrologV2" README, ops-transformer: function
+// description and formulas; parameter table; constraints incl. the
+// quantisation-scenario and dtype/shape tables).
+//
+//   A1  h = x . W^DQ, g = x . [W^DKV | W^KR]   one logical GEMM, N = Hcq+Hckv+Dr
+//   A2  c^Q = RmsNorm(h)                       (+ smooth, per-token int8 in the
+//                                               partial-quant scenarios)
+//   A3  c^KV = RmsNorm(g[:, :Hckv])  -> kv_cache[cache_index[t]]
+//   A4  k^R = RoPE(g[:, Hckv:])      -> kr_cache[cache_index[t]]
+//   A6  y = c^Q . [W^UQ | W^QR]                (int8 x int8 -> int32, dequant
+//                                               per token x per channel)
+//   A7  q^R = RoPE(y[:, N*D:])       -> query_rope; q^C = y[:, :N*D]
+//   A8  q^N[:, n] = q^C[:, n] . W^UK[n] -> query
+//
+// Two plans.  Decode-sized T (<= 128) streams every weight byte exactly once
+// through "skinny" kernels: each wave owns a 32-column slice of the packed
+// weight and a range of K, holds all T rows (up to four 32-row MFMA blocks)
+// in registers, and the down projection is split over K across workgroups
+// with fp32 partials reduced in a fixed order (deterministic, no atomics).
+// Larger T uses 128x128 LDS-tiled MFMA GEMMs.  Both share the epilogues.
+//
+// Weights arrive in the K16 blocked layout (see mla_pack_weight in the
+// public header): the 8 (bf16) or 16 (int8) consecutive-k values of one
+// column are one 16-byte chunk, which is exactly one lane's MFMA operand.
+#include "device_common.h"
+#include "launch.h"
+
+namespace qkvnr {
+
+namespace {
+
+enum AKind { A_BF16 = 0, A_I8 = 1, A_F32SPLIT = 2 };
+enum EpiKind { EPI_PARTIAL = 0, EPI_UQQR = 1, EPI_UK = 2 };
+
+struct GemmParams {
+  // A: activations, row-major; row m of batch z starts at A + z*a_bstride + m*lda
+  // (element units of the A type).
+  const void* A;
+  int64_t lda;
+  int64_t a_bstride;
+  // B: packed weights as 16-byte chunks; chunk (kc, n) at kc*N + n.  Tiles
+  // [0, ntiles0) read B0 (N0 columns), the rest read B1 (N1 columns, output
+  // columns offset by N0).  Batch z adds z*b_bstride chunks.
+  const uint4* B0;
+  int64_t N0;
+  const uint4* B1;
+  int64_t N1;
+  int64_t b_bstride;
+  int64_t M, K;
+  int ntiles0;
+  int64_t steps_per_split;  // k-steps handled per blockIdx.y
+  // EPI_PARTIAL: part[m][part_ld] of this launch's split (the skinny kernel
+  // offsets it by its split index)
+  float* part;
+  int64_t part_ld;
+  // EPI_UQQR
+  int64_t ND;  // N*D: first rope column
+  int Dr;
+  const uint16_t* cosb;  // (T, Dr)
+  const uint16_t* sinb;
+  const float* cq_scale;  // (T) per-token scale (int8 A)
+  const float* dq;        // per-column dequant (int8 A)
+  void* qc_out;           // (T, N*D): bf16, or fp32 when qc_f32
+  int qc_f32;
+  uint16_t* qr_out;  // (T, N, Dr)
+  int64_t qr_ld;     // N*Dr
+  // EPI_UK
+  uint16_t* q_out;  // (T, N, Hckv)
+  int64_t q_ld;     // N*Hckv
+  int64_t q_bstride;  // Hckv (per head)
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ i32x4_t as_i32x4(uint4 v) { return __builtin_bit_cast(i32x4_t, v); }
+
+// Split 8 fp32 values into bf16 hi + bf16 lo (hi + lo carries ~16 bits).
+__device__ __forceinline__ void split8(const float4 a, const float4 b, uint4& hi, uint4& lo) {
+  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = f32_to_bf16(f[2 * i]), h1 = f32_to_bf16(f[2 * i + 1]);
+    const float r0 = f[2 * i] - bf16_to_f32(h0), r1 = f[2 * i + 1] - bf16_to_f32(h1);
+    h[i] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+    l[i] = pack_bf16x2(r0, r1);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+template <int AK>
+struct AccT {
+  typedef f32x16_t type;
+};
+template <>
+struct AccT<A_I8> {
+  typedef i32x16_t type;
+};
+
+// acc += A(16B/lane) x B(16B/lane) for one MFMA k-step.
+template <int AK>
+__device__ __forceinline__ void mfma_step(typename AccT<AK>::type& acc, uint4 a, uint4 b) {
+  if constexpr (AK == A_I8) {
+    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_i32x4(a), as_i32x4(b), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue over 8 consecutive output columns of one row.  `v` are the raw
+// accumulator sums (int32 bit patterns for int8 A), `vp` the same for the
+// RoPE partner columns (col +/- Dr/2) when the columns are rope columns.
+// ---------------------------------------------------------------------------
+template <int AK, int EPI>
+struct Epilogue {
+  static __device__ __forceinline__ void to_float(const uint32_t* raw, float* v) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = (AK == A_I8) ? static_cast<float>(static_cast<int>(raw[e])) : __uint_as_float(raw[e]);
+  }
+
+  // Does this 8-column group need its RoPE partner, and where is it (offset
+  // in columns relative to the group)?
+  static __device__ __forceinline__ int partner_offset(const GemmParams& p, int64_t gcol) {
+    if (EPI != EPI_UQQR || gcol < p.ND) return 0;
+    const int i0 = static_cast<int>((gcol - p.ND) % p.Dr);
+    const int half = p.Dr >> 1;
+    return i0 < half ? half : -half;
+  }
+
+  static __device__ __forceinline__ void dequant(const GemmParams& p, int64_t m, int64_t gcol,
+                                                 float* v) {
+    if constexpr (AK == A_I8) {
+      const float s = p.cq_scale[m];
+      const float4 d0 = *reinterpret_cast<const float4*>(p.dq + gcol);
+      const float4 d1 = *reinterpret_cast<const float4*>(p.dq + gcol + 4);
+      const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * s * d[e];
+    }
+  }
+
+  // m: token row; gcol: column within this weight; ocol: output column in
+  // the partial buffer (gcol + offset of B1); z: batch (head) index.
+  static __device__ __forceinline__ void apply(const GemmParams& p, int64_t m, int64_t gcol,
+                                               int64_t ocol, int z, const uint32_t* raw,
+                                               const uint32_t* raw_partner) {
+    float v[8];
+    to_float(raw, v);
+    if constexpr (EPI == EPI_PARTIAL) {
+      float* dst = p.part + m * p.part_ld + ocol;
+      reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+      reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else if constexpr (EPI == EPI_UK) {
+      uint16_t* dst = p.q_out + m * p.q_ld + static_cast<int64_t>(z) * p.q_bstride + gcol;
+      st16(dst, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+    } else {  // EPI_UQQR
+      dequant(p, m, gcol, v);
+      if (gcol < p.ND) {
+        if (p.qc_f32) {
+          float* dst = static_cast<float*>(p.qc_out) + m * p.ND + gcol;
+          reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.qc_out) + m * p.ND + gcol;
+          st16(dst, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+        }
+      } else {
+        const int64_t r = gcol - p.ND;
+        const int64_t head = r / p.Dr;
+        const int i0 = static_cast<int>(r % p.Dr);
+        const int half = p.Dr >> 1;
+        const int64_t pcol = i0 < half ? gcol + half : gcol - half;
+        float w[8];
+        to_float(raw_partner, w);
+        dequant(p, m, pcol, w);
+        const uint4 c4 = ld16(p.cosb + m * p.Dr + i0);
+        const uint4 s4 = ld16(p.sinb + m * p.Dr + i0);
+        const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
+        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float c = (e & 1) ? bf16hi(cw[e >> 1]) : bf16lo(cw[e >> 1]);
+          const float s = (e & 1) ? bf16hi(sw[e >> 1]) : bf16lo(sw[e >> 1]);
+          // cat(-y2, y1) * sin: first half subtracts the partner
+          o[e] = i0 < half ? v[e] * c - w[e] * s : v[e] * c + w[e] * s;
+        }
+        uint16_t* out = p.qr_out + m * p.qr_ld + head * p.Dr + i0;
+        st16(out, make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                             pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])));
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Skinny GEMM: all M (<= 32*MB) rows per wave, NW waves across N (32 columns
+// each), KW waves across K; the KW partial tiles are summed in LDS in wave
+// order, then the epilogue runs on 8-column groups.
+// ---------------------------------------------------------------------------
+template <int AK, int MB, int NW, int KW, int EPI>
+__global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
+  typedef typename AccT<AK>::type Acc;
+  constexpr int KSTEP = (AK == A_I8) ? 32 : 16;  // k per MFMA
+  constexpr int TN = 32 * NW;
+  constexpr int PITCH = TN + 4;  // words per LDS row
+  constexpr int U = 8;           // k-steps in flight per wave
+  __shared__ uint32_t lds[KW][MB * 32][PITCH];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = wave % NW;
+  const int kw = wave / NW;
+  const int g = lane >> 5;
+  const int li = lane & 31;
+  const int z = blockIdx.z;
+
+  const uint4* B;
+  int64_t N, n0, ocol0;
+  if (static_cast<int>(blockIdx.x) < p.ntiles0) {
+    B = p.B0;
+    N = p.N0;
+    n0 = static_cast<int64_t>(blockIdx.x) * TN;
+    ocol0 = 0;
+  } else {
+    B = p.B1;
+    N = p.N1;
+    n0 = static_cast<int64_t>(blockIdx.x - p.ntiles0) * TN;
+    ocol0 = p.N0;
+  }
+  B += static_cast<int64_t>(z) * p.b_bstride;
+
+  const int64_t nsteps = p.K / KSTEP;
+  const int64_t s_lo = static_cast<int64_t>(blockIdx.y) * p.steps_per_split;
+  const int64_t s_hi = min(s_lo + p.steps_per_split, nsteps);
+  const int64_t cnt = s_hi > s_lo ? s_hi - s_lo : 0;
+  const int64_t w_lo = s_lo + cnt * kw / KW;
+  const int64_t w_hi = s_lo + cnt * (kw + 1) / KW;
+
+  const int64_t n = n0 + nw * 32 + li;
+  const bool n_ok = n < N;
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+
+  // A row pointers (byte addressing), one per m-block
+  const char* Abase = static_cast<const char*>(p.A);
+  constexpr int AEB = (AK == A_I8) ? 1 : (AK == A_F32SPLIT ? 4 : 2);  // A element bytes
+  const int64_t a_row_bytes = p.lda * AEB;
+  const char* arow[MB];
+  bool m_ok[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t m = mb * 32 + li;
+    m_ok[mb] = m < p.M;
+    arow[mb] = Abase + (static_cast<int64_t>(z) * p.a_bstride) * AEB + m * a_row_bytes;
+  }
+
+  Acc acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = Acc{};
+
+  auto a_frag = [&](int mb, int64_t s, uint4& hi, uint4& lo) {
+    if constexpr (AK == A_F32SPLIT) {
+      const float* src = reinterpret_cast<const float*>(arow[mb]) + s * 16 + 8 * g;
+      float4 f0 = make_float4(0.f, 0.f, 0.f, 0.f), f1 = f0;
+      if (m_ok[mb]) {
+        f0 = reinterpret_cast<const float4*>(src)[0];
+        f1 = reinterpret_cast<const float4*>(src)[1];
+      }
+      split8(f0, f1, hi, lo);
+    } else {
+      // bf16: 16 k = 32 bytes per step, lane group g takes bytes [16g, 16g+16)
+      // int8: 32 k = 32 bytes per step, same byte offsets
+      hi = m_ok[mb] ? ld16(arow[mb] + s * 32 + 16 * g) : zero4;
+      lo = zero4;
+    }
+  };
+
+  int64_t s = w_lo;
+  for (; s + U <= w_hi; s += U) {
+    uint4 bfr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) bfr[u] = n_ok ? B[(2 * (s + u) + g) * N + n] : zero4;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint4 ah, al;
+        a_frag(mb, s + u, ah, al);
+        mfma_step<AK>(acc[mb], ah, bfr[u]);
+        if constexpr (AK == A_F32SPLIT) mfma_step<AK>(acc[mb], al, bfr[u]);
+      }
+    }
+  }
+  for (; s < w_hi; ++s) {
+    const uint4 b = n_ok ? B[(2 * s + g) * N + n] : zero4;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      uint4 ah, al;
+      a_frag(mb, s, ah, al);
+      mfma_step<AK>(acc[mb], ah, b);
+      if constexpr (AK == A_F32SPLIT) mfma_step<AK>(acc[mb], al, b);
+    }
+  }
+
+  // Stage: 32x32 MFMA output, lane l / register r -> row 8*(r/4) + 4*(l/32)
+  // + r%4, column l%32.
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      uint32_t bits;
+      if constexpr (AK == A_I8)
+        bits = static_cast<uint32_t>(acc[mb][r]);
+      else
+        bits = __float_as_uint(acc[mb][r]);
+      lds[kw][row][nw * 32 + li] = bits;
+    }
+  }
+  __syncthreads();
+
+  // Epilogue: 8-column groups of the (MB*32) x TN tile.
+  GemmParams pe = p;
+  if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(blockIdx.y) * p.M * p.part_ld;
+  constexpr int GROUPS = MB * 32 * (TN / 8);
+  for (int it = threadIdx.x; it < GROUPS; it += 64 * NW * KW) {
+    const int row = it / (TN / 8);
+    const int c0 = (it % (TN / 8)) * 8;
+    const int64_t m = row;
+    const int64_t gcol = n0 + c0;
+    if (m >= p.M || gcol >= N) continue;
+    uint32_t raw[8], rawp[8];
+    const int poff = Epilogue<AK, EPI>::partner_offset(p, gcol);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (AK == A_I8) {
+        int si = 0, sp = 0;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          si += static_cast<int>(lds[k][row][c0 + e]);
+          if (poff) sp += static_cast<int>(lds[k][row][c0 + poff + e]);
+        }
+        raw[e] = static_cast<uint32_t>(si);
+        rawp[e] = static_cast<uint32_t>(sp);
+      } else {
+        float sf = 0.f, spf = 0.f;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          sf += __uint_as_float(lds[k][row][c0 + e]);
+          if (poff) spf += __uint_as_float(lds[k][row][c0 + poff + e]);
+        }
+        raw[e] = __float_as_uint(sf);
+        rawp[e] = __float_as_uint(spf);
+      }
+    }
+    Epilogue<AK, EPI>::apply(pe, m, gcol, ocol0 + gcol, z, raw, rawp);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled GEMM for large M: 128x128 output tile per 256-thread workgroup, 4
+// waves as 2x2 of 64x64 (2x2 MFMA 32x32 blocks each).  A stage holds 64 bytes
+// of K per row (32 bf16 / 64 int8 = two MFMA k-steps); stages are double
+// buffered in LDS with one barrier per stage.  The epilogue stages each wave's
+// 64x64 fp32 tile through LDS so every lane stores 8 consecutive columns.
+// ---------------------------------------------------------------------------
+constexpr int TBM = 128, TBN = 128;
+constexpr int A_PITCH = 80;  // bytes per A row in LDS (64 + 16 pad)
+constexpr int A_STAGE = TBM * A_PITCH;          // 10240
+constexpr int B_STAGE = 4 * TBN * 16;            // 8192
+constexpr int EPI_PITCH = 68;                    // words per staged row
+constexpr int EPI_WAVE = 64 * EPI_PITCH * 4;     // 17408 bytes per wave
+constexpr int TILED_LDS = 4 * EPI_WAVE;          // 69632 >= 2*(2*A_STAGE+B_STAGE)
+
+template <int AK, int EPI>
+__global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
+  typedef typename AccT<AK>::type Acc;
+  constexpr bool SPLIT = AK == A_F32SPLIT;
+  constexpr int NA = SPLIT ? 2 : 1;  // A tiles per stage (hi, lo)
+  constexpr int STAGE = NA * A_STAGE + B_STAGE;
+  static_assert(2 * STAGE <= TILED_LDS, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[TILED_LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5;
+  const int li = lane & 31;
+  const int z = blockIdx.z;
+
+  const uint4* B;
+  int64_t N, n0, ocol0;
+  if (static_cast<int>(blockIdx.x) < p.ntiles0) {
+    B = p.B0;
+    N = p.N0;
+    n0 = static_cast<int64_t>(blockIdx.x) * TBN;
+    ocol0 = 0;
+  } else {
+    B = p.B1;
+    N = p.N1;
+    n0 = static_cast<int64_t>(blockIdx.x - p.ntiles0) * TBN;
+    ocol0 = p.N0;
+  }
+  B += static_cast<int64_t>(z) * p.b_bstride;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * TBM;
+
+  constexpr int AEB = (AK == A_I8) ? 1 : (SPLIT ? 4 : 2);
+  const char* Abase = static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_bstride * AEB;
+  const int64_t a_row_bytes = p.lda * AEB;
+  constexpr int KPS = (AK == A_I8) ? 64 : 32;  // k per stage
+  const int64_t nstages = p.K / KPS;
+
+  // Global -> register loads of one stage.  A: 128 rows x 64 B (bf16/int8)
+  // = 512 chunks of 16 B, 2 per thread; fp32 A: 128 rows x 128 B, 4 per
+  // thread.  B: 4 chunk-rows x 128 columns, 2 per thread.
+  constexpr int ACH = SPLIT ? 4 : 2;
+  uint4 ra[ACH], rb[2];
+  const uint4 zero4 = make_uint4(0, 0, 0, 0);
+  auto gload = [&](int64_t st) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = SPLIT ? (c >> 3) : (c >> 2);
+      const int q = SPLIT ? (c & 7) : (c & 3);
+      const int64_t m = m0 + row;
+      const char* src = Abase + m * a_row_bytes + st * (SPLIT ? 128 : 64) + 16 * q;
+      ra[i] = m < p.M ? ld16(src) : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int kc = c >> 7;
+      const int col = c & 127;
+      const int64_t n = n0 + col;
+      rb[i] = n < N ? B[(st * 4 + kc) * N + n] : zero4;
+    }
+  };
+  auto swrite = [&](int buf) {
+    char* sa = smem + buf * STAGE;
+    char* sb = sa + NA * A_STAGE;
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c >> 3;
+        const int q = c & 7;  // 4 fp32 = k [4q, 4q+4)
+        const float f[4] = {__uint_as_float(ra[i].x), __uint_as_float(ra[i].y),
+                            __uint_as_float(ra[i].z), __uint_as_float(ra[i].w)};
+        uint16_t h[4];
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = f32_to_bf16(f[e]);
+          r[e] = f[e] - bf16_to_f32(h[e]);
+        }
+        uint2 hv = make_uint2(static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16),
+                              static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16));
+        uint2 lv = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+        *reinterpret_cast<uint2*>(sa + row * A_PITCH + 8 * q) = hv;
+        *reinterpret_cast<uint2*>(sa + A_STAGE + row * A_PITCH + 8 * q) = lv;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < ACH; ++i) {
+        const int c = tid + 256 * i;
+        *reinterpret_cast<uint4*>(sa + (c >> 2) * A_PITCH + 16 * (c & 3)) = ra[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<uint4*>(sb + 16 * c) = rb[i];
+    }
+  };
+
+  Acc acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = Acc{};
+
+  if (nstages > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int64_t st = 0; st < nstages; ++st) {
+    const int buf = static_cast<int>(st & 1);
+    if (st + 1 < nstages) gload(st + 1);
+    const char* sa = smem + buf * STAGE;
+    const char* sb = sa + NA * A_STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 af[2], afl[2], bfr[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wm * 64 + mb * 32 + li;
+        af[mb] = *reinterpret_cast<const uint4*>(sa + row * A_PITCH + ks * 32 + 16 * g);
+        if constexpr (SPLIT)
+          afl[mb] = *reinterpret_cast<const uint4*>(sa + A_STAGE + row * A_PITCH + ks * 32 + 16 * g);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = wn * 64 + nb * 32 + li;
+        bfr[nb] = *reinterpret_cast<const uint4*>(sb + ((ks * 2 + g) * TBN + col) * 16);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          mfma_step<AK>(acc[mb][nb], af[mb], bfr[nb]);
+          if constexpr (SPLIT) mfma_step<AK>(acc[mb][nb], afl[mb], bfr[nb]);
+        }
+    }
+    if (st + 1 < nstages) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue staging: this wave's 64x64 tile in its own LDS slice.
+  uint32_t* ew = reinterpret_cast<uint32_t*>(smem + wave * EPI_WAVE);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int col = nb * 32 + li;
+        uint32_t bits;
+        if constexpr (AK == A_I8)
+          bits = static_cast<uint32_t>(acc[mb][nb][r]);
+        else
+          bits = __float_as_uint(acc[mb][nb][r]);
+        ew[row * EPI_PITCH + col] = bits;
+      }
+  __syncthreads();
+
+  for (int it = lane; it < 64 * 8; it += 64) {
+    const int row = it >> 3;
+    const int c0 = (it & 7) * 8;
+    const int64_t m = m0 + wm * 64 + row;
+    const int64_t gcol = n0 + wn * 64 + c0;
+    if (m >= p.M || gcol >= N) continue;
+    uint32_t raw[8], rawp[8];
+    const int poff = Epilogue<AK, EPI>::partner_offset(p, gcol);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      raw[e] = ew[row * EPI_PITCH + c0 + e];
+      rawp[e] = poff ? ew[row * EPI_PITCH + c0 + poff + e] : 0u;
+    }
+    Epilogue<AK, EPI>::apply(p, m, gcol, ocol0 + gcol, z, raw, rawp);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down-projection finish: one workgroup per token.  Sums the split-K
+// partials in split order, RmsNorms c^Q (and quantises it per token in the
+// partial-quant scenarios), RmsNorms c^KV, rotates k^R and writes both cache
+// rows at the token's slot.
+// ---------------------------------------------------------------------------
+struct FinishParams {
+  const float* part;
+  int ksplit;
+  int64_t T;
+  int Hcq, Hckv, Dr;
+  float eps_cq, eps_ckv;
+  const uint16_t* gamma_cq;
+  const uint16_t* gamma_ckv;
+  const float* smooth;
+  const float* qs_ckv;
+  const float* qs_ckr;
+  const uint16_t* cosb;
+  const uint16_t* sinb;
+  const int64_t* index;
+  int64_t slots;
+  void* kv_cache;
+  void* kr_cache;
+  uint16_t* cq_bf16;
+  int8_t* cq_i8;
+  float* cq_scale;
+  int8_t* dbg_cq_i8;
+  float* dbg_cq_scale;
+};
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = group_sum<64>(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  v = group_max<64>(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// QM: 0 none, 1 partial with bf16 caches, 2 partial with int8 caches.
+template <int QM>
+__global__ __launch_bounds__(256) void k_down_finish(FinishParams p) {
+  extern __shared__ float row[];  // Hcq + Hckv + Dr
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ntot = p.Hcq + p.Hckv + p.Dr;
+
+  for (int c = tid; c < ntot; c += 256) {
+    float v = 0.f;
+    for (int s = 0; s < p.ksplit; ++s) v += p.part[(static_cast<int64_t>(s) * p.T + t) * ntot + c];
+    row[c] = v;
+  }
+  __syncthreads();
+
+  float sq = 0.f, skv = 0.f;
+  for (int c = tid; c < p.Hcq; c += 256) sq += row[c] * row[c];
+  for (int c = tid; c < p.Hckv; c += 256) skv += row[p.Hcq + c] * row[p.Hcq + c];
+  sq = block_sum256(sq, red);
+  skv = block_sum256(skv, red);
+  const float rq = 1.0f / __builtin_sqrtf(sq / static_cast<float>(p.Hcq) + p.eps_cq);
+  const float rkv = 1.0f / __builtin_sqrtf(skv / static_cast<float>(p.Hckv) + p.eps_ckv);
+
+  // c^Q
+  if (QM == 0) {
+    for (int c = tid; c < p.Hcq; c += 256)
+      p.cq_bf16[t * p.Hcq + c] = f32_to_bf16(row[c] * rq * bf16_to_f32(p.gamma_cq[c]));
+  } else {
+    float amax = 0.f;
+    for (int c = tid; c < p.Hcq; c += 256) {
+      const float u = row[c] * rq * bf16_to_f32(p.gamma_cq[c]) * p.smooth[c];
+      row[c] = u;
+      amax = fmaxf(amax, fabsf(u));
+    }
+    amax = block_max256(amax, red);
+    const float s = amax / 127.0f;
+    for (int c = tid; c < p.Hcq; c += 256) {
+      const int code = s > 0.f ? sat_rne(row[c] / s, -127, 127) : 0;
+      p.cq_i8[t * p.Hcq + c] = static_cast<int8_t>(code);
+      if (p.dbg_cq_i8) p.dbg_cq_i8[t * p.Hcq + c] = static_cast<int8_t>(code);
+    }
+    if (tid == 0) {
+      p.cq_scale[t] = s;
+      if (p.dbg_cq_scale) p.dbg_cq_scale[t] = s;
+    }
+  }
+
+  const int64_t slot = p.index[t];
+  if (slot < 0 || slot >= p.slots) return;
+  // c^KV row
+  for (int c = tid; c < p.Hckv; c += 256) {
+    const float v = row[p.Hcq + c] * rkv * bf16_to_f32(p.gamma_ckv[c]);
+    if (QM == 2)
+      static_cast<int8_t*>(p.kv_cache)[slot * p.Hckv + c] =
+          static_cast<int8_t>(sat_rne(v / p.qs_ckv[c], -128, 127));
+    else
+      static_cast<uint16_t*>(p.kv_cache)[slot * p.Hckv + c] = f32_to_bf16(v);
+  }
+  // k^R row: half-and-half RoPE with the token's (cos, sin)
+  const int half = p.Dr >> 1;
+  const float* kr = row + p.Hcq + p.Hckv;
+  for (int i = tid; i < p.Dr; i += 256) {
+    const float c = bf16_to_f32(p.cosb[t * p.Dr + i]);
+    const float s = bf16_to_f32(p.sinb[t * p.Dr + i]);
+    const float o = i < half ? kr[i] * c - kr[i + half] * s : kr[i] * c + kr[i - half] * s;
+    if (QM == 2)
+      static_cast<int8_t*>(p.kr_cache)[slot * p.Dr + i] =
+          static_cast<int8_t>(sat_rne(o / p.qs_ckr[i], -128, 127));
+    else
+      static_cast<uint16_t*>(p.kr_cache)[slot * p.Dr + i] = f32_to_bf16(o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing: one thread per 16-byte output chunk.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint4* __restrict__ dst,
+                                              int64_t batch, int64_t K, int64_t N, int eb) {
+  const int G = 16 / eb;
+  const int64_t kc_n = (K / G) * N;
+  const int64_t total = batch * kc_n;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t b = c / kc_n;
+    const int64_t r = c % kc_n;
+    const int64_t kc = r / N;
+    const int64_t n = r % N;
+    const char* s = src + ((b * K + kc * G) * N + n) * eb;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (eb == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t v = *reinterpret_cast<const uint16_t*>(s + static_cast<int64_t>(e) * N * 2);
+        w[e >> 1] |= v << (16 * (e & 1));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t v = static_cast<uint8_t>(s[static_cast<int64_t>(e) * N]);
+        w[e >> 2] |= v << (8 * (e & 3));
+      }
+    }
+    dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+template <int AK, int MB, int NW, int KW, int EPI>
+void skinny(const GemmParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_skinny<AK, MB, NW, KW, EPI>), grid, dim3(64 * NW * KW), 0, st, p);
+}
+
+
+template <int AK, int EPI>
+void tiled(const GemmParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_tiled<AK, EPI>), grid, dim3(256), 0, st, p);
+}
+
+// Decode plan: three weight-streaming launches plus the down-projection
+// finish (launched by the caller between A1 and A6).
+template <int MB>
+void skinny_a1(const GemmParams& g1, const MlaPlan& pl, hipStream_t st) {
+  const unsigned nt = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + 63) / 64);
+  skinny<A_BF16, MB, 2, 2, EPI_PARTIAL>(g1, dim3(nt, pl.ksplit, 1), st);
+}
+template <int MB>
+void skinny_a6(const GemmParams& g6, bool quant, hipStream_t st) {
+  const unsigned nt = static_cast<unsigned>((g6.N0 + 63) / 64);
+  if (quant)
+    skinny<A_I8, MB, 2, 2, EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+  else
+    skinny<A_BF16, MB, 2, 2, EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+}
+template <int MB>
+void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
+  const unsigned nt = static_cast<unsigned>((g8.N0 + 127) / 128);
+  if (quant)
+    skinny<A_F32SPLIT, MB, 4, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
+  else
+    skinny<A_BF16, MB, 4, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
+}
+
+}  // namespace
+
+int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
+                       int elem_bytes, hipStream_t stream) {
+  const int G = 16 / elem_bytes;
+  const int64_t total = batch * (K / G) * N;
+  if (total == 0) return QKVNR_OK;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_pack, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const char*>(src), static_cast<uint4*>(dst), batch, K, N,
+                     elem_bytes);
+  return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;
+}
+
+MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
+  MlaPlan pl{};
+  const int64_t T = a->B * a->S;
+  const bool quant = a->quant_mode != MLA_QUANT_NONE;
+  const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
+  pl.skinny = T <= 128;
+  pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
+  const int64_t steps = a->He / 16;
+  if (pl.skinny) {
+    // Spread the down projection's weight stream over ~3 workgroups per CU:
+    // split K so that (column tiles x splits) is about 768 workgroups, with
+    // each split a multiple of 16 k-steps (2 waves x 8 steps in flight).
+    const int64_t ntiles = (a->Hcq + 63) / 64 + (a->Hckv + a->Dr + 63) / 64;
+    int64_t want = 768 / (ntiles > 0 ? ntiles : 1);
+    if (want < 1) want = 1;
+    int64_t sps = (steps + want - 1) / want;
+    sps = ((sps + 15) / 16) * 16;
+    if (sps < 16) sps = 16;
+    pl.steps_per_split = sps;
+    pl.ksplit = static_cast<int>((steps + sps - 1) / sps);
+  } else {
+    pl.steps_per_split = steps;
+    pl.ksplit = 1;
+  }
+  size_t off = 0;
+  if (a->weight_layout == MLA_WEIGHT_ND) {
+    const size_t eb_uq = quant ? 1 : 2;
+    pl.off_wdq = off;
+    off += align256(static_cast<size_t>(a->He * a->Hcq) * 2);
+    pl.off_wdkvkr = off;
+    off += align256(static_cast<size_t>(a->He * (a->Hckv + a->Dr)) * 2);
+    pl.off_wuqqr = off;
+    off += align256(static_cast<size_t>(a->Hcq * a->N * (a->D + a->Dr)) * eb_uq);
+    pl.off_wuk = off;
+    off += align256(static_cast<size_t>(a->N * a->D * a->Hckv) * 2);
+  }
+  pl.off_part = off;
+  off += align256(static_cast<size_t>(pl.ksplit) * T * ntot * 4);
+  pl.off_cq = off;
+  off += align256(static_cast<size_t>(T * a->Hcq) * (quant ? 1 : 2));
+  pl.off_cq_scale = off;
+  off += align256(static_cast<size_t>(T) * 4);
+  pl.off_qc = off;
+  off += align256(static_cast<size_t>(T * a->N * a->D) * (quant ? 4 : 2));
+  pl.total = T > 0 ? off : 0;
+  return pl;
+}
+
+int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* workspace,
+                         hipStream_t st) {
+  const int64_t T = a->B * a->S;
+  if (T == 0) return QKVNR_OK;
+  const bool quant = a->quant_mode != MLA_QUANT_NONE;
+  const int qm = a->quant_mode;  // 0, 1, 2
+  char* ws = static_cast<char*>(workspace);
+  const int64_t NDR = a->N * (a->D + a->Dr);
+  const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
+
+  const uint4 *wdq, *wdkvkr, *wuqqr, *wuk;
+  if (a->weight_layout == MLA_WEIGHT_ND) {
+    int rc = launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, 2, st);
+    if (rc == QKVNR_OK)
+      rc = launch_pack_weight(a->weight_dkv_kr, ws + pl.off_wdkvkr, 1, a->He, a->Hckv + a->Dr, 2,
+                              st);
+    if (rc == QKVNR_OK)
+      rc = launch_pack_weight(a->weight_uq_qr, ws + pl.off_wuqqr, 1, a->Hcq, NDR, quant ? 1 : 2,
+                              st);
+    if (rc == QKVNR_OK)
+      rc = launch_pack_weight(a->weight_uk, ws + pl.off_wuk, a->N, a->D, a->Hckv, 2, st);
+    if (rc != QKVNR_OK) return rc;
+    wdq = reinterpret_cast<const uint4*>(ws + pl.off_wdq);
+    wdkvkr = reinterpret_cast<const uint4*>(ws + pl.off_wdkvkr);
+    wuqqr = reinterpret_cast<const uint4*>(ws + pl.off_wuqqr);
+    wuk = reinterpret_cast<const uint4*>(ws + pl.off_wuk);
+  } else {
+    wdq = static_cast<const uint4*>(a->weight_dq);
+    wdkvkr = static_cast<const uint4*>(a->weight_dkv_kr);
+    wuqqr = static_cast<const uint4*>(a->weight_uq_qr);
+    wuk = static_cast<const uint4*>(a->weight_uk);
+  }
+  float* part = reinterpret_cast<float*>(ws + pl.off_part);
+  void* cq = ws + pl.off_cq;
+  float* cq_scale = reinterpret_cast<float*>(ws + pl.off_cq_scale);
+  void* qc = ws + pl.off_qc;
+
+  // ---- A1: x . [W^DQ | W^DKV_KR] -> fp32 (partials) ----
+  GemmParams g1{};
+  g1.A = a->token_x;
+  g1.lda = a->He;
+  g1.B0 = wdq;
+  g1.N0 = a->Hcq;
+  g1.B1 = wdkvkr;
+  g1.N1 = a->Hckv + a->Dr;
+  g1.M = T;
+  g1.K = a->He;
+  g1.steps_per_split = pl.steps_per_split;
+  g1.part = part;
+  g1.part_ld = ntot;
+
+  // ---- A6: c^Q . [W^UQ | W^QR] -> q^C (workspace) and RoPE'd q^R ----
+  GemmParams g6{};
+  g6.A = cq;
+  g6.lda = a->Hcq;
+  g6.B0 = wuqqr;
+  g6.N0 = NDR;
+  g6.M = T;
+  g6.K = a->Hcq;
+  g6.ntiles0 = 1 << 30;  // every tile reads B0
+  g6.steps_per_split = a->Hcq / (quant ? 32 : 16);
+  g6.ND = a->N * a->D;
+  g6.Dr = static_cast<int>(a->Dr);
+  g6.cosb = static_cast<const uint16_t*>(a->rope_cos);
+  g6.sinb = static_cast<const uint16_t*>(a->rope_sin);
+  g6.cq_scale = cq_scale;
+  g6.dq = a->dequant_scale_w_uq_qr;
+  g6.qc_out = qc;
+  g6.qc_f32 = quant ? 1 : 0;
+  g6.qr_out = static_cast<uint16_t*>(a->query_rope);
+  g6.qr_ld = a->N * a->Dr;
+
+  // ---- A8: per head q^C[:, n] . W^UK[n] -> query ----
+  GemmParams g8{};
+  g8.A = qc;
+  g8.lda = a->N * a->D;
+  g8.a_bstride = a->D;
+  g8.B0 = wuk;
+  g8.N0 = a->Hckv;
+  g8.b_bstride = (a->D / 8) * a->Hckv;
+  g8.M = T;
+  g8.K = a->D;
+  g8.ntiles0 = 1 << 30;
+  g8.steps_per_split = a->D / 16;
+  g8.q_out = static_cast<uint16_t*>(a->query);
+  g8.q_ld = a->N * a->Hckv;
+  g8.q_bstride = a->Hckv;
+
+  // ---- finish of A1 ----
+  FinishParams f{};
+  f.part = part;
+  f.ksplit = pl.ksplit;
+  f.T = T;
+  f.Hcq = static_cast<int>(a->Hcq);
+  f.Hckv = static_cast<int>(a->Hckv);
+  f.Dr = static_cast<int>(a->Dr);
+  f.eps_cq = static_cast<float>(a->rmsnorm_epsilon_cq);
+  f.eps_ckv = static_cast<float>(a->rmsnorm_epsilon_ckv);
+  f.gamma_cq = static_cast<const uint16_t*>(a->rmsnorm_gamma_cq);
+  f.gamma_ckv = static_cast<const uint16_t*>(a->rmsnorm_gamma_ckv);
+  f.smooth = a->smooth_scales_cq;
+  f.qs_ckv = a->quant_scale_ckv;
+  f.qs_ckr = a->quant_scale_ckr;
+  f.cosb = static_cast<const uint16_t*>(a->rope_cos);
+  f.sinb = static_cast<const uint16_t*>(a->rope_sin);
+  f.index = a->cache_index;
+  f.slots = a->block_num * a->block_size;
+  f.kv_cache = a->kv_cache;
+  f.kr_cache = a->kr_cache;
+  f.cq_bf16 = static_cast<uint16_t*>(cq);
+  f.cq_i8 = static_cast<int8_t*>(cq);
+  f.cq_scale = cq_scale;
+  f.dbg_cq_i8 = a->dbg_cq_int8;
+  f.dbg_cq_scale = a->dbg_cq_scale;
+  const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
+
+  // Phase events (instrumentation only).
+  auto mark = [&](int i) {
+    if (i < a->n_phase_events && a->phase_events[i] != nullptr)
+      hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st);
+  };
+
+  auto finish = [&]() {
+    const dim3 grid(static_cast<unsigned>(T));
+    if (qm == 0)
+      hipLaunchKernelGGL(k_down_finish<0>, grid, dim3(256), fin_smem, st, f);
+    else if (qm == 1)
+      hipLaunchKernelGGL(k_down_finish<1>, grid, dim3(256), fin_smem, st, f);
+    else
+      hipLaunchKernelGGL(k_down_finish<2>, grid, dim3(256), fin_smem, st, f);
+  };
+
+  const int nh = static_cast<int>(a->N);
+  mark(MLA_PHASE_START);
+  if (pl.skinny) {
+    g1.ntiles0 = static_cast<int>((g1.N0 + 63) / 64);
+    switch (pl.mb) {
+      case 1: skinny_a1<1>(g1, pl, st); break;
+      case 2: skinny_a1<2>(g1, pl, st); break;
+      default: skinny_a1<4>(g1, pl, st); break;
+    }
+    mark(MLA_PHASE_AFTER_DOWN);
+    finish();
+    mark(MLA_PHASE_AFTER_NORM);
+    switch (pl.mb) {
+      case 1: skinny_a6<1>(g6, quant, st); break;
+      case 2: skinny_a6<2>(g6, quant, st); break;
+      default: skinny_a6<4>(g6, quant, st); break;
+    }
+    mark(MLA_PHASE_AFTER_UQQR);
+    switch (pl.mb) {
+      case 1: skinny_a8<1>(g8, nh, quant, st); break;
+      case 2: skinny_a8<2>(g8, nh, quant, st); break;
+      default: skinny_a8<4>(g8, nh, quant, st); break;
+    }
+  } else {
+    const unsigned mt = static_cast<unsigned>((T + TBM - 1) / TBM);
+    g1.ntiles0 = static_cast<int>((g1.N0 + TBN - 1) / TBN);
+    const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + TBN - 1) / TBN);
+    tiled<A_BF16, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), st);
+    mark(MLA_PHASE_AFTER_DOWN);
+    finish();
+    mark(MLA_PHASE_AFTER_NORM);
+    const unsigned nt6 = static_cast<unsigned>((g6.N0 + TBN - 1) / TBN);
+    if (quant)
+      tiled<A_I8, EPI_UQQR>(g6, dim3(nt6, mt, 1), st);
+    else
+      tiled<A_BF16, EPI_UQQR>(g6, dim3(nt6, mt, 1), st);
+    mark(MLA_PHASE_AFTER_UQQR);
+    const unsigned nt8 = static_cast<unsigned>((g8.N0 + TBN - 1) / TBN);
+    if (quant)
+      tiled<A_F32SPLIT, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), st);
+    else
+      tiled<A_BF16, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), st);
+  }
+  mark(MLA_PHASE_AFTER_UK);
+  return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;
+}
+
+}  // namespace qkvnr

@@ -1,0 +1,256 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every function
+the public header declares, and its host-side validation returns the
+documented status codes.  No kernel runs here (there is no GPU): every call
+either is a pure validation entry point or fails validation / is empty before
+any HIP call.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import qkv_norm_rope_amd as qn
+from qkv_norm_rope_amd import _binding as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include",
+                      "qkvnr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(b.LIB_PATH),
+                                reason="libqkvnr.so not built")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(b.EXPORTS) == header_functions()
+
+
+def test_library_exports_every_header_symbol():
+    lib = ctypes.CDLL(b.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert qn.version() == "0.1.0"
+    assert qn.status_string(0) == "ok"
+    assert qn.status_string(-4) == "unsupported configuration"
+    assert qn.status_string(12345) == "unknown status"
+
+
+# ---- fake device pointers: validation never dereferences them -------------
+_FAKE = [0x10000000]
+
+
+def fake(align=256):
+    _FAKE[0] += 1 << 20
+    return _FAKE[0] - (_FAKE[0] % align)
+
+
+def mla_args(T=32, quant="none", He=7168, Hcq=1536, N=128, D=128, Hckv=512,
+             Dr=64, bn=192, bs=128, layout=b.MLA_WEIGHT_PACKED_K16):
+    a = b.MlaPrologV2Args()
+    a.struct_size = ctypes.sizeof(b.MlaPrologV2Args)
+    a.quant_mode = b.MLA_QUANT[quant]
+    a.weight_layout = layout
+    a.B, a.S = T, 1
+    a.He, a.Hcq, a.N, a.D, a.Hckv, a.Dr, a.Nkv = He, Hcq, N, D, Hckv, Dr, 1
+    a.block_num, a.block_size = bn, bs
+    a.rmsnorm_epsilon_cq = a.rmsnorm_epsilon_ckv = 1e-5
+    for f in ("token_x", "weight_dq", "weight_uq_qr", "weight_uk",
+              "weight_dkv_kr", "rmsnorm_gamma_cq", "rmsnorm_gamma_ckv",
+              "rope_sin", "rope_cos", "cache_index", "kv_cache", "kr_cache",
+              "query", "query_rope"):
+        setattr(a, f, fake())
+    if quant != "none":
+        a.dequant_scale_w_uq_qr = fake()
+        a.smooth_scales_cq = fake()
+    if quant == "partial_kv_int8":
+        a.quant_scale_ckv = fake()
+        a.quant_scale_ckr = fake()
+    return a
+
+
+def mla_validate(a):
+    return b.load_library().mla_prolog_v2_validate(ctypes.byref(a))
+
+
+def test_mla_valid_args_pass():
+    for q in ("none", "partial_kv_bf16", "partial_kv_int8"):
+        assert mla_validate(mla_args(quant=q)) == 0
+    assert mla_validate(mla_args(T=4, He=256, Hcq=128, N=4, D=32, Hckv=64,
+                                 Dr=16, bn=4, bs=16)) == 0
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "struct_size", 8), -8),
+    (lambda a: setattr(a, "reserved0", 1), -8),
+    (lambda a: setattr(a, "quant_mode", 3), -4),   # full quant, kv bf16
+    (lambda a: setattr(a, "quant_mode", 4), -4),   # full quant, kv int8
+    (lambda a: setattr(a, "quant_mode", 9), -3),
+    (lambda a: setattr(a, "weight_layout", 7), -3),
+    (lambda a: setattr(a, "cache_mode", b"PA_NZ"), -4),
+    (lambda a: setattr(a, "cache_mode", b"bogus"), -3),
+    (lambda a: setattr(a, "B", -1), -2),
+    (lambda a: setattr(a, "He", 0), -2),
+    (lambda a: setattr(a, "Dr", 15), -2),
+    (lambda a: setattr(a, "Nkv", 2), -4),
+    (lambda a: setattr(a, "He", 7000), -4),        # not a multiple of 32
+    (lambda a: setattr(a, "Dr", 48), -4),
+    (lambda a: setattr(a, "rmsnorm_epsilon_cq", -1.0), -7),
+    (lambda a: setattr(a, "rmsnorm_epsilon_ckv", float("nan")), -7),
+    (lambda a: setattr(a, "dequant_scale_x", fake()), -5),
+    (lambda a: setattr(a, "dequant_scale_w_dq", fake()), -5),
+    (lambda a: setattr(a, "dequant_scale_w_dkv_kr", fake()), -5),
+    (lambda a: setattr(a, "dequant_scale_q_nope", fake()), -5),
+    (lambda a: setattr(a, "token_x", None), -1),
+    (lambda a: setattr(a, "weight_uk", None), -1),
+    (lambda a: setattr(a, "cache_index", None), -1),
+    (lambda a: setattr(a, "kv_cache", None), -1),
+    (lambda a: setattr(a, "query_rope", None), -1),
+    (lambda a: setattr(a, "token_x", fake() + 2), -9),
+    (lambda a: setattr(a, "cache_index", fake() + 4), -9),
+])
+def test_mla_validation_errors(mutate, code):
+    a = mla_args()
+    mutate(a)
+    assert mla_validate(a) == code
+
+
+def test_mla_quant_mode_needs_its_scales():
+    a = mla_args(quant="partial_kv_int8")
+    a.quant_scale_ckr = None
+    assert mla_validate(a) == -1
+    a = mla_args(quant="partial_kv_bf16")
+    a.smooth_scales_cq = None
+    assert mla_validate(a) == -1
+    # Hcq must be a multiple of 64 for the int8 up-projection
+    assert mla_validate(mla_args(quant="partial_kv_bf16", Hcq=1568)) == -4
+
+
+def test_mla_empty_cases():
+    lib = b.load_library()
+    # T = 0: every per-token pointer may be NULL; nothing is launched.
+    a = mla_args(T=0)
+    for f in ("token_x", "rope_sin", "rope_cos", "cache_index", "query",
+              "query_rope"):
+        setattr(a, f, None)
+    assert mla_validate(a) == 0
+    n = ctypes.c_size_t(99)
+    assert lib.mla_prolog_v2_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.mla_prolog_v2(ctypes.byref(a), None, 0, None) == 0
+    # no cache slots: caches may be NULL, queries are still required
+    a = mla_args(bn=0)
+    a.kv_cache = a.kr_cache = None
+    assert mla_validate(a) == 0
+
+
+def test_mla_workspace_size_and_too_small():
+    lib = b.load_library()
+    n = ctypes.c_size_t(0)
+    a = mla_args()
+    assert lib.mla_prolog_v2_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    packed = n.value
+    # decode: split-K partials + c^Q + q^C, a few MB
+    assert 1 << 20 < packed < 64 << 20
+    a = mla_args(layout=b.MLA_WEIGHT_ND)
+    assert lib.mla_prolog_v2_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    # ND weights are packed into the workspace on every call
+    assert n.value >= packed + 122_552_320
+    a = mla_args()
+    assert lib.mla_prolog_v2(ctypes.byref(a), ctypes.c_void_p(fake()),
+                             packed - 1, None) == -6
+    assert lib.mla_prolog_v2_workspace_size(ctypes.byref(a), None) == -1
+    bad = mla_args(He=0)
+    n = ctypes.c_size_t(5)
+    assert lib.mla_prolog_v2_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == -2
+    assert n.value == 0
+
+
+def test_pack_weight_validation():
+    lib = b.load_library()
+    assert lib.mla_pack_weight(None, None, 1, 16, 8, 3, None) == -3
+    assert lib.mla_pack_weight(None, None, 1, 12, 8, 2, None) == -2
+    assert lib.mla_pack_weight(None, None, 1, 24, 8, 1, None) == -2
+    assert lib.mla_pack_weight(None, None, 0, 16, 8, 2, None) == 0
+    assert lib.mla_pack_weight(None, None, 1, 16, 8, 2, None) == -1
+    assert lib.mla_pack_weight(ctypes.c_void_p(fake()),
+                               ctypes.c_void_p(fake() + 8), 1, 16, 8, 2,
+                               None) == -9
+
+
+# ---- QkvRmsNormRopeCache ---------------------------------------------------
+
+def qkv_args(B=64, S=128, quant="symmetric", bn=64, bs=128, D=128):
+    a = b.QkvRmsNormRopeCacheArgs()
+    a.struct_size = ctypes.sizeof(b.QkvRmsNormRopeCacheArgs)
+    a.quant_mode = b.QKV_QUANT[quant]
+    a.dtype = 0
+    a.B, a.S, a.Nq, a.Nk, a.Nv, a.D = B, S, 32, 8, 8, D
+    a.block_num, a.block_size = bn, bs
+    a.epsilon = 1e-6
+    for f in ("qkv", "gamma_q", "gamma_k", "cos", "sin", "index", "k_cache",
+              "v_cache", "q_out"):
+        setattr(a, f, fake())
+    if quant != "none":
+        a.k_scale, a.v_scale = fake(), fake()
+    if quant == "asymmetric":
+        a.k_offset, a.v_offset = fake(), fake()
+    return a
+
+
+def qkv_validate(a):
+    return b.load_library().qkv_rmsnorm_rope_cache_validate(ctypes.byref(a))
+
+
+def test_qkv_valid_args_pass():
+    for q in ("none", "symmetric", "asymmetric"):
+        assert qkv_validate(qkv_args(quant=q)) == 0
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "struct_size", 4), -8),
+    (lambda a: setattr(a, "quant_mode", 3), -3),
+    (lambda a: setattr(a, "dtype", 2), -3),
+    (lambda a: setattr(a, "cache_mode", b"PA_NZ"), -4),
+    (lambda a: setattr(a, "Nv", 7), -2),           # Nk != Nv
+    (lambda a: setattr(a, "D", 64), -4),           # only D = 128
+    (lambda a: setattr(a, "D", 127), -2),          # D even
+    (lambda a: setattr(a, "block_num", 63), -2),   # BlockNum >= ceil(S/BS)*B
+    (lambda a: setattr(a, "block_size", 0), -2),
+    (lambda a: setattr(a, "epsilon", -1e-6), -7),
+    (lambda a: setattr(a, "k_scale", None), -1),
+    (lambda a: setattr(a, "index", None), -1),
+    (lambda a: setattr(a, "qkv", fake() + 8), -9),
+    (lambda a: setattr(a, "q_before_quant", fake() + 2), -9),
+])
+def test_qkv_validation_errors(mutate, code):
+    a = qkv_args()
+    mutate(a)
+    assert qkv_validate(a) == code
+
+
+def test_qkv_asymmetric_needs_offsets_and_empty_is_noop():
+    a = qkv_args(quant="asymmetric")
+    a.v_offset = None
+    assert qkv_validate(a) == -1
+    lib = b.load_library()
+    e = qkv_args(B=0)
+    for f in ("qkv", "cos", "sin", "index", "q_out"):
+        setattr(e, f, None)
+    assert lib.qkv_rmsnorm_rope_cache(ctypes.byref(e), None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(16, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qn.mla_pack_weight(w)

@@ -1,0 +1,234 @@
+"""GPU parity: the HIP library against the float64 oracle, element by
+element, on seeded workloads (all calls go through the C ABI via the
+binding).  Needs an MI355X and the built library; a missing library fails
+these tests rather than skipping them.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import qkv_norm_rope_amd as qn
+from tests import gpu_helpers as gh
+from workloads import get_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qn.load_library()  # raises if the HIP library is not built
+    torch.cuda.init()
+
+
+def _before(dev, names):
+    return {k: gh.raw_bits(dev[k]).copy() for k in names}
+
+
+# ---- weight packing: pure index work, bit-exact ----------------------------
+
+@pytest.mark.parametrize("shape,dtype", [((64, 48), "bf16"), ((3, 32, 40), "bf16"),
+                                         ((96, 80), "int8"), ((7168, 64), "bf16")])
+def test_pack_weight_bit_exact(shape, dtype):
+    gh.announce(f"pack {shape} {dtype}")
+    rng = np.random.default_rng(5)
+    if dtype == "bf16":
+        bits = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        t = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        G = 8
+    else:
+        bits = rng.integers(-128, 128, size=shape).astype(np.int8)
+        t = torch.from_numpy(bits).cuda()
+        G = 16
+    p = qn.mla_pack_weight(t)
+    torch.cuda.synchronize()
+    got = gh.raw_bits(p).reshape(-1)
+    src = bits.reshape((-1,) + shape[-2:])
+    B, K, N = src.shape
+    # expected: element (k, n) at ((k // G) * N + n) * G + k % G per batch
+    want = src.reshape(B, K // G, G, N).transpose(0, 1, 3, 2).reshape(-1)
+    np.testing.assert_array_equal(got.view(want.dtype), want)
+
+
+# ---- MLA prolog --------------------------------------------------------------
+
+MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3"]
+
+
+@pytest.mark.parametrize("key", MLA_SMALL)
+@pytest.mark.parametrize("layout", ["packed", "nd"])
+def test_mla_parity_small(key, layout):
+    w = make_workload(key)
+    gh.announce(f"mla {w.cfg.name} T={w.cfg.T} quant={w.cfg.quant_mode} {layout}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev, layout=layout)
+    torch.cuda.synchronize()
+    stats = gh.check_mla(w, out, before)
+    gh.announce(f"  ok {stats}")
+
+
+def test_mla_parity_decode_T32():
+    w = make_workload(1)
+    gh.announce(f"mla {w.cfg.name} full size")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev, bsh=True)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
+def test_mla_parity_partial_quant_T64():
+    w = make_workload(3)
+    gh.announce(f"mla {w.cfg.name} full size")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
+def test_mla_parity_prefill_T4096_sampled():
+    # Full-size run; the oracle checks a sample of tokens spread over every
+    # 128-row tile, and the whole cache for placement.
+    w = make_workload(2)
+    gh.announce(f"mla {w.cfg.name} full size")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev, bsh=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    tokens = np.sort(np.concatenate([
+        np.arange(0, w.cfg.T, 128) + rng.integers(0, 128, w.cfg.T // 128),
+        [0, w.cfg.T - 1]]))
+    tokens = np.unique(tokens)
+    gh.announce(f"  checking {tokens.size} sampled tokens")
+    gh.announce(f"  ok {gh.check_mla(w, out, before, tokens=tokens)}")
+
+
+def test_mla_prefill_partial_quant_tiled_path():
+    # T > 128 takes the tiled kernels in the partial-quant scenario too.
+    cfg = get_config("mla_ragged_q").replace(B=3, S=67, block_num=8,
+                                            block_size=32, n_skip=9,
+                                            seed=2010, layout="BSH")
+    w = make_workload(cfg)
+    gh.announce(f"mla tiled quant T={cfg.T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev, bsh=True)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
+@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3])
+def test_mla_deterministic(key):
+    w = make_workload(key)
+    gh.announce(f"mla determinism {w.cfg.name}")
+    outs = []
+    for _ in range(2):
+        dev = gh.upload(w)
+        o = gh.run_mla_gpu(w, dev)
+        torch.cuda.synchronize()
+        outs.append({k: gh.raw_bits(v) for k, v in o.items()})
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
+
+
+def test_mla_T0_and_no_slots():
+    w = make_workload(0)
+    cfg = w.cfg
+    gh.announce("mla T=0 and BlockNum=0")
+    dev = gh.upload(w)
+    # T = 0: nothing happens, caches untouched
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    e = {k: v[:0] for k, v in dev.items()
+         if k in ("token_x", "rope_cos", "rope_sin", "cache_index")}
+    d0 = dict(dev, **e)
+    q, qr = qn.mla_prolog_v2(
+        d0["token_x"], dev["weight_dq"], dev["weight_uq_qr"], dev["weight_uk"],
+        dev["weight_dkv_kr"], dev["rmsnorm_gamma_cq"], dev["rmsnorm_gamma_ckv"],
+        d0["rope_sin"], d0["rope_cos"], d0["cache_index"], dev["kv_cache"],
+        dev["kr_cache"], weight_layout=qn.MLA_WEIGHT_ND)
+    torch.cuda.synchronize()
+    assert q.shape == (0, cfg.N, cfg.Hckv) and qr.shape == (0, cfg.N, cfg.Dr)
+    np.testing.assert_array_equal(gh.raw_bits(dev["kv_cache"]), before["kv_cache"])
+    # BlockNum = 0: queries as usual
+    empty_kv = dev["kv_cache"][:0]
+    empty_kr = dev["kr_cache"][:0]
+    q1, qr1 = qn.mla_prolog_v2(
+        dev["token_x"], dev["weight_dq"], dev["weight_uq_qr"], dev["weight_uk"],
+        dev["weight_dkv_kr"], dev["rmsnorm_gamma_cq"], dev["rmsnorm_gamma_ckv"],
+        dev["rope_sin"], dev["rope_cos"], dev["cache_index"], empty_kv, empty_kr,
+        weight_layout=qn.MLA_WEIGHT_ND)
+    full = gh.run_mla_gpu(w, gh.upload(w), layout="nd")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gh.raw_bits(q1), gh.raw_bits(full["query"]))
+    np.testing.assert_array_equal(gh.raw_bits(qr1), gh.raw_bits(full["query_rope"]))
+
+
+def test_mla_packed_equals_nd():
+    w = make_workload("mla_ragged")
+    gh.announce("mla packed vs ND layouts")
+    a = gh.run_mla_gpu(w, gh.upload(w), layout="packed")
+    b = gh.run_mla_gpu(w, gh.upload(w), layout="nd")
+    torch.cuda.synchronize()
+    for k in a:
+        np.testing.assert_array_equal(gh.raw_bits(a[k]), gh.raw_bits(b[k]), err_msg=k)
+
+
+# ---- QkvRmsNormRopeCache -----------------------------------------------------
+
+@pytest.mark.parametrize("key", ["qkv_ragged", "qkv_ragged_none", "qkv_ragged_asym", 4])
+def test_qkv_parity(key):
+    w = make_workload(key)
+    gh.announce(f"qkv {w.cfg.name} T={w.cfg.T} quant={w.cfg.quant_mode}")
+    dev = gh.upload(w)
+    before = _before(dev, ["k_cache", "v_cache"])
+    out = gh.run_qkv_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_qkv(w, out, before)}")
+
+
+def test_qkv_deterministic_and_bf16_input():
+    w = make_workload("qkv_ragged")
+    gh.announce("qkv determinism")
+    outs = []
+    for _ in range(2):
+        o = gh.run_qkv_gpu(w, gh.upload(w))
+        torch.cuda.synchronize()
+        outs.append({k: gh.raw_bits(v) for k, v in o.items()})
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
+    # bf16 inputs: same op on bf16-rounded copies of the fp16 inputs
+    import oracle
+    from workloads.gen import bf16_bits_from_f64
+    wb = make_workload("qkv_ragged")
+    for k in ("qkv", "gamma_q", "gamma_k", "cos", "sin"):
+        wb.arrays[k] = bf16_bits_from_f64(w.arrays[k].astype(np.float64))
+        wb.dtypes[k] = "bf16"
+    dev = gh.upload(wb)
+    before = _before(dev, ["k_cache", "v_cache"])
+    out = gh.run_qkv_gpu(wb, dev)
+    torch.cuda.synchronize()
+    assert out["q_out"].dtype == torch.bfloat16
+    gh.announce(f"  bf16 ok {gh.check_qkv(wb, out, before)}")
+    del oracle
+
+
+def test_qkv_empty():
+    w = make_workload("qkv_ragged")
+    dev = gh.upload(w)
+    gh.announce("qkv T=0")
+    cfg = w.cfg
+    before = _before(dev, ["k_cache", "v_cache"])
+    q = qn.qkv_rmsnorm_rope_cache(
+        dev["qkv"][:0], dev["gamma_q"], dev["gamma_k"], dev["cos"][:0],
+        dev["sin"][:0], dev["index"][:0], dev["k_cache"], dev["v_cache"],
+        Nq=cfg.Nq, Nk=cfg.Nk, Nv=cfg.Nv, k_scale=dev["k_scale"],
+        v_scale=dev["v_scale"], B=0, S=cfg.S)
+    torch.cuda.synchronize()
+    assert q.shape[0] == 0
+    np.testing.assert_array_equal(gh.raw_bits(dev["k_cache"]), before["k_cache"])
