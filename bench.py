@@ -8,12 +8,15 @@ batch of seeded synthetic tokens.  The headline workload is DeepSeek-V3-
 shaped decode, T = 32 tokens (bf16).  Inputs are resident in HBM before the
 timed region; steps rotate over several independent copies of weights,
 activations, caches and outputs so the working set exceeds the 256 MB
-last-level cache and bytes really come from HBM.
+last-level cache and bytes really come from HBM.  The timed decode steps
+are a HIP-graph replay of prepared calls (how decode steps are served: no
+host launch gaps); an eager pass over the same steps records per-kernel
+phase events.
 
 Prints ONE JSON line.  Besides the headline value it carries:
 * roofline - the dominant kernel (the c^Q . [W^UQ | W^QR] up projection),
-  its algorithmic bytes over its average duration measured with HIP events
-  recorded by the library on the launch stream during the timed steps;
+  its algorithmic bytes over its average duration, measured with HIP events
+  the library records on the launch stream between its kernels;
 * step_roofline - the whole call's algorithmic bytes over the step time;
 * prefill - the same prolog at T = 4096 (bf16 MFMA-bound);
 * qkv_rmsnorm_rope_cache - the fused qkv op on its (B=64, S=128) workload;
@@ -114,56 +117,117 @@ def prepare_mla_sets(w, n_sets, torch, qn, gh):
     return sets
 
 
-def run_mla(cfg, sets, steps, warmup, torch, qn):
-    """Time `steps` calls cycling over the sets; phase events on every step."""
-    ws = None
+class HipEvents:
+    """Timing events created with a device-scope release (no L2 writeback at
+    each record), through the HIP runtime torch already loaded."""
+
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [
+            ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [
+            ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    class Event:
+        def __init__(self, handle):
+            self.cuda_event = handle
+
+    def create(self):
+        h = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(h),
+                                              self.RELEASE_TO_DEVICE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        return self.Event(h.value)
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev.cuda_event, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a.cuda_event,
+                                        b.cuda_event) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev.cuda_event)
+
+
+def _hold_gpu(torch, ms=20.0):
+    """Keep the GPU busy for ~ms so the host can enqueue the whole timed
+    region before it starts (no host launch gaps inside it)."""
+    torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+
+
+def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
+    """Time `steps` calls cycling over the sets.
+
+    Returns (ms per step under HIP-graph replay, or eager when graph is
+    False; per-phase ms from the eager region; eager ms per step).  The
+    eager region records the library's phase events (device-scope release)
+    on every step, with the GPU held until the whole region is enqueued.
+    """
     nph = len(qn.MLA_PHASES)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nph)]
-          for _ in range(steps)]
+    kw = dict(quant_mode=cfg.quant_mode, rmsnorm_epsilon_cq=cfg.eps_cq,
+              rmsnorm_epsilon_ckv=cfg.eps_ckv)
+    names = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk",
+             "weight_dkv_kr", "rmsnorm_gamma_cq", "rmsnorm_gamma_ckv",
+             "rope_sin", "rope_cos", "cache_index", "kv_cache", "kr_cache",
+             "query", "query_rope")
+    calls = [qn.PreparedMlaPrologV2(*[s[k] for k in names], **kw)
+             for s in sets[:1]]
+    ws = calls[0].workspace
+    calls += [qn.PreparedMlaPrologV2(*[s[k] for k in names], workspace=ws,
+                                     **kw) for s in sets[1:]]
     stream = torch.cuda.current_stream()
-    for row in ev:  # materialise the events on this stream
-        for e in row:
-            e.record(stream)
-
-    def call(s, phase_events=None):
-        nonlocal ws
-        q, qr = qn.mla_prolog_v2(
-            s["token_x"], s["weight_dq"], s["weight_uq_qr"], s["weight_uk"],
-            s["weight_dkv_kr"], s["rmsnorm_gamma_cq"], s["rmsnorm_gamma_ckv"],
-            s["rope_sin"], s["rope_cos"], s["cache_index"], s["kv_cache"],
-            s["kr_cache"], quant_mode=cfg.quant_mode,
-            rmsnorm_epsilon_cq=cfg.eps_cq, rmsnorm_epsilon_ckv=cfg.eps_ckv,
-            query=s["query"], query_rope=s["query_rope"], workspace=ws,
-            phase_events=phase_events)
-        return q
-
-    # one call to size and keep the workspace
-    from qkv_norm_rope_amd import _binding as b
-    s0 = sets[0]
-    a = b.mla_prolog_v2_args(
-        s0["token_x"], s0["weight_dq"], s0["weight_uq_qr"], s0["weight_uk"],
-        s0["weight_dkv_kr"], s0["rmsnorm_gamma_cq"], s0["rmsnorm_gamma_ckv"],
-        s0["rope_sin"], s0["rope_cos"], s0["cache_index"], s0["kv_cache"],
-        s0["kr_cache"], s0["query"], s0["query_rope"],
-        quant_mode=cfg.quant_mode)
-    ws = torch.empty(max(1, b.mla_prolog_v2_workspace_size(a)),
-                     dtype=torch.uint8, device="cuda")
+    he = HipEvents()
+    ev = [[he.create() for _ in range(nph)] for _ in range(steps)]
     for i in range(warmup):
-        call(sets[i % len(sets)])
+        calls[i % len(calls)]()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
+    t0, t1 = he.create(), he.create()
+    _hold_gpu(torch, 5.0 + 0.1 * steps)
+    he.record(t0, stream)
     for i in range(steps):
-        call(sets[i % len(sets)], ev[i])
-    t1.record(stream)
+        calls[i % len(calls)](phase_events=ev[i])
+    he.record(t1, stream)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    ms_eager = he.elapsed_ms(t0, t1) / steps
     phase_ms = [0.0] * (nph - 1)
     for row in ev:
         for p in range(nph - 1):
-            phase_ms[p] += row[p].elapsed_time(row[p + 1]) / steps
-    return ms_step, phase_ms
+            phase_ms[p] += he.elapsed_ms(row[p], row[p + 1]) / steps
+    for row in ev:
+        for e in row:
+            he.destroy(e)
+    ms_step = ms_eager
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        reps = max(1, steps // len(calls))
+        g.replay()
+        torch.cuda.synchronize()
+        _hold_gpu(torch, 2.0)
+        he.record(t0, stream)
+        for _ in range(reps):
+            g.replay()
+        he.record(t1, stream)
+        torch.cuda.synchronize()
+        ms_step = he.elapsed_ms(t0, t1) / (reps * len(calls))
+        del g
+    he.destroy(t0)
+    he.destroy(t1)
+    return ms_step, phase_ms, ms_eager
 
 
 def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
@@ -190,6 +254,7 @@ def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
     s = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    _hold_gpu(torch, 5.0)
     t0.record(s)
     for i in range(steps):
         call(sets[i % 2])
@@ -250,7 +315,8 @@ def main():
     w = make_workload(1)
     cfg = w.cfg
     sets = prepare_mla_sets(w, args.rotate, torch, qn, gh)
-    ms, phase_ms = run_mla(cfg, sets, args.steps, args.warmup, torch, qn)
+    ms, phase_ms, ms_eager = run_mla(cfg, sets, args.steps, args.warmup,
+                                     torch, qn)
     step_bytes = mla_bytes(cfg)
     a6_ms = phase_ms[2]
     a6_bytes = uqqr_bytes(cfg)
@@ -286,6 +352,12 @@ def main():
                           "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS},
         "phase_us": dict(zip(("down", "norm_cache", "up_qr", "uk"),
                              [p * 1e3 for p in phase_ms])),
+        "timing": "value and ms_per_step: HIP-graph replay of the prepared "
+                  "calls; phase_us and roofline: device-release HIP events "
+                  "the library records between its launches in an eager "
+                  "region of the same steps",
+        "eager": {"ms_per_step": ms_eager,
+                  "tokens_per_s": cfg.T / (ms_eager * 1e-3)},
     }
     del sets
     torch.cuda.empty_cache()
@@ -296,8 +368,8 @@ def main():
         pc = wp.cfg
         psets = prepare_mla_sets(wp, 1, torch, qn, gh)
         psteps = max(3, args.steps // 20)
-        pms, pph = run_mla(pc, psets, psteps, max(2, args.warmup // 10),
-                           torch, qn)
+        pms, pph, _ = run_mla(pc, psets, psteps, max(2, args.warmup // 10),
+                              torch, qn, graph=False)
         fl = mla_flops(pc)
         a6f = uqqr_flops(pc)
         out["prefill"] = {

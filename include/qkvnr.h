@@ -105,13 +105,16 @@ enum {
  *   weight_uk).  The library packs ND weights into the workspace on every
  *   call (convenient, slower).
  * PACKED_K16: the MFMA-native blocked layout produced once by
- *   mla_pack_weight(): for a (K, N) matrix with G = 16 / element_bytes
- *   (8 for bf16, 16 for int8), element (k, n) is stored at
- *       ((k / G) * N + n) * G + (k % G),
- *   so the G consecutive-k values of one column form one 16-byte chunk.
+ *   mla_pack_weight().  For a (K, N) matrix with G = 16 / element_bytes
+ *   (8 for bf16, 16 for int8), KC = K / G chunk rows and NB = ceil(N / 32)
+ *   column blocks (the last one zero-padded), element (k, n) is stored at
+ *       ((((n / 32) * KC + k / G) * 32) + n % 32) * G + k % G.
+ *   The G consecutive-k values of one column form one 16-byte chunk (one
+ *   lane's MFMA operand), and each 32-column block's whole K range is one
+ *   contiguous run, so a weight-streaming wave reads one contiguous stream.
  *   weight_uk packs each head's (D, Hckv) matrix this way, heads in order.
- *   This plays the role that the pages' FRACTAL_NZ weight format plays for
- *   their hardware. */
+ *   A packed matrix holds K * NB * 32 elements.  This plays the role that the
+ *   pages' FRACTAL_NZ weight format plays for their hardware. */
 enum { MLA_WEIGHT_ND = 0, MLA_WEIGHT_PACKED_K16 = 1 };
 
 typedef struct MlaPrologV2Args {
@@ -211,9 +214,9 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
 
 /* Pack `batch` row-major (K, N) matrices (each K*N elements of
  * `elem_bytes` = 2 (bf16/fp16) or 1 (int8), batches contiguous) into the
- * MLA_WEIGHT_PACKED_K16 layout at dst (same total size, distinct buffer).
- * K must be a multiple of 16 / elem_bytes.  Device pointers; enqueued on
- * `stream`. */
+ * MLA_WEIGHT_PACKED_K16 layout at dst, a distinct buffer of
+ * batch * K * ceil(N/32)*32 elements.  K must be a multiple of
+ * 16 / elem_bytes.  Device pointers; enqueued on `stream`. */
 int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K,
                     int64_t N, int32_t elem_bytes, void* stream);
 

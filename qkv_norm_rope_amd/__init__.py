@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     MLA_WEIGHT_PACKED_K16,
     QKV_QUANT,
     MlaPrologV2Args,
+    PreparedMlaPrologV2,
     QkvRmsNormRopeCacheArgs,
     QkvnrError,
     load_library,

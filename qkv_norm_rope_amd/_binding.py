@@ -170,8 +170,9 @@ def _need(t, dtype, name):
 def mla_pack_weight(w: torch.Tensor, stream=None) -> torch.Tensor:
     """Pack a (K, N) or (batch, K, N) weight into the K16 blocked layout.
 
-    The result has w's shape and dtype; only the element order changes (see
-    MLA_WEIGHT_PACKED_K16 in include/qkvnr.h).
+    Returns a tensor of shape (K, Np) or (batch, K, Np) with Np = N rounded
+    up to a multiple of 32 and w's dtype; only the element order (and the
+    zero padding) differ (see MLA_WEIGHT_PACKED_K16 in include/qkvnr.h).
     """
     lib = load_library()
     if w.dim() not in (2, 3):
@@ -179,7 +180,8 @@ def mla_pack_weight(w: torch.Tensor, stream=None) -> torch.Tensor:
     batch = 1 if w.dim() == 2 else w.shape[0]
     K, N = w.shape[-2], w.shape[-1]
     eb = w.element_size()
-    out = torch.empty_like(w)
+    out = torch.empty(tuple(w.shape[:-1]) + ((N + 31) // 32 * 32,),
+                      dtype=w.dtype, device=w.device)
     _check(lib.mla_pack_weight(_ptr(w), _ptr(out), batch, K, N, eb,
                                _stream(stream)), "mla_pack_weight")
     return out
@@ -215,8 +217,10 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
             else (T, 1)
     a.B, a.S = int(B), int(S)
     a.He = int(He)
-    a.Hcq = int(weight_dq.shape[-1])
-    a.N, a.D, a.Hckv = (int(v) for v in weight_uk.shape)
+    # Hcq and Hckv come from the gammas: packed weights pad their columns.
+    a.Hcq = int(rmsnorm_gamma_cq.shape[-1])
+    a.N, a.D = int(weight_uk.shape[0]), int(weight_uk.shape[1])
+    a.Hckv = int(rmsnorm_gamma_ckv.shape[-1])
     a.Dr = int(rope_sin.shape[-1])
     a.Nkv = int(kv_cache.shape[2])
     a.block_num, a.block_size = int(kv_cache.shape[0]), int(kv_cache.shape[1])
@@ -278,7 +282,8 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
     He = token_x.shape[-1]
     lead = tuple(token_x.shape[:-1])
     T = token_x.numel() // He if He else 0
-    N, D, Hckv = weight_uk.shape
+    N = weight_uk.shape[0]
+    Hckv = rmsnorm_gamma_ckv.shape[-1]
     Dr = rope_sin.shape[-1]
     dev = token_x.device
     if query is None:
@@ -288,7 +293,7 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                                  device=dev)
     dbg8 = dbgs = None
     if return_cq_quant:
-        dbg8 = torch.empty((T, weight_dq.shape[-1]), dtype=torch.int8,
+        dbg8 = torch.empty((T, rmsnorm_gamma_cq.shape[-1]), dtype=torch.int8,
                            device=dev)
         dbgs = torch.empty((T,), dtype=torch.float32, device=dev)
     a = mla_prolog_v2_args(
@@ -316,6 +321,57 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
     if return_cq_quant:
         return query, query_rope, dbg8, dbgs
     return query, query_rope
+
+
+class PreparedMlaPrologV2:
+    """One mla_prolog_v2 call with its argument struct and workspace built
+    once, for callers that issue the same call repeatedly (serving loops,
+    graph capture).  Calling it runs the library on the current stream;
+    the tensors passed at construction must stay alive and in place.
+    """
+
+    def __init__(self, token_x, weight_dq, weight_uq_qr, weight_uk,
+                 weight_dkv_kr, rmsnorm_gamma_cq, rmsnorm_gamma_ckv, rope_sin,
+                 rope_cos, cache_index, kv_cache, kr_cache, query, query_rope,
+                 workspace=None, **kw):
+        self._lib = load_library()
+        lead = tuple(token_x.shape[:-1])
+        self._keep = (token_x, weight_dq, weight_uq_qr, weight_uk,
+                      weight_dkv_kr, rmsnorm_gamma_cq, rmsnorm_gamma_ckv,
+                      rope_sin, rope_cos, cache_index, kv_cache, kr_cache,
+                      query, query_rope, kw)
+        self.args = mla_prolog_v2_args(
+            token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
+            rmsnorm_gamma_cq, rmsnorm_gamma_ckv, rope_sin, rope_cos,
+            cache_index, kv_cache, kr_cache, query, query_rope,
+            B=lead[0] if len(lead) == 2 else None,
+            S=lead[1] if len(lead) == 2 else None, **kw)
+        nbytes = mla_prolog_v2_workspace_size(self.args)
+        if workspace is None or \
+                workspace.numel() * workspace.element_size() < nbytes:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8,
+                                    device=token_x.device)
+        self.workspace = workspace
+        self._ws = ctypes.c_void_p(_ptr(workspace))
+        self._nbytes = workspace.numel() * workspace.element_size()
+        self._ref = ctypes.byref(self.args)
+        self.query, self.query_rope = query, query_rope
+
+    def __call__(self, stream=None, phase_events=None):
+        a = self.args
+        if phase_events:
+            handles = (_vp * len(phase_events))(
+                *[e.cuda_event for e in phase_events])
+            a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
+            a.n_phase_events = len(phase_events)
+        else:
+            handles = None
+            a.n_phase_events = 0
+            a.phase_events = None
+        rc = self._lib.mla_prolog_v2(self._ref, self._ws, self._nbytes,
+                                     _stream(stream))
+        _check(rc, "mla_prolog_v2")
+        return self.query, self.query_rope
 
 
 # ---------------------------------------------------------------------------

@@ -89,8 +89,48 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-// 16-byte global load/store helpers.
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// Global-memory accessors.  Pointers reach the kernels inside by-value
+// argument structs, where the compiler cannot always prove they address
+// global memory; it then emits flat instructions, which count against the
+// LDS counter too and force full waits that serialise the load pipeline.
+// Casting to address space 1 makes every access a global_load / store.
+#define QKVNR_GLOBAL __attribute__((address_space(1)))
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4_t v = *(const QKVNR_GLOBAL u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  *(QKVNR_GLOBAL u32x4_t*)p = w;
+}
+__device__ __forceinline__ void st8(void* p, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  *(QKVNR_GLOBAL u32x2_t*)p = w;
+}
+template <class T>
+__device__ __forceinline__ T gld(const T* p) {
+  return *(const QKVNR_GLOBAL T*)p;
+}
+template <class T>
+__device__ __forceinline__ void gst(T* p, T v) {
+  *(QKVNR_GLOBAL T*)p = v;
+}
+// 8 fp32 values from / to 32 bytes of global memory.
+__device__ __forceinline__ void ld8f(const float* p, float* f) {
+  const uint4 a = ld16(p), b = ld16(p + 4);
+  f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
+  f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+  f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y);
+  f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+}
+__device__ __forceinline__ void st8f(float* p, const float* f) {
+  st16(p, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                     __float_as_uint(f[3])));
+  st16(p + 4, make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]),
+                         __float_as_uint(f[7])));
+}
 
 }  // namespace qkvnr

@@ -28,6 +28,8 @@ struct MlaPlan {
   // workspace offsets (bytes) and total size
   size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
   size_t off_part, off_cq, off_cq_scale, off_qc;
+  size_t off_xfrag;   // token_x in fragment layout (skinny plan)
+  int64_t rows;       // token rows padded to the plan's 32-row blocks
   size_t total;
 };
 

@@ -33,11 +33,17 @@ enum AKind { A_BF16 = 0, A_I8 = 1, A_F32SPLIT = 2 };
 enum EpiKind { EPI_PARTIAL = 0, EPI_UQQR = 1, EPI_UK = 2 };
 
 struct GemmParams {
-  // A: activations, row-major; row m of batch z starts at A + z*a_bstride + m*lda
-  // (element units of the A type).
+  // A: activations.  Row-major (a_frag == 0): row m of batch z starts at
+  // A + z*a_bstride + m*lda (element units of the A type).  Fragment layout
+  // (a_frag == 1, skinny kernels only): the 32-row block mb, k-step s of
+  // batch z is 64 lanes x CB contiguous bytes at
+  // A + z*a_zs + mb*a_mbs + s*64*CB, lane (g, i) holding row 32*mb + i and
+  // the k-step's g-th half (CB = 16, or 32 for fp32 A).
   const void* A;
   int64_t lda;
   int64_t a_bstride;
+  int a_frag;
+  int64_t a_mbs, a_zs;
   // B: packed weights as 16-byte chunks; chunk (kc, n) at kc*N + n.  Tiles
   // [0, ntiles0) read B0 (N0 columns), the rest read B1 (N1 columns, output
   // columns offset by N0).  Batch z adds z*b_bstride chunks.
@@ -62,6 +68,9 @@ struct GemmParams {
   const float* dq;        // per-column dequant (int8 A)
   void* qc_out;           // (T, N*D): bf16, or fp32 when qc_f32
   int qc_f32;
+  int qc_frag;            // write q^C in per-head fragment layout
+  int64_t qc_D;           // head dim D (fragment layout)
+  int64_t qc_mblocks;     // 32-row blocks per head (fragment layout)
   uint16_t* qr_out;  // (T, N, Dr)
   int64_t qr_ld;     // N*Dr
   // EPI_UK
@@ -132,10 +141,9 @@ struct Epilogue {
   static __device__ __forceinline__ void dequant(const GemmParams& p, int64_t m, int64_t gcol,
                                                  float* v) {
     if constexpr (AK == A_I8) {
-      const float s = p.cq_scale[m];
-      const float4 d0 = *reinterpret_cast<const float4*>(p.dq + gcol);
-      const float4 d1 = *reinterpret_cast<const float4*>(p.dq + gcol + 4);
-      const float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      const float s = gld(p.cq_scale + m);
+      float d[8];
+      ld8f(p.dq + gcol, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = v[e] * s * d[e];
     }
@@ -149,9 +157,7 @@ struct Epilogue {
     float v[8];
     to_float(raw, v);
     if constexpr (EPI == EPI_PARTIAL) {
-      float* dst = p.part + m * p.part_ld + ocol;
-      reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+      st8f(p.part + m * p.part_ld + ocol, v);
     } else if constexpr (EPI == EPI_UK) {
       uint16_t* dst = p.q_out + m * p.q_ld + static_cast<int64_t>(z) * p.q_bstride + gcol;
       st16(dst, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
@@ -159,14 +165,22 @@ struct Epilogue {
     } else {  // EPI_UQQR
       dequant(p, m, gcol, v);
       if (gcol < p.ND) {
-        if (p.qc_f32) {
-          float* dst = static_cast<float*>(p.qc_out) + m * p.ND + gcol;
-          reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
-          reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        // 8 columns of q^C = 8 consecutive k of one head: one A chunk of the
+        // per-head product in fragment layout, or 8 row-major elements.
+        int64_t off;
+        if (p.qc_frag) {
+          const int64_t head = gcol / p.qc_D, d = gcol % p.qc_D;
+          const int64_t lanei = ((d % 16) / 8) * 32 + (m % 32);
+          off = (((head * p.qc_mblocks + m / 32) * (p.qc_D / 16) + d / 16) * 64 + lanei) * 8;
         } else {
-          uint16_t* dst = static_cast<uint16_t*>(p.qc_out) + m * p.ND + gcol;
-          st16(dst, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+          off = m * p.ND + gcol;
+        }
+        if (p.qc_f32) {
+          st8f(static_cast<float*>(p.qc_out) + off, v);
+        } else {
+          st16(static_cast<uint16_t*>(p.qc_out) + off,
+               make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
         }
       } else {
         const int64_t r = gcol - p.ND;
@@ -198,17 +212,33 @@ struct Epilogue {
 };
 
 // ---------------------------------------------------------------------------
-// Skinny GEMM: all M (<= 32*MB) rows per wave, NW waves across N (32 columns
-// each), KW waves across K; the KW partial tiles are summed in LDS in wave
-// order, then the epilogue runs on 8-column groups.
+// Skinny GEMM (decode): all M (<= 32*MB) rows stay in registers while the
+// weight streams past.  A workgroup owns a tile of NW*NB 32-column blocks and
+// a K range split over KW waves; each wave streams NB column blocks over its
+// K sub-range.  In the N32-blocked packed layout one k-step of one column
+// block is 1 KB contiguous (64 lanes x 16 B), and a wave's whole K sub-range
+// is one contiguous run, read exactly once.  Loads are software-pipelined in
+// register batches of P k-steps (the next batch is in flight while the
+// current one feeds the MFMAs).  The KW partial tiles are summed in LDS in
+// wave order (deterministic), then the epilogue runs on 8-column groups.
 // ---------------------------------------------------------------------------
-template <int AK, int MB, int NW, int KW, int EPI>
+template <int AK, int MB, int NB>
+struct SkinnyDepth {
+  // k-steps per register batch: about 32 VGPRs of loads per batch (two
+  // batches live), the rest of the in-flight bytes coming from many waves.
+  static constexpr int per_step = NB + MB * ((AK == A_F32SPLIT) ? 2 : 1);
+  static constexpr int value = (8 / per_step) > 0 ? (8 / per_step) : 1;
+};
+
+template <int AK, int MB, int NB, int NW, int KW, int EPI,
+          int P = SkinnyDepth<AK, MB, NB>::value>
 __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   typedef typename AccT<AK>::type Acc;
   constexpr int KSTEP = (AK == A_I8) ? 32 : 16;  // k per MFMA
-  constexpr int TN = 32 * NW;
+  constexpr int G = (AK == A_I8) ? 16 : 8;       // k per 16-byte chunk
+  constexpr int TN = 32 * NB * NW;
   constexpr int PITCH = TN + 4;  // words per LDS row
-  constexpr int U = 8;           // k-steps in flight per wave
+  constexpr int NA = (AK == A_F32SPLIT) ? 2 : 1;  // 16-byte A loads per fragment
   __shared__ uint32_t lds[KW][MB * 32][PITCH];
 
   const int lane = threadIdx.x & 63;
@@ -233,6 +263,7 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
     ocol0 = p.N0;
   }
   B += static_cast<int64_t>(z) * p.b_bstride;
+  const int64_t KC = p.K / G;  // 16-byte chunk rows per column
 
   const int64_t nsteps = p.K / KSTEP;
   const int64_t s_lo = static_cast<int64_t>(blockIdx.y) * p.steps_per_split;
@@ -241,68 +272,117 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   const int64_t w_lo = s_lo + cnt * kw / KW;
   const int64_t w_hi = s_lo + cnt * (kw + 1) / KW;
 
-  const int64_t n = n0 + nw * 32 + li;
-  const bool n_ok = n < N;
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-
-  // A row pointers (byte addressing), one per m-block
-  const char* Abase = static_cast<const char*>(p.A);
-  constexpr int AEB = (AK == A_I8) ? 1 : (AK == A_F32SPLIT ? 4 : 2);  // A element bytes
-  const int64_t a_row_bytes = p.lda * AEB;
-  const char* arow[MB];
-  bool m_ok[MB];
+  // Column blocks of this wave: chunk (block nb, row kc, column j) sits at
+  // (nb*KC + kc)*32 + j, and lane (g, j) of k-step s reads row 2s+g, so the
+  // lane's chunk for step s is block_base + 64*s + lane.
+  //
+  // Every load below is unconditional: a column block past N, a row past M
+  // and a step past the wave's range are clamped to valid memory and their
+  // products are never stored (rows and columns of a product are
+  // independent).  Branch-free loads let the compiler wait only for the
+  // batch being consumed instead of draining every load in flight.
+  const int64_t nblk = (N + 31) / 32;
+  const uint4* bptr[NB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int64_t m = mb * 32 + li;
-    m_ok[mb] = m < p.M;
-    arow[mb] = Abase + (static_cast<int64_t>(z) * p.a_bstride) * AEB + m * a_row_bytes;
+  for (int b = 0; b < NB; ++b) {
+    int64_t nb = n0 / 32 + nw * NB + b;
+    nb = nb < nblk ? nb : nblk - 1;
+    bptr[b] = B + nb * KC * 32 + lane;
   }
 
-  Acc acc[MB];
+  constexpr int AEB = (AK == A_I8) ? 1 : (AK == A_F32SPLIT ? 4 : 2);  // A element bytes
+  constexpr int CB = (AK == A_F32SPLIT) ? 32 : 16;  // A bytes per lane per k-step
+  const char* arow[MB];
+  int64_t astep;  // A bytes between consecutive k-steps of one lane
+  if (p.a_frag) {
+    const char* base = static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_zs + lane * CB;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = Acc{};
+    for (int mb = 0; mb < MB; ++mb) arow[mb] = base + mb * p.a_mbs;
+    astep = 64 * CB;
+  } else {
+    const char* base =
+        static_cast<const char*>(p.A) + (static_cast<int64_t>(z) * p.a_bstride) * AEB;
+    const int64_t a_row_bytes = p.lda * AEB;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      int64_t m = mb * 32 + li;
+      m = m < p.M ? m : p.M - 1;
+      // bf16: 16 k = 32 bytes per step, lane group g takes bytes [16g, 16g+16);
+      // int8: 32 k = 32 bytes, same offsets; fp32: 16 k = 64 bytes, group g
+      // takes [32g, 32g+32).
+      arow[mb] = base + m * a_row_bytes + g * CB;
+    }
+    astep = 2 * CB;
+  }
 
-  auto a_frag = [&](int mb, int64_t s, uint4& hi, uint4& lo) {
-    if constexpr (AK == A_F32SPLIT) {
-      const float* src = reinterpret_cast<const float*>(arow[mb]) + s * 16 + 8 * g;
-      float4 f0 = make_float4(0.f, 0.f, 0.f, 0.f), f1 = f0;
-      if (m_ok[mb]) {
-        f0 = reinterpret_cast<const float4*>(src)[0];
-        f1 = reinterpret_cast<const float4*>(src)[1];
+  Acc acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mb][b] = Acc{};
+
+  // One register batch: B chunks and raw A chunks of P k-steps.
+  struct Batch {
+    uint4 b[P][NB];
+    uint4 a[P][MB][NA];
+  };
+  const int64_t s_last = w_hi - 1;
+  auto load = [&](Batch& x, int64_t s0) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int64_t s = (s0 + u) < s_last ? (s0 + u) : s_last;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) x.b[u][b] = ld16(bptr[b] + s * 64);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        x.a[u][mb][0] = ld16(arow[mb] + s * astep);
+        if constexpr (AK == A_F32SPLIT) x.a[u][mb][1] = ld16(arow[mb] + s * astep + 16);
       }
-      split8(f0, f1, hi, lo);
-    } else {
-      // bf16: 16 k = 32 bytes per step, lane group g takes bytes [16g, 16g+16)
-      // int8: 32 k = 32 bytes per step, same byte offsets
-      hi = m_ok[mb] ? ld16(arow[mb] + s * 32 + 16 * g) : zero4;
-      lo = zero4;
+    }
+  };
+  auto compute = [&](const Batch& x, int64_t count) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if (u >= count) break;  // wave-uniform; only MFMAs are skipped
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (AK == A_F32SPLIT) {
+          uint4 hi, lo;
+          const uint4 r0 = x.a[u][mb][0], r1 = x.a[u][mb][1];
+          split8(make_float4(__uint_as_float(r0.x), __uint_as_float(r0.y), __uint_as_float(r0.z),
+                             __uint_as_float(r0.w)),
+                 make_float4(__uint_as_float(r1.x), __uint_as_float(r1.y), __uint_as_float(r1.z),
+                             __uint_as_float(r1.w)),
+                 hi, lo);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            mfma_step<AK>(acc[mb][b], hi, x.b[u][b]);
+            mfma_step<AK>(acc[mb][b], lo, x.b[u][b]);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) mfma_step<AK>(acc[mb][b], x.a[u][mb][0], x.b[u][b]);
+        }
+      }
     }
   };
 
-  int64_t s = w_lo;
-  for (; s + U <= w_hi; s += U) {
-    uint4 bfr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) bfr[u] = n_ok ? B[(2 * (s + u) + g) * N + n] : zero4;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        uint4 ah, al;
-        a_frag(mb, s + u, ah, al);
-        mfma_step<AK>(acc[mb], ah, bfr[u]);
-        if constexpr (AK == A_F32SPLIT) mfma_step<AK>(acc[mb], al, bfr[u]);
-      }
-    }
-  }
-  for (; s < w_hi; ++s) {
-    const uint4 b = n_ok ? B[(2 * s + g) * N + n] : zero4;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      uint4 ah, al;
-      a_frag(mb, s, ah, al);
-      mfma_step<AK>(acc[mb], ah, b);
-      if constexpr (AK == A_F32SPLIT) mfma_step<AK>(acc[mb], al, b);
+  // Ping-pong over batches: the next batch's loads are issued before the
+  // current batch's MFMAs.  The last prefetch re-reads the final batch (cache
+  // hits) so the load sequence never depends on a branch.
+  if (w_lo < w_hi) {
+    Batch X, Y;
+    int64_t s = w_lo;
+    load(X, s);
+    for (;;) {
+      load(Y, s + P < w_hi ? s + P : s);
+      compute(X, w_hi - s);
+      s += P;
+      if (s >= w_hi) break;
+      load(X, s + P < w_hi ? s + P : s);
+      compute(Y, w_hi - s);
+      s += P;
+      if (s >= w_hi) break;
     }
   }
 
@@ -311,14 +391,17 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      uint32_t bits;
-      if constexpr (AK == A_I8)
-        bits = static_cast<uint32_t>(acc[mb][r]);
-      else
-        bits = __float_as_uint(acc[mb][r]);
-      lds[kw][row][nw * 32 + li] = bits;
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        uint32_t bits;
+        if constexpr (AK == A_I8)
+          bits = static_cast<uint32_t>(acc[mb][b][r]);
+        else
+          bits = __float_as_uint(acc[mb][b][r]);
+        lds[kw][row][(nw * NB + b) * 32 + li] = bits;
+      }
     }
   }
   __syncthreads();
@@ -414,6 +497,7 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
   const int64_t a_row_bytes = p.lda * AEB;
   constexpr int KPS = (AK == A_I8) ? 64 : 32;  // k per stage
   const int64_t nstages = p.K / KPS;
+  const int64_t KC = p.K / ((AK == A_I8) ? 16 : 8);  // chunk rows per column
 
   // Global -> register loads of one stage.  A: 128 rows x 64 B (bf16/int8)
   // = 512 chunks of 16 B, 2 per thread; fp32 A: 128 rows x 128 B, 4 per
@@ -433,11 +517,14 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      // 4 column blocks x 4 chunk rows x 32 columns; each (block, row) run
+      // is 512 contiguous bytes of the N32-blocked weight.
       const int c = tid + 256 * i;
-      const int kc = c >> 7;
-      const int col = c & 127;
-      const int64_t n = n0 + col;
-      rb[i] = n < N ? B[(st * 4 + kc) * N + n] : zero4;
+      const int nbl = c >> 7;
+      const int kc = (c >> 5) & 3;
+      const int j = c & 31;
+      const int64_t nb = n0 / 32 + nbl;
+      rb[i] = nb * 32 < N ? ld16(B + (nb * KC + st * 4 + kc) * 32 + j) : zero4;
     }
   };
   auto swrite = [&](int buf) {
@@ -474,7 +561,8 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<uint4*>(sb + 16 * c) = rb[i];
+      const int col = (c >> 7) * 32 + (c & 31);
+      *reinterpret_cast<uint4*>(sb + (((c >> 5) & 3) * TBN + col) * 16) = rb[i];
     }
   };
 
@@ -582,129 +670,199 @@ struct FinishParams {
   void* kr_cache;
   uint16_t* cq_bf16;
   int8_t* cq_i8;
+  int cq_frag;  // write c^Q in the skinny kernels' A fragment layout
   float* cq_scale;
   int8_t* dbg_cq_i8;
   float* dbg_cq_scale;
 };
 
-__device__ __forceinline__ float block_sum256(float v, float* red) {
+constexpr int FIN_THREADS = 1024;
+constexpr int FIN_WAVES = FIN_THREADS / 64;
+constexpr int FIN_MAXSPLIT = 8;
+constexpr int FIN_COLS = 3;  // columns per thread per pass (2112 = 3 passes x 704)
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
   v = group_sum<64>(v);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < FIN_WAVES; ++w) t += red[w];
+  return t;
 }
-__device__ __forceinline__ float block_max256(float v, float* red) {
+__device__ __forceinline__ float block_max(float v, float* red) {
   v = group_max<64>(v);
   const int wave = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < FIN_WAVES; ++w) t = fmaxf(t, red[w]);
+  return t;
 }
 
 // QM: 0 none, 1 partial with bf16 caches, 2 partial with int8 caches.
 template <int QM>
-__global__ __launch_bounds__(256) void k_down_finish(FinishParams p) {
+__global__ __launch_bounds__(FIN_THREADS) void k_down_finish(FinishParams p) {
   extern __shared__ float row[];  // Hcq + Hckv + Dr
-  __shared__ float red[4];
+  __shared__ float red[FIN_WAVES];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
   const int ntot = p.Hcq + p.Hckv + p.Dr;
 
-  for (int c = tid; c < ntot; c += 256) {
-    float v = 0.f;
-    for (int s = 0; s < p.ksplit; ++s) v += p.part[(static_cast<int64_t>(s) * p.T + t) * ntot + c];
-    row[c] = v;
+  // Sum the split-K partials in split order.  Loads are unconditional
+  // (clamped column and split indexes) so all FIN_COLS x FIN_MAXSPLIT of a
+  // thread's loads are in flight together.
+  for (int c0 = 0; c0 < ntot; c0 += FIN_COLS * FIN_THREADS) {
+    float v[FIN_COLS][FIN_MAXSPLIT];
+#pragma unroll
+    for (int i = 0; i < FIN_COLS; ++i) {
+      int c = c0 + tid + i * FIN_THREADS;
+      c = c < ntot ? c : ntot - 1;
+#pragma unroll
+      for (int s = 0; s < FIN_MAXSPLIT; ++s) {
+        const int se = s < p.ksplit ? s : p.ksplit - 1;
+        v[i][s] = gld(p.part + (static_cast<int64_t>(se) * p.T + t) * ntot + c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < FIN_COLS; ++i) {
+      const int c = c0 + tid + i * FIN_THREADS;
+      float a = 0.f;
+#pragma unroll
+      for (int s = 0; s < FIN_MAXSPLIT; ++s) a += s < p.ksplit ? v[i][s] : 0.f;
+      if (c < ntot) row[c] = a;
+    }
   }
   __syncthreads();
 
   float sq = 0.f, skv = 0.f;
-  for (int c = tid; c < p.Hcq; c += 256) sq += row[c] * row[c];
-  for (int c = tid; c < p.Hckv; c += 256) skv += row[p.Hcq + c] * row[p.Hcq + c];
-  sq = block_sum256(sq, red);
-  skv = block_sum256(skv, red);
+  for (int c = tid; c < p.Hcq; c += FIN_THREADS) sq += row[c] * row[c];
+  for (int c = tid; c < p.Hckv; c += FIN_THREADS) skv += row[p.Hcq + c] * row[p.Hcq + c];
+  sq = block_sum(sq, red);
+  skv = block_sum(skv, red);
   const float rq = 1.0f / __builtin_sqrtf(sq / static_cast<float>(p.Hcq) + p.eps_cq);
   const float rkv = 1.0f / __builtin_sqrtf(skv / static_cast<float>(p.Hckv) + p.eps_ckv);
 
-  // c^Q
+  // c^Q.  Fragment layout: element (t, c) of a K-step of `ks` values sits at
+  // ((mb*(Hcq/ks) + c/ks)*64 + g*32 + t%32)*(ks/2) + c%(ks/2), g = (c%ks)/(ks/2).
+  auto cq_off = [&](int c, int ks) -> int64_t {
+    if (!p.cq_frag) return t * p.Hcq + c;
+    const int h = ks / 2;
+    return ((static_cast<int64_t>(t / 32) * (p.Hcq / ks) + c / ks) * 64 + ((c % ks) / h) * 32 +
+            (t % 32)) * h + c % h;
+  };
   if (QM == 0) {
-    for (int c = tid; c < p.Hcq; c += 256)
-      p.cq_bf16[t * p.Hcq + c] = f32_to_bf16(row[c] * rq * bf16_to_f32(p.gamma_cq[c]));
+    for (int c = tid; c < p.Hcq; c += FIN_THREADS)
+      gst(p.cq_bf16 + cq_off(c, 16),
+          f32_to_bf16(row[c] * rq * bf16_to_f32(gld(p.gamma_cq + c))));
   } else {
     float amax = 0.f;
-    for (int c = tid; c < p.Hcq; c += 256) {
-      const float u = row[c] * rq * bf16_to_f32(p.gamma_cq[c]) * p.smooth[c];
+    for (int c = tid; c < p.Hcq; c += FIN_THREADS) {
+      const float u = row[c] * rq * bf16_to_f32(gld(p.gamma_cq + c)) * gld(p.smooth + c);
       row[c] = u;
       amax = fmaxf(amax, fabsf(u));
     }
-    amax = block_max256(amax, red);
+    amax = block_max(amax, red);
     const float s = amax / 127.0f;
-    for (int c = tid; c < p.Hcq; c += 256) {
+    for (int c = tid; c < p.Hcq; c += FIN_THREADS) {
       const int code = s > 0.f ? sat_rne(row[c] / s, -127, 127) : 0;
-      p.cq_i8[t * p.Hcq + c] = static_cast<int8_t>(code);
-      if (p.dbg_cq_i8) p.dbg_cq_i8[t * p.Hcq + c] = static_cast<int8_t>(code);
+      gst(p.cq_i8 + cq_off(c, 32), static_cast<int8_t>(code));
+      if (p.dbg_cq_i8) gst(p.dbg_cq_i8 + t * p.Hcq + c, static_cast<int8_t>(code));
     }
     if (tid == 0) {
-      p.cq_scale[t] = s;
-      if (p.dbg_cq_scale) p.dbg_cq_scale[t] = s;
+      gst(p.cq_scale + t, s);
+      if (p.dbg_cq_scale) gst(p.dbg_cq_scale + t, s);
     }
   }
 
-  const int64_t slot = p.index[t];
+  const int64_t slot = gld(p.index + t);
   if (slot < 0 || slot >= p.slots) return;
   // c^KV row
-  for (int c = tid; c < p.Hckv; c += 256) {
-    const float v = row[p.Hcq + c] * rkv * bf16_to_f32(p.gamma_ckv[c]);
+  for (int c = tid; c < p.Hckv; c += FIN_THREADS) {
+    const float v = row[p.Hcq + c] * rkv * bf16_to_f32(gld(p.gamma_ckv + c));
     if (QM == 2)
-      static_cast<int8_t*>(p.kv_cache)[slot * p.Hckv + c] =
-          static_cast<int8_t>(sat_rne(v / p.qs_ckv[c], -128, 127));
+      gst(static_cast<int8_t*>(p.kv_cache) + slot * p.Hckv + c,
+          static_cast<int8_t>(sat_rne(v / gld(p.qs_ckv + c), -128, 127)));
     else
-      static_cast<uint16_t*>(p.kv_cache)[slot * p.Hckv + c] = f32_to_bf16(v);
+      gst(static_cast<uint16_t*>(p.kv_cache) + slot * p.Hckv + c, f32_to_bf16(v));
   }
   // k^R row: half-and-half RoPE with the token's (cos, sin)
   const int half = p.Dr >> 1;
   const float* kr = row + p.Hcq + p.Hckv;
-  for (int i = tid; i < p.Dr; i += 256) {
-    const float c = bf16_to_f32(p.cosb[t * p.Dr + i]);
-    const float s = bf16_to_f32(p.sinb[t * p.Dr + i]);
+  for (int i = tid; i < p.Dr; i += FIN_THREADS) {
+    const float c = bf16_to_f32(gld(p.cosb + t * p.Dr + i));
+    const float s = bf16_to_f32(gld(p.sinb + t * p.Dr + i));
     const float o = i < half ? kr[i] * c - kr[i + half] * s : kr[i] * c + kr[i - half] * s;
     if (QM == 2)
-      static_cast<int8_t*>(p.kr_cache)[slot * p.Dr + i] =
-          static_cast<int8_t>(sat_rne(o / p.qs_ckr[i], -128, 127));
+      gst(static_cast<int8_t*>(p.kr_cache) + slot * p.Dr + i,
+          static_cast<int8_t>(sat_rne(o / gld(p.qs_ckr + i), -128, 127)));
     else
-      static_cast<uint16_t*>(p.kr_cache)[slot * p.Dr + i] = f32_to_bf16(o);
+      gst(static_cast<uint16_t*>(p.kr_cache) + slot * p.Dr + i, f32_to_bf16(o));
   }
 }
 
 // ---------------------------------------------------------------------------
-// Weight packing: one thread per 16-byte output chunk.
+// Activation packing for the skinny kernels: bf16 rows (M, K) into the A
+// fragment layout, one thread per 16-byte chunk (32-row block mb, k-step s,
+// lane (g, i)) = row 32*mb + i, k in [16s + 8g, 16s + 8g + 8).  Rows past M
+// are zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src,
+                                                uint4* __restrict__ dst, int64_t M, int64_t K,
+                                                int64_t mblocks) {
+  // Thread c reads the 16 bytes k in [8*q, 8*q+8) of row m (reads coalesce
+  // along the row) and writes them to their fragment chunk.
+  const int64_t steps = K / 16;
+  const int64_t per_row = K / 8;
+  const int64_t total = mblocks * 32 * per_row;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t m = c / per_row;
+    const int64_t q = c % per_row;
+    const int64_t chunk = ((m / 32) * steps + q / 2) * 64 + (q % 2) * 32 + (m % 32);
+    st16(dst + chunk, m < M ? ld16(src + m * K + 8 * q) : make_uint4(0, 0, 0, 0));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing into the N32-blocked K16 layout, one thread per 16-byte
+// output chunk (block nb, chunk row kc, column j): the G = 16/eb consecutive
+// k values of column 32*nb + j.  Columns past N (the last block's padding)
+// are zero.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint4* __restrict__ dst,
                                               int64_t batch, int64_t K, int64_t N, int eb) {
   const int G = 16 / eb;
-  const int64_t kc_n = (K / G) * N;
-  const int64_t total = batch * kc_n;
+  const int64_t KC = K / G;
+  const int64_t nblk = (N + 31) / 32;
+  const int64_t per = nblk * KC * 32;
+  const int64_t total = batch * per;
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
        c += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t b = c / kc_n;
-    const int64_t r = c % kc_n;
-    const int64_t kc = r / N;
-    const int64_t n = r % N;
-    const char* s = src + ((b * K + kc * G) * N + n) * eb;
+    const int64_t b = c / per;
+    const int64_t r = c % per;
+    const int64_t nb = r / (KC * 32);
+    const int64_t kc = (r / 32) % KC;
+    const int64_t n = nb * 32 + (r % 32);
     uint32_t w[4] = {0, 0, 0, 0};
-    if (eb == 2) {
+    if (n < N) {
+      const char* s = src + ((b * K + kc * G) * N + n) * eb;
+      if (eb == 2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t v = *reinterpret_cast<const uint16_t*>(s + static_cast<int64_t>(e) * N * 2);
-        w[e >> 1] |= v << (16 * (e & 1));
-      }
-    } else {
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t v = *reinterpret_cast<const uint16_t*>(s + static_cast<int64_t>(e) * N * 2);
+          w[e >> 1] |= v << (16 * (e & 1));
+        }
+      } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t v = static_cast<uint8_t>(s[static_cast<int64_t>(e) * N]);
-        w[e >> 2] |= v << (8 * (e & 3));
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t v = static_cast<uint8_t>(s[static_cast<int64_t>(e) * N]);
+          w[e >> 2] |= v << (8 * (e & 3));
+        }
       }
     }
     dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -713,11 +871,10 @@ __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-template <int AK, int MB, int NW, int KW, int EPI>
+template <int AK, int MB, int NB, int NW, int KW, int EPI>
 void skinny(const GemmParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_skinny<AK, MB, NW, KW, EPI>), grid, dim3(64 * NW * KW), 0, st, p);
+  hipLaunchKernelGGL((k_skinny<AK, MB, NB, NW, KW, EPI>), grid, dim3(64 * NW * KW), 0, st, p);
 }
-
 
 template <int AK, int EPI>
 void tiled(const GemmParams& p, dim3 grid, hipStream_t st) {
@@ -725,27 +882,43 @@ void tiled(const GemmParams& p, dim3 grid, hipStream_t st) {
 }
 
 // Decode plan: three weight-streaming launches plus the down-projection
-// finish (launched by the caller between A1 and A6).
+// finish (launched by the caller between A1 and A6).  Many short per-wave
+// weight runs keep the most bytes in flight: A1 gives each 1024-thread
+// workgroup one 32-column block and splits its K range over 16 waves
+// (fewer when more 32-row blocks fill the registers); A6 uses 64-column
+// tiles of 128 columns (two blocks per wave and two waves across, so every
+// RoPE pair of q^R lies in one tile) with K over 4 waves; A8 puts 8 (or 4) waves on different column blocks of one
+// head.  Every tile's LDS stays near 70 KB, two workgroups per CU.
+template <int MB>
+constexpr int a1_kw() { return MB >= 4 ? 2 : (MB == 2 ? 4 : 8); }
+template <int MB>
+constexpr int a6_kw() { return MB >= 4 ? 1 : (MB == 2 ? 2 : 4); }
+constexpr int kA6Cols = 128;  // A6 tile: two column blocks per wave, two waves across
+template <int MB>
+constexpr int a8_nw() { return 4; }
+constexpr int kA1Cols = 64;  // A1 tile width (two column blocks per wave)
+
 template <int MB>
 void skinny_a1(const GemmParams& g1, const MlaPlan& pl, hipStream_t st) {
-  const unsigned nt = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + 63) / 64);
-  skinny<A_BF16, MB, 2, 2, EPI_PARTIAL>(g1, dim3(nt, pl.ksplit, 1), st);
+  const unsigned nt = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + kA1Cols - 1) / kA1Cols);
+  skinny<A_BF16, MB, 2, 1, a1_kw<MB>(), EPI_PARTIAL>(g1, dim3(nt, pl.ksplit, 1), st);
 }
 template <int MB>
 void skinny_a6(const GemmParams& g6, bool quant, hipStream_t st) {
-  const unsigned nt = static_cast<unsigned>((g6.N0 + 63) / 64);
+  const unsigned nt = static_cast<unsigned>((g6.N0 + kA6Cols - 1) / kA6Cols);
   if (quant)
-    skinny<A_I8, MB, 2, 2, EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+    skinny<A_I8, MB, 2, 2, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
   else
-    skinny<A_BF16, MB, 2, 2, EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+    skinny<A_BF16, MB, 2, 2, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
 }
 template <int MB>
 void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
-  const unsigned nt = static_cast<unsigned>((g8.N0 + 127) / 128);
+  constexpr int NW = a8_nw<MB>();
+  const unsigned nt = static_cast<unsigned>((g8.N0 + 32 * NW - 1) / (32 * NW));
   if (quant)
-    skinny<A_F32SPLIT, MB, 4, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
+    skinny<A_F32SPLIT, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
   else
-    skinny<A_BF16, MB, 4, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
+    skinny<A_BF16, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
 }
 
 }  // namespace
@@ -753,7 +926,7 @@ void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
 int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
                        int elem_bytes, hipStream_t stream) {
   const int G = 16 / elem_bytes;
-  const int64_t total = batch * (K / G) * N;
+  const int64_t total = batch * (K / G) * ((N + 31) / 32) * 32;
   if (total == 0) return QKVNR_OK;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
@@ -772,41 +945,47 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
   const int64_t steps = a->He / 16;
   if (pl.skinny) {
-    // Spread the down projection's weight stream over ~3 workgroups per CU:
-    // split K so that (column tiles x splits) is about 768 workgroups, with
-    // each split a multiple of 16 k-steps (2 waves x 8 steps in flight).
-    const int64_t ntiles = (a->Hcq + 63) / 64 + (a->Hckv + a->Dr + 63) / 64;
-    int64_t want = 768 / (ntiles > 0 ? ntiles : 1);
-    if (want < 1) want = 1;
-    int64_t sps = (steps + want - 1) / want;
-    sps = ((sps + 15) / 16) * 16;
-    if (sps < 16) sps = 16;
-    pl.steps_per_split = sps;
-    pl.ksplit = static_cast<int>((steps + sps - 1) / sps);
+    // Split the down projection over K so that (64-column tiles x splits)
+    // stays within one wave of workgroups over the 256 CUs (no tail round),
+    // at most FIN_MAXSPLIT splits (the finish kernel sums them) and at least
+    // one k-step per wave.
+    const int kw = pl.mb >= 4 ? 2 : (pl.mb == 2 ? 4 : 8);
+    const int64_t ntiles = (a->Hcq + kA1Cols - 1) / kA1Cols + (a->Hckv + a->Dr + kA1Cols - 1) / kA1Cols;
+    int64_t ks = 256 / (ntiles > 0 ? ntiles : 1);
+    if (ks > FIN_MAXSPLIT) ks = FIN_MAXSPLIT;
+    if (ks > steps / kw) ks = steps / kw;
+    if (ks < 1) ks = 1;
+    pl.steps_per_split = (steps + ks - 1) / ks;
+    pl.ksplit = static_cast<int>((steps + pl.steps_per_split - 1) / pl.steps_per_split);
   } else {
     pl.steps_per_split = steps;
     pl.ksplit = 1;
   }
+  pl.rows = pl.skinny ? 32 * pl.mb : T;
   size_t off = 0;
   if (a->weight_layout == MLA_WEIGHT_ND) {
+    // packed copies: columns padded to whole 32-column blocks
     const size_t eb_uq = quant ? 1 : 2;
+    auto pad32 = [](int64_t n) { return static_cast<size_t>((n + 31) / 32 * 32); };
     pl.off_wdq = off;
-    off += align256(static_cast<size_t>(a->He * a->Hcq) * 2);
+    off += align256(static_cast<size_t>(a->He) * pad32(a->Hcq) * 2);
     pl.off_wdkvkr = off;
-    off += align256(static_cast<size_t>(a->He * (a->Hckv + a->Dr)) * 2);
+    off += align256(static_cast<size_t>(a->He) * pad32(a->Hckv + a->Dr) * 2);
     pl.off_wuqqr = off;
-    off += align256(static_cast<size_t>(a->Hcq * a->N * (a->D + a->Dr)) * eb_uq);
+    off += align256(static_cast<size_t>(a->Hcq) * pad32(a->N * (a->D + a->Dr)) * eb_uq);
     pl.off_wuk = off;
-    off += align256(static_cast<size_t>(a->N * a->D * a->Hckv) * 2);
+    off += align256(static_cast<size_t>(a->N * a->D) * pad32(a->Hckv) * 2);
   }
   pl.off_part = off;
   off += align256(static_cast<size_t>(pl.ksplit) * T * ntot * 4);
   pl.off_cq = off;
-  off += align256(static_cast<size_t>(T * a->Hcq) * (quant ? 1 : 2));
+  off += align256(static_cast<size_t>(pl.rows * a->Hcq) * (quant ? 1 : 2));
   pl.off_cq_scale = off;
   off += align256(static_cast<size_t>(T) * 4);
   pl.off_qc = off;
-  off += align256(static_cast<size_t>(T * a->N * a->D) * (quant ? 4 : 2));
+  off += align256(static_cast<size_t>(pl.rows * a->N * a->D) * (quant ? 4 : 2));
+  pl.off_xfrag = off;
+  if (pl.skinny) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
   pl.total = T > 0 ? off : 0;
   return pl;
 }
@@ -849,9 +1028,18 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   void* qc = ws + pl.off_qc;
 
   // ---- A1: x . [W^DQ | W^DKV_KR] -> fp32 (partials) ----
+  // The skinny plan reads every A operand in fragment layout: x is packed
+  // by k_pack_a, c^Q by the finish kernel and q^C by A6's epilogue.
+  const bool frag = pl.skinny;
+  const int64_t mblocks = pl.rows / 32;
   GemmParams g1{};
   g1.A = a->token_x;
   g1.lda = a->He;
+  if (frag) {
+    g1.A = ws + pl.off_xfrag;
+    g1.a_frag = 1;
+    g1.a_mbs = a->He * 64;
+  }
   g1.B0 = wdq;
   g1.N0 = a->Hcq;
   g1.B1 = wdkvkr;
@@ -882,6 +1070,13 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   g6.qc_f32 = quant ? 1 : 0;
   g6.qr_out = static_cast<uint16_t*>(a->query_rope);
   g6.qr_ld = a->N * a->Dr;
+  if (frag) {
+    g6.a_frag = 1;
+    g6.a_mbs = a->Hcq * (quant ? 32 : 64);  // 32 rows x Hcq int8 / bf16
+    g6.qc_frag = 1;
+    g6.qc_D = a->D;
+    g6.qc_mblocks = mblocks;
+  }
 
   // ---- A8: per head q^C[:, n] . W^UK[n] -> query ----
   GemmParams g8{};
@@ -890,7 +1085,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   g8.a_bstride = a->D;
   g8.B0 = wuk;
   g8.N0 = a->Hckv;
-  g8.b_bstride = (a->D / 8) * a->Hckv;
+  g8.b_bstride = ((a->Hckv + 31) / 32) * (a->D / 8) * 32;  // chunks per packed head
   g8.M = T;
   g8.K = a->D;
   g8.ntiles0 = 1 << 30;
@@ -898,6 +1093,11 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   g8.q_out = static_cast<uint16_t*>(a->query);
   g8.q_ld = a->N * a->Hckv;
   g8.q_bstride = a->Hckv;
+  if (frag) {
+    g8.a_frag = 1;
+    g8.a_mbs = a->D * (quant ? 128 : 64);  // 32 rows x D fp32 / bf16
+    g8.a_zs = mblocks * g8.a_mbs;
+  }
 
   // ---- finish of A1 ----
   FinishParams f{};
@@ -923,6 +1123,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   f.cq_bf16 = static_cast<uint16_t*>(cq);
   f.cq_i8 = static_cast<int8_t*>(cq);
   f.cq_scale = cq_scale;
+  f.cq_frag = frag ? 1 : 0;
   f.dbg_cq_i8 = a->dbg_cq_int8;
   f.dbg_cq_scale = a->dbg_cq_scale;
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
@@ -930,23 +1131,29 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   // Phase events (instrumentation only).
   auto mark = [&](int i) {
     if (i < a->n_phase_events && a->phase_events[i] != nullptr)
-      hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st);
+      (void)hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st);
   };
 
   auto finish = [&]() {
     const dim3 grid(static_cast<unsigned>(T));
     if (qm == 0)
-      hipLaunchKernelGGL(k_down_finish<0>, grid, dim3(256), fin_smem, st, f);
+      hipLaunchKernelGGL(k_down_finish<0>, grid, dim3(FIN_THREADS), fin_smem, st, f);
     else if (qm == 1)
-      hipLaunchKernelGGL(k_down_finish<1>, grid, dim3(256), fin_smem, st, f);
+      hipLaunchKernelGGL(k_down_finish<1>, grid, dim3(FIN_THREADS), fin_smem, st, f);
     else
-      hipLaunchKernelGGL(k_down_finish<2>, grid, dim3(256), fin_smem, st, f);
+      hipLaunchKernelGGL(k_down_finish<2>, grid, dim3(FIN_THREADS), fin_smem, st, f);
   };
 
   const int nh = static_cast<int>(a->N);
   mark(MLA_PHASE_START);
   if (pl.skinny) {
-    g1.ntiles0 = static_cast<int>((g1.N0 + 63) / 64);
+    {
+      const int64_t chunks = mblocks * 32 * (a->He / 8);
+      hipLaunchKernelGGL(k_pack_a, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                         st, static_cast<const uint16_t*>(a->token_x),
+                         reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, a->He, mblocks);
+    }
+    g1.ntiles0 = static_cast<int>((g1.N0 + kA1Cols - 1) / kA1Cols);
     switch (pl.mb) {
       case 1: skinny_a1<1>(g1, pl, st); break;
       case 2: skinny_a1<2>(g1, pl, st); break;

@@ -57,12 +57,6 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                     ET::pack(f[6], f[7]));
 }
 
-__device__ __forceinline__ void load8f(const float* __restrict__ p, float* f) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-}
 
 // v / scale (+ offset), round half to even, saturate to int8; 8 lanes' worth
 // packed into 8 bytes.
@@ -70,8 +64,8 @@ template <int QM>
 __device__ __forceinline__ uint2 quant8(const float* v, const float* __restrict__ sc,
                                         const float* __restrict__ off) {
   float s[8], o[8];
-  load8f(sc, s);
-  if (QM == 2) load8f(off, o);
+  ld8f(sc, s);
+  if (QM == 2) ld8f(off, o);
   int c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -102,7 +96,7 @@ __global__ __launch_bounds__(256) void k_qkv_rmsnorm_rope_cache(QkvParams p) {
   unpack8<ET>(ld16(p.gk + 8 * j), gk);
   unpack8<ET>(ld16(p.gk + 8 * jp), gkp);
 
-  const int64_t slot = p.index[t];
+  const int64_t slot = gld(p.index + t);
   const bool write_cache = slot >= 0 && slot < p.slots;
 
   const uint16_t* __restrict__ src = p.qkv + t * static_cast<int64_t>(H) * kD + 8 * j;
@@ -158,7 +152,7 @@ __global__ __launch_bounds__(256) void k_qkv_rmsnorm_rope_cache(QkvParams p) {
               st16(static_cast<uint16_t*>(p.kc) + o, packed);
             } else {
               const uint2 q8 = quant8<QM>(y, p.ks + hk * kD + 8 * j, p.ko + hk * kD + 8 * j);
-              *reinterpret_cast<uint2*>(static_cast<int8_t*>(p.kc) + o) = q8;
+              st8(static_cast<int8_t*>(p.kc) + o, q8);
             }
           }
         }
@@ -171,7 +165,7 @@ __global__ __launch_bounds__(256) void k_qkv_rmsnorm_rope_cache(QkvParams p) {
             st16(static_cast<uint16_t*>(p.vc) + o, raw[c]);
           } else {
             const uint2 q8 = quant8<QM>(x, p.vs + hv * kD + 8 * j, p.vo + hv * kD + 8 * j);
-            *reinterpret_cast<uint2*>(static_cast<int8_t*>(p.vc) + o) = q8;
+            st8(static_cast<int8_t*>(p.vc) + o, q8);
           }
         }
       }

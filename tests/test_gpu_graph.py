@@ -1,0 +1,74 @@
+"""HIP-graph capture of the library calls: every replay must reproduce the
+eager result bit for bit, with eager work (output clearing, cache restore,
+another eager call) between replays."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import qkv_norm_rope_amd as qn
+from tests import gpu_helpers as gh
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr",
+         "rmsnorm_gamma_cq", "rmsnorm_gamma_ckv", "rope_sin", "rope_cos",
+         "cache_index", "kv_cache", "kr_cache")
+
+
+def _prepared(w, d):
+    cfg = w.cfg
+    for k in ("weight_dq", "weight_dkv_kr", "weight_uq_qr", "weight_uk"):
+        d[k] = qn.mla_pack_weight(d[k])
+    q = torch.empty((cfg.T, cfg.N, cfg.Hckv), dtype=torch.bfloat16,
+                    device="cuda")
+    qr = torch.empty((cfg.T, cfg.N, cfg.Dr), dtype=torch.bfloat16,
+                     device="cuda")
+    kw = {}
+    if cfg.quant_mode != "none":
+        kw = dict(dequant_scale_w_uq_qr=d["dequant_scale_w_uq_qr"],
+                  smooth_scales_cq=d["smooth_scales_cq"])
+    if cfg.quant_mode == "partial_kv_int8":
+        kw.update(quant_scale_ckv=d["quant_scale_ckv"],
+                  quant_scale_ckr=d["quant_scale_ckr"])
+    return qn.PreparedMlaPrologV2(*[d[k] for k in NAMES], q, qr,
+                                  quant_mode=cfg.quant_mode,
+                                  rmsnorm_epsilon_cq=cfg.eps_cq,
+                                  rmsnorm_epsilon_ckv=cfg.eps_ckv, **kw)
+
+
+@pytest.mark.parametrize("key", [1, 3, "mla_mid_dsv3"])
+def test_mla_graph_replays_match_eager(key):
+    w = make_workload(key)
+    gh.announce(f"graph replay {w.cfg.name}")
+    d = gh.upload(w)
+    kv0, kr0 = d["kv_cache"].clone(), d["kr_cache"].clone()
+    call = _prepared(w, d)
+    q, qr = call()
+    torch.cuda.synchronize()
+    ref = {"q": gh.raw_bits(q), "qr": gh.raw_bits(qr),
+           "kv": gh.raw_bits(d["kv_cache"]), "kr": gh.raw_bits(d["kr_cache"])}
+    # a second, independent eager call used as eager work between replays
+    d2 = gh.upload(w)
+    other = _prepared(w, d2)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        q.zero_()
+        qr.zero_()
+        d["kv_cache"].copy_(kv0)
+        d["kr_cache"].copy_(kr0)
+        other()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gh.raw_bits(q), ref["q"], err_msg=f"rep {rep}")
+        np.testing.assert_array_equal(gh.raw_bits(qr), ref["qr"], err_msg=f"rep {rep}")
+        np.testing.assert_array_equal(gh.raw_bits(d["kv_cache"]), ref["kv"])
+        np.testing.assert_array_equal(gh.raw_bits(d["kr_cache"]), ref["kr"])
+    del g

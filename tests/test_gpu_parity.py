@@ -31,7 +31,8 @@ def _before(dev, names):
 # ---- weight packing: pure index work, bit-exact ----------------------------
 
 @pytest.mark.parametrize("shape,dtype", [((64, 48), "bf16"), ((3, 32, 40), "bf16"),
-                                         ((96, 80), "int8"), ((7168, 64), "bf16")])
+                                         ((96, 80), "int8"), ((7168, 64), "bf16"),
+                                         ((32, 576), "bf16")])
 def test_pack_weight_bit_exact(shape, dtype):
     gh.announce(f"pack {shape} {dtype}")
     rng = np.random.default_rng(5)
@@ -48,8 +49,12 @@ def test_pack_weight_bit_exact(shape, dtype):
     got = gh.raw_bits(p).reshape(-1)
     src = bits.reshape((-1,) + shape[-2:])
     B, K, N = src.shape
-    # expected: element (k, n) at ((k // G) * N + n) * G + k % G per batch
-    want = src.reshape(B, K // G, G, N).transpose(0, 1, 3, 2).reshape(-1)
+    Np = (N + 31) // 32 * 32
+    assert p.shape == tuple(shape[:-1]) + (Np,)
+    # expected: element (k, n) at ((n//32 * K/G + k//G) * 32 + n%32) * G + k%G
+    pad = np.zeros((B, K, Np), dtype=src.dtype)
+    pad[:, :, :N] = src
+    want = pad.reshape(B, K // G, G, Np // 32, 32).transpose(0, 3, 1, 4, 2).reshape(-1)
     np.testing.assert_array_equal(got.view(want.dtype), want)
 
 
