@@ -183,10 +183,22 @@ typedef struct MlaPrologV2Args {
    * ND-layout weight packing happens before MLA_PHASE_START. */
   void* const* phase_events;
   int32_t n_phase_events;
-  int32_t reserved1;                /* must be 0 */
+
+  /* Execution plan: MLA_PLAN_AUTO and MLA_PLAN_MULTI_KERNEL use separate
+   * kernels per step; MLA_PLAN_FUSED requires the persistent fused decode
+   * kernel (T <= 32, non-quantised; QKVNR_ERR_UNSUPPORTED otherwise).  Both
+   * plans meet the same accuracy; the fused one is currently slower. */
+  int32_t plan;
 } MlaPrologV2Args;
 
-/* Phase boundaries of one mla_prolog_v2 call, in launch order. */
+enum { MLA_PLAN_AUTO = 0, MLA_PLAN_MULTI_KERNEL = 1, MLA_PLAN_FUSED = 2 };
+
+/* Phase boundaries of one mla_prolog_v2 call, in launch order.  In the
+ * multi-kernel plan each boundary follows one kernel.  The fused plan runs a
+ * small prologue (x re-layout, barrier reset) and one persistent kernel:
+ * MLA_PHASE_START precedes the prologue, MLA_PHASE_AFTER_DOWN,
+ * MLA_PHASE_AFTER_NORM and MLA_PHASE_AFTER_UQQR are recorded together after
+ * the prologue, and MLA_PHASE_AFTER_UK after the persistent kernel. */
 enum {
   MLA_PHASE_START = 0,        /* before the first kernel */
   MLA_PHASE_AFTER_DOWN = 1,   /* after x . [W^DQ | W^DKV_KR] */
@@ -195,6 +207,18 @@ enum {
   MLA_PHASE_AFTER_UK = 4,     /* after q^C . W^UK per head (end of call) */
   MLA_PHASE_COUNT = 5
 };
+
+/* Workspace bytes [0, 8) hold the fused plan's grid-barrier words.  After a
+ * fused call has completed on the stream, the 32-bit word at byte offset 4
+ * is nonzero if and only if a barrier wait timed out (a workgroup never
+ * arrived within ~0.25 s); the outputs of that call are then invalid.  The
+ * fused kernel assumes its workgroups (one per CU) can all be resident at
+ * once; the timeout guarantees it finishes when they cannot.  Words
+ * [2, 18) (bytes 8..71) then hold eight 64-bit readings of the device's
+ * constant 100 MHz clock taken by workgroup 0 at the fused kernel's phase
+ * boundaries: start, after the down projection, after the first barrier,
+ * after the norm/cache phase, after the second barrier, after the up
+ * projection, after the third barrier, and at the end (profiling aid). */
 
 /* Bytes of device workspace mla_prolog_v2() needs for these arguments
  * (depends on the dims, T, quant mode and weight layout).  Writes *bytes

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     MLA_PHASES,
+    MLA_PLAN,
     MLA_QUANT,
     MLA_WEIGHT_ND,
     MLA_WEIGHT_PACKED_K16,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     QkvRmsNormRopeCacheArgs,
     QkvnrError,
     load_library,
+    fused_barrier_timed_out,
     mla_pack_weight,
     mla_prolog_v2,
     mla_prolog_v2_args,

@@ -30,6 +30,7 @@ STATUS_NAMES = {
 MLA_QUANT = {"none": 0, "partial_kv_bf16": 1, "partial_kv_int8": 2,
              "full_kv_bf16": 3, "full_kv_int8": 4}
 MLA_WEIGHT_ND, MLA_WEIGHT_PACKED_K16 = 0, 1
+MLA_PLAN = {"auto": 0, "multi_kernel": 1, "fused": 2}
 MLA_PHASES = ("start", "after_down", "after_norm", "after_uqqr", "after_uk")
 QKV_QUANT = {"none": 0, "symmetric": 1, "asymmetric": 2}
 QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
@@ -66,7 +67,7 @@ class MlaPrologV2Args(ctypes.Structure):
         ("query", _vp), ("query_rope", _vp), ("dequant_scale_q_nope", _vp),
         ("dbg_cq_int8", _vp), ("dbg_cq_scale", _vp),
         ("phase_events", ctypes.POINTER(_vp)), ("n_phase_events", ctypes.c_int32),
-        ("reserved1", ctypes.c_int32),
+        ("plan", ctypes.c_int32),
     ]
 
 
@@ -200,7 +201,7 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
                        dequant_scale_w_uq_qr=None, quant_scale_ckv=None,
                        quant_scale_ckr=None, smooth_scales_cq=None,
                        dbg_cq_int8=None, dbg_cq_scale=None, cache_mode=None,
-                       B=None, S=None) -> MlaPrologV2Args:
+                       B=None, S=None, plan="auto") -> MlaPrologV2Args:
     """Fill the C struct from tensors.  Dims come from the tensor shapes:
     token_x (T, He) or (B, S, He); weight_dq (He, Hcq); weight_uk
     (N, D, Hckv); rope tables (T, Dr); caches (BlockNum, BlockSize, Nkv, H).
@@ -227,6 +228,7 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
     a.rmsnorm_epsilon_cq = float(rmsnorm_epsilon_cq)
     a.rmsnorm_epsilon_ckv = float(rmsnorm_epsilon_ckv)
     a.cache_mode = cache_mode.encode() if cache_mode else None
+    a.plan = MLA_PLAN[plan] if isinstance(plan, str) else int(plan)
     if T > 0:
         a.token_x = _ptr(token_x)
         a.rope_sin = _ptr(rope_sin)
@@ -270,7 +272,7 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   quant_scale_ckr=None, smooth_scales_cq=None,
                   query=None, query_rope=None, workspace=None,
                   return_cq_quant=False, cache_mode=None, stream=None,
-                  phase_events=None):
+                  phase_events=None, plan="auto"):
     """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
 
     Returns (query, query_rope), plus (cq_int8, cq_scale) when
@@ -307,7 +309,7 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
         smooth_scales_cq=smooth_scales_cq, dbg_cq_int8=dbg8, dbg_cq_scale=dbgs,
         cache_mode=cache_mode,
         B=lead[0] if len(lead) == 2 else None,
-        S=lead[1] if len(lead) == 2 else None)
+        S=lead[1] if len(lead) == 2 else None, plan=plan)
     if phase_events:
         handles = (_vp * len(phase_events))(*[e.cuda_event for e in phase_events])
         a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
@@ -321,6 +323,13 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
     if return_cq_quant:
         return query, query_rope, dbg8, dbgs
     return query, query_rope
+
+
+def fused_barrier_timed_out(workspace: torch.Tensor) -> bool:
+    """True if the last fused-plan call on this workspace had a grid-barrier
+    wait time out (include/qkvnr.h: workspace word at byte offset 4).
+    Synchronises with the device copy."""
+    return bool(workspace[4:8].view(torch.int32).item())
 
 
 class PreparedMlaPrologV2:

@@ -27,8 +27,8 @@ constexpr int64_t kDimCap = int64_t(1) << 30;
 
 int validate_mla(const MlaPrologV2Args* a) {
   if (a == nullptr) return QKVNR_ERR_NULL_ARG;
-  if (a->struct_size != sizeof(MlaPrologV2Args) || a->reserved0 != 0 || a->reserved1 != 0)
-    return QKVNR_ERR_BAD_STRUCT;
+  if (a->struct_size != sizeof(MlaPrologV2Args) || a->reserved0 != 0) return QKVNR_ERR_BAD_STRUCT;
+  if (a->plan < MLA_PLAN_AUTO || a->plan > MLA_PLAN_FUSED) return QKVNR_ERR_BAD_MODE;
   if (a->n_phase_events < 0 || (a->n_phase_events > 0 && a->phase_events == nullptr))
     return QKVNR_ERR_NULL_ARG;
   if (a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8)
@@ -70,6 +70,7 @@ int validate_mla(const MlaPrologV2Args* a) {
       a->dequant_scale_q_nope)
     return QKVNR_ERR_RESERVED_NONNULL;
 
+  if (a->plan == MLA_PLAN_FUSED && !mla_fused_supported(a)) return QKVNR_ERR_UNSUPPORTED;
   if (T == 0) return QKVNR_OK;  // empty tensors are allowed; nothing runs
   const void* need[] = {a->token_x,   a->weight_dq,       a->weight_uq_qr,      a->weight_uk,
                         a->weight_dkv_kr, a->rmsnorm_gamma_cq, a->rmsnorm_gamma_ckv, a->rope_sin,

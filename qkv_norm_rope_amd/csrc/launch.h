@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/qkvnr.h"
+#include "qkvnr.h"
 
 namespace qkvnr {
 
@@ -21,6 +21,7 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
 // split-K factor of the down projection and the workspace carve-up.  A pure
 // function of the arguments, so workspace sizing and execution agree.
 struct MlaPlan {
+  bool fused;         // persistent fused decode kernel (T <= 32, bf16)
   bool skinny;        // decode-sized T: weight-streaming kernels
   int mb;             // 32-row blocks held per wave (skinny only)
   int ksplit;         // down-projection split-K factor
@@ -29,11 +30,22 @@ struct MlaPlan {
   size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
   size_t off_part, off_cq, off_cq_scale, off_qc;
   size_t off_xfrag;   // token_x in fragment layout (skinny plan)
+  size_t off_fused;   // start of the fused path's region (fused plan)
   int64_t rows;       // token rows padded to the plan's 32-row blocks
   size_t total;
 };
 
 MlaPlan make_mla_plan(const MlaPrologV2Args* a);
+
+// Fused decode path (mla_decode_fused.hip).
+struct FusedLayout {
+  size_t off_bar, off_part, off_cq, off_qc, off_yrope, off_xfrag, total;
+};
+bool mla_fused_supported(const MlaPrologV2Args* a);
+void mla_fused_layout(const MlaPrologV2Args* a, int64_t ksplit, FusedLayout* layout);
+int launch_mla_decode_fused(const MlaPrologV2Args* a, const MlaPlan& plan, void* workspace,
+                            const void* wdq, const void* wdkvkr, const void* wuqqr,
+                            const void* wuk, hipStream_t stream);
 
 // Launch the prolog; arguments validated, workspace large enough.
 int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& plan, void* workspace,

@@ -24,12 +24,12 @@
 // column are one 16-byte chunk, which is exactly one lane's MFMA operand.
 #include "device_common.h"
 #include "launch.h"
+#include "mla_device.h"
 
 namespace qkvnr {
 
 namespace {
 
-enum AKind { A_BF16 = 0, A_I8 = 1, A_F32SPLIT = 2 };
 enum EpiKind { EPI_PARTIAL = 0, EPI_UQQR = 1, EPI_UK = 2 };
 
 struct GemmParams {
@@ -78,43 +78,6 @@ struct GemmParams {
   int64_t q_ld;     // N*Hckv
   int64_t q_bstride;  // Hckv (per head)
 };
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-__device__ __forceinline__ i32x4_t as_i32x4(uint4 v) { return __builtin_bit_cast(i32x4_t, v); }
-
-// Split 8 fp32 values into bf16 hi + bf16 lo (hi + lo carries ~16 bits).
-__device__ __forceinline__ void split8(const float4 a, const float4 b, uint4& hi, uint4& lo) {
-  const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint16_t h0 = f32_to_bf16(f[2 * i]), h1 = f32_to_bf16(f[2 * i + 1]);
-    const float r0 = f[2 * i] - bf16_to_f32(h0), r1 = f[2 * i + 1] - bf16_to_f32(h1);
-    h[i] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-    l[i] = pack_bf16x2(r0, r1);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-template <int AK>
-struct AccT {
-  typedef f32x16_t type;
-};
-template <>
-struct AccT<A_I8> {
-  typedef i32x16_t type;
-};
-
-// acc += A(16B/lane) x B(16B/lane) for one MFMA k-step.
-template <int AK>
-__device__ __forceinline__ void mfma_step(typename AccT<AK>::type& acc, uint4 a, uint4 b) {
-  if constexpr (AK == A_I8) {
-    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(as_i32x4(a), as_i32x4(b), acc, 0, 0, 0);
-  } else {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Epilogue over 8 consecutive output columns of one row.  `v` are the raw
@@ -962,7 +925,21 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     pl.ksplit = 1;
   }
   pl.rows = pl.skinny ? 32 * pl.mb : T;
+  // The persistent fused kernel is opt-in: on this part its grid barriers
+  // need a whole-L2 writeback and invalidate per workgroup (the XCD L2s are
+  // not coherent with each other), which costs more than the kernel
+  // boundaries it removes.
+  pl.fused = a->plan == MLA_PLAN_FUSED && mla_fused_supported(a);
   size_t off = 0;
+  if (pl.fused) {
+    // barrier words first (workspace bytes [0, 8)), then the fused region
+    FusedLayout L;
+    mla_fused_layout(a, pl.ksplit, &L);
+    pl.off_fused = 0;
+    off = L.total;
+  } else {
+    off = 256;  // same leading reserve in every plan
+  }
   if (a->weight_layout == MLA_WEIGHT_ND) {
     // packed copies: columns padded to whole 32-column blocks
     const size_t eb_uq = quant ? 1 : 2;
@@ -975,6 +952,10 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     off += align256(static_cast<size_t>(a->Hcq) * pad32(a->N * (a->D + a->Dr)) * eb_uq);
     pl.off_wuk = off;
     off += align256(static_cast<size_t>(a->N * a->D) * pad32(a->Hckv) * 2);
+  }
+  if (pl.fused) {
+    pl.total = T > 0 ? off : 0;
+    return pl;
   }
   pl.off_part = off;
   off += align256(static_cast<size_t>(pl.ksplit) * T * ntot * 4);
@@ -1022,6 +1003,14 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     wuqqr = static_cast<const uint4*>(a->weight_uq_qr);
     wuk = static_cast<const uint4*>(a->weight_uk);
   }
+  // Phase events (instrumentation only).
+  auto mark = [&](int i) {
+    if (i < a->n_phase_events && a->phase_events[i] != nullptr)
+      (void)hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st);
+  };
+
+  if (pl.fused) return launch_mla_decode_fused(a, pl, workspace, wdq, wdkvkr, wuqqr, wuk, st);
+
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
   void* cq = ws + pl.off_cq;
   float* cq_scale = reinterpret_cast<float*>(ws + pl.off_cq_scale);
@@ -1127,12 +1116,6 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   f.dbg_cq_i8 = a->dbg_cq_int8;
   f.dbg_cq_scale = a->dbg_cq_scale;
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
-
-  // Phase events (instrumentation only).
-  auto mark = [&](int i) {
-    if (i < a->n_phase_events && a->phase_events[i] != nullptr)
-      (void)hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st);
-  };
 
   auto finish = [&]() {
     const dim3 grid(static_cast<unsigned>(T));

@@ -116,7 +116,8 @@ def mla_dims(cfg):
                 Dr=cfg.Dr)
 
 
-def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None):
+def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None,
+                plan="auto"):
     """Run the library on workload w.  Returns dict of device tensors."""
     cfg = w.cfg
     d = dev if dev is not None else upload(w)
@@ -144,7 +145,7 @@ def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None):
         quant_scale_ckv=d.get("quant_scale_ckv"),
         quant_scale_ckr=d.get("quant_scale_ckr"),
         smooth_scales_cq=d.get("smooth_scales_cq"),
-        return_cq_quant=quant != "none", workspace=workspace)
+        return_cq_quant=quant != "none", workspace=workspace, plan=plan)
     out = {"query": res[0], "query_rope": res[1], "kv_cache": d["kv_cache"],
            "kr_cache": d["kr_cache"]}
     if quant != "none":

@@ -174,6 +174,52 @@ def test_mla_T0_and_no_slots():
     np.testing.assert_array_equal(gh.raw_bits(qr1), gh.raw_bits(full["query_rope"]))
 
 
+FUSED_CASES = [0, 1, "mla_ragged_fused", "mla_wide_fused"]
+
+
+def _fused_case(key):
+    if key == "mla_ragged_fused":  # ragged dims, T = 21 (one partial 32-row block)
+        return make_workload(get_config("mla_ragged").replace(B=21, n_skip=2,
+                                                             seed=2011))
+    return make_workload(key)
+
+
+@pytest.mark.parametrize("key", FUSED_CASES)
+@pytest.mark.parametrize("plan", ["fused", "multi_kernel"])
+def test_mla_decode_plans(key, plan):
+    # T <= 32, non-quantised: both the persistent fused kernel and the
+    # multi-kernel plan must meet the oracle; the fused plan must report no
+    # barrier timeout.
+    w = _fused_case(key)
+    gh.announce(f"mla plan={plan} {w.cfg.name} T={w.cfg.T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    out = gh.run_mla_gpu(w, dev, plan=plan, workspace=ws)
+    torch.cuda.synchronize()
+    if plan == "fused":
+        assert not qn.fused_barrier_timed_out(ws)
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
+def test_mla_fused_repeat_and_rejects_quant():
+    # back-to-back fused calls on one workspace reuse the barrier words
+    w = make_workload(1)
+    gh.announce("mla fused repeated calls")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        o = gh.run_mla_gpu(w, gh.upload(w), plan="fused", workspace=ws)
+        torch.cuda.synchronize()
+        assert not qn.fused_barrier_timed_out(ws)
+        outs.append({k: gh.raw_bits(v) for k, v in o.items()})
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[2][k], err_msg=k)
+    wq = make_workload(3)
+    with pytest.raises(qn.QkvnrError):
+        gh.run_mla_gpu(wq, gh.upload(wq), plan="fused")
+
+
 def test_mla_packed_equals_nd():
     w = make_workload("mla_ragged")
     gh.announce("mla packed vs ND layouts")

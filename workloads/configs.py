@@ -130,6 +130,12 @@ CONFIGS = {
                               block_num=8, block_size=128, n_skip=5,
                               seed=2004, layout="BSH",
                               **{**_DSV3, "N": 16}),
+    # more heads and a wider kv latent than one pass of the fused decode
+    # kernel's 256 workgroups covers (second passes in its later phases)
+    "mla_wide_fused": MlaConfig("mla_wide_fused_T8", B=8, S=1, He=1024,
+                                Hcq=512, N=160, D=128, Hckv=1024, Dr=64,
+                                block_num=2, block_size=64, n_skip=1,
+                                seed=2005),
     "qkv_ragged": QkvConfig("qkv_ragged_B3_S50", B=3, S=50, Nq=4, Nk=2, Nv=2,
                             D=128, block_num=3, block_size=64,
                             quant_mode="symmetric", seed=2101),
