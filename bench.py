@@ -100,7 +100,8 @@ def prepare_mla_sets(w, n_sets, torch, qn, gh):
         "token_x": d["token_x"].view(cfg.B, cfg.S, cfg.He),
         "weight_dq": qn.mla_pack_weight(d["weight_dq"]),
         "weight_dkv_kr": qn.mla_pack_weight(d["weight_dkv_kr"]),
-        "weight_uq_qr": qn.mla_pack_weight(d["weight_uq_qr"]),
+        "weight_uq_qr": qn.mla_pack_weight_uq_qr(d["weight_uq_qr"], cfg.N,
+                                                 cfg.D, cfg.Dr),
         "weight_uk": qn.mla_pack_weight(d["weight_uk"]),
     }
     for k in ("rmsnorm_gamma_cq", "rmsnorm_gamma_ckv", "rope_sin", "rope_cos",

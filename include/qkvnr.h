@@ -67,7 +67,9 @@ enum {
   QKVNR_ERR_WORKSPACE_TOO_SMALL = -6,
   QKVNR_ERR_BAD_EPS = -7,           /* epsilon negative or not finite */
   QKVNR_ERR_BAD_STRUCT = -8,        /* struct_size does not match */
-  QKVNR_ERR_BAD_ALIGNMENT = -9,     /* a pointer is not 16-byte aligned */
+  QKVNR_ERR_BAD_ALIGNMENT = -9,     /* a pointer is not 16-byte aligned
+                                       (cache_index and dbg_cq_int8: 8,
+                                       dbg_cq_scale: 4) */
   QKVNR_ERR_LAUNCH_FAILED = -10,    /* hipGetLastError after a launch */
   QKVNR_ERR_BAD_INDEX = -11         /* host index check (debug flag) */
 };
@@ -114,7 +116,13 @@ enum {
  *   contiguous run, so a weight-streaming wave reads one contiguous stream.
  *   weight_uk packs each head's (D, Hckv) matrix this way, heads in order.
  *   A packed matrix holds K * NB * 32 elements.  This plays the role that the
- *   pages' FRACTAL_NZ weight format plays for their hardware. */
+ *   pages' FRACTAL_NZ weight format plays for their hardware.
+ *   weight_uq_qr is packed by mla_pack_weight_uq_qr(), which also reorders
+ *   the W^QR columns when Dr = 64: within each head, packed 32-column block
+ *   b (b = 0, 1) holds rope columns [16b, 16b + 16) followed by
+ *   [32 + 16b, 32 + 16b + 16), so every column and its RoPE partner (the
+ *   column Dr/2 away) sit in one 32-column block.  For Dr = 16 and 32 the
+ *   natural order already has that property and is kept. */
 enum { MLA_WEIGHT_ND = 0, MLA_WEIGHT_PACKED_K16 = 1 };
 
 typedef struct MlaPrologV2Args {
@@ -183,22 +191,10 @@ typedef struct MlaPrologV2Args {
    * ND-layout weight packing happens before MLA_PHASE_START. */
   void* const* phase_events;
   int32_t n_phase_events;
-
-  /* Execution plan: MLA_PLAN_AUTO and MLA_PLAN_MULTI_KERNEL use separate
-   * kernels per step; MLA_PLAN_FUSED requires the persistent fused decode
-   * kernel (T <= 32, non-quantised; QKVNR_ERR_UNSUPPORTED otherwise).  Both
-   * plans meet the same accuracy; the fused one is currently slower. */
-  int32_t plan;
 } MlaPrologV2Args;
 
-enum { MLA_PLAN_AUTO = 0, MLA_PLAN_MULTI_KERNEL = 1, MLA_PLAN_FUSED = 2 };
-
-/* Phase boundaries of one mla_prolog_v2 call, in launch order.  In the
- * multi-kernel plan each boundary follows one kernel.  The fused plan runs a
- * small prologue (x re-layout, barrier reset) and one persistent kernel:
- * MLA_PHASE_START precedes the prologue, MLA_PHASE_AFTER_DOWN,
- * MLA_PHASE_AFTER_NORM and MLA_PHASE_AFTER_UQQR are recorded together after
- * the prologue, and MLA_PHASE_AFTER_UK after the persistent kernel. */
+/* Phase boundaries of one mla_prolog_v2 call, in launch order; each one
+ * follows one kernel. */
 enum {
   MLA_PHASE_START = 0,        /* before the first kernel */
   MLA_PHASE_AFTER_DOWN = 1,   /* after x . [W^DQ | W^DKV_KR] */
@@ -207,18 +203,6 @@ enum {
   MLA_PHASE_AFTER_UK = 4,     /* after q^C . W^UK per head (end of call) */
   MLA_PHASE_COUNT = 5
 };
-
-/* Workspace bytes [0, 8) hold the fused plan's grid-barrier words.  After a
- * fused call has completed on the stream, the 32-bit word at byte offset 4
- * is nonzero if and only if a barrier wait timed out (a workgroup never
- * arrived within ~0.25 s); the outputs of that call are then invalid.  The
- * fused kernel assumes its workgroups (one per CU) can all be resident at
- * once; the timeout guarantees it finishes when they cannot.  Words
- * [2, 18) (bytes 8..71) then hold eight 64-bit readings of the device's
- * constant 100 MHz clock taken by workgroup 0 at the fused kernel's phase
- * boundaries: start, after the down projection, after the first barrier,
- * after the norm/cache phase, after the second barrier, after the up
- * projection, after the third barrier, and at the end (profiling aid). */
 
 /* Bytes of device workspace mla_prolog_v2() needs for these arguments
  * (depends on the dims, T, quant mode and weight layout).  Writes *bytes
@@ -243,6 +227,17 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
  * 16 / elem_bytes.  Device pointers; enqueued on `stream`. */
 int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K,
                     int64_t N, int32_t elem_bytes, void* stream);
+
+/* Pack weight_uq_qr, a row-major (Hcq, N*(D+Dr)) matrix of `elem_bytes` = 2
+ * (bf16) or 1 (int8) elements, into the MLA_WEIGHT_PACKED_K16 layout with
+ * the W^QR column order described above, at dst (a distinct buffer of
+ * Hcq * ceil(N*(D+Dr)/32)*32 elements).  Dims must pass the same checks as
+ * mla_prolog_v2 (D a multiple of 32, Dr in {16, 32, 64}, Hcq a multiple of
+ * 16 / elem_bytes), else QKVNR_ERR_BAD_SHAPE or QKVNR_ERR_UNSUPPORTED.
+ * Device pointers; enqueued on `stream`. */
+int mla_pack_weight_uq_qr(const void* src, void* dst, int64_t Hcq, int64_t N,
+                          int64_t D, int64_t Dr, int32_t elem_bytes,
+                          void* stream);
 
 /* ======================================================================= */
 /* QkvRmsNormRopeCache                                                      */

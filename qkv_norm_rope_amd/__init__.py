@@ -4,8 +4,9 @@ Python names mirror the C ABI in include/qkvnr.h:
 
 * :func:`mla_prolog_v2` - the MlaPrologV2 prolog (c^Q, q^N, q^R, c^KV and
   k^R with paged-cache scatter), non-quantised and partially quantised;
-* :func:`mla_pack_weight` - one-time packing of a (K, N) weight into the
-  MFMA-native K16 blocked layout the prolog streams;
+* :func:`mla_pack_weight` / :func:`mla_pack_weight_uq_qr` - one-time
+  packing of a (K, N) weight into the MFMA-native K16 blocked layout the
+  prolog streams;
 * :func:`qkv_rmsnorm_rope_cache` - the fused qkv split / RmsNorm / RoPE /
   quant / scatter op.
 
@@ -17,7 +18,6 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     MLA_PHASES,
-    MLA_PLAN,
     MLA_QUANT,
     MLA_WEIGHT_ND,
     MLA_WEIGHT_PACKED_K16,
@@ -27,8 +27,8 @@ from ._binding import (  # noqa: F401
     QkvRmsNormRopeCacheArgs,
     QkvnrError,
     load_library,
-    fused_barrier_timed_out,
     mla_pack_weight,
+    mla_pack_weight_uq_qr,
     mla_prolog_v2,
     mla_prolog_v2_args,
     mla_prolog_v2_workspace_size,

@@ -30,7 +30,6 @@ STATUS_NAMES = {
 MLA_QUANT = {"none": 0, "partial_kv_bf16": 1, "partial_kv_int8": 2,
              "full_kv_bf16": 3, "full_kv_int8": 4}
 MLA_WEIGHT_ND, MLA_WEIGHT_PACKED_K16 = 0, 1
-MLA_PLAN = {"auto": 0, "multi_kernel": 1, "fused": 2}
 MLA_PHASES = ("start", "after_down", "after_norm", "after_uqqr", "after_uk")
 QKV_QUANT = {"none": 0, "symmetric": 1, "asymmetric": 2}
 QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
@@ -38,6 +37,7 @@ QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
 EXPORTS = (
     "qkvnr_status_string", "qkvnr_version", "mla_prolog_v2_workspace_size",
     "mla_prolog_v2_validate", "mla_prolog_v2", "mla_pack_weight",
+    "mla_pack_weight_uq_qr",
     "qkv_rmsnorm_rope_cache_validate", "qkv_rmsnorm_rope_cache",
 )
 
@@ -67,7 +67,6 @@ class MlaPrologV2Args(ctypes.Structure):
         ("query", _vp), ("query_rope", _vp), ("dequant_scale_q_nope", _vp),
         ("dbg_cq_int8", _vp), ("dbg_cq_scale", _vp),
         ("phase_events", ctypes.POINTER(_vp)), ("n_phase_events", ctypes.c_int32),
-        ("plan", ctypes.c_int32),
     ]
 
 
@@ -121,6 +120,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_pack_weight.restype = ctypes.c_int
     lib.mla_pack_weight.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_int32,
                                     _vp]
+    lib.mla_pack_weight_uq_qr.restype = ctypes.c_int
+    lib.mla_pack_weight_uq_qr.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64,
+                                          ctypes.c_int32, _vp]
     lib.qkv_rmsnorm_rope_cache_validate.restype = ctypes.c_int
     lib.qkv_rmsnorm_rope_cache_validate.argtypes = [
         ctypes.POINTER(QkvRmsNormRopeCacheArgs)]
@@ -188,6 +190,24 @@ def mla_pack_weight(w: torch.Tensor, stream=None) -> torch.Tensor:
     return out
 
 
+def mla_pack_weight_uq_qr(w: torch.Tensor, N: int, D: int, Dr: int,
+                          stream=None) -> torch.Tensor:
+    """Pack weight_uq_qr (Hcq, N*(D+Dr)) into the K16 blocked layout with
+    the RoPE-partner column order of its W^QR part (include/qkvnr.h,
+    MLA_WEIGHT_PACKED_K16).  Returns (Hcq, Np), Np = N*(D+Dr) rounded up to
+    a multiple of 32, with w's dtype."""
+    lib = load_library()
+    if w.dim() != 2 or w.shape[1] != N * (D + Dr):
+        raise ValueError("weight_uq_qr must be (Hcq, N*(D+Dr))")
+    Hcq, NDR = w.shape
+    out = torch.empty((Hcq, (NDR + 31) // 32 * 32), dtype=w.dtype,
+                      device=w.device)
+    _check(lib.mla_pack_weight_uq_qr(_ptr(w), _ptr(out), Hcq, N, D, Dr,
+                                     w.element_size(), _stream(stream)),
+           "mla_pack_weight_uq_qr")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # MlaPrologV2
 # ---------------------------------------------------------------------------
@@ -201,7 +221,7 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
                        dequant_scale_w_uq_qr=None, quant_scale_ckv=None,
                        quant_scale_ckr=None, smooth_scales_cq=None,
                        dbg_cq_int8=None, dbg_cq_scale=None, cache_mode=None,
-                       B=None, S=None, plan="auto") -> MlaPrologV2Args:
+                       B=None, S=None) -> MlaPrologV2Args:
     """Fill the C struct from tensors.  Dims come from the tensor shapes:
     token_x (T, He) or (B, S, He); weight_dq (He, Hcq); weight_uk
     (N, D, Hckv); rope tables (T, Dr); caches (BlockNum, BlockSize, Nkv, H).
@@ -228,7 +248,6 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
     a.rmsnorm_epsilon_cq = float(rmsnorm_epsilon_cq)
     a.rmsnorm_epsilon_ckv = float(rmsnorm_epsilon_ckv)
     a.cache_mode = cache_mode.encode() if cache_mode else None
-    a.plan = MLA_PLAN[plan] if isinstance(plan, str) else int(plan)
     if T > 0:
         a.token_x = _ptr(token_x)
         a.rope_sin = _ptr(rope_sin)
@@ -272,7 +291,7 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   quant_scale_ckr=None, smooth_scales_cq=None,
                   query=None, query_rope=None, workspace=None,
                   return_cq_quant=False, cache_mode=None, stream=None,
-                  phase_events=None, plan="auto"):
+                  phase_events=None):
     """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
 
     Returns (query, query_rope), plus (cq_int8, cq_scale) when
@@ -309,7 +328,7 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
         smooth_scales_cq=smooth_scales_cq, dbg_cq_int8=dbg8, dbg_cq_scale=dbgs,
         cache_mode=cache_mode,
         B=lead[0] if len(lead) == 2 else None,
-        S=lead[1] if len(lead) == 2 else None, plan=plan)
+        S=lead[1] if len(lead) == 2 else None)
     if phase_events:
         handles = (_vp * len(phase_events))(*[e.cuda_event for e in phase_events])
         a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
@@ -323,13 +342,6 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
     if return_cq_quant:
         return query, query_rope, dbg8, dbgs
     return query, query_rope
-
-
-def fused_barrier_timed_out(workspace: torch.Tensor) -> bool:
-    """True if the last fused-plan call on this workspace had a grid-barrier
-    wait time out (include/qkvnr.h: workspace word at byte offset 4).
-    Synchronises with the device copy."""
-    return bool(workspace[4:8].view(torch.int32).item())
 
 
 class PreparedMlaPrologV2:

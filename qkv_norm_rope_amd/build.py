@@ -23,8 +23,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqkvnr.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["capi.hip", "qkv_rmsnorm_rope_cache.hip", "mla_prolog_v2.hip",
-           "mla_decode_fused.hip"]
+SOURCES = ["capi.hip", "qkv_rmsnorm_rope_cache.hip", "mla_prolog_v2.hip"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every device compile.

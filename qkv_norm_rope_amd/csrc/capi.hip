@@ -24,11 +24,11 @@ int check_cache_mode(const char* m) {
 }
 
 constexpr int64_t kDimCap = int64_t(1) << 30;
+constexpr int64_t kKCap = int64_t(1) << 22;
 
 int validate_mla(const MlaPrologV2Args* a) {
   if (a == nullptr) return QKVNR_ERR_NULL_ARG;
   if (a->struct_size != sizeof(MlaPrologV2Args) || a->reserved0 != 0) return QKVNR_ERR_BAD_STRUCT;
-  if (a->plan < MLA_PLAN_AUTO || a->plan > MLA_PLAN_FUSED) return QKVNR_ERR_BAD_MODE;
   if (a->n_phase_events < 0 || (a->n_phase_events > 0 && a->phase_events == nullptr))
     return QKVNR_ERR_NULL_ARG;
   if (a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8)
@@ -61,6 +61,9 @@ int validate_mla(const MlaPrologV2Args* a) {
   if (!(a->Dr == 16 || a->Dr == 32 || a->Dr == 64) || (a->N * a->D) % a->Dr != 0)
     return QKVNR_ERR_UNSUPPORTED;
   if ((a->Hcq + a->Hckv + a->Dr) * 4 > 64 * 1024) return QKVNR_ERR_UNSUPPORTED;
+  // GEMM K dims: the weight-streaming kernels address one column block's
+  // run and one A operand with 32-bit buffer offsets.
+  if (a->He > kKCap || a->Hcq > kKCap || a->D > kKCap) return QKVNR_ERR_UNSUPPORTED;
   if (!good_eps(a->rmsnorm_epsilon_cq) || !good_eps(a->rmsnorm_epsilon_ckv))
     return QKVNR_ERR_BAD_EPS;
 
@@ -70,7 +73,6 @@ int validate_mla(const MlaPrologV2Args* a) {
       a->dequant_scale_q_nope)
     return QKVNR_ERR_RESERVED_NONNULL;
 
-  if (a->plan == MLA_PLAN_FUSED && !mla_fused_supported(a)) return QKVNR_ERR_UNSUPPORTED;
   if (T == 0) return QKVNR_OK;  // empty tensors are allowed; nothing runs
   const void* need[] = {a->token_x,   a->weight_dq,       a->weight_uq_qr,      a->weight_uk,
                         a->weight_dkv_kr, a->rmsnorm_gamma_cq, a->rmsnorm_gamma_ckv, a->rope_sin,
@@ -92,6 +94,13 @@ int validate_mla(const MlaPrologV2Args* a) {
     if (!aligned16(p)) return QKVNR_ERR_BAD_ALIGNMENT;
   if (!aligned8(a->cache_index)) return QKVNR_ERR_BAD_ALIGNMENT;
   if (quant && (!aligned16(a->dequant_scale_w_uq_qr) || !aligned16(a->smooth_scales_cq)))
+    return QKVNR_ERR_BAD_ALIGNMENT;
+  if (slots && (!aligned16(a->kv_cache) || !aligned16(a->kr_cache))) return QKVNR_ERR_BAD_ALIGNMENT;
+  if (a->quant_mode == MLA_QUANT_PARTIAL_KV_INT8 &&
+      (!aligned16(a->quant_scale_ckv) || !aligned16(a->quant_scale_ckr)))
+    return QKVNR_ERR_BAD_ALIGNMENT;
+  if ((a->dbg_cq_int8 && !aligned8(a->dbg_cq_int8)) ||
+      (a->dbg_cq_scale && (reinterpret_cast<uintptr_t>(a->dbg_cq_scale) & 3u)))
     return QKVNR_ERR_BAD_ALIGNMENT;
   return QKVNR_OK;
 }
@@ -200,7 +209,23 @@ int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_
   if (src == nullptr || dst == nullptr) return QKVNR_ERR_NULL_ARG;
   if (!aligned16(dst) || (elem_bytes == 2 && (reinterpret_cast<uintptr_t>(src) & 1u)))
     return QKVNR_ERR_BAD_ALIGNMENT;
-  return launch_pack_weight(src, dst, batch, K, N, elem_bytes, static_cast<hipStream_t>(stream));
+  return launch_pack_weight(src, dst, batch, K, N, elem_bytes, N, 0,
+                            static_cast<hipStream_t>(stream));
+}
+
+int mla_pack_weight_uq_qr(const void* src, void* dst, int64_t Hcq, int64_t N, int64_t D,
+                          int64_t Dr, int32_t elem_bytes, void* stream) {
+  if (elem_bytes != 1 && elem_bytes != 2) return QKVNR_ERR_BAD_MODE;
+  if (Hcq < 0 || N < 0 || D < 0 || Dr < 0 || Hcq > kDimCap || N > 65535 || D > kDimCap ||
+      Dr > kDimCap || Hcq % (16 / elem_bytes) != 0)
+    return QKVNR_ERR_BAD_SHAPE;
+  if (Hcq * N == 0) return QKVNR_OK;
+  if (D % 32 != 0 || !(Dr == 16 || Dr == 32 || Dr == 64)) return QKVNR_ERR_UNSUPPORTED;
+  if (src == nullptr || dst == nullptr) return QKVNR_ERR_NULL_ARG;
+  if (!aligned16(dst) || (elem_bytes == 2 && (reinterpret_cast<uintptr_t>(src) & 1u)))
+    return QKVNR_ERR_BAD_ALIGNMENT;
+  return launch_pack_weight(src, dst, 1, Hcq, N * (D + Dr), elem_bytes, N * D, Dr,
+                            static_cast<hipStream_t>(stream));
 }
 
 int qkv_rmsnorm_rope_cache_validate(const QkvRmsNormRopeCacheArgs* args) {

@@ -133,4 +133,30 @@ __device__ __forceinline__ void st8f(float* p, const float* f) {
                          __float_as_uint(f[7])));
 }
 
+// Workgroup barrier ordering LDS accesses only: waits for this wave's LDS
+// (and scalar) operations, then s_barrier.  Unlike __syncthreads it does not
+// drain the wave's global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- buffer loads -------------------------------------------------------------
+// A raw buffer resource over [base, base + bytes): loads through it take a
+// per-lane VGPR offset plus a wave-uniform SGPR offset, so a stream's
+// per-step address is one scalar add, and a load whose offset falls outside
+// the range returns zeros instead of touching memory.  base must be
+// wave-uniform.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit data format (gfx9 family)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                          static_cast<int>(soff), 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace qkvnr

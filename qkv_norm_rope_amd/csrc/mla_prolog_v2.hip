@@ -93,30 +93,74 @@ struct Epilogue {
   }
 
   // Does this 8-column group need its RoPE partner, and where is it (offset
-  // in columns relative to the group)?
+  // in packed columns relative to the group)?  The rope region starts on a
+  // 32-column block and its packed order keeps every partner in the same
+  // block: Dr = 16 pairs columns 8 apart, Dr = 32 and the reordered Dr = 64
+  // pair columns 16 apart.
   static __device__ __forceinline__ int partner_offset(const GemmParams& p, int64_t gcol) {
     if (EPI != EPI_UQQR || gcol < p.ND) return 0;
-    const int i0 = static_cast<int>((gcol - p.ND) % p.Dr);
-    const int half = p.Dr >> 1;
-    return i0 < half ? half : -half;
+    const int w = static_cast<int>((gcol - p.ND) & 31);
+    const int hp = p.Dr >= 32 ? 16 : (p.Dr >> 1);
+    return (w % (2 * hp)) < hp ? hp : -hp;
   }
 
-  static __device__ __forceinline__ void dequant(const GemmParams& p, int64_t m, int64_t gcol,
-                                                 float* v) {
+  // Natural rope index (position within the head's Dr columns) of packed
+  // rope column r = gcol - ND.  For Dr = 64, packed block b of a head holds
+  // natural columns [16b, 16b + 16) then [32 + 16b, 32 + 16b + 16).
+  static __device__ __forceinline__ int rope_index(const GemmParams& p, int64_t r) {
+    const int pj = static_cast<int>(r % p.Dr);
+    if (p.Dr <= 32) return pj;
+    const int b = pj >> 5, w = pj & 31;
+    return w < 16 ? 16 * b + w : (p.Dr >> 1) + 16 * b + (w - 16);
+  }
+
+  // Everything the epilogue of one 8-column group reads from global memory
+  // besides the accumulators: the token's RoPE cos/sin for rope columns and,
+  // for int8 A, the token's scale and the columns' (and partners')
+  // dequant scales.  Loaded by prefetch() before the main loop so the
+  // epilogue does not wait on memory.
+  struct Pre {
+    uint4 c4, s4;
+    float cs;
+    float d[8], dp[8];
+  };
+
+  // Branch-free: every address is valid for any in-range (m, gcol), so the
+  // loads can stay in flight across the main loop (a load under a divergent
+  // branch would be waited for at the branch's join).
+  static __device__ __forceinline__ Pre prefetch(const GemmParams& p, int64_t m, int64_t gcol) {
+    Pre r{};
+    if constexpr (EPI == EPI_UQQR) {
+      const bool rope = gcol >= p.ND;
+      const int64_t rr = rope ? gcol - p.ND : 0;
+      const int i0 = rope_index(p, rr);
+      const int half = p.Dr >> 1;
+      const int64_t ncol = rope ? p.ND + (rr / p.Dr) * p.Dr + i0 : gcol;
+      const int64_t pcol = rope ? (i0 < half ? ncol + half : ncol - half) : gcol;
+      r.c4 = ld16(p.cosb + m * p.Dr + i0);
+      r.s4 = ld16(p.sinb + m * p.Dr + i0);
+      if constexpr (AK == A_I8) {
+        r.cs = gld(p.cq_scale + m);
+        ld8f(p.dq + ncol, r.d);
+        ld8f(p.dq + pcol, r.dp);
+      }
+    }
+    return r;
+  }
+
+  static __device__ __forceinline__ void dequant(float s, const float* d, float* v) {
     if constexpr (AK == A_I8) {
-      const float s = gld(p.cq_scale + m);
-      float d[8];
-      ld8f(p.dq + gcol, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = v[e] * s * d[e];
     }
   }
 
   // m: token row; gcol: column within this weight; ocol: output column in
-  // the partial buffer (gcol + offset of B1); z: batch (head) index.
+  // the partial buffer (gcol + offset of B1); z: batch (head) index; pre:
+  // prefetch(p, m, gcol).
   static __device__ __forceinline__ void apply(const GemmParams& p, int64_t m, int64_t gcol,
                                                int64_t ocol, int z, const uint32_t* raw,
-                                               const uint32_t* raw_partner) {
+                                               const uint32_t* raw_partner, const Pre& pre) {
     float v[8];
     to_float(raw, v);
     if constexpr (EPI == EPI_PARTIAL) {
@@ -126,8 +170,8 @@ struct Epilogue {
       st16(dst, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
     } else {  // EPI_UQQR
-      dequant(p, m, gcol, v);
       if (gcol < p.ND) {
+        dequant(pre.cs, pre.d, v);
         // 8 columns of q^C = 8 consecutive k of one head: one A chunk of the
         // per-head product in fragment layout, or 8 row-major elements.
         int64_t off;
@@ -148,16 +192,14 @@ struct Epilogue {
       } else {
         const int64_t r = gcol - p.ND;
         const int64_t head = r / p.Dr;
-        const int i0 = static_cast<int>(r % p.Dr);
+        const int i0 = rope_index(p, r);
         const int half = p.Dr >> 1;
-        const int64_t pcol = i0 < half ? gcol + half : gcol - half;
+        dequant(pre.cs, pre.d, v);
         float w[8];
         to_float(raw_partner, w);
-        dequant(p, m, pcol, w);
-        const uint4 c4 = ld16(p.cosb + m * p.Dr + i0);
-        const uint4 s4 = ld16(p.sinb + m * p.Dr + i0);
-        const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
-        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+        dequant(pre.cs, pre.dp, w);
+        const uint32_t cw[4] = {pre.c4.x, pre.c4.y, pre.c4.z, pre.c4.w};
+        const uint32_t sw[4] = {pre.s4.x, pre.s4.y, pre.s4.z, pre.s4.w};
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -193,8 +235,12 @@ struct SkinnyDepth {
   static constexpr int value = (8 / per_step) > 0 ? (8 / per_step) : 1;
 };
 
+// A_LDS_STEPS: most k-steps of one split whose A operand (32 rows, bf16) a
+// workgroup can stage in LDS (64 KB).
+constexpr int A_LDS_STEPS = 64;
+
 template <int AK, int MB, int NB, int NW, int KW, int EPI,
-          int P = SkinnyDepth<AK, MB, NB>::value>
+          int P = SkinnyDepth<AK, MB, NB>::value, bool ALDS = false>
 __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   typedef typename AccT<AK>::type Acc;
   constexpr int KSTEP = (AK == A_I8) ? 32 : 16;  // k per MFMA
@@ -203,9 +249,15 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   constexpr int PITCH = TN + 4;  // words per LDS row
   constexpr int NA = (AK == A_F32SPLIT) ? 2 : 1;  // 16-byte A loads per fragment
   __shared__ uint32_t lds[KW][MB * 32][PITCH];
+  // ALDS: row-major A (bf16, MB = 1) staged in fragment order for this
+  // workgroup's split: chunk (step s, lane) at s*64 + lane.
+  static_assert(!ALDS || (MB == 1 && AK == A_BF16), "LDS-staged A: one bf16 row block");
+  __shared__ uint4 alds[ALDS ? A_LDS_STEPS * 64 : 1];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave-level quantities live in SGPRs: the per-step load offsets below are
+  // scalar, so the loop's address arithmetic costs no VGPRs.
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int nw = wave % NW;
   const int kw = wave / NW;
   const int g = lane >> 5;
@@ -226,18 +278,18 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
     ocol0 = p.N0;
   }
   B += static_cast<int64_t>(z) * p.b_bstride;
-  const int64_t KC = p.K / G;  // 16-byte chunk rows per column
+  const int KC = static_cast<int>(p.K / G);  // 16-byte chunk rows per column
 
-  const int64_t nsteps = p.K / KSTEP;
-  const int64_t s_lo = static_cast<int64_t>(blockIdx.y) * p.steps_per_split;
-  const int64_t s_hi = min(s_lo + p.steps_per_split, nsteps);
-  const int64_t cnt = s_hi > s_lo ? s_hi - s_lo : 0;
-  const int64_t w_lo = s_lo + cnt * kw / KW;
-  const int64_t w_hi = s_lo + cnt * (kw + 1) / KW;
+  const int nsteps = static_cast<int>(p.K / KSTEP);
+  const int s_lo = static_cast<int>(blockIdx.y * p.steps_per_split);
+  const int s_hi = min(s_lo + static_cast<int>(p.steps_per_split), nsteps);
+  const int cnt = s_hi > s_lo ? s_hi - s_lo : 0;
+  const int w_lo = s_lo + cnt * kw / KW;
+  const int w_hi = s_lo + cnt * (kw + 1) / KW;
 
   // Column blocks of this wave: chunk (block nb, row kc, column j) sits at
   // (nb*KC + kc)*32 + j, and lane (g, j) of k-step s reads row 2s+g, so the
-  // lane's chunk for step s is block_base + 64*s + lane.
+  // lane's chunk for step s is 16*lane + 1024*s bytes into the block's run.
   //
   // Every load below is unconditional: a column block past N, a row past M
   // and a step past the wave's range are clamped to valid memory and their
@@ -245,37 +297,57 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   // independent).  Branch-free loads let the compiler wait only for the
   // batch being consumed instead of draining every load in flight.
   const int64_t nblk = (N + 31) / 32;
-  const uint4* bptr[NB];
+  rsrc_t rb[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     int64_t nb = n0 / 32 + nw * NB + b;
     nb = nb < nblk ? nb : nblk - 1;
-    bptr[b] = B + nb * KC * 32 + lane;
+    rb[b] = make_rsrc(B + nb * KC * 32, static_cast<uint32_t>(KC) * 512u);
   }
+  const uint32_t vb = static_cast<uint32_t>(lane) * 16u;
 
   constexpr int AEB = (AK == A_I8) ? 1 : (AK == A_F32SPLIT ? 4 : 2);  // A element bytes
   constexpr int CB = (AK == A_F32SPLIT) ? 32 : 16;  // A bytes per lane per k-step
-  const char* arow[MB];
-  int64_t astep;  // A bytes between consecutive k-steps of one lane
+  rsrc_t ra[MB];
+  uint32_t va[MB];     // lane's byte offset into its A resource
+  uint32_t astep;      // A bytes between consecutive k-steps (scalar)
   if (p.a_frag) {
-    const char* base = static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_zs + lane * CB;
+    const char* base = static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_zs;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) arow[mb] = base + mb * p.a_mbs;
+    for (int mb = 0; mb < MB; ++mb) {
+      ra[mb] = make_rsrc(base + mb * p.a_mbs, static_cast<uint32_t>(nsteps) * 64u * CB);
+      va[mb] = static_cast<uint32_t>(lane) * CB;
+    }
     astep = 64 * CB;
   } else {
     const char* base =
         static_cast<const char*>(p.A) + (static_cast<int64_t>(z) * p.a_bstride) * AEB;
-    const int64_t a_row_bytes = p.lda * AEB;
+    const uint32_t a_row_bytes = static_cast<uint32_t>(p.lda) * AEB;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      int64_t m = mb * 32 + li;
-      m = m < p.M ? m : p.M - 1;
+      int m = mb * 32 + li;
+      m = m < p.M ? m : static_cast<int>(p.M) - 1;
       // bf16: 16 k = 32 bytes per step, lane group g takes bytes [16g, 16g+16);
       // int8: 32 k = 32 bytes, same offsets; fp32: 16 k = 64 bytes, group g
       // takes [32g, 32g+32).
-      arow[mb] = base + m * a_row_bytes + g * CB;
+      ra[mb] = make_rsrc(base, static_cast<uint32_t>(p.M) * a_row_bytes);
+      va[mb] = static_cast<uint32_t>(m) * a_row_bytes + g * CB;
     }
     astep = 2 * CB;
+  }
+
+  // Epilogue operands of this thread's first 8-column group, loaded now so
+  // they arrive during the main loop.
+  constexpr int GROUPS = MB * 32 * (TN / 8);
+  typedef Epilogue<AK, EPI> Epi;
+  typename Epi::Pre pre0;
+  {
+    // clamped into range; the values of clamped groups are never used
+    int64_t m = static_cast<int>(threadIdx.x % GROUPS) / (TN / 8);
+    int64_t gcol = n0 + (threadIdx.x % (TN / 8)) * 8;
+    m = m < p.M ? m : p.M - 1;
+    gcol = gcol < N ? gcol : N - 8;
+    pre0 = Epi::prefetch(p, m, gcol);
   }
 
   Acc acc[MB][NB];
@@ -289,21 +361,37 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
     uint4 b[P][NB];
     uint4 a[P][MB][NA];
   };
-  const int64_t s_last = w_hi - 1;
-  auto load = [&](Batch& x, int64_t s0) {
+  const int s_last = w_hi - 1;
+  auto load_b = [&](Batch& x, int s0) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
-      const int64_t s = (s0 + u) < s_last ? (s0 + u) : s_last;
+      int s = (s0 + u) < s_last ? (s0 + u) : s_last;
+      s = s > 0 ? s : 0;  // a wave with an empty range still loads in bounds
 #pragma unroll
-      for (int b = 0; b < NB; ++b) x.b[u][b] = ld16(bptr[b] + s * 64);
+      for (int b = 0; b < NB; ++b) x.b[u][b] = bld16(rb[b], vb, static_cast<uint32_t>(s) * 1024u);
+    }
+  };
+  auto load_a = [&](Batch& x, int s0) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        x.a[u][mb][0] = ld16(arow[mb] + s * astep);
-        if constexpr (AK == A_F32SPLIT) x.a[u][mb][1] = ld16(arow[mb] + s * astep + 16);
+    for (int u = 0; u < P; ++u) {
+      const int s = (s0 + u) < s_last ? (s0 + u) : s_last;
+      if constexpr (ALDS) {
+        x.a[u][0][0] = alds[(s - s_lo) * 64 + lane];
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          x.a[u][mb][0] = bld16(ra[mb], va[mb], static_cast<uint32_t>(s) * astep);
+          if constexpr (AK == A_F32SPLIT)
+            x.a[u][mb][1] = bld16(ra[mb], va[mb] + 16u, static_cast<uint32_t>(s) * astep);
+        }
       }
     }
   };
-  auto compute = [&](const Batch& x, int64_t count) {
+  auto load = [&](Batch& x, int s0) {
+    load_b(x, s0);
+    load_a(x, s0);
+  };
+  auto compute = [&](const Batch& x, int count) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       if (u >= count) break;  // wave-uniform; only MFMAs are skipped
@@ -333,10 +421,45 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   // Ping-pong over batches: the next batch's loads are issued before the
   // current batch's MFMAs.  The last prefetch re-reads the final batch (cache
   // hits) so the load sequence never depends on a branch.
+  Batch X, Y;
+  if constexpr (ALDS) if (cnt > 0) {  // cnt is uniform over the workgroup
+    // Stage rows 0..31 of A over this split's k range [16*s_lo, 16*s_hi):
+    // thread c of the 64*cnt 16-byte chunks takes row c / (2*cnt), chunk
+    // c % (2*cnt), so each wave reads 1 KB of consecutive row bytes.  Rows
+    // past M repeat row M-1 (their products are never stored); surplus
+    // threads repeat the last chunk.  The loads are issued before the first
+    // weight batch, so both are in flight together.
+    constexpr int NT = 64 * NW * KW;
+    constexpr int PER = (A_LDS_STEPS * 64 + NT - 1) / NT;
+    const int total = 64 * cnt;
+    const int per_row = 2 * cnt;
+    // Buffer loads like the weight stream (loads of one kind complete in
+    // order, so waiting for these does not drain the weight batch).
+    const rsrc_t rx = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(s_lo) * 32,
+                                static_cast<uint32_t>(p.M * p.lda * 2 - s_lo * 32));
+    uint4 st[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = static_cast<int>(threadIdx.x) + i * NT;
+      c = c < total ? c : total - 1;
+      int m = c / per_row;
+      m = m < p.M ? m : static_cast<int>(p.M) - 1;
+      st[i] = bld16(rx, static_cast<uint32_t>(m * p.lda * 2 + (c % per_row) * 16), 0u);
+    }
+    load_b(X, w_lo);  // unconditional: a branch here would drain the staging loads
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = static_cast<int>(threadIdx.x) + i * NT;
+      c = c < total ? c : total - 1;
+      const int row = c / per_row, q = c % per_row;
+      alds[(q >> 1) * 64 + (q & 1) * 32 + row] = st[i];
+    }
+    lds_barrier();  // keeps the first weight batch in flight
+    if (w_lo < w_hi) load_a(X, w_lo);
+  }
   if (w_lo < w_hi) {
-    Batch X, Y;
-    int64_t s = w_lo;
-    load(X, s);
+    int s = w_lo;
+    if constexpr (!ALDS) load(X, s);
     for (;;) {
       load(Y, s + P < w_hi ? s + P : s);
       compute(X, w_hi - s);
@@ -372,7 +495,6 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   // Epilogue: 8-column groups of the (MB*32) x TN tile.
   GemmParams pe = p;
   if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(blockIdx.y) * p.M * p.part_ld;
-  constexpr int GROUPS = MB * 32 * (TN / 8);
   for (int it = threadIdx.x; it < GROUPS; it += 64 * NW * KW) {
     const int row = it / (TN / 8);
     const int c0 = (it % (TN / 8)) * 8;
@@ -380,7 +502,9 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
     const int64_t gcol = n0 + c0;
     if (m >= p.M || gcol >= N) continue;
     uint32_t raw[8], rawp[8];
-    const int poff = Epilogue<AK, EPI>::partner_offset(p, gcol);
+    const int poff = Epi::partner_offset(p, gcol);
+    typename Epi::Pre pre = pre0;
+    if (it != static_cast<int>(threadIdx.x)) pre = Epi::prefetch(p, m, gcol);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if constexpr (AK == A_I8) {
@@ -403,7 +527,7 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
         rawp[e] = __float_as_uint(spf);
       }
     }
-    Epilogue<AK, EPI>::apply(pe, m, gcol, ocol0 + gcol, z, raw, rawp);
+    Epi::apply(pe, m, gcol, ocol0 + gcol, z, raw, rawp, pre);
   }
 }
 
@@ -604,15 +728,19 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
       raw[e] = ew[row * EPI_PITCH + c0 + e];
       rawp[e] = poff ? ew[row * EPI_PITCH + c0 + poff + e] : 0u;
     }
-    Epilogue<AK, EPI>::apply(p, m, gcol, ocol0 + gcol, z, raw, rawp);
+    Epilogue<AK, EPI>::apply(p, m, gcol, ocol0 + gcol, z, raw, rawp,
+                             Epilogue<AK, EPI>::prefetch(p, m, gcol));
   }
 }
 
 // ---------------------------------------------------------------------------
-// Down-projection finish: one workgroup per token.  Sums the split-K
-// partials in split order, RmsNorms c^Q (and quantises it per token in the
-// partial-quant scenarios), RmsNorms c^KV, rotates k^R and writes both cache
-// rows at the token's slot.
+// Down-projection finish: one workgroup per token, each thread owning 8
+// consecutive columns of the token's Hcq + Hckv + Dr outputs.  Sums the
+// split-K partials in split order, RmsNorms c^Q (and quantises it per token
+// in the partial-quant scenarios), RmsNorms c^KV, rotates k^R and writes both
+// cache rows at the token's slot.  A thread's global loads for its first
+// chunk (partials, gammas, scales, cos/sin) and the slot are all issued at
+// the start, so the kernel waits on memory once.
 // ---------------------------------------------------------------------------
 struct FinishParams {
   const float* part;
@@ -639,155 +767,205 @@ struct FinishParams {
   float* dbg_cq_scale;
 };
 
-constexpr int FIN_THREADS = 1024;
-constexpr int FIN_WAVES = FIN_THREADS / 64;
+constexpr int FIN_MAX_THREADS = 1024;
 constexpr int FIN_MAXSPLIT = 8;
-constexpr int FIN_COLS = 3;  // columns per thread per pass (2112 = 3 passes x 704)
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = group_sum<64>(v);
+// Workgroup size of the finish kernel for ntot columns: one thread per
+// 8-column chunk, whole waves, at most FIN_MAX_THREADS (more chunks loop).
+inline int fin_threads(int64_t ntot) {
+  const int64_t t = (ntot / 8 + 63) / 64 * 64;
+  return static_cast<int>(t < 64 ? 64 : (t > FIN_MAX_THREADS ? FIN_MAX_THREADS : t));
+}
+
+// Sum (op = 0) or max (op = 1) of two values over the workgroup.
+template <int OP>
+__device__ __forceinline__ float2 block_reduce2(float2 v, float2* red) {
+  if (OP == 0) {
+    v.x = group_sum<64>(v.x);
+    v.y = group_sum<64>(v.y);
+  } else {
+    v.x = group_max<64>(v.x);
+    v.y = group_max<64>(v.y);
+  }
   const int wave = threadIdx.x >> 6;
-  __syncthreads();
+  __syncthreads();  // red[] free from an earlier reduction
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < FIN_WAVES; ++w) t += red[w];
+  float2 t = red[0];
+  for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) {
+    t.x = OP == 0 ? t.x + red[w].x : fmaxf(t.x, red[w].x);
+    t.y = OP == 0 ? t.y + red[w].y : fmaxf(t.y, red[w].y);
+  }
   return t;
 }
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = group_max<64>(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.f;
+
+__device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int w = 0; w < FIN_WAVES; ++w) t = fmaxf(t, red[w]);
-  return t;
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf16lo(u[e]);
+    f[2 * e + 1] = bf16hi(u[e]);
+  }
 }
 
 // QM: 0 none, 1 partial with bf16 caches, 2 partial with int8 caches.
 template <int QM>
-__global__ __launch_bounds__(FIN_THREADS) void k_down_finish(FinishParams p) {
-  extern __shared__ float row[];  // Hcq + Hckv + Dr
-  __shared__ float red[FIN_WAVES];
+__global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p) {
+  extern __shared__ float row[];  // Hcq + Hckv + Dr summed values
+  __shared__ float2 red[FIN_MAX_THREADS / 64];
   const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
   const int ntot = p.Hcq + p.Hckv + p.Dr;
+  const int nch = ntot / 8;
+  const int half = p.Dr >> 1;
+  const int64_t slot = gld(p.index + t);
 
-  // Sum the split-K partials in split order.  Loads are unconditional
-  // (clamped column and split indexes) so all FIN_COLS x FIN_MAXSPLIT of a
-  // thread's loads are in flight together.
-  for (int c0 = 0; c0 < ntot; c0 += FIN_COLS * FIN_THREADS) {
-    float v[FIN_COLS][FIN_MAXSPLIT];
+  // Parameters of one chunk: pa = its gammas (c^Q, c^KV) or cos (k^R), pb =
+  // sin (k^R), pf = smooth scales (c^Q) or int8 cache scales (c^KV, k^R).
+  // Every pointer formed is valid whatever the region.
+  uint4 pa, pb;
+  float pf[8];
+  auto load_params = [&](int j) {
+    const int c0 = 8 * j;
+    const bool cq = c0 < p.Hcq, ckv = !cq && c0 < p.Hcq + p.Hckv;
+    const int i0 = cq || ckv ? 0 : c0 - p.Hcq - p.Hckv;
+    pa = ld16(cq ? p.gamma_cq + c0
+                 : (ckv ? p.gamma_ckv + (c0 - p.Hcq) : p.cosb + t * p.Dr + i0));
+    pb = ld16(p.sinb + t * p.Dr + i0);
+    if (QM != 0) {
+      const float* f = p.smooth + (cq ? c0 : 0);
+      if (QM == 2 && ckv) f = p.qs_ckv + (c0 - p.Hcq);
+      if (QM == 2 && !cq && !ckv) f = p.qs_ckr + i0;
+      ld8f(f, pf);
+    }
+  };
+  // The first chunk's parameters load together with its partials; with one
+  // round of chunks (the DeepSeek-V3 shapes) nothing is loaded later.
+  if (static_cast<int>(threadIdx.x) < nch) load_params(threadIdx.x);
+
+  // Pass 1: per chunk, sum the partials in split order into row[].
+  float sq = 0.f, skv = 0.f, amax = 0.f;
+  for (int j = threadIdx.x; j < nch; j += blockDim.x) {
+    const int c0 = 8 * j;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float v[FIN_MAXSPLIT][8];
 #pragma unroll
-    for (int i = 0; i < FIN_COLS; ++i) {
-      int c = c0 + tid + i * FIN_THREADS;
-      c = c < ntot ? c : ntot - 1;
-#pragma unroll
-      for (int s = 0; s < FIN_MAXSPLIT; ++s) {
-        const int se = s < p.ksplit ? s : p.ksplit - 1;
-        v[i][s] = gld(p.part + (static_cast<int64_t>(se) * p.T + t) * ntot + c);
-      }
+    for (int s = 0; s < FIN_MAXSPLIT; ++s) {
+      const int se = s < p.ksplit ? s : p.ksplit - 1;
+      ld8f(p.part + (static_cast<int64_t>(se) * p.T + t) * ntot + c0, v[s]);
     }
 #pragma unroll
-    for (int i = 0; i < FIN_COLS; ++i) {
-      const int c = c0 + tid + i * FIN_THREADS;
-      float a = 0.f;
+    for (int s = 0; s < FIN_MAXSPLIT; ++s)
 #pragma unroll
-      for (int s = 0; s < FIN_MAXSPLIT; ++s) a += s < p.ksplit ? v[i][s] : 0.f;
-      if (c < ntot) row[c] = a;
+      for (int e = 0; e < 8; ++e) acc[e] += s < p.ksplit ? v[s][e] : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      row[c0 + e] = acc[e];
+      if (c0 < p.Hcq)
+        sq += acc[e] * acc[e];
+      else if (c0 < p.Hcq + p.Hckv)
+        skv += acc[e] * acc[e];
     }
   }
-  __syncthreads();
+  const float2 ss = block_reduce2<0>(make_float2(sq, skv), red);  // barrier: row[] complete
+  const float rq = 1.0f / __builtin_sqrtf(ss.x / static_cast<float>(p.Hcq) + p.eps_cq);
+  const float rkv = 1.0f / __builtin_sqrtf(ss.y / static_cast<float>(p.Hckv) + p.eps_ckv);
 
-  float sq = 0.f, skv = 0.f;
-  for (int c = tid; c < p.Hcq; c += FIN_THREADS) sq += row[c] * row[c];
-  for (int c = tid; c < p.Hckv; c += FIN_THREADS) skv += row[p.Hcq + c] * row[p.Hcq + c];
-  sq = block_sum(sq, red);
-  skv = block_sum(skv, red);
-  const float rq = 1.0f / __builtin_sqrtf(sq / static_cast<float>(p.Hcq) + p.eps_cq);
-  const float rkv = 1.0f / __builtin_sqrtf(skv / static_cast<float>(p.Hckv) + p.eps_ckv);
-
-  // c^Q.  Fragment layout: element (t, c) of a K-step of `ks` values sits at
-  // ((mb*(Hcq/ks) + c/ks)*64 + g*32 + t%32)*(ks/2) + c%(ks/2), g = (c%ks)/(ks/2).
+  // c^Q fragment layout: element (t, c) of a K-step of `ks` values sits at
+  // ((mb*(Hcq/ks) + c/ks)*64 + g*32 + t%32)*(ks/2) + c%(ks/2),
+  // g = (c%ks)/(ks/2); 8 consecutive c (c % 8 == 0) are contiguous.
   auto cq_off = [&](int c, int ks) -> int64_t {
     if (!p.cq_frag) return t * p.Hcq + c;
     const int h = ks / 2;
     return ((static_cast<int64_t>(t / 32) * (p.Hcq / ks) + c / ks) * 64 + ((c % ks) / h) * 32 +
             (t % 32)) * h + c % h;
   };
-  if (QM == 0) {
-    for (int c = tid; c < p.Hcq; c += FIN_THREADS)
-      gst(p.cq_bf16 + cq_off(c, 16),
-          f32_to_bf16(row[c] * rq * bf16_to_f32(gld(p.gamma_cq + c))));
-  } else {
-    float amax = 0.f;
-    for (int c = tid; c < p.Hcq; c += FIN_THREADS) {
-      const float u = row[c] * rq * bf16_to_f32(gld(p.gamma_cq + c)) * gld(p.smooth + c);
-      row[c] = u;
-      amax = fmaxf(amax, fabsf(u));
-    }
-    amax = block_max(amax, red);
-    const float s = amax / 127.0f;
-    for (int c = tid; c < p.Hcq; c += FIN_THREADS) {
-      const int code = s > 0.f ? sat_rne(row[c] / s, -127, 127) : 0;
-      gst(p.cq_i8 + cq_off(c, 32), static_cast<int8_t>(code));
-      if (p.dbg_cq_i8) gst(p.dbg_cq_i8 + t * p.Hcq + c, static_cast<int8_t>(code));
-    }
-    if (tid == 0) {
-      gst(p.cq_scale + t, s);
-      if (p.dbg_cq_scale) gst(p.dbg_cq_scale + t, s);
-    }
-  }
+  const bool write_cache = slot >= 0 && slot < p.slots;
 
-  const int64_t slot = gld(p.index + t);
-  if (slot < 0 || slot >= p.slots) return;
-  // c^KV row
-  for (int c = tid; c < p.Hckv; c += FIN_THREADS) {
-    const float v = row[p.Hcq + c] * rkv * bf16_to_f32(gld(p.gamma_ckv + c));
-    if (QM == 2)
-      gst(static_cast<int8_t*>(p.kv_cache) + slot * p.Hckv + c,
-          static_cast<int8_t>(sat_rne(v / gld(p.qs_ckv + c), -128, 127)));
-    else
-      gst(static_cast<uint16_t*>(p.kv_cache) + slot * p.Hckv + c, f32_to_bf16(v));
+  // Pass 2: outputs.
+  for (int j = threadIdx.x; j < nch; j += blockDim.x) {
+    const int c0 = 8 * j;
+    if (j != static_cast<int>(threadIdx.x)) load_params(j);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = row[c0 + e];
+    if (c0 < p.Hcq) {
+      float g[8];
+      unpack_bf16x8(pa, g);
+      if (QM == 0) {
+        st16(p.cq_bf16 + cq_off(c0, 16),
+             make_uint4(pack_bf16x2(x[0] * rq * g[0], x[1] * rq * g[1]),
+                        pack_bf16x2(x[2] * rq * g[2], x[3] * rq * g[3]),
+                        pack_bf16x2(x[4] * rq * g[4], x[5] * rq * g[5]),
+                        pack_bf16x2(x[6] * rq * g[6], x[7] * rq * g[7])));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float u = x[e] * rq * g[e] * pf[e];
+          row[c0 + e] = u;  // this thread's own columns: no barrier needed
+          amax = fmaxf(amax, fabsf(u));
+        }
+      }
+    } else if (c0 < p.Hcq + p.Hckv) {
+      if (!write_cache) continue;
+      const int c = c0 - p.Hcq;
+      float g[8], o[8];
+      unpack_bf16x8(pa, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = x[e] * rkv * g[e];
+      if (QM == 2) {
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = sat_rne(o[e] / pf[e], -128, 127);
+        st8(static_cast<int8_t*>(p.kv_cache) + slot * p.Hckv + c,
+            make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])));
+      } else {
+        st16(static_cast<uint16_t*>(p.kv_cache) + slot * p.Hckv + c,
+             make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                        pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])));
+      }
+    } else {
+      // k^R: half-and-half RoPE with the token's (cos, sin); the partner
+      // chunk lies Dr/2 columns away in row[].
+      if (!write_cache) continue;
+      const int i0 = c0 - p.Hcq - p.Hckv;
+      const float* kr = row + p.Hcq + p.Hckv;
+      float cs[8], sn[8], o[8];
+      unpack_bf16x8(pa, cs);
+      unpack_bf16x8(pb, sn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] = i0 < half ? x[e] * cs[e] - kr[i0 + half + e] * sn[e]
+                         : x[e] * cs[e] + kr[i0 - half + e] * sn[e];
+      if (QM == 2) {
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = sat_rne(o[e] / pf[e], -128, 127);
+        st8(static_cast<int8_t*>(p.kr_cache) + slot * p.Dr + i0,
+            make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])));
+      } else {
+        st16(static_cast<uint16_t*>(p.kr_cache) + slot * p.Dr + i0,
+             make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                        pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])));
+      }
+    }
   }
-  // k^R row: half-and-half RoPE with the token's (cos, sin)
-  const int half = p.Dr >> 1;
-  const float* kr = row + p.Hcq + p.Hckv;
-  for (int i = tid; i < p.Dr; i += FIN_THREADS) {
-    const float c = bf16_to_f32(gld(p.cosb + t * p.Dr + i));
-    const float s = bf16_to_f32(gld(p.sinb + t * p.Dr + i));
-    const float o = i < half ? kr[i] * c - kr[i + half] * s : kr[i] * c + kr[i - half] * s;
-    if (QM == 2)
-      gst(static_cast<int8_t*>(p.kr_cache) + slot * p.Dr + i,
-          static_cast<int8_t>(sat_rne(o / gld(p.qs_ckr + i), -128, 127)));
-    else
-      gst(static_cast<uint16_t*>(p.kr_cache) + slot * p.Dr + i, f32_to_bf16(o));
-  }
-}
+  if (QM == 0) return;
 
-// ---------------------------------------------------------------------------
-// Activation packing for the skinny kernels: bf16 rows (M, K) into the A
-// fragment layout, one thread per 16-byte chunk (32-row block mb, k-step s,
-// lane (g, i)) = row 32*mb + i, k in [16s + 8g, 16s + 8g + 8).  Rows past M
-// are zero.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src,
-                                                uint4* __restrict__ dst, int64_t M, int64_t K,
-                                                int64_t mblocks) {
-  // Thread c reads the 16 bytes k in [8*q, 8*q+8) of row m (reads coalesce
-  // along the row) and writes them to their fragment chunk.
-  const int64_t steps = K / 16;
-  const int64_t per_row = K / 8;
-  const int64_t total = mblocks * 32 * per_row;
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
-       c += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t m = c / per_row;
-    const int64_t q = c % per_row;
-    const int64_t chunk = ((m / 32) * steps + q / 2) * 64 + (q % 2) * 32 + (m % 32);
-    st16(dst + chunk, m < M ? ld16(src + m * K + 8 * q) : make_uint4(0, 0, 0, 0));
+  // Partial quant: per-token dynamic int8 of the smoothed c^Q (max-abs/127).
+  const float am = block_reduce2<1>(make_float2(amax, 0.f), red).x;
+  const float sc = am / 127.0f;
+  for (int j = threadIdx.x; 8 * j < p.Hcq; j += blockDim.x) {
+    const int c0 = 8 * j;
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = sc > 0.f ? sat_rne(row[c0 + e] / sc, -127, 127) : 0;
+    const uint2 w = make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
+    st8(p.cq_i8 + cq_off(c0, 32), w);
+    if (p.dbg_cq_i8) st8(p.dbg_cq_i8 + t * p.Hcq + c0, w);
+  }
+  if (threadIdx.x == 0) {
+    gst(p.cq_scale + t, sc);
+    if (p.dbg_cq_scale) gst(p.dbg_cq_scale + t, sc);
   }
 }
 
@@ -795,10 +973,13 @@ __global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src
 // Weight packing into the N32-blocked K16 layout, one thread per 16-byte
 // output chunk (block nb, chunk row kc, column j): the G = 16/eb consecutive
 // k values of column 32*nb + j.  Columns past N (the last block's padding)
-// are zero.
+// are zero.  Columns from rope_col0 on are rope heads of rope_dim columns;
+// when rope_dim > 32 they are reordered so that packed block b of a head
+// holds natural columns [16b, 16b + 16) then [rope_dim/2 + 16b, ... + 16).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint4* __restrict__ dst,
-                                              int64_t batch, int64_t K, int64_t N, int eb) {
+                                              int64_t batch, int64_t K, int64_t N, int eb,
+                                              int64_t rope_col0, int64_t rope_dim) {
   const int G = 16 / eb;
   const int64_t KC = K / G;
   const int64_t nblk = (N + 31) / 32;
@@ -813,7 +994,13 @@ __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint
     const int64_t n = nb * 32 + (r % 32);
     uint32_t w[4] = {0, 0, 0, 0};
     if (n < N) {
-      const char* s = src + ((b * K + kc * G) * N + n) * eb;
+      int64_t ns = n;  // source column
+      if (n >= rope_col0 && rope_dim > 32) {
+        const int64_t rr = n - rope_col0;
+        const int64_t pj = rr % rope_dim, bb = pj / 32, ww = pj % 32;
+        ns = rope_col0 + (rr - pj) + (ww < 16 ? 16 * bb + ww : rope_dim / 2 + 16 * bb + ww - 16);
+      }
+      const char* s = src + ((b * K + kc * G) * N + ns) * eb;
       if (eb == 2) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -845,34 +1032,46 @@ void tiled(const GemmParams& p, dim3 grid, hipStream_t st) {
 }
 
 // Decode plan: three weight-streaming launches plus the down-projection
-// finish (launched by the caller between A1 and A6).  Many short per-wave
-// weight runs keep the most bytes in flight: A1 gives each 1024-thread
-// workgroup one 32-column block and splits its K range over 16 waves
-// (fewer when more 32-row blocks fill the registers); A6 uses 64-column
-// tiles of 128 columns (two blocks per wave and two waves across, so every
-// RoPE pair of q^R lies in one tile) with K over 4 waves; A8 puts 8 (or 4) waves on different column blocks of one
-// head.  Every tile's LDS stays near 70 KB, two workgroups per CU.
+// finish (launched between A1 and A6).  Many short per-wave weight runs keep
+// the most bytes in flight.  A1: 64-column tiles (two column blocks per
+// wave) with the K range split over ksplit workgroups and, inside one, over
+// 8 waves (fewer when more 32-row blocks fill the registers).  A6: 96-column
+// tiles, three waves across with one column block each and K over two waves
+// (256 tiles for the DeepSeek-V3 shape: one per CU).  A8: 4 waves on
+// different column blocks of one head.
 template <int MB>
 constexpr int a1_kw() { return MB >= 4 ? 2 : (MB == 2 ? 4 : 8); }
 template <int MB>
-constexpr int a6_kw() { return MB >= 4 ? 1 : (MB == 2 ? 2 : 4); }
-constexpr int kA6Cols = 128;  // A6 tile: two column blocks per wave, two waves across
+constexpr int a6_kw() { return MB >= 4 ? 1 : 2; }
+constexpr int kA6Cols = 96;  // A6 tile: three waves across, one column block each
 template <int MB>
 constexpr int a8_nw() { return 4; }
 constexpr int kA1Cols = 64;  // A1 tile width (two column blocks per wave)
 
+// A1 reads x row-major: with one 32-row block each workgroup stages its
+// split of x in LDS (fragment order), otherwise lanes load rows directly.
 template <int MB>
 void skinny_a1(const GemmParams& g1, const MlaPlan& pl, hipStream_t st) {
-  const unsigned nt = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + kA1Cols - 1) / kA1Cols);
-  skinny<A_BF16, MB, 2, 1, a1_kw<MB>(), EPI_PARTIAL>(g1, dim3(nt, pl.ksplit, 1), st);
+  const dim3 grid(static_cast<unsigned>(g1.ntiles0 + (g1.N1 + kA1Cols - 1) / kA1Cols),
+                  static_cast<unsigned>(pl.ksplit), 1);
+  constexpr int KW = a1_kw<MB>();
+  if constexpr (MB == 1) {
+    if (pl.steps_per_split <= A_LDS_STEPS) {
+      hipLaunchKernelGGL((k_skinny<A_BF16, 1, 2, 1, KW, EPI_PARTIAL,
+                                   SkinnyDepth<A_BF16, 1, 2>::value, true>),
+                         grid, dim3(64 * KW), 0, st, g1);
+      return;
+    }
+  }
+  skinny<A_BF16, MB, 2, 1, KW, EPI_PARTIAL>(g1, grid, st);
 }
 template <int MB>
 void skinny_a6(const GemmParams& g6, bool quant, hipStream_t st) {
   const unsigned nt = static_cast<unsigned>((g6.N0 + kA6Cols - 1) / kA6Cols);
   if (quant)
-    skinny<A_I8, MB, 2, 2, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+    skinny<A_I8, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
   else
-    skinny<A_BF16, MB, 2, 2, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+    skinny<A_BF16, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
 }
 template <int MB>
 void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
@@ -887,7 +1086,7 @@ void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
 }  // namespace
 
 int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
-                       int elem_bytes, hipStream_t stream) {
+                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream) {
   const int G = 16 / elem_bytes;
   const int64_t total = batch * (K / G) * ((N + 31) / 32) * 32;
   if (total == 0) return QKVNR_OK;
@@ -895,7 +1094,7 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(k_pack, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                      static_cast<const char*>(src), static_cast<uint4*>(dst), batch, K, N,
-                     elem_bytes);
+                     elem_bytes, rope_col0, rope_dim);
   return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;
 }
 
@@ -925,21 +1124,7 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     pl.ksplit = 1;
   }
   pl.rows = pl.skinny ? 32 * pl.mb : T;
-  // The persistent fused kernel is opt-in: on this part its grid barriers
-  // need a whole-L2 writeback and invalidate per workgroup (the XCD L2s are
-  // not coherent with each other), which costs more than the kernel
-  // boundaries it removes.
-  pl.fused = a->plan == MLA_PLAN_FUSED && mla_fused_supported(a);
   size_t off = 0;
-  if (pl.fused) {
-    // barrier words first (workspace bytes [0, 8)), then the fused region
-    FusedLayout L;
-    mla_fused_layout(a, pl.ksplit, &L);
-    pl.off_fused = 0;
-    off = L.total;
-  } else {
-    off = 256;  // same leading reserve in every plan
-  }
   if (a->weight_layout == MLA_WEIGHT_ND) {
     // packed copies: columns padded to whole 32-column blocks
     const size_t eb_uq = quant ? 1 : 2;
@@ -953,10 +1138,6 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     pl.off_wuk = off;
     off += align256(static_cast<size_t>(a->N * a->D) * pad32(a->Hckv) * 2);
   }
-  if (pl.fused) {
-    pl.total = T > 0 ? off : 0;
-    return pl;
-  }
   pl.off_part = off;
   off += align256(static_cast<size_t>(pl.ksplit) * T * ntot * 4);
   pl.off_cq = off;
@@ -965,8 +1146,6 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   off += align256(static_cast<size_t>(T) * 4);
   pl.off_qc = off;
   off += align256(static_cast<size_t>(pl.rows * a->N * a->D) * (quant ? 4 : 2));
-  pl.off_xfrag = off;
-  if (pl.skinny) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
   pl.total = T > 0 ? off : 0;
   return pl;
 }
@@ -983,15 +1162,16 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
 
   const uint4 *wdq, *wdkvkr, *wuqqr, *wuk;
   if (a->weight_layout == MLA_WEIGHT_ND) {
-    int rc = launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, 2, st);
+    int rc = launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, 2, a->Hcq, 0, st);
     if (rc == QKVNR_OK)
       rc = launch_pack_weight(a->weight_dkv_kr, ws + pl.off_wdkvkr, 1, a->He, a->Hckv + a->Dr, 2,
-                              st);
+                              a->Hckv + a->Dr, 0, st);
     if (rc == QKVNR_OK)
       rc = launch_pack_weight(a->weight_uq_qr, ws + pl.off_wuqqr, 1, a->Hcq, NDR, quant ? 1 : 2,
-                              st);
+                              a->N * a->D, a->Dr, st);
     if (rc == QKVNR_OK)
-      rc = launch_pack_weight(a->weight_uk, ws + pl.off_wuk, a->N, a->D, a->Hckv, 2, st);
+      rc = launch_pack_weight(a->weight_uk, ws + pl.off_wuk, a->N, a->D, a->Hckv, 2, a->Hckv, 0,
+                              st);
     if (rc != QKVNR_OK) return rc;
     wdq = reinterpret_cast<const uint4*>(ws + pl.off_wdq);
     wdkvkr = reinterpret_cast<const uint4*>(ws + pl.off_wdkvkr);
@@ -1009,26 +1189,19 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       (void)hipEventRecord(static_cast<hipEvent_t>(a->phase_events[i]), st);
   };
 
-  if (pl.fused) return launch_mla_decode_fused(a, pl, workspace, wdq, wdkvkr, wuqqr, wuk, st);
-
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
   void* cq = ws + pl.off_cq;
   float* cq_scale = reinterpret_cast<float*>(ws + pl.off_cq_scale);
   void* qc = ws + pl.off_qc;
 
   // ---- A1: x . [W^DQ | W^DKV_KR] -> fp32 (partials) ----
-  // The skinny plan reads every A operand in fragment layout: x is packed
-  // by k_pack_a, c^Q by the finish kernel and q^C by A6's epilogue.
+  // The skinny plan reads c^Q and q^C in fragment layout (written so by the
+  // finish kernel and A6's epilogue); x is read row-major.
   const bool frag = pl.skinny;
   const int64_t mblocks = pl.rows / 32;
   GemmParams g1{};
   g1.A = a->token_x;
   g1.lda = a->He;
-  if (frag) {
-    g1.A = ws + pl.off_xfrag;
-    g1.a_frag = 1;
-    g1.a_mbs = a->He * 64;
-  }
   g1.B0 = wdq;
   g1.N0 = a->Hcq;
   g1.B1 = wdkvkr;
@@ -1116,26 +1289,21 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   f.dbg_cq_i8 = a->dbg_cq_int8;
   f.dbg_cq_scale = a->dbg_cq_scale;
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
+  const dim3 fin_block(static_cast<unsigned>(fin_threads(ntot)));
 
   auto finish = [&]() {
     const dim3 grid(static_cast<unsigned>(T));
     if (qm == 0)
-      hipLaunchKernelGGL(k_down_finish<0>, grid, dim3(FIN_THREADS), fin_smem, st, f);
+      hipLaunchKernelGGL(k_down_finish<0>, grid, fin_block, fin_smem, st, f);
     else if (qm == 1)
-      hipLaunchKernelGGL(k_down_finish<1>, grid, dim3(FIN_THREADS), fin_smem, st, f);
+      hipLaunchKernelGGL(k_down_finish<1>, grid, fin_block, fin_smem, st, f);
     else
-      hipLaunchKernelGGL(k_down_finish<2>, grid, dim3(FIN_THREADS), fin_smem, st, f);
+      hipLaunchKernelGGL(k_down_finish<2>, grid, fin_block, fin_smem, st, f);
   };
 
   const int nh = static_cast<int>(a->N);
   mark(MLA_PHASE_START);
   if (pl.skinny) {
-    {
-      const int64_t chunks = mblocks * 32 * (a->He / 8);
-      hipLaunchKernelGGL(k_pack_a, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
-                         st, static_cast<const uint16_t*>(a->token_x),
-                         reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, a->He, mblocks);
-    }
     g1.ntiles0 = static_cast<int>((g1.N0 + kA1Cols - 1) / kA1Cols);
     switch (pl.mb) {
       case 1: skinny_a1<1>(g1, pl, st); break;

@@ -116,8 +116,7 @@ def mla_dims(cfg):
                 Dr=cfg.Dr)
 
 
-def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None,
-                plan="auto"):
+def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None):
     """Run the library on workload w.  Returns dict of device tensors."""
     cfg = w.cfg
     d = dev if dev is not None else upload(w)
@@ -125,7 +124,8 @@ def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None,
     if layout == "packed":
         wdq = qn.mla_pack_weight(d["weight_dq"])
         wdkvkr = qn.mla_pack_weight(d["weight_dkv_kr"])
-        wuqqr = qn.mla_pack_weight(d["weight_uq_qr"])
+        wuqqr = qn.mla_pack_weight_uq_qr(d["weight_uq_qr"], cfg.N, cfg.D,
+                                         cfg.Dr)
         wuk = qn.mla_pack_weight(d["weight_uk"])
         lay = qn.MLA_WEIGHT_PACKED_K16
     else:
@@ -145,7 +145,7 @@ def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None,
         quant_scale_ckv=d.get("quant_scale_ckv"),
         quant_scale_ckr=d.get("quant_scale_ckr"),
         smooth_scales_cq=d.get("smooth_scales_cq"),
-        return_cq_quant=quant != "none", workspace=workspace, plan=plan)
+        return_cq_quant=quant != "none", workspace=workspace)
     out = {"query": res[0], "query_rope": res[1], "kv_cache": d["kv_cache"],
            "kr_cache": d["kr_cache"]}
     if quant != "none":

@@ -187,6 +187,21 @@ def test_pack_weight_validation():
                                None) == -9
 
 
+def test_pack_weight_uq_qr_validation():
+    lib = b.load_library()
+    f = lib.mla_pack_weight_uq_qr
+    assert f(None, None, 64, 4, 32, 64, 3, None) == -3       # element size
+    assert f(None, None, 12, 4, 32, 64, 2, None) == -2       # Hcq % 8
+    assert f(None, None, 24, 4, 32, 64, 1, None) == -2       # Hcq % 16 (int8)
+    assert f(None, None, 64, -1, 32, 64, 2, None) == -2
+    assert f(None, None, 0, 4, 32, 64, 2, None) == 0         # empty: nothing
+    assert f(None, None, 64, 4, 48, 64, 2, None) == -4       # D % 32
+    assert f(None, None, 64, 4, 32, 48, 2, None) == -4       # Dr not 16/32/64
+    assert f(None, None, 64, 4, 32, 64, 2, None) == -1
+    assert f(ctypes.c_void_p(fake()), ctypes.c_void_p(fake() + 8), 64, 4, 32,
+             64, 2, None) == -9
+
+
 # ---- QkvRmsNormRopeCache ---------------------------------------------------
 
 def qkv_args(B=64, S=128, quant="symmetric", bn=64, bs=128, D=128):

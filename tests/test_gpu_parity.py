@@ -58,6 +58,49 @@ def test_pack_weight_bit_exact(shape, dtype):
     np.testing.assert_array_equal(got.view(want.dtype), want)
 
 
+def _rope_pair_order(N, D, Dr):
+    """Source column of each packed column of weight_uq_qr: W^UQ in place;
+    for Dr = 64 each head's packed 32-column block b holds rope columns
+    [16b, 16b+16) then [32+16b, 32+16b+16)."""
+    cols = list(range(N * D))
+    for n in range(N):
+        base = N * D + n * Dr
+        if Dr <= 32:
+            cols += [base + j for j in range(Dr)]
+        else:
+            for b in range(Dr // 32):
+                cols += [base + 16 * b + j for j in range(16)]
+                cols += [base + Dr // 2 + 16 * b + j for j in range(16)]
+    return np.array(cols)
+
+
+@pytest.mark.parametrize("N,D,Dr,dtype", [(3, 32, 64, "bf16"), (5, 64, 32, "bf16"),
+                                          (4, 32, 16, "bf16"), (2, 32, 64, "int8")])
+def test_pack_weight_uq_qr_bit_exact(N, D, Dr, dtype):
+    gh.announce(f"pack uq_qr N={N} D={D} Dr={Dr} {dtype}")
+    rng = np.random.default_rng(6)
+    Hcq = 64
+    shape = (Hcq, N * (D + Dr))
+    if dtype == "bf16":
+        bits = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+        t = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        G = 8
+    else:
+        bits = rng.integers(-128, 128, size=shape).astype(np.int8)
+        t = torch.from_numpy(bits).cuda()
+        G = 16
+    p = qn.mla_pack_weight_uq_qr(t, N, D, Dr)
+    torch.cuda.synchronize()
+    got = gh.raw_bits(p).reshape(-1)
+    src = bits[:, _rope_pair_order(N, D, Dr)]
+    K, Nc = src.shape
+    Np = (Nc + 31) // 32 * 32
+    pad = np.zeros((K, Np), dtype=src.dtype)
+    pad[:, :Nc] = src
+    want = pad.reshape(K // G, G, Np // 32, 32).transpose(2, 0, 3, 1).reshape(-1)
+    np.testing.assert_array_equal(got.view(want.dtype), want)
+
+
 # ---- MLA prolog --------------------------------------------------------------
 
 MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3"]
@@ -174,50 +217,27 @@ def test_mla_T0_and_no_slots():
     np.testing.assert_array_equal(gh.raw_bits(qr1), gh.raw_bits(full["query_rope"]))
 
 
-FUSED_CASES = [0, 1, "mla_ragged_fused", "mla_wide_fused"]
+# decode-sized shapes beyond the small list: a ragged T = 21 (one partial
+# 32-row block) and wider N / Hckv than one pass of 256 workgroups covers
+DECODE_CASES = ["mla_ragged_t21", "mla_wide"]
 
 
-def _fused_case(key):
-    if key == "mla_ragged_fused":  # ragged dims, T = 21 (one partial 32-row block)
+def _decode_case(key):
+    if key == "mla_ragged_t21":
         return make_workload(get_config("mla_ragged").replace(B=21, n_skip=2,
                                                              seed=2011))
     return make_workload(key)
 
 
-@pytest.mark.parametrize("key", FUSED_CASES)
-@pytest.mark.parametrize("plan", ["fused", "multi_kernel"])
-def test_mla_decode_plans(key, plan):
-    # T <= 32, non-quantised: both the persistent fused kernel and the
-    # multi-kernel plan must meet the oracle; the fused plan must report no
-    # barrier timeout.
-    w = _fused_case(key)
-    gh.announce(f"mla plan={plan} {w.cfg.name} T={w.cfg.T}")
+@pytest.mark.parametrize("key", DECODE_CASES)
+def test_mla_decode_shapes(key):
+    w = _decode_case(key)
+    gh.announce(f"mla decode {w.cfg.name} T={w.cfg.T}")
     dev = gh.upload(w)
     before = _before(dev, ["kv_cache", "kr_cache"])
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
-    out = gh.run_mla_gpu(w, dev, plan=plan, workspace=ws)
+    out = gh.run_mla_gpu(w, dev)
     torch.cuda.synchronize()
-    if plan == "fused":
-        assert not qn.fused_barrier_timed_out(ws)
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
-
-
-def test_mla_fused_repeat_and_rejects_quant():
-    # back-to-back fused calls on one workspace reuse the barrier words
-    w = make_workload(1)
-    gh.announce("mla fused repeated calls")
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
-    outs = []
-    for _ in range(3):
-        o = gh.run_mla_gpu(w, gh.upload(w), plan="fused", workspace=ws)
-        torch.cuda.synchronize()
-        assert not qn.fused_barrier_timed_out(ws)
-        outs.append({k: gh.raw_bits(v) for k, v in o.items()})
-    for k in outs[0]:
-        np.testing.assert_array_equal(outs[0][k], outs[2][k], err_msg=k)
-    wq = make_workload(3)
-    with pytest.raises(qn.QkvnrError):
-        gh.run_mla_gpu(wq, gh.upload(wq), plan="fused")
 
 
 def test_mla_packed_equals_nd():

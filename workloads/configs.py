@@ -130,9 +130,8 @@ CONFIGS = {
                               block_num=8, block_size=128, n_skip=5,
                               seed=2004, layout="BSH",
                               **{**_DSV3, "N": 16}),
-    # more heads and a wider kv latent than one pass of the fused decode
-    # kernel's 256 workgroups covers (second passes in its later phases)
-    "mla_wide_fused": MlaConfig("mla_wide_fused_T8", B=8, S=1, He=1024,
+    # more heads and a wider kv latent than the headline decode shape
+    "mla_wide": MlaConfig("mla_wide_T8", B=8, S=1, He=1024,
                                 Hcq=512, N=160, D=128, Hckv=1024, Dr=64,
                                 block_num=2, block_size=64, n_skip=1,
                                 seed=2005),
