@@ -64,6 +64,8 @@ int validate_mla(const MlaPrologV2Args* a) {
   // GEMM K dims: the weight-streaming kernels address one column block's
   // run and one A operand with 32-bit buffer offsets.
   if (a->He > kKCap || a->Hcq > kKCap || a->D > kKCap) return QKVNR_ERR_UNSUPPORTED;
+  // Output column indexes are 32-bit in the epilogues.
+  if (a->N * (a->D + a->Dr) >= (int64_t(1) << 31)) return QKVNR_ERR_UNSUPPORTED;
   if (!good_eps(a->rmsnorm_epsilon_cq) || !good_eps(a->rmsnorm_epsilon_ckv))
     return QKVNR_ERR_BAD_EPS;
 

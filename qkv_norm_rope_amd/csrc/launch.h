@@ -24,12 +24,14 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
 // function of the arguments, so workspace sizing and execution agree.
 struct MlaPlan {
   bool skinny;        // decode-sized T: weight-streaming kernels
+  bool gemm256;       // large T, bf16: 256x256-tile MFMA GEMMs
   int mb;             // 32-row blocks held per wave (skinny only)
   int ksplit;         // down-projection split-K factor
   int64_t steps_per_split;
   // workspace offsets (bytes) and total size
   size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
   size_t off_part, off_cq, off_cq_scale, off_qc;
+  size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
   int64_t rows;       // token rows padded to the plan's 32-row blocks
   size_t total;
 };

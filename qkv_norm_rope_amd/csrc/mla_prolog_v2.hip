@@ -22,6 +22,8 @@
 // Weights arrive in the K16 blocked layout (see mla_pack_weight in the
 // public header): the 8 (bf16) or 16 (int8) consecutive-k values of one
 // column are one 16-byte chunk, which is exactly one lane's MFMA operand.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "mla_device.h"
@@ -97,18 +99,20 @@ struct Epilogue {
   // 32-column block and its packed order keeps every partner in the same
   // block: Dr = 16 pairs columns 8 apart, Dr = 32 and the reordered Dr = 64
   // pair columns 16 apart.
+  // (Column and row indexes fit 32 bits: N*(D+Dr) < 2^31 and T <= 2^23
+  // are validated, so the index arithmetic below is 32-bit.)
   static __device__ __forceinline__ int partner_offset(const GemmParams& p, int64_t gcol) {
     if (EPI != EPI_UQQR || gcol < p.ND) return 0;
     const int w = static_cast<int>((gcol - p.ND) & 31);
     const int hp = p.Dr >= 32 ? 16 : (p.Dr >> 1);
-    return (w % (2 * hp)) < hp ? hp : -hp;
+    return (w & (2 * hp - 1)) < hp ? hp : -hp;
   }
 
   // Natural rope index (position within the head's Dr columns) of packed
   // rope column r = gcol - ND.  For Dr = 64, packed block b of a head holds
   // natural columns [16b, 16b + 16) then [32 + 16b, 32 + 16b + 16).
   static __device__ __forceinline__ int rope_index(const GemmParams& p, int64_t r) {
-    const int pj = static_cast<int>(r % p.Dr);
+    const int pj = static_cast<int>(static_cast<uint32_t>(r) % static_cast<uint32_t>(p.Dr));
     if (p.Dr <= 32) return pj;
     const int b = pj >> 5, w = pj & 31;
     return w < 16 ? 16 * b + w : (p.Dr >> 1) + 16 * b + (w - 16);
@@ -135,7 +139,8 @@ struct Epilogue {
       const int64_t rr = rope ? gcol - p.ND : 0;
       const int i0 = rope_index(p, rr);
       const int half = p.Dr >> 1;
-      const int64_t ncol = rope ? p.ND + (rr / p.Dr) * p.Dr + i0 : gcol;
+      const uint32_t hd = static_cast<uint32_t>(rr) / static_cast<uint32_t>(p.Dr);
+      const int64_t ncol = rope ? p.ND + static_cast<int64_t>(hd) * p.Dr + i0 : gcol;
       const int64_t pcol = rope ? (i0 < half ? ncol + half : ncol - half) : gcol;
       r.c4 = ld16(p.cosb + m * p.Dr + i0);
       r.s4 = ld16(p.sinb + m * p.Dr + i0);
@@ -176,9 +181,12 @@ struct Epilogue {
         // per-head product in fragment layout, or 8 row-major elements.
         int64_t off;
         if (p.qc_frag) {
-          const int64_t head = gcol / p.qc_D, d = gcol % p.qc_D;
-          const int64_t lanei = ((d % 16) / 8) * 32 + (m % 32);
-          off = (((head * p.qc_mblocks + m / 32) * (p.qc_D / 16) + d / 16) * 64 + lanei) * 8;
+          const uint32_t gc = static_cast<uint32_t>(gcol), D = static_cast<uint32_t>(p.qc_D);
+          const uint32_t head = gc / D, d = gc - head * D;
+          const uint32_t mm = static_cast<uint32_t>(m);
+          const uint32_t lanei = ((d >> 3) & 1) * 32 + (mm & 31);
+          off = ((static_cast<int64_t>(head) * p.qc_mblocks + (mm >> 5)) * (D >> 4) + (d >> 4)) *
+                    512 + lanei * 8;
         } else {
           off = m * p.ND + gcol;
         }
@@ -191,7 +199,7 @@ struct Epilogue {
         }
       } else {
         const int64_t r = gcol - p.ND;
-        const int64_t head = r / p.Dr;
+        const int64_t head = static_cast<uint32_t>(r) / static_cast<uint32_t>(p.Dr);
         const int i0 = rope_index(p, r);
         const int half = p.Dr >> 1;
         dequant(pre.cs, pre.d, v);
@@ -734,6 +742,295 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Large-M bf16 GEMM (prefill): one TM x 256 output tile per 256-thread
+// workgroup, 4 waves as 2x2 of (TM/2) x 128, each a (TM/64) x 4 grid of
+// 32x32 MFMA blocks (TM = 256: 256 fp32 accumulators per lane in AGPRs, one
+// workgroup per CU; TM = 128: 128, two workgroups per CU).  One stage covers
+// 32 k: for each of its two k-steps, TM/32 A blocks and 8 B blocks of 1 KB
+// each in MFMA operand (lane) order, so every LDS read is one conflict-free
+// ds_read_b128 per lane.  Stages are filled by direct buffer->LDS loads and
+// rotate through NBUF separate LDS arrays: the loads of the next NBUF-1
+// stages fly during the MFMAs of the current one, and before reading a stage
+// a wave waits only for its own loads of it, then one barrier publishes all
+// of them.  (With one array indexed by stage the compiler cannot tell the
+// stages apart and drains every LDS load before each LDS read.)
+// ---------------------------------------------------------------------------
+constexpr int G_TN = 256;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint4* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16,
+                                           static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+}
+
+// Wait until at most N of this wave's loads are in flight, then barrier.
+// The "memory" clobber keeps LDS accesses on their side of it.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear id;
+// when the tiles of one z-slice divide evenly, consecutive chunks of tiles go
+// to one XCD, ordered in groups of G_GROUP tile rows (column index slowest
+// within a group), so the ~32 tiles an XCD runs at once share A and B tiles
+// in its L2.
+constexpr int G_GROUP = 4;
+__device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
+  const int n = nx * ny;
+  int l = static_cast<int>(blockIdx.x) + nx * static_cast<int>(blockIdx.y);
+  if (n % 8 == 0) l = (l % 8) * (n / 8) + l / 8;
+  const int gsz = G_GROUP * nx;
+  const int grp = l / gsz;
+  const int rows = min(G_GROUP, ny - grp * G_GROUP);
+  const int in = l - grp * gsz;
+  ty = grp * G_GROUP + in % rows;
+  tx = in / rows;
+}
+
+// EPI_PARTIAL: blockIdx.z is the split-K index (k-steps [z*steps_per_split,
+// ...), partials at part + z*M*part_ld).  Otherwise blockIdx.z is the batch
+// (head) index.  K must be a multiple of 32 and steps_per_split even.
+template <int EPI, int TM, int NBUF>
+__global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
+  typedef Epilogue<A_BF16, EPI> Epi;
+  constexpr int MA = TM / 32;   // A blocks per k-step
+  constexpr int MI = TM / 64;   // m-blocks per wave
+  constexpr int AW = MA / 4;    // A blocks loaded per wave per k-step
+  constexpr int LPW = 2 * (AW + 2);  // loads per wave per stage
+  static_assert(TM == 256 || TM == 128, "tile height");
+  static_assert(NBUF >= 3 && NBUF <= 4, "stage buffers");
+  __shared__ uint4 sa0[2][MA][64], sa1[2][MA][64], sa2[2][MA][64], sa3[NBUF == 4 ? 2 : 1][MA][64];
+  __shared__ uint4 sb0[2][8][64], sb1[2][8][64], sb2[2][8][64], sb3[NBUF == 4 ? 2 : 1][8][64];
+  auto SA = [&](auto bufc) -> uint4 (&)[2][MA][64] {
+    constexpr int B = decltype(bufc)::value;
+    if constexpr (B == 0) return sa0;
+    else if constexpr (B == 1) return sa1;
+    else if constexpr (B == 2) return sa2;
+    else return *reinterpret_cast<uint4(*)[2][MA][64]>(&sa3);
+  };
+  auto SB = [&](auto bufc) -> uint4 (&)[2][8][64] {
+    constexpr int B = decltype(bufc)::value;
+    if constexpr (B == 0) return sb0;
+    else if constexpr (B == 1) return sb1;
+    else if constexpr (B == 2) return sb2;
+    else return *reinterpret_cast<uint4(*)[2][8][64]>(&sb3);
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wm = w >> 1, wn = w & 1;
+  const int g = lane >> 5, li = lane & 31;
+  const int z = blockIdx.z;
+  const int zb = EPI == EPI_PARTIAL ? 0 : z;  // batch index
+  int tx, ty;
+  gemm_tile(static_cast<int>(gridDim.x), static_cast<int>(gridDim.y), tx, ty);
+
+  const uint4* B;
+  int64_t N, n0, ocol0;
+  if (tx < p.ntiles0) {
+    B = p.B0;
+    N = p.N0;
+    n0 = static_cast<int64_t>(tx) * G_TN;
+    ocol0 = 0;
+  } else {
+    B = p.B1;
+    N = p.N1;
+    n0 = static_cast<int64_t>(tx - p.ntiles0) * G_TN;
+    ocol0 = p.N0;
+  }
+  B += static_cast<int64_t>(zb) * p.b_bstride;
+  const int64_t m0 = static_cast<int64_t>(ty) * TM;
+  const int KC = static_cast<int>(p.K / 8);
+  const int nsteps = static_cast<int>(p.K / 16);
+  int s_lo = 0, s_hi = nsteps;
+  if constexpr (EPI == EPI_PARTIAL) {
+    s_lo = z * static_cast<int>(p.steps_per_split);
+    s_hi = min(s_lo + static_cast<int>(p.steps_per_split), nsteps);
+  }
+  const int nst = s_hi > s_lo ? (s_hi - s_lo) / 2 : 0;
+
+  // B: the tile's 8 column blocks; blocks past N read as zeros.  Wave w
+  // loads blocks 2w and 2w+1 of each k-step.
+  const int64_t nblk = (N + 31) / 32;
+  const int64_t nb0 = n0 / 32;
+  const rsrc_t rb = make_rsrc(B + nb0 * KC * 32, static_cast<uint32_t>((nblk - nb0) * KC * 512));
+  uint32_t vb[2], va[AW];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) vb[j] = lane * 16u + static_cast<uint32_t>((2 * w + j) * KC) * 512u;
+  // A in fragment layout (1 KB per 32-row block and k-step); wave w loads
+  // blocks AW*w .. AW*w+AW-1.  Blocks past the buffer read as zeros.
+  const int64_t mb0 = m0 / 32, mbt = (p.M + 31) / 32;
+  const rsrc_t ra = make_rsrc(static_cast<const char*>(p.A) + zb * p.a_zs + mb0 * p.a_mbs,
+                              static_cast<uint32_t>((mbt - mb0) * p.a_mbs));
+#pragma unroll
+  for (int j = 0; j < AW; ++j) va[j] = lane * 16u + static_cast<uint32_t>((AW * w + j) * p.a_mbs);
+
+  // Loads of stage t (clamped to the last stage: the pipeline always issues
+  // NBUF-1 stages ahead, and a repeated last stage lands in a buffer nobody
+  // reads again).
+  auto issue = [&](auto bufc, int t) {
+    t = t < nst ? t : nst - 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t s = static_cast<uint32_t>(s_lo + 2 * t + ks);
+#pragma unroll
+      for (int j = 0; j < AW; ++j) dma16(ra, va[j], s * 1024u, &SA(bufc)[ks][AW * w + j][0]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dma16(rb, vb[j], s * 1024u, &SB(bufc)[ks][2 * w + j][0]);
+    }
+  };
+
+  f32x16_t acc[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  auto compute = [&](auto bufc) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 a[MI], b[4];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) a[i] = SA(bufc)[ks][MI * wm + i][lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = SB(bufc)[ks][4 * wn + j][lane];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]),
+                                                               acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // One pipeline step: stage t is in buffer BUF.  Every step has issued the
+  // LPW loads per wave of each of the NBUF-2 stages after t, so waiting
+  // until at most that many loads are in flight means this wave's loads of
+  // stage t have landed; the barrier then covers every wave's, and also
+  // tells that all waves are done reading the buffer the step refills
+  // (stage t-1's).  The main loop is branch-free: branches inside it split
+  // the accumulators' live ranges and the register allocator then spills.
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  auto step = [&](auto bufc, int t) {
+    constexpr int BUF = decltype(bufc)::value;
+    vm_barrier<LPW*(NBUF - 2)>();
+    issue(std::integral_constant<int, (BUF + NBUF - 1) % NBUF>{}, t + NBUF - 1);
+    compute(bufc);
+  };
+
+  if (nst > 0) {
+    issue(C0{}, 0);
+    issue(C1{}, 1);
+    if constexpr (NBUF == 4) issue(C2{}, 2);
+    const int nstb = nst / NBUF * NBUF;
+    for (int t = 0; t < nstb; t += NBUF) {
+      step(C0{}, t);
+      step(C1{}, t + 1);
+      step(C2{}, t + 2);
+      if constexpr (NBUF == 4) step(C3{}, t + 3);
+    }
+    // the remaining stages sit in buffers 0.. with q later stages issued
+    const int rem = nst - nstb;
+    if (rem >= 1) {
+      vm_barrier<LPW*(NBUF - 2)>();
+      compute(C0{});
+    }
+    if (rem >= 2) {
+      vm_barrier<LPW*(NBUF - 3)>();
+      compute(C1{});
+    }
+    if constexpr (NBUF == 4) {
+      if (rem >= 3) {
+        vm_barrier<0>();
+        compute(C2{});
+      }
+    }
+  }
+  // No load into LDS outlives the loop, and every wave is done reading the
+  // stage buffers before they hold the epilogue's staging.
+  vm_barrier<0>();
+
+  // Epilogue.  Wave w stages 32-row pieces of its tile (32 x 128 fp32) in
+  // two 8 KB halves of the stage buffers (rows 0-15 and 16-31: waves 0-2 use
+  // their B buffer sb<w>, wave 3 uses sb3 or, with three buffers, sa0 and
+  // sa1), 128 words per row with 32-word halves swapped on every other 4-row
+  // group (so the two lane halves of an accumulator write hit different
+  // banks).  Then each lane takes 8 groups of 8 consecutive columns: 16
+  // lanes cover one row's 128 columns, so a wave's stores are 4 rows x 256
+  // contiguous bytes (bf16).  RoPE partners lie in the same 32-column block,
+  // so in the same row.
+  static_assert(sizeof(sa0) >= 8192, "an A stage buffer holds a 16-row piece");
+  uint32_t* se_lo;
+  uint32_t* se_hi;
+  switch (w) {
+    case 0: se_lo = &sb0[0][0][0].x; se_hi = se_lo + 2048; break;
+    case 1: se_lo = &sb1[0][0][0].x; se_hi = se_lo + 2048; break;
+    case 2: se_lo = &sb2[0][0][0].x; se_hi = se_lo + 2048; break;
+    default:
+      if constexpr (NBUF == 4) {
+        se_lo = &sb3[0][0][0].x;
+        se_hi = se_lo + 2048;
+      } else {
+        se_lo = &sa0[0][0][0].x;
+        se_hi = &sa1[0][0][0].x;
+      }
+      break;
+  }
+  auto sep = [&](int row, int col) -> uint32_t& {
+    uint32_t* base = row < 16 ? se_lo : se_hi;
+    return base[(row & 15) * 128 + (col ^ (((row >> 2) & 1) << 5))];
+  };
+  // Only tiles holding q^R columns need the RoPE tables (uniform per tile).
+  const bool need_pre = EPI == EPI_UQQR && n0 + G_TN > p.ND;
+  GemmParams pe = p;
+  if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(z) * p.M * p.part_ld;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sep(8 * (r >> 2) + 4 * g + (r & 3), 32 * j + li) = __float_as_uint(acc[i][j][r]);
+    // Rolled over 2 batches of 4 groups: the accumulators must stay
+    // statically indexed, which needs the unrolled loop above to stay
+    // small.  A batch issues its RoPE-table loads together.
+#pragma unroll 1
+    for (int k = 0; k < 8; k += 4) {
+      typename Epi::Pre pre[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int it = lane + 64 * (k + u);
+        const int64_t m = m0 + (TM / 2) * wm + 32 * i + (it >> 4);
+        const int64_t gcol = n0 + 128 * wn + (it & 15) * 8;
+        pre[u] = typename Epi::Pre{};
+        if (need_pre && m < p.M && gcol < N) pre[u] = Epi::prefetch(p, m, gcol);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int it = lane + 64 * (k + u);
+        const int row = it >> 4;
+        const int c0 = (it & 15) * 8;
+        const int64_t m = m0 + (TM / 2) * wm + 32 * i + row;
+        const int64_t gcol = n0 + 128 * wn + c0;
+        if (m >= p.M || gcol >= N) continue;
+        uint32_t raw[8], rawp[8];
+        const int poff = Epi::partner_offset(p, gcol);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          raw[e] = sep(row, c0 + e);
+          rawp[e] = poff ? sep(row, c0 + poff + e) : 0u;
+        }
+        Epi::apply(pe, m, gcol, ocol0 + gcol, zb, raw, rawp, pre[u]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Down-projection finish: one workgroup per token, each thread owning 8
 // consecutive columns of the token's Hcq + Hckv + Dr outputs.  Sums the
 // split-K partials in split order, RmsNorms c^Q (and quantises it per token
@@ -970,6 +1267,41 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Activation packing for the 256-tile GEMM: bf16 rows (M, K) into the MFMA
+// fragment layout, where chunk (32-row block mb, k-step s, lane (g, i))
+// holds row 32*mb + i, k in [16s + 8g, 16s + 8g + 8).  One workgroup moves a
+// 32-row x 256-k block through LDS: thread c reads 16 bytes at (row c/32,
+// chunk c%32) -- 512 contiguous bytes per row -- into LDS slot
+// (chunk)*32 + row, which is exactly the block's fragment order, so the
+// writes are 16 KB contiguous.  Rows past M are zeros.
+// ---------------------------------------------------------------------------
+constexpr int PA_STEPS = 16;  // k-steps per workgroup (256 k)
+__global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src,
+                                                uint4* __restrict__ dst, int64_t M, int64_t K) {
+  __shared__ uint4 blk[PA_STEPS * 64];
+  const int64_t steps = K / 16;
+  const int64_t mb = blockIdx.y;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * PA_STEPS;
+  const int ns = static_cast<int>(min<int64_t>(PA_STEPS, steps - s0));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    const int row = c >> 5, q = c & 31;
+    const int64_t m = mb * 32 + row;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (q < 2 * ns && m < M) v = ld16(src + m * K + (s0 * 16 + 8 * q));
+    blk[q * 32 + row] = v;
+  }
+  __syncthreads();
+  uint4* out = dst + (mb * steps + s0) * 64;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int o = threadIdx.x + 256 * u;
+    if (o < ns * 64) st16(out + o, blk[o]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Weight packing into the N32-blocked K16 layout, one thread per 16-byte
 // output chunk (block nb, chunk row kc, column j): the G = 16/eb consecutive
 // k values of column 32*nb + j.  Columns past N (the last block's padding)
@@ -1104,9 +1436,30 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   const bool quant = a->quant_mode != MLA_QUANT_NONE;
   const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
   pl.skinny = T <= 128;
+  pl.gemm256 = !pl.skinny && !quant;
   pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
   const int64_t steps = a->He / 16;
-  if (pl.skinny) {
+  if (pl.gemm256) {
+    // Split the down projection over K so that the 256x256 tiles times the
+    // splits fill whole rounds of the 256 CUs best: minimise
+    // ceil(tiles * ks / 256) / ks over ks <= 4 (more splits cost partial-sum
+    // traffic), with steps per split even (32-k pipeline stages).
+    const int64_t tiles = (T + 255) / 256 *
+                          ((a->Hcq + G_TN - 1) / G_TN + (a->Hckv + a->Dr + G_TN - 1) / G_TN);
+    int64_t best = 1;
+    double best_cost = 1e30;
+    for (int64_t ks = 1; ks <= 4; ++ks) {
+      const double cost = static_cast<double>((tiles * ks + 255) / 256) / static_cast<double>(ks);
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = ks;
+      }
+    }
+    int64_t sps = (steps + best - 1) / best;
+    sps += sps & 1;
+    pl.steps_per_split = sps;
+    pl.ksplit = static_cast<int>((steps + sps - 1) / sps);
+  } else if (pl.skinny) {
     // Split the down projection over K so that (64-column tiles x splits)
     // stays within one wave of workgroups over the 256 CUs (no tail round),
     // at most FIN_MAXSPLIT splits (the finish kernel sums them) and at least
@@ -1123,7 +1476,7 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     pl.steps_per_split = steps;
     pl.ksplit = 1;
   }
-  pl.rows = pl.skinny ? 32 * pl.mb : T;
+  pl.rows = pl.skinny ? 32 * pl.mb : (pl.gemm256 ? (T + 31) / 32 * 32 : T);
   size_t off = 0;
   if (a->weight_layout == MLA_WEIGHT_ND) {
     // packed copies: columns padded to whole 32-column blocks
@@ -1146,6 +1499,8 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   off += align256(static_cast<size_t>(T) * 4);
   pl.off_qc = off;
   off += align256(static_cast<size_t>(pl.rows * a->N * a->D) * (quant ? 4 : 2));
+  pl.off_xfrag = off;
+  if (pl.gemm256) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
   pl.total = T > 0 ? off : 0;
   return pl;
 }
@@ -1195,9 +1550,10 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   void* qc = ws + pl.off_qc;
 
   // ---- A1: x . [W^DQ | W^DKV_KR] -> fp32 (partials) ----
-  // The skinny plan reads c^Q and q^C in fragment layout (written so by the
-  // finish kernel and A6's epilogue); x is read row-major.
-  const bool frag = pl.skinny;
+  // The skinny and 256-tile plans read c^Q and q^C in fragment layout
+  // (written so by the finish kernel and A6's epilogue); x is read
+  // row-major.
+  const bool frag = pl.skinny || pl.gemm256;
   const int64_t mblocks = pl.rows / 32;
   GemmParams g1{};
   g1.A = a->token_x;
@@ -1324,6 +1680,35 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       case 2: skinny_a8<2>(g8, nh, quant, st); break;
       default: skinny_a8<4>(g8, nh, quant, st); break;
     }
+  } else if (pl.gemm256) {
+    // x into fragment layout first: the GEMM's A loads are then 1 KB
+    // contiguous per wave (row-major x costs 32 cache lines per load).
+    hipLaunchKernelGGL(k_pack_a,
+                       dim3(static_cast<unsigned>((a->He / 16 + PA_STEPS - 1) / PA_STEPS),
+                            static_cast<unsigned>(mblocks)),
+                       dim3(256), 0, st, static_cast<const uint16_t*>(a->token_x),
+                       reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, a->He);
+    g1.A = ws + pl.off_xfrag;
+    g1.a_frag = 1;
+    g1.a_mbs = a->He * 64;
+    // A1 and A6: 256x256 tiles, four stage buffers.  A8 (K = D, a short
+    // loop and a large bf16 output): 128x256 tiles and three buffers, two
+    // workgroups per CU so one's stores overlap the other's loads.
+    const unsigned mt = static_cast<unsigned>((T + 255) / 256);
+    g1.ntiles0 = static_cast<int>((g1.N0 + G_TN - 1) / G_TN);
+    const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + G_TN - 1) / G_TN);
+    hipLaunchKernelGGL((k_gemm<EPI_PARTIAL, 256, 4>),
+                       dim3(nt1, mt, static_cast<unsigned>(pl.ksplit)), dim3(256), 0, st, g1);
+    mark(MLA_PHASE_AFTER_DOWN);
+    finish();
+    mark(MLA_PHASE_AFTER_NORM);
+    const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
+    hipLaunchKernelGGL((k_gemm<EPI_UQQR, 256, 4>), dim3(nt6, mt, 1), dim3(256), 0, st, g6);
+    mark(MLA_PHASE_AFTER_UQQR);
+    const unsigned nt8 = static_cast<unsigned>((g8.N0 + G_TN - 1) / G_TN);
+    hipLaunchKernelGGL((k_gemm<EPI_UK, 128, 3>),
+                       dim3(nt8, static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>(nh)),
+                       dim3(256), 0, st, g8);
   } else {
     const unsigned mt = static_cast<unsigned>((T + TBM - 1) / TBM);
     g1.ntiles0 = static_cast<int>((g1.N0 + TBN - 1) / TBN);

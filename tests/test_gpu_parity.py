@@ -103,7 +103,8 @@ def test_pack_weight_uq_qr_bit_exact(N, D, Dr, dtype):
 
 # ---- MLA prolog --------------------------------------------------------------
 
-MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3"]
+MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3",
+             "mla_prefill_ragged"]
 
 
 @pytest.mark.parametrize("key", MLA_SMALL)

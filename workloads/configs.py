@@ -135,6 +135,11 @@ CONFIGS = {
                                 Hcq=512, N=160, D=128, Hckv=1024, Dr=64,
                                 block_num=2, block_size=64, n_skip=1,
                                 seed=2005),
+    # prefill-sized T with no dimension a multiple of the 256x256 GEMM tile
+    "mla_prefill_ragged": MlaConfig("mla_prefill_ragged_T300", B=3, S=100,
+                                    He=512, Hcq=320, N=5, D=64, Hckv=96,
+                                    Dr=32, block_num=4, block_size=128,
+                                    n_skip=7, seed=2006, layout="BSH"),
     "qkv_ragged": QkvConfig("qkv_ragged_B3_S50", B=3, S=50, Nq=4, Nk=2, Nv=2,
                             D=128, block_num=3, block_size=64,
                             quant_mode="symmetric", seed=2101),
