@@ -114,8 +114,12 @@ enum {
  *   The G consecutive-k values of one column form one 16-byte chunk (one
  *   lane's MFMA operand), and each 32-column block's whole K range is one
  *   contiguous run, so a weight-streaming wave reads one contiguous stream.
- *   weight_uk packs each head's (D, Hckv) matrix this way, heads in order.
- *   A packed matrix holds K * NB * 32 elements.  This plays the role that the
+ *   A packed matrix holds K * NB * 32 elements.
+ *   weight_uk is packed by mla_pack_weight_uk(): each head's (D, Hckv)
+ *   matrix this way, heads in order, except that within every 16-k step
+ *   the two 8-k chunks hold k offsets {0-3, 8-11} and {4-7, 12-15} (the
+ *   order in which an MFMA result holds the rows it feeds into the W^UK
+ *   product).  This plays the role that the
  *   pages' FRACTAL_NZ weight format plays for their hardware.
  *   weight_uq_qr is packed by mla_pack_weight_uq_qr(), which also reorders
  *   the W^QR columns when Dr = 64: within each head, packed 32-column block
@@ -227,6 +231,14 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
  * 16 / elem_bytes.  Device pointers; enqueued on `stream`. */
 int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K,
                     int64_t N, int32_t elem_bytes, void* stream);
+
+/* Pack weight_uk, N row-major (D, Hckv) bf16 matrices, into the
+ * MLA_WEIGHT_PACKED_K16 layout with the k order described above, at dst (a
+ * distinct buffer of N * D * ceil(Hckv/32)*32 elements).  D must be a
+ * multiple of 16, else QKVNR_ERR_BAD_SHAPE.  Device pointers; enqueued on
+ * `stream`. */
+int mla_pack_weight_uk(const void* src, void* dst, int64_t N, int64_t D,
+                       int64_t Hckv, void* stream);
 
 /* Pack weight_uq_qr, a row-major (Hcq, N*(D+Dr)) matrix of `elem_bytes` = 2
  * (bf16) or 1 (int8) elements, into the MLA_WEIGHT_PACKED_K16 layout with

@@ -4,7 +4,8 @@ Python names mirror the C ABI in include/qkvnr.h:
 
 * :func:`mla_prolog_v2` - the MlaPrologV2 prolog (c^Q, q^N, q^R, c^KV and
   k^R with paged-cache scatter), non-quantised and partially quantised;
-* :func:`mla_pack_weight` / :func:`mla_pack_weight_uq_qr` - one-time
+* :func:`mla_pack_weight` / :func:`mla_pack_weight_uq_qr` /
+  :func:`mla_pack_weight_uk` - one-time
   packing of a (K, N) weight into the MFMA-native K16 blocked layout the
   prolog streams;
 * :func:`qkv_rmsnorm_rope_cache` - the fused qkv split / RmsNorm / RoPE /
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     QkvnrError,
     load_library,
     mla_pack_weight,
+    mla_pack_weight_uk,
     mla_pack_weight_uq_qr,
     mla_prolog_v2,
     mla_prolog_v2_args,

@@ -37,7 +37,7 @@ QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
 EXPORTS = (
     "qkvnr_status_string", "qkvnr_version", "mla_prolog_v2_workspace_size",
     "mla_prolog_v2_validate", "mla_prolog_v2", "mla_pack_weight",
-    "mla_pack_weight_uq_qr",
+    "mla_pack_weight_uq_qr", "mla_pack_weight_uk",
     "qkv_rmsnorm_rope_cache_validate", "qkv_rmsnorm_rope_cache",
 )
 
@@ -120,6 +120,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_pack_weight.restype = ctypes.c_int
     lib.mla_pack_weight.argtypes = [_vp, _vp, _i64, _i64, _i64, ctypes.c_int32,
                                     _vp]
+    lib.mla_pack_weight_uk.restype = ctypes.c_int
+    lib.mla_pack_weight_uk.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp]
     lib.mla_pack_weight_uq_qr.restype = ctypes.c_int
     lib.mla_pack_weight_uq_qr.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64,
                                           ctypes.c_int32, _vp]
@@ -187,6 +189,21 @@ def mla_pack_weight(w: torch.Tensor, stream=None) -> torch.Tensor:
                       dtype=w.dtype, device=w.device)
     _check(lib.mla_pack_weight(_ptr(w), _ptr(out), batch, K, N, eb,
                                _stream(stream)), "mla_pack_weight")
+    return out
+
+
+def mla_pack_weight_uk(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pack weight_uk (N, D, Hckv) bf16 into the K16 blocked layout with the
+    k order of include/qkvnr.h (MLA_WEIGHT_PACKED_K16).  Returns (N, D, Hp),
+    Hp = Hckv rounded up to a multiple of 32."""
+    lib = load_library()
+    if w.dim() != 3 or w.dtype != torch.bfloat16:
+        raise ValueError("weight_uk must be a bf16 (N, D, Hckv) tensor")
+    N, D, H = w.shape
+    out = torch.empty((N, D, (H + 31) // 32 * 32), dtype=w.dtype,
+                      device=w.device)
+    _check(lib.mla_pack_weight_uk(_ptr(w), _ptr(out), N, D, H,
+                                  _stream(stream)), "mla_pack_weight_uk")
     return out
 
 

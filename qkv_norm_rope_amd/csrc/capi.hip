@@ -215,6 +215,17 @@ int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_
                             static_cast<hipStream_t>(stream));
 }
 
+int mla_pack_weight_uk(const void* src, void* dst, int64_t N, int64_t D, int64_t Hckv,
+                       void* stream) {
+  if (N < 0 || D < 0 || Hckv < 0 || N > 65535 || D > kDimCap || Hckv > kDimCap || D % 16 != 0)
+    return QKVNR_ERR_BAD_SHAPE;
+  if (N * D * Hckv == 0) return QKVNR_OK;
+  if (src == nullptr || dst == nullptr) return QKVNR_ERR_NULL_ARG;
+  if (!aligned16(dst) || (reinterpret_cast<uintptr_t>(src) & 1u)) return QKVNR_ERR_BAD_ALIGNMENT;
+  return launch_pack_weight(src, dst, N, D, Hckv, 2, Hckv, 0, static_cast<hipStream_t>(stream),
+                            /*kperm=*/true);
+}
+
 int mla_pack_weight_uq_qr(const void* src, void* dst, int64_t Hcq, int64_t N, int64_t D,
                           int64_t Dr, int32_t elem_bytes, void* stream) {
   if (elem_bytes != 1 && elem_bytes != 2) return QKVNR_ERR_BAD_MODE;

@@ -16,8 +16,11 @@ int launch_qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* a, hipStream_t 
 // Pack (batch, K, N) row-major weights into the K16 blocked layout; columns
 // from rope_col0 on are rope heads of rope_dim columns, reordered into the
 // partner-in-block order when rope_dim > 32 (rope_col0 = N: no rope columns).
+// kperm (bf16, K % 16 == 0): within each 16-k step the two 8-k chunks hold
+// k offsets {0-3, 8-11} and {4-7, 12-15}.
 int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
-                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream);
+                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream,
+                       bool kperm = false);
 
 // Execution plan of one MlaPrologV2 call: which kernel family runs, the
 // split-K factor of the down projection and the workspace carve-up.  A pure
@@ -25,6 +28,7 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
 struct MlaPlan {
   bool skinny;        // decode-sized T: weight-streaming kernels
   bool gemm256;       // large T, bf16: 256x256-tile MFMA GEMMs
+  bool fuse_uk;       // gemm256 with the W^UK product fused into A6's q^C tiles
   int mb;             // 32-row blocks held per wave (skinny only)
   int ksplit;         // down-projection split-K factor
   int64_t steps_per_split;

@@ -32,7 +32,7 @@ namespace qkvnr {
 
 namespace {
 
-enum EpiKind { EPI_PARTIAL = 0, EPI_UQQR = 1, EPI_UK = 2 };
+enum EpiKind { EPI_PARTIAL = 0, EPI_UQQR = 1, EPI_UK = 2, EPI_QN = 3 };
 
 struct GemmParams {
   // A: activations.  Row-major (a_frag == 0): row m of batch z starts at
@@ -75,10 +75,16 @@ struct GemmParams {
   int64_t qc_mblocks;     // 32-row blocks per head (fragment layout)
   uint16_t* qr_out;  // (T, N, Dr)
   int64_t qr_ld;     // N*Dr
-  // EPI_UK
+  // EPI_UK (and EPI_QN's output)
   uint16_t* q_out;  // (T, N, Hckv)
   int64_t q_ld;     // N*Hckv
   int64_t q_bstride;  // Hckv (per head)
+  // EPI_QN: q^C never leaves registers; the W^UK product runs in the
+  // epilogue.  Buk: packed W^UK (heads uk_bstride chunks apart), uk_N = Hckv;
+  // qc_D is the head dim D.
+  const uint4* Buk;
+  int64_t uk_bstride;
+  int64_t uk_N;
 };
 
 // ---------------------------------------------------------------------------
@@ -179,23 +185,39 @@ struct Epilogue {
         dequant(pre.cs, pre.d, v);
         // 8 columns of q^C = 8 consecutive k of one head: one A chunk of the
         // per-head product in fragment layout, or 8 row-major elements.
-        int64_t off;
         if (p.qc_frag) {
+          // The W^UK product's A operand, in the k order of the packed W^UK:
+          // within a 16-k step, lane half h holds d offsets {4h..4h+3} in
+          // slots 0-3 and {8+4h..8+4h+3} in slots 4-7.  These 8 columns
+          // (d0 = 8*(d/8)) split into two 4-element halves.
           const uint32_t gc = static_cast<uint32_t>(gcol), D = static_cast<uint32_t>(p.qc_D);
           const uint32_t head = gc / D, d = gc - head * D;
           const uint32_t mm = static_cast<uint32_t>(m);
-          const uint32_t lanei = ((d >> 3) & 1) * 32 + (mm & 31);
-          off = ((static_cast<int64_t>(head) * p.qc_mblocks + (mm >> 5)) * (D >> 4) + (d >> 4)) *
-                    512 + lanei * 8;
+          const int64_t base =
+              ((static_cast<int64_t>(head) * p.qc_mblocks + (mm >> 5)) * (D >> 4) + (d >> 4)) * 512 +
+              (mm & 31) * 8 + ((d >> 3) & 1) * 4;  // slots 0-3 or 4-7
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int64_t off = base + hh * 32 * 8;  // lane half hh
+            if (p.qc_f32) {
+              st16(static_cast<float*>(p.qc_out) + off,
+                   make_uint4(__float_as_uint(v[4 * hh]), __float_as_uint(v[4 * hh + 1]),
+                              __float_as_uint(v[4 * hh + 2]), __float_as_uint(v[4 * hh + 3])));
+            } else {
+              st8(static_cast<uint16_t*>(p.qc_out) + off,
+                  make_uint2(pack_bf16x2(v[4 * hh], v[4 * hh + 1]),
+                             pack_bf16x2(v[4 * hh + 2], v[4 * hh + 3])));
+            }
+          }
         } else {
-          off = m * p.ND + gcol;
-        }
-        if (p.qc_f32) {
-          st8f(static_cast<float*>(p.qc_out) + off, v);
-        } else {
-          st16(static_cast<uint16_t*>(p.qc_out) + off,
-               make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+          const int64_t off = m * p.ND + gcol;
+          if (p.qc_f32) {
+            st8f(static_cast<float*>(p.qc_out) + off, v);
+          } else {
+            st16(static_cast<uint16_t*>(p.qc_out) + off,
+                 make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+          }
         }
       } else {
         const int64_t r = gcol - p.ND;
@@ -683,9 +705,21 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int row = wm * 64 + mb * 32 + li;
-        af[mb] = *reinterpret_cast<const uint4*>(sa + row * A_PITCH + ks * 32 + 16 * g);
-        if constexpr (SPLIT)
-          afl[mb] = *reinterpret_cast<const uint4*>(sa + A_STAGE + row * A_PITCH + ks * 32 + 16 * g);
+        if constexpr (EPI == EPI_UK) {
+          // packed W^UK k order: lane half g takes k offsets {4g..4g+3} and
+          // {8+4g..8+4g+3} of the 16-k step
+          auto ld = [&](const char* base) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(base + ks * 32 + 8 * g);
+            const uint2 hi = *reinterpret_cast<const uint2*>(base + ks * 32 + 16 + 8 * g);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+          };
+          af[mb] = ld(sa + row * A_PITCH);
+          if constexpr (SPLIT) afl[mb] = ld(sa + A_STAGE + row * A_PITCH);
+        } else {
+          af[mb] = *reinterpret_cast<const uint4*>(sa + row * A_PITCH + ks * 32 + 16 * g);
+          if constexpr (SPLIT)
+            afl[mb] = *reinterpret_cast<const uint4*>(sa + A_STAGE + row * A_PITCH + ks * 32 + 16 * g);
+        }
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -749,18 +783,29 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
 // 32 k: for each of its two k-steps, TM/32 A blocks and 8 B blocks of 1 KB
 // each in MFMA operand (lane) order, so every LDS read is one conflict-free
 // ds_read_b128 per lane.  Stages are filled by direct buffer->LDS loads and
-// rotate through NBUF separate LDS arrays: the loads of the next NBUF-1
-// stages fly during the MFMAs of the current one, and before reading a stage
-// a wave waits only for its own loads of it, then one barrier publishes all
-// of them.  (With one array indexed by stage the compiler cannot tell the
-// stages apart and drains every LDS load before each LDS read.)
+// rotate through NBUF LDS buffers: the loads of the next NBUF-1 stages fly
+// during the MFMAs of the current one, and before reading a stage a wave
+// waits only for its own loads of it, then one barrier publishes all of
+// them.
 // ---------------------------------------------------------------------------
 constexpr int G_TN = 256;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint4* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16,
-                                           static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+// One wave's 16-byte-per-lane buffer -> LDS load (buffer_load_dwordx4 ...
+// lds): lane l's 16 bytes land at lds + 16*l.  Issued from inline assembly
+// so that the compiler does not track it as an LDS write: it cannot tell
+// this kernel's many stage arrays apart and would otherwise drain every load
+// in flight before each LDS access.  The GEMM orders these loads itself:
+// before reading a stage (or reusing LDS) a wave waits for its own loads
+// with an explicit vmcnt and then a barrier.  Untracked loads only make the
+// compiler's own vmcnt waits stricter (they count in the same in-order
+// counter), never looser.  The asm sets M0; no compiler-generated code in
+// these kernels uses M0.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, const uint4* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(l), "v"(voff),
+               "s"(r), "s"(soff)
+               : "memory");
 }
 
 // Wait until at most N of this wave's loads are in flight, then barrier.
@@ -791,30 +836,49 @@ __device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
 // EPI_PARTIAL: blockIdx.z is the split-K index (k-steps [z*steps_per_split,
 // ...), partials at part + z*M*part_ld).  Otherwise blockIdx.z is the batch
 // (head) index.  K must be a multiple of 32 and steps_per_split even.
-template <int EPI, int TM, int NBUF>
+//
+// EPI_QN (TM = 256, DH = the head dim D = 128): the tile is q^C columns
+// only (two heads), and the W^UK product follows in the epilogue.  The main
+// loop then swaps the MFMA operands, so the accumulators hold q^C
+// transposed: lane l of block (i, j) holds token 32*(4wm+i) + l%32 and, in
+// registers r, q^C columns 32*(4wn+j) + 8(r/4) + 4(l/32) + r%4.  Rounded to
+// bf16, registers 8h..8h+7 are then directly the token-side operand of a
+// 16-k step of the W^UK product -- in exactly the k order mla_pack_weight_uk
+// gives W^UK -- so q^C never leaves the registers.
+template <int EPI, int TM, int NBUF, int DH = 0>
 __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
-  typedef Epilogue<A_BF16, EPI> Epi;
+  typedef Epilogue<A_BF16, EPI == EPI_QN ? EPI_UQQR : EPI> Epi;
+  constexpr bool SWAP = EPI == EPI_QN;
+  static_assert(!SWAP || (TM == 256 && DH == 128 && NBUF == 4),
+                "fused W^UK product: 256-row tiles, one 128-wide head per wave");
   constexpr int MA = TM / 32;   // A blocks per k-step
   constexpr int MI = TM / 64;   // m-blocks per wave
   constexpr int AW = MA / 4;    // A blocks loaded per wave per k-step
   constexpr int LPW = 2 * (AW + 2);  // loads per wave per stage
   static_assert(TM == 256 || TM == 128, "tile height");
   static_assert(NBUF >= 3 && NBUF <= 4, "stage buffers");
-  __shared__ uint4 sa0[2][MA][64], sa1[2][MA][64], sa2[2][MA][64], sa3[NBUF == 4 ? 2 : 1][MA][64];
-  __shared__ uint4 sb0[2][8][64], sb1[2][8][64], sb2[2][8][64], sb3[NBUF == 4 ? 2 : 1][8][64];
+  // Stage t: A blocks in sa<t>, B blocks in sb<t>, per k-step.  (Separate
+  // arrays: with A and B in one array per stage the compiler drains the
+  // loads in flight before each stage's second k-step.  sa3/sb3 are
+  // referenced only with four buffers, so three-buffer instances do not
+  // allocate them.)
+  __shared__ uint4 sa0[2][MA][64], sa1[2][MA][64], sa2[2][MA][64], sa3[2][MA][64];
+  __shared__ uint4 sb0[2][8][64], sb1[2][8][64], sb2[2][8][64], sb3[2][8][64];
   auto SA = [&](auto bufc) -> uint4 (&)[2][MA][64] {
     constexpr int B = decltype(bufc)::value;
+    static_assert(B < NBUF, "stage buffer");
     if constexpr (B == 0) return sa0;
     else if constexpr (B == 1) return sa1;
     else if constexpr (B == 2) return sa2;
-    else return *reinterpret_cast<uint4(*)[2][MA][64]>(&sa3);
+    else return sa3;
   };
   auto SB = [&](auto bufc) -> uint4 (&)[2][8][64] {
     constexpr int B = decltype(bufc)::value;
+    static_assert(B < NBUF, "stage buffer");
     if constexpr (B == 0) return sb0;
     else if constexpr (B == 1) return sb1;
     else if constexpr (B == 2) return sb2;
-    else return *reinterpret_cast<uint4(*)[2][8][64]>(&sb3);
+    else return sb3;
   };
 
   const int lane = threadIdx.x & 63;
@@ -898,9 +962,14 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]),
-                                                               acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (SWAP)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b[j]), as_bf16x8(a[i]),
+                                                                 acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]),
+                                                                 acc[i][j], 0, 0, 0);
+        }
     }
   };
 
@@ -954,16 +1023,138 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
   // stage buffers before they hold the epilogue's staging.
   vm_barrier<0>();
 
+  if constexpr (EPI == EPI_QN) {
+    // q^C as bf16 operand fragments in registers: qc[i][k] = 16-k step k of
+    // the wave's 128 q^C columns (its head) for m-block i.
+    uint4 qc[MI][8];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const f32x16_t& c = acc[i][k >> 1];
+        const int o = 8 * (k & 1);
+        qc[i][k] = make_uint4(pack_bf16x2(c[o], c[o + 1]), pack_bf16x2(c[o + 2], c[o + 3]),
+                              pack_bf16x2(c[o + 4], c[o + 5]), pack_bf16x2(c[o + 6], c[o + 7]));
+      }
+    // The tile's two heads (wn = 0, 1) run the W^UK product over 64-column
+    // passes of Hckv (4 m-blocks x 2 column blocks of accumulators: the rest
+    // of the AGPRs and the VGPRs hold qc).  A pass's W^UK operands (2 heads x
+    // 8 k-steps x 2 column blocks of 1 KB) are loaded into LDS by
+    // buffer->LDS loads one pass ahead: pass buffer b is stage b's arrays,
+    // sa<b> for the pass's first column block and sb<b> for its second
+    // (16 KB each), as [head*8 + k-step][lane].
+    constexpr int PB = 2;
+    const int KC2 = DH / 8;
+    const int64_t nblk2 = (p.uk_N + 31) / 32;
+    const int npass = static_cast<int>((nblk2 + PB - 1) / PB);
+    const int64_t head0 = n0 / DH;
+    const int hs = w >> 1, kw = 4 * (w & 1);  // this wave's load share: head hs, k-steps kw..kw+3
+    const rsrc_t ruk = make_rsrc(p.Buk + (head0 + hs) * p.uk_bstride,
+                                 static_cast<uint32_t>(nblk2 * KC2 * 512));
+    auto issue_uk = [&](auto bc, int pp) {
+#pragma unroll
+      for (int jb = 0; jb < PB; ++jb) {
+        int64_t nb2 = PB * pp + jb;
+        nb2 = nb2 < nblk2 ? nb2 : nblk2 - 1;  // clamped blocks are never stored
+        const uint32_t vo = lane * 16u + static_cast<uint32_t>(nb2 * KC2) * 512u;
+        uint4* dst = jb == 0 ? &SA(bc)[0][0][0] : &SB(bc)[0][0][0];  // jb is static
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+          dma16(ruk, vo, static_cast<uint32_t>(kw + k4) * 1024u, dst + (hs * 8 + kw + k4) * 64);
+      }
+    };
+    const int64_t head = head0 + wn;
+    // Output staging: a 4 KB slice per wave of its own array.
+    __shared__ uint4 qn_stage[4][256];
+    char* stg = reinterpret_cast<char*>(&qn_stage[w][0]);
+    const bool rows_in = m0 + 128 * wm + 127 < p.M;  // all of this wave's tokens are rows
+    // Returns whether the pass issued exactly 16 stores (all in range).
+    auto pass_uk = [&](auto bc, int pp) -> bool {
+      f32x16_t o[MI][PB];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jb = 0; jb < PB; ++jb) o[i][jb] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 wf[PB];
+#pragma unroll
+        for (int jb = 0; jb < PB; ++jb)
+          wf[jb] = (jb == 0 ? &SA(bc)[0][0][0] : &SB(bc)[0][0][0])[(wn * 8 + ks) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int jb = 0; jb < PB; ++jb)
+            o[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[jb]), as_bf16x8(qc[i][ks]),
+                                                                o[i][jb], 0, 0, 0);
+      }
+      // o[i][jb]: lane l holds token 32*(4wm+i) + l%32, registers r the
+      // output columns 32*(PB*pp+jb) + 8(r/4) + 4g + r%4.  Transpose each
+      // m-block through the wave's 4 KB staging slice (32 tokens x 64 columns
+      // bf16, 16-byte chunk c of row t stored at chunk c ^ (t & 7)); then
+      // each store instruction writes 8 whole 128-byte rows.
+      const int cc = lane & 7;
+      const int64_t nc = 64 * pp + 8 * cc;
+      const bool full = rows_in && 64 * (pp + 1) <= p.uk_N;  // uniform per wave
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int jb = 0; jb < PB; ++jb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = (4 * jb + q) ^ (li & 7);
+            *reinterpret_cast<uint2*>(stg + li * 128 + c * 16 + g * 8) =
+                make_uint2(pack_bf16x2(o[i][jb][4 * q], o[i][jb][4 * q + 1]),
+                           pack_bf16x2(o[i][jb][4 * q + 2], o[i][jb][4 * q + 3]));
+          }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int tr = 8 * k + (lane >> 3);
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + tr * 128 + ((cc ^ (tr & 7)) * 16));
+          const int64_t m = m0 + 128 * wm + 32 * i + tr;
+          if (full || (m < p.M && nc < p.uk_N))
+            st16(p.q_out + m * p.q_ld + head * p.q_bstride + nc, v);
+        }
+      }
+      return full;
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    // Each step: wait for this wave's loads of the pass -- only the previous
+    // pass's 16 stores were issued after them when that pass was full, so
+    // those stay in flight -- then a barrier (everybody's loads landed,
+    // everybody done with the other buffer), start the next pass's loads,
+    // compute and store.
+    auto wait_pass = [&](bool prev_full) {
+      if (prev_full)
+        vm_barrier<16>();
+      else
+        vm_barrier<0>();
+    };
+    issue_uk(P0{}, 0);
+    bool prev_full = false;
+    for (int pp = 0; pp < npass; pp += 2) {
+      wait_pass(prev_full);
+      if (pp + 1 < npass) issue_uk(P1{}, pp + 1);
+      prev_full = pass_uk(P0{}, pp);
+      if (pp + 1 >= npass) break;
+      wait_pass(prev_full);
+      if (pp + 2 < npass) issue_uk(P0{}, pp + 2);
+      prev_full = pass_uk(P1{}, pp + 1);
+    }
+    return;
+  }
+
   // Epilogue.  Wave w stages 32-row pieces of its tile (32 x 128 fp32) in
-  // two 8 KB halves of the stage buffers (rows 0-15 and 16-31: waves 0-2 use
-  // their B buffer sb<w>, wave 3 uses sb3 or, with three buffers, sa0 and
-  // sa1), 128 words per row with 32-word halves swapped on every other 4-row
-  // group (so the two lane halves of an accumulator write hit different
-  // banks).  Then each lane takes 8 groups of 8 consecutive columns: 16
-  // lanes cover one row's 128 columns, so a wave's stores are 4 rows x 256
-  // contiguous bytes (bf16).  RoPE partners lie in the same 32-column block,
-  // so in the same row.
-  static_assert(sizeof(sa0) >= 8192, "an A stage buffer holds a 16-row piece");
+  // two 8 KB halves (rows 0-15 and 16-31) of B stage buffer sb<w> (with
+  // three buffers, wave 3 uses sa0 and sa1), 128 words
+  // per row with 32-word halves swapped on every other 4-row group (so the
+  // two lane halves of an accumulator write hit different banks).  Then
+  // each lane takes 8 groups of 8 consecutive columns: 16 lanes cover one
+  // row's 128 columns, so a wave's stores are 4 rows x 256 contiguous bytes
+  // (bf16).  RoPE partners lie in the same 32-column block, so in the same
+  // row.
+  static_assert(sizeof(sb0) >= 16384 && sizeof(sa0) >= 8192, "staging space");
   uint32_t* se_lo;
   uint32_t* se_hi;
   switch (w) {
@@ -972,7 +1163,7 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
     case 2: se_lo = &sb2[0][0][0].x; se_hi = se_lo + 2048; break;
     default:
       if constexpr (NBUF == 4) {
-        se_lo = &sb3[0][0][0].x;
+        se_lo = &SB(std::integral_constant<int, 3>{})[0][0][0].x;
         se_hi = se_lo + 2048;
       } else {
         se_lo = &sa0[0][0][0].x;
@@ -1311,7 +1502,7 @@ __global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint4* __restrict__ dst,
                                               int64_t batch, int64_t K, int64_t N, int eb,
-                                              int64_t rope_col0, int64_t rope_dim) {
+                                              int64_t rope_col0, int64_t rope_dim, int kperm) {
   const int G = 16 / eb;
   const int64_t KC = K / G;
   const int64_t nblk = (N + 31) / 32;
@@ -1334,9 +1525,13 @@ __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint
       }
       const char* s = src + ((b * K + kc * G) * N + ns) * eb;
       if (eb == 2) {
+        // kperm: chunk kc = 2*step + h holds k = 16*step + {4h..4h+3, 8+4h..8+4h+3}
+        const char* s2 = src + ((b * K + (kc & ~int64_t(1)) * G) * N + ns) * eb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const uint32_t v = *reinterpret_cast<const uint16_t*>(s + static_cast<int64_t>(e) * N * 2);
+          const int64_t ke = kperm ? ((e < 4 ? 0 : 8) + 4 * (kc & 1) + (e & 3)) : e;
+          const uint32_t v =
+              *reinterpret_cast<const uint16_t*>((kperm ? s2 : s) + ke * N * 2);
           w[e >> 1] |= v << (16 * (e & 1));
         }
       } else {
@@ -1418,7 +1613,8 @@ void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
 }  // namespace
 
 int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
-                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream) {
+                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream,
+                       bool kperm) {
   const int G = 16 / elem_bytes;
   const int64_t total = batch * (K / G) * ((N + 31) / 32) * 32;
   if (total == 0) return QKVNR_OK;
@@ -1426,7 +1622,7 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(k_pack, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                      static_cast<const char*>(src), static_cast<uint4*>(dst), batch, K, N,
-                     elem_bytes, rope_col0, rope_dim);
+                     elem_bytes, rope_col0, rope_dim, kperm ? 1 : 0);
   return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;
 }
 
@@ -1477,6 +1673,10 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     pl.ksplit = 1;
   }
   pl.rows = pl.skinny ? 32 * pl.mb : (pl.gemm256 ? (T + 31) / 32 * 32 : T);
+  // Prefill fuses the W^UK product into the q^C tiles of A6 when a wave's
+  // 128 q^C columns are exactly one head (D = 128) and the q^C columns end
+  // on a tile boundary.
+  pl.fuse_uk = pl.gemm256 && a->D == 128 && (a->N * a->D) % G_TN == 0;
   size_t off = 0;
   if (a->weight_layout == MLA_WEIGHT_ND) {
     // packed copies: columns padded to whole 32-column blocks
@@ -1526,7 +1726,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
                               a->N * a->D, a->Dr, st);
     if (rc == QKVNR_OK)
       rc = launch_pack_weight(a->weight_uk, ws + pl.off_wuk, a->N, a->D, a->Hckv, 2, a->Hckv, 0,
-                              st);
+                              st, /*kperm=*/true);
     if (rc != QKVNR_OK) return rc;
     wdq = reinterpret_cast<const uint4*>(ws + pl.off_wdq);
     wdkvkr = reinterpret_cast<const uint4*>(ws + pl.off_wdkvkr);
@@ -1702,13 +1902,38 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
-    const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
-    hipLaunchKernelGGL((k_gemm<EPI_UQQR, 256, 4>), dim3(nt6, mt, 1), dim3(256), 0, st, g6);
-    mark(MLA_PHASE_AFTER_UQQR);
-    const unsigned nt8 = static_cast<unsigned>((g8.N0 + G_TN - 1) / G_TN);
-    hipLaunchKernelGGL((k_gemm<EPI_UK, 128, 3>),
-                       dim3(nt8, static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>(nh)),
-                       dim3(256), 0, st, g8);
+    if (pl.fuse_uk) {
+      // q^R: the W^QR columns alone (packed columns from N*D on; with the
+      // rope region at column 0 every column is a rope column).
+      const int64_t ND = a->N * a->D;
+      GemmParams gr = g6;
+      gr.B0 = wuqqr + (ND / 32) * (a->Hcq / 8) * 32;
+      gr.N0 = a->N * a->Dr;
+      gr.ND = 0;
+      hipLaunchKernelGGL((k_gemm<EPI_UQQR, 256, 4>),
+                         dim3(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt, 1), dim3(256),
+                         0, st, gr);
+      mark(MLA_PHASE_AFTER_UQQR);
+      // q^C tiles with the W^UK product in the epilogue.
+      GemmParams gq = g6;
+      gq.N0 = ND;
+      gq.Buk = wuk;
+      gq.uk_bstride = g8.b_bstride;
+      gq.uk_N = a->Hckv;
+      gq.q_out = g8.q_out;
+      gq.q_ld = g8.q_ld;
+      gq.q_bstride = g8.q_bstride;
+      hipLaunchKernelGGL((k_gemm<EPI_QN, 256, 4, 128>),
+                         dim3(static_cast<unsigned>(ND / G_TN), mt, 1), dim3(256), 0, st, gq);
+    } else {
+      const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
+      hipLaunchKernelGGL((k_gemm<EPI_UQQR, 256, 4>), dim3(nt6, mt, 1), dim3(256), 0, st, g6);
+      mark(MLA_PHASE_AFTER_UQQR);
+      const unsigned nt8 = static_cast<unsigned>((g8.N0 + G_TN - 1) / G_TN);
+      hipLaunchKernelGGL((k_gemm<EPI_UK, 128, 3>),
+                         dim3(nt8, static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>(nh)),
+                         dim3(256), 0, st, g8);
+    }
   } else {
     const unsigned mt = static_cast<unsigned>((T + TBM - 1) / TBM);
     g1.ntiles0 = static_cast<int>((g1.N0 + TBN - 1) / TBN);

@@ -126,7 +126,7 @@ def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None):
         wdkvkr = qn.mla_pack_weight(d["weight_dkv_kr"])
         wuqqr = qn.mla_pack_weight_uq_qr(d["weight_uq_qr"], cfg.N, cfg.D,
                                          cfg.Dr)
-        wuk = qn.mla_pack_weight(d["weight_uk"])
+        wuk = qn.mla_pack_weight_uk(d["weight_uk"])
         lay = qn.MLA_WEIGHT_PACKED_K16
     else:
         wdq, wdkvkr, wuqqr, wuk = (d["weight_dq"], d["weight_dkv_kr"],

@@ -187,6 +187,17 @@ def test_pack_weight_validation():
                                None) == -9
 
 
+def test_pack_weight_uk_validation():
+    lib = b.load_library()
+    f = lib.mla_pack_weight_uk
+    assert f(None, None, 2, 24, 32, None) == -2        # D % 16
+    assert f(None, None, -1, 32, 32, None) == -2
+    assert f(None, None, 0, 32, 32, None) == 0         # empty: nothing
+    assert f(None, None, 2, 32, 32, None) == -1
+    assert f(ctypes.c_void_p(fake()), ctypes.c_void_p(fake() + 8), 2, 32, 32,
+             None) == -9
+
+
 def test_pack_weight_uq_qr_validation():
     lib = b.load_library()
     f = lib.mla_pack_weight_uq_qr

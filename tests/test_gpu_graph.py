@@ -21,8 +21,9 @@ NAMES = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk", "weight_dkv_kr",
 
 def _prepared(w, d):
     cfg = w.cfg
-    for k in ("weight_dq", "weight_dkv_kr", "weight_uk"):
+    for k in ("weight_dq", "weight_dkv_kr"):
         d[k] = qn.mla_pack_weight(d[k])
+    d["weight_uk"] = qn.mla_pack_weight_uk(d["weight_uk"])
     d["weight_uq_qr"] = qn.mla_pack_weight_uq_qr(d["weight_uq_qr"], cfg.N,
                                                  cfg.D, cfg.Dr)
     q = torch.empty((cfg.T, cfg.N, cfg.Hckv), dtype=torch.bfloat16,

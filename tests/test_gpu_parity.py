@@ -101,6 +101,27 @@ def test_pack_weight_uq_qr_bit_exact(N, D, Dr, dtype):
     np.testing.assert_array_equal(got.view(want.dtype), want)
 
 
+@pytest.mark.parametrize("N,D,H", [(3, 32, 40), (2, 128, 512), (1, 16, 32)])
+def test_pack_weight_uk_bit_exact(N, D, H):
+    gh.announce(f"pack uk N={N} D={D} Hckv={H}")
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 16, size=(N, D, H), dtype=np.uint16)
+    t = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    p = qn.mla_pack_weight_uk(t)
+    torch.cuda.synchronize()
+    got = gh.raw_bits(p).reshape(-1)
+    # k order inside each 16-k step: {0-3, 8-11, 4-7, 12-15}
+    perm = np.concatenate([16 * s + np.array([0, 1, 2, 3, 8, 9, 10, 11,
+                                              4, 5, 6, 7, 12, 13, 14, 15])
+                           for s in range(D // 16)])
+    src = bits[:, perm, :]
+    Hp = (H + 31) // 32 * 32
+    pad = np.zeros((N, D, Hp), dtype=np.uint16)
+    pad[:, :, :H] = src
+    want = pad.reshape(N, D // 8, 8, Hp // 32, 32).transpose(0, 3, 1, 4, 2).reshape(-1)
+    np.testing.assert_array_equal(got.view(np.uint16), want)
+
+
 # ---- MLA prolog --------------------------------------------------------------
 
 MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3",
