@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="first run a plain device copy of MB megabytes "
+                         "(a known-size reference for HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -94,6 +97,54 @@ def qkv_bytes(c, n_valid):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, as measured by the rocprofv3 counter
+# runs recorded under profiles/ (FETCH_SIZE and WRITE_SIZE, scaled by the
+# counters of a plain copy of known size).  Reported only while the kernel
+# source still hashes to what was profiled; otherwise null.
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                            "profiles", "mla_decode_up_projection_hbm_traffic.md")
+KERNEL_SOURCES = ("qkv_norm_rope_amd/csrc/mla_prolog_v2.hip",
+                  "qkv_norm_rope_amd/csrc/device_common.h",
+                  "qkv_norm_rope_amd/csrc/mla_device.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """(bytes per launch, source hash) from the traffic summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        for key in ("traffic_bytes_per_launch", "source_sha256"):
+            if line.strip().startswith(key + " ="):
+                vals[key] = line.split("=", 1)[1].strip()
+    if len(vals) != 2:
+        return None
+    return float(vals["traffic_bytes_per_launch"]), vals["source_sha256"]
+
+
+def calibrate_copy(torch, mb):
+    n = mb * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
 
 def prepare_mla_sets(w, n_sets, torch, qn, gh):
     """Upload one seeded workload, pack its weights, and clone it n_sets-1
@@ -143,10 +194,10 @@ class HipEvents:
         def __init__(self, handle):
             self.cuda_event = handle
 
-    def create(self):
+    def create(self, flags=None):
         h = self.ct.c_void_p()
-        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(h),
-                                              self.RELEASE_TO_DEVICE)
+        rc = self.hip.hipEventCreateWithFlags(
+            self.ct.byref(h), self.RELEASE_TO_DEVICE if flags is None else flags)
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
         return self.Event(h.value)
@@ -176,11 +227,14 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     """Time `steps` calls cycling over the sets.
 
     Returns (ms per step under HIP-graph replay, or eager when graph is
-    False; per-phase ms from the eager region; eager ms per step).  The
-    eager region records the library's phase events (device-scope release)
-    on every step, with the GPU held until the whole region is enqueued.
+    False; per-phase ms from the eager region; eager ms per step; per-kernel
+    ms).  The eager region records, on every step, the library's phase
+    events (device-scope release, between its launches) and its per-kernel
+    start/stop events (taken by each main kernel's own dispatch), with the
+    GPU held until the whole region is enqueued.
     """
     nph = len(qn.MLA_PHASES)
+    nk = len(qn.MLA_KERNELS)
     kw = dict(quant_mode=cfg.quant_mode, rmsnorm_epsilon_cq=cfg.eps_cq,
               rmsnorm_epsilon_ckv=cfg.eps_ckv)
     names = ("token_x", "weight_dq", "weight_uq_qr", "weight_uk",
@@ -195,6 +249,7 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     stream = torch.cuda.current_stream()
     he = HipEvents()
     ev = [[he.create() for _ in range(nph)] for _ in range(steps)]
+    kev = [[he.create(0) for _ in range(2 * nk)] for _ in range(steps)]
     for i in range(warmup):
         calls[i % len(calls)]()
     torch.cuda.synchronize()
@@ -202,7 +257,7 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     _hold_gpu(torch, 5.0 + 0.1 * steps)
     he.record(t0, stream)
     for i in range(steps):
-        calls[i % len(calls)](phase_events=ev[i])
+        calls[i % len(calls)](phase_events=ev[i], kernel_events=kev[i])
     he.record(t1, stream)
     torch.cuda.synchronize()
     ms_eager = he.elapsed_ms(t0, t1) / steps
@@ -210,7 +265,11 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     for row in ev:
         for p in range(nph - 1):
             phase_ms[p] += he.elapsed_ms(row[p], row[p + 1]) / steps
-    for row in ev:
+    kernel_ms = [0.0] * nk
+    for row in kev:
+        for k in range(nk):
+            kernel_ms[k] += he.elapsed_ms(row[2 * k], row[2 * k + 1]) / steps
+    for row in ev + kev:
         for e in row:
             he.destroy(e)
     ms_step = ms_eager
@@ -232,7 +291,7 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
         del g
     he.destroy(t0)
     he.destroy(t1)
-    return ms_step, phase_ms, ms_eager
+    return ms_step, phase_ms, ms_eager, kernel_ms
 
 
 def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
@@ -316,17 +375,23 @@ def main():
     qn.load_library()  # fail loudly without the HIP library
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.calibrate_copy > 0:
+        calibrate_copy(torch, args.calibrate_copy)
+
     # ---- decode, T = 32 -------------------------------------------------
     w = make_workload(1)
     cfg = w.cfg
     sets = prepare_mla_sets(w, args.rotate, torch, qn, gh)
-    ms, phase_ms, ms_eager = run_mla(cfg, sets, args.steps, args.warmup,
-                                     torch, qn)
+    ms, phase_ms, ms_eager, kernel_ms = run_mla(cfg, sets, args.steps,
+                                                args.warmup, torch, qn)
     step_bytes = mla_bytes(cfg)
-    a6_ms = phase_ms[2]
+    a6_ms = kernel_ms[2]  # the up projection's own start/stop events
     a6_bytes = uqqr_bytes(cfg)
     a6_gbs = a6_bytes / (a6_ms * 1e-3) / 1e9
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    rec = recorded_traffic()
+    traffic = rec[0] if rec is not None and rec[1] == kernel_source_hash() \
+        else None
     out = {
         "metric": METRIC,
         "value": cfg.T / (ms * 1e-3),
@@ -350,17 +415,20 @@ def main():
         "roofline": {"kernel": "up projection c^Q.[W^UQ|W^QR] + RoPE q^R",
                      "bound": "hbm", "achieved": a6_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": a6_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": a6_bytes,
+                     "traffic": traffic, "algorithmic_bytes": a6_bytes,
                      "avg_launch_us": a6_ms * 1e3},
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes,
                           "achieved": step_gbs, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS},
+        "kernel_us": dict(zip(qn.MLA_KERNELS, [k * 1e3 for k in kernel_ms])),
         "phase_us": dict(zip(("down", "norm_cache", "up_qr", "uk"),
                              [p * 1e3 for p in phase_ms])),
         "timing": "value and ms_per_step: HIP-graph replay of the prepared "
-                  "calls; phase_us and roofline: device-release HIP events "
-                  "the library records between its launches in an eager "
-                  "region of the same steps",
+                  "calls; kernel_us and roofline: start/stop events taken "
+                  "by each main kernel's own dispatch (hipExtLaunchKernel, "
+                  "on the launch stream) in an eager region of the same "
+                  "steps; phase_us: events recorded between the launches "
+                  "(kernel plus dispatch)",
         "eager": {"ms_per_step": ms_eager,
                   "tokens_per_s": cfg.T / (ms_eager * 1e-3)},
     }
@@ -373,19 +441,22 @@ def main():
         pc = wp.cfg
         psets = prepare_mla_sets(wp, 1, torch, qn, gh)
         psteps = max(3, args.steps // 20)
-        pms, pph, _ = run_mla(pc, psets, psteps, max(2, args.warmup // 10),
-                              torch, qn, graph=False)
+        pms, pph, _, pk = run_mla(pc, psets, psteps,
+                                  max(2, args.warmup // 10), torch, qn,
+                                  graph=False)
         fl = mla_flops(pc)
         # The prefill plan fuses q^C.W^UK into the q^C tiles of the up
         # projection: the two launches after the norm phase (q^R tiles, then
         # q^C tiles with the W^UK product) are one roofline unit.
         upf = uqqr_flops(pc) + uk_flops(pc)
-        up_ms = pph[2] + pph[3]
+        up_ms = pk[2] + pk[3]
         out["prefill"] = {
             "workload": pc.name, "tokens_per_s": pc.T / (pms * 1e-3),
             "ms_per_step": pms, "steps": psteps, "algorithmic_flops": fl,
             "step_TFLOPs": fl / (pms * 1e-3) / 1e12,
             "mfma_frac": fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "kernel_us": dict(zip(("down", "norm", "up_qr_rope",
+                                   "up_qc_uk"), [k * 1e3 for k in pk])),
             "phase_us": dict(zip(("down", "norm_cache", "up_qr_rope",
                                   "up_qc_uk"),
                                  [p * 1e3 for p in pph])),

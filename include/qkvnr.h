@@ -195,7 +195,27 @@ typedef struct MlaPrologV2Args {
    * ND-layout weight packing happens before MLA_PHASE_START. */
   void* const* phase_events;
   int32_t n_phase_events;
+
+  /* ---- optional per-kernel timing (host array of hipEvent_t handles) ----
+   * When n_kernel_events > 2*i+1, the main kernel MLA_KERNEL_i below is
+   * launched with kernel_events[2*i] and kernel_events[2*i+1] as its start
+   * and stop events (hipExtLaunchKernel: taken by the kernel's own dispatch,
+   * so their interval is the kernel's execution time).  The work is exactly
+   * that of a normal call. */
+  void* const* kernel_events;
+  int32_t n_kernel_events;
 } MlaPrologV2Args;
+
+/* The main kernels of one call, for kernel_events.  With the large-T plan
+ * that fuses the W^UK product, MLA_KERNEL_UQQR is the q^R-column launch and
+ * MLA_KERNEL_UK the q^C-column launch with the fused W^UK product. */
+enum {
+  MLA_KERNEL_DOWN = 0,  /* x . [W^DQ | W^DKV_KR] */
+  MLA_KERNEL_NORM = 1,  /* RmsNorms, c^Q quant, RoPE k^R, cache scatter */
+  MLA_KERNEL_UQQR = 2,  /* c^Q . [W^UQ | W^QR], RoPE q^R */
+  MLA_KERNEL_UK = 3,    /* q^C . W^UK per head */
+  MLA_KERNEL_COUNT = 4
+};
 
 /* Phase boundaries of one mla_prolog_v2 call, in launch order; each one
  * follows one kernel. */

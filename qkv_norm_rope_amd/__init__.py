@@ -18,6 +18,7 @@ All work runs in the HIP library ``lib/libqkvnr.so``; build it with
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    MLA_KERNELS,
     MLA_PHASES,
     MLA_QUANT,
     MLA_WEIGHT_ND,

@@ -31,6 +31,7 @@ MLA_QUANT = {"none": 0, "partial_kv_bf16": 1, "partial_kv_int8": 2,
              "full_kv_bf16": 3, "full_kv_int8": 4}
 MLA_WEIGHT_ND, MLA_WEIGHT_PACKED_K16 = 0, 1
 MLA_PHASES = ("start", "after_down", "after_norm", "after_uqqr", "after_uk")
+MLA_KERNELS = ("down", "norm", "uqqr", "uk")
 QKV_QUANT = {"none": 0, "symmetric": 1, "asymmetric": 2}
 QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
 
@@ -67,6 +68,7 @@ class MlaPrologV2Args(ctypes.Structure):
         ("query", _vp), ("query_rope", _vp), ("dequant_scale_q_nope", _vp),
         ("dbg_cq_int8", _vp), ("dbg_cq_scale", _vp),
         ("phase_events", ctypes.POINTER(_vp)), ("n_phase_events", ctypes.c_int32),
+        ("kernel_events", ctypes.POINTER(_vp)), ("n_kernel_events", ctypes.c_int32),
     ]
 
 
@@ -308,7 +310,7 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   quant_scale_ckr=None, smooth_scales_cq=None,
                   query=None, query_rope=None, workspace=None,
                   return_cq_quant=False, cache_mode=None, stream=None,
-                  phase_events=None):
+                  phase_events=None, kernel_events=None):
     """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
 
     Returns (query, query_rope), plus (cq_int8, cq_scale) when
@@ -350,6 +352,11 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
         handles = (_vp * len(phase_events))(*[e.cuda_event for e in phase_events])
         a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
         a.n_phase_events = len(phase_events)
+    if kernel_events:
+        khandles = (_vp * len(kernel_events))(
+            *[e.cuda_event for e in kernel_events])
+        a.kernel_events = ctypes.cast(khandles, ctypes.POINTER(_vp))
+        a.n_kernel_events = len(kernel_events)
     nbytes = mla_prolog_v2_workspace_size(a)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -395,17 +402,31 @@ class PreparedMlaPrologV2:
         self._ref = ctypes.byref(self.args)
         self.query, self.query_rope = query, query_rope
 
-    def __call__(self, stream=None, phase_events=None):
+    def __call__(self, stream=None, phase_events=None, kernel_events=None):
+        """phase_events: MLA_PHASES events recorded between the launches;
+        kernel_events: 2 * len(MLA_KERNELS) events, (start, stop) of each
+        main kernel taken at its dispatch.  Either may be a list of
+        torch.cuda.Event or of raw hipEvent_t handles (ints)."""
         a = self.args
+
+        def handles_of(evs):
+            return (_vp * len(evs))(*[getattr(e, "cuda_event", e) for e in evs])
         if phase_events:
-            handles = (_vp * len(phase_events))(
-                *[e.cuda_event for e in phase_events])
+            handles = handles_of(phase_events)
             a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
             a.n_phase_events = len(phase_events)
         else:
             handles = None
             a.n_phase_events = 0
             a.phase_events = None
+        if kernel_events:
+            khandles = handles_of(kernel_events)
+            a.kernel_events = ctypes.cast(khandles, ctypes.POINTER(_vp))
+            a.n_kernel_events = len(kernel_events)
+        else:
+            khandles = None
+            a.n_kernel_events = 0
+            a.kernel_events = None
         rc = self._lib.mla_prolog_v2(self._ref, self._ws, self._nbytes,
                                      _stream(stream))
         _check(rc, "mla_prolog_v2")

@@ -31,6 +31,8 @@ int validate_mla(const MlaPrologV2Args* a) {
   if (a->struct_size != sizeof(MlaPrologV2Args) || a->reserved0 != 0) return QKVNR_ERR_BAD_STRUCT;
   if (a->n_phase_events < 0 || (a->n_phase_events > 0 && a->phase_events == nullptr))
     return QKVNR_ERR_NULL_ARG;
+  if (a->n_kernel_events < 0 || (a->n_kernel_events > 0 && a->kernel_events == nullptr))
+    return QKVNR_ERR_NULL_ARG;
   if (a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8)
     return QKVNR_ERR_UNSUPPORTED;
   if (a->quant_mode < MLA_QUANT_NONE || a->quant_mode > MLA_QUANT_PARTIAL_KV_INT8)

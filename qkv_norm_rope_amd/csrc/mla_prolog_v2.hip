@@ -22,6 +22,8 @@
 // Weights arrive in the K16 blocked layout (see mla_pack_weight in the
 // public header): the 8 (bf16) or 16 (int8) consecutive-k values of one
 // column are one 16-byte chunk, which is exactly one lane's MFMA operand.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "device_common.h"
@@ -1548,14 +1550,30 @@ __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// One launch: the stream and, when the caller asked for per-kernel timing,
+// the start and stop events (hipExtLaunchKernel takes them at the kernel's
+// own dispatch, so they bracket exactly its execution).
+struct Launch {
+  hipStream_t st;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+template <typename F, typename... Args>
+void launch(const Launch& L, F kernel, dim3 grid, dim3 block, uint32_t shmem, Args... args) {
+  if (L.start != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, L.st, L.start, L.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shmem, L.st, args...);
+}
+
 template <int AK, int MB, int NB, int NW, int KW, int EPI>
-void skinny(const GemmParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_skinny<AK, MB, NB, NW, KW, EPI>), grid, dim3(64 * NW * KW), 0, st, p);
+void skinny(const GemmParams& p, dim3 grid, const Launch& L) {
+  launch(L, k_skinny<AK, MB, NB, NW, KW, EPI>, grid, dim3(64 * NW * KW), 0, p);
 }
 
 template <int AK, int EPI>
-void tiled(const GemmParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_tiled<AK, EPI>), grid, dim3(256), 0, st, p);
+void tiled(const GemmParams& p, dim3 grid, const Launch& L) {
+  launch(L, k_tiled<AK, EPI>, grid, dim3(256), 0, p);
 }
 
 // Decode plan: three weight-streaming launches plus the down-projection
@@ -1578,36 +1596,35 @@ constexpr int kA1Cols = 64;  // A1 tile width (two column blocks per wave)
 // A1 reads x row-major: with one 32-row block each workgroup stages its
 // split of x in LDS (fragment order), otherwise lanes load rows directly.
 template <int MB>
-void skinny_a1(const GemmParams& g1, const MlaPlan& pl, hipStream_t st) {
+void skinny_a1(const GemmParams& g1, const MlaPlan& pl, const Launch& L) {
   const dim3 grid(static_cast<unsigned>(g1.ntiles0 + (g1.N1 + kA1Cols - 1) / kA1Cols),
                   static_cast<unsigned>(pl.ksplit), 1);
   constexpr int KW = a1_kw<MB>();
   if constexpr (MB == 1) {
     if (pl.steps_per_split <= A_LDS_STEPS) {
-      hipLaunchKernelGGL((k_skinny<A_BF16, 1, 2, 1, KW, EPI_PARTIAL,
-                                   SkinnyDepth<A_BF16, 1, 2>::value, true>),
-                         grid, dim3(64 * KW), 0, st, g1);
+      launch(L, k_skinny<A_BF16, 1, 2, 1, KW, EPI_PARTIAL, SkinnyDepth<A_BF16, 1, 2>::value, true>,
+             grid, dim3(64 * KW), 0, g1);
       return;
     }
   }
-  skinny<A_BF16, MB, 2, 1, KW, EPI_PARTIAL>(g1, grid, st);
+  skinny<A_BF16, MB, 2, 1, KW, EPI_PARTIAL>(g1, grid, L);
 }
 template <int MB>
-void skinny_a6(const GemmParams& g6, bool quant, hipStream_t st) {
+void skinny_a6(const GemmParams& g6, bool quant, const Launch& L) {
   const unsigned nt = static_cast<unsigned>((g6.N0 + kA6Cols - 1) / kA6Cols);
   if (quant)
-    skinny<A_I8, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+    skinny<A_I8, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
   else
-    skinny<A_BF16, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), st);
+    skinny<A_BF16, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
 }
 template <int MB>
-void skinny_a8(const GemmParams& g8, int nheads, bool quant, hipStream_t st) {
+void skinny_a8(const GemmParams& g8, int nheads, bool quant, const Launch& L) {
   constexpr int NW = a8_nw<MB>();
   const unsigned nt = static_cast<unsigned>((g8.N0 + 32 * NW - 1) / (32 * NW));
   if (quant)
-    skinny<A_F32SPLIT, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
+    skinny<A_F32SPLIT, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), L);
   else
-    skinny<A_BF16, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), st);
+    skinny<A_BF16, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), L);
 }
 
 }  // namespace
@@ -1847,14 +1864,29 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
   const dim3 fin_block(static_cast<unsigned>(fin_threads(ntot)));
 
+  // Launch contexts of the main kernels (optional per-kernel timing).
+  Launch Lk[MLA_KERNEL_COUNT];
+  for (int i = 0; i < MLA_KERNEL_COUNT; ++i) {
+    Lk[i] = {st, nullptr, nullptr};
+    if (a->n_kernel_events > 2 * i + 1) {
+      Lk[i].start = static_cast<hipEvent_t>(a->kernel_events[2 * i]);
+      Lk[i].stop = static_cast<hipEvent_t>(a->kernel_events[2 * i + 1]);
+    }
+  }
+  const Launch L0{st, nullptr, nullptr};
+  const Launch& L1 = Lk[MLA_KERNEL_DOWN];
+  const Launch& Lf = Lk[MLA_KERNEL_NORM];
+  const Launch& L6 = Lk[MLA_KERNEL_UQQR];
+  const Launch& L8 = Lk[MLA_KERNEL_UK];
+
   auto finish = [&]() {
     const dim3 grid(static_cast<unsigned>(T));
     if (qm == 0)
-      hipLaunchKernelGGL(k_down_finish<0>, grid, fin_block, fin_smem, st, f);
+      launch(Lf, k_down_finish<0>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
     else if (qm == 1)
-      hipLaunchKernelGGL(k_down_finish<1>, grid, fin_block, fin_smem, st, f);
+      launch(Lf, k_down_finish<1>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
     else
-      hipLaunchKernelGGL(k_down_finish<2>, grid, fin_block, fin_smem, st, f);
+      launch(Lf, k_down_finish<2>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
   };
 
   const int nh = static_cast<int>(a->N);
@@ -1862,32 +1894,32 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   if (pl.skinny) {
     g1.ntiles0 = static_cast<int>((g1.N0 + kA1Cols - 1) / kA1Cols);
     switch (pl.mb) {
-      case 1: skinny_a1<1>(g1, pl, st); break;
-      case 2: skinny_a1<2>(g1, pl, st); break;
-      default: skinny_a1<4>(g1, pl, st); break;
+      case 1: skinny_a1<1>(g1, pl, L1); break;
+      case 2: skinny_a1<2>(g1, pl, L1); break;
+      default: skinny_a1<4>(g1, pl, L1); break;
     }
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
     switch (pl.mb) {
-      case 1: skinny_a6<1>(g6, quant, st); break;
-      case 2: skinny_a6<2>(g6, quant, st); break;
-      default: skinny_a6<4>(g6, quant, st); break;
+      case 1: skinny_a6<1>(g6, quant, L6); break;
+      case 2: skinny_a6<2>(g6, quant, L6); break;
+      default: skinny_a6<4>(g6, quant, L6); break;
     }
     mark(MLA_PHASE_AFTER_UQQR);
     switch (pl.mb) {
-      case 1: skinny_a8<1>(g8, nh, quant, st); break;
-      case 2: skinny_a8<2>(g8, nh, quant, st); break;
-      default: skinny_a8<4>(g8, nh, quant, st); break;
+      case 1: skinny_a8<1>(g8, nh, quant, L8); break;
+      case 2: skinny_a8<2>(g8, nh, quant, L8); break;
+      default: skinny_a8<4>(g8, nh, quant, L8); break;
     }
   } else if (pl.gemm256) {
     // x into fragment layout first: the GEMM's A loads are then 1 KB
     // contiguous per wave (row-major x costs 32 cache lines per load).
-    hipLaunchKernelGGL(k_pack_a,
-                       dim3(static_cast<unsigned>((a->He / 16 + PA_STEPS - 1) / PA_STEPS),
-                            static_cast<unsigned>(mblocks)),
-                       dim3(256), 0, st, static_cast<const uint16_t*>(a->token_x),
-                       reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, a->He);
+    launch(L0, k_pack_a,
+           dim3(static_cast<unsigned>((a->He / 16 + PA_STEPS - 1) / PA_STEPS),
+                static_cast<unsigned>(mblocks)),
+           dim3(256), 0, static_cast<const uint16_t*>(a->token_x),
+           reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, a->He);
     g1.A = ws + pl.off_xfrag;
     g1.a_frag = 1;
     g1.a_mbs = a->He * 64;
@@ -1897,8 +1929,8 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     const unsigned mt = static_cast<unsigned>((T + 255) / 256);
     g1.ntiles0 = static_cast<int>((g1.N0 + G_TN - 1) / G_TN);
     const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + G_TN - 1) / G_TN);
-    hipLaunchKernelGGL((k_gemm<EPI_PARTIAL, 256, 4>),
-                       dim3(nt1, mt, static_cast<unsigned>(pl.ksplit)), dim3(256), 0, st, g1);
+    launch(L1, k_gemm<EPI_PARTIAL, 256, 4>, dim3(nt1, mt, static_cast<unsigned>(pl.ksplit)),
+           dim3(256), 0, g1);
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
@@ -1910,9 +1942,8 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gr.B0 = wuqqr + (ND / 32) * (a->Hcq / 8) * 32;
       gr.N0 = a->N * a->Dr;
       gr.ND = 0;
-      hipLaunchKernelGGL((k_gemm<EPI_UQQR, 256, 4>),
-                         dim3(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt, 1), dim3(256),
-                         0, st, gr);
+      launch(L6, k_gemm<EPI_UQQR, 256, 4>,
+             dim3(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt, 1), dim3(256), 0, gr);
       mark(MLA_PHASE_AFTER_UQQR);
       // q^C tiles with the W^UK product in the epilogue.
       GemmParams gq = g6;
@@ -1923,36 +1954,36 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gq.q_out = g8.q_out;
       gq.q_ld = g8.q_ld;
       gq.q_bstride = g8.q_bstride;
-      hipLaunchKernelGGL((k_gemm<EPI_QN, 256, 4, 128>),
-                         dim3(static_cast<unsigned>(ND / G_TN), mt, 1), dim3(256), 0, st, gq);
+      launch(L8, k_gemm<EPI_QN, 256, 4, 128>, dim3(static_cast<unsigned>(ND / G_TN), mt, 1),
+             dim3(256), 0, gq);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
-      hipLaunchKernelGGL((k_gemm<EPI_UQQR, 256, 4>), dim3(nt6, mt, 1), dim3(256), 0, st, g6);
+      launch(L6, k_gemm<EPI_UQQR, 256, 4>, dim3(nt6, mt, 1), dim3(256), 0, g6);
       mark(MLA_PHASE_AFTER_UQQR);
       const unsigned nt8 = static_cast<unsigned>((g8.N0 + G_TN - 1) / G_TN);
-      hipLaunchKernelGGL((k_gemm<EPI_UK, 128, 3>),
-                         dim3(nt8, static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>(nh)),
-                         dim3(256), 0, st, g8);
+      launch(L8, k_gemm<EPI_UK, 128, 3>,
+             dim3(nt8, static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>(nh)),
+             dim3(256), 0, g8);
     }
   } else {
     const unsigned mt = static_cast<unsigned>((T + TBM - 1) / TBM);
     g1.ntiles0 = static_cast<int>((g1.N0 + TBN - 1) / TBN);
     const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + TBN - 1) / TBN);
-    tiled<A_BF16, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), st);
+    tiled<A_BF16, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), L1);
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
     const unsigned nt6 = static_cast<unsigned>((g6.N0 + TBN - 1) / TBN);
     if (quant)
-      tiled<A_I8, EPI_UQQR>(g6, dim3(nt6, mt, 1), st);
+      tiled<A_I8, EPI_UQQR>(g6, dim3(nt6, mt, 1), L6);
     else
-      tiled<A_BF16, EPI_UQQR>(g6, dim3(nt6, mt, 1), st);
+      tiled<A_BF16, EPI_UQQR>(g6, dim3(nt6, mt, 1), L6);
     mark(MLA_PHASE_AFTER_UQQR);
     const unsigned nt8 = static_cast<unsigned>((g8.N0 + TBN - 1) / TBN);
     if (quant)
-      tiled<A_F32SPLIT, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), st);
+      tiled<A_F32SPLIT, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
     else
-      tiled<A_BF16, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), st);
+      tiled<A_BF16, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
   }
   mark(MLA_PHASE_AFTER_UK);
   return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;
