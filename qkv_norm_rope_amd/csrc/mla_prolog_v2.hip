@@ -268,11 +268,18 @@ struct SkinnyDepth {
 };
 
 // A_LDS_STEPS: most k-steps of one split whose A operand (32 rows, bf16) a
-// workgroup can stage in LDS (64 KB).
+// workgroup stages in LDS by default (64 KB).
 constexpr int A_LDS_STEPS = 64;
 
+// Where the skinny kernel's A operand comes from: global memory on every
+// k-step, or staged once per workgroup in LDS (in fragment order) from a
+// row-major or a fragment-layout A.  Staging reads A once per workgroup
+// instead of once per wave, and leaves the vector-memory queue to the weight
+// stream.
+enum { ALDS_NONE = 0, ALDS_ROWMAJOR = 1, ALDS_FRAG = 2 };
+
 template <int AK, int MB, int NB, int NW, int KW, int EPI,
-          int P = SkinnyDepth<AK, MB, NB>::value, bool ALDS = false>
+          int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS>
 __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   typedef typename AccT<AK>::type Acc;
   constexpr int KSTEP = (AK == A_I8) ? 32 : 16;  // k per MFMA
@@ -281,10 +288,10 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   constexpr int PITCH = TN + 4;  // words per LDS row
   constexpr int NA = (AK == A_F32SPLIT) ? 2 : 1;  // 16-byte A loads per fragment
   __shared__ uint32_t lds[KW][MB * 32][PITCH];
-  // ALDS: row-major A (bf16, MB = 1) staged in fragment order for this
-  // workgroup's split: chunk (step s, lane) at s*64 + lane.
-  static_assert(!ALDS || (MB == 1 && AK == A_BF16), "LDS-staged A: one bf16 row block");
-  __shared__ uint4 alds[ALDS ? A_LDS_STEPS * 64 : 1];
+  // LDS-staged A (bf16, MB = 1), up to ACAP k-steps of this workgroup's
+  // split in fragment order: chunk (step s, lane) at (s - s_lo)*64 + lane.
+  static_assert(ALDS == ALDS_NONE || (MB == 1 && AK == A_BF16), "LDS-staged A: one bf16 row block");
+  __shared__ uint4 alds[ALDS != ALDS_NONE ? ACAP * 64 : 1];
 
   const int lane = threadIdx.x & 63;
   // Wave-level quantities live in SGPRs: the per-step load offsets below are
@@ -407,7 +414,7 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       const int s = (s0 + u) < s_last ? (s0 + u) : s_last;
-      if constexpr (ALDS) {
+      if constexpr (ALDS != ALDS_NONE) {
         x.a[u][0][0] = alds[(s - s_lo) * 64 + lane];
       } else {
 #pragma unroll
@@ -454,7 +461,32 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   // current batch's MFMAs.  The last prefetch re-reads the final batch (cache
   // hits) so the load sequence never depends on a branch.
   Batch X, Y;
-  if constexpr (ALDS) if (cnt > 0) {  // cnt is uniform over the workgroup
+  if constexpr (ALDS == ALDS_FRAG) if (cnt > 0) {  // cnt is uniform over the workgroup
+    // Fragment-layout A: the split's chunks are one contiguous run of
+    // 64*cnt 16-byte chunks, copied straight into LDS (cnt <= ACAP).
+    constexpr int NT = 64 * NW * KW;
+    constexpr int PER = (ACAP * 64 + NT - 1) / NT;
+    const int total = 64 * cnt;
+    const rsrc_t rx = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_zs +
+                                    static_cast<int64_t>(s_lo) * 1024,
+                                static_cast<uint32_t>(total) * 16u);
+    uint4 st[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = static_cast<int>(threadIdx.x) + i * NT;
+      c = c < total ? c : total - 1;
+      st[i] = bld16(rx, static_cast<uint32_t>(c) * 16u, 0u);
+    }
+    load_b(X, w_lo);  // unconditional: a branch here would drain the staging loads
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = static_cast<int>(threadIdx.x) + i * NT;
+      if (c < total) alds[c] = st[i];
+    }
+    lds_barrier();  // keeps the first weight batch in flight
+    if (w_lo < w_hi) load_a(X, w_lo);
+  }
+  if constexpr (ALDS == ALDS_ROWMAJOR) if (cnt > 0) {
     // Stage rows 0..31 of A over this split's k range [16*s_lo, 16*s_hi):
     // thread c of the 64*cnt 16-byte chunks takes row c / (2*cnt), chunk
     // c % (2*cnt), so each wave reads 1 KB of consecutive row bytes.  Rows
@@ -491,7 +523,7 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   }
   if (w_lo < w_hi) {
     int s = w_lo;
-    if constexpr (!ALDS) load(X, s);
+    if constexpr (ALDS == ALDS_NONE) load(X, s);
     for (;;) {
       load(Y, s + P < w_hi ? s + P : s);
       compute(X, w_hi - s);
@@ -1578,12 +1610,14 @@ void tiled(const GemmParams& p, dim3 grid, const Launch& L) {
 
 // Decode plan: three weight-streaming launches plus the down-projection
 // finish (launched between A1 and A6).  Many short per-wave weight runs keep
-// the most bytes in flight.  A1: 64-column tiles (two column blocks per
-// wave) with the K range split over ksplit workgroups and, inside one, over
-// 8 waves (fewer when more 32-row blocks fill the registers).  A6: 96-column
-// tiles, three waves across with one column block each and K over two waves
-// (256 tiles for the DeepSeek-V3 shape: one per CU).  A8: 4 waves on
-// different column blocks of one head.
+// the most bytes in flight.  A1: 64-column tiles with the K range split over
+// ksplit workgroups and, inside one, over 8 waves (fewer when more 32-row
+// blocks fill the registers); with one row block, x is staged in LDS and two
+// waves across take one column block each.  A6: 96-column tiles, three waves
+// across with one column block each (256 tiles for the DeepSeek-V3 shape:
+// one per CU); with one row block each wave streams the whole K in batches
+// of 8 k-steps, otherwise K is split over waves.  A8: 4 waves on different
+// column blocks of one head, the head's q^C staged in LDS.
 template <int MB>
 constexpr int a1_kw() { return MB >= 4 ? 2 : (MB == 2 ? 4 : 8); }
 template <int MB>
@@ -1602,8 +1636,9 @@ void skinny_a1(const GemmParams& g1, const MlaPlan& pl, const Launch& L) {
   constexpr int KW = a1_kw<MB>();
   if constexpr (MB == 1) {
     if (pl.steps_per_split <= A_LDS_STEPS) {
-      launch(L, k_skinny<A_BF16, 1, 2, 1, KW, EPI_PARTIAL, SkinnyDepth<A_BF16, 1, 2>::value, true>,
-             grid, dim3(64 * KW), 0, g1);
+      // one column block per wave, two waves across, K over 8 waves
+      launch(L, k_skinny<A_BF16, 1, 1, 2, KW, EPI_PARTIAL, 4, ALDS_ROWMAJOR>, grid,
+             dim3(64 * 2 * KW), 0, g1);
       return;
     }
   }
@@ -1614,17 +1649,26 @@ void skinny_a6(const GemmParams& g6, bool quant, const Launch& L) {
   const unsigned nt = static_cast<unsigned>((g6.N0 + kA6Cols - 1) / kA6Cols);
   if (quant)
     skinny<A_I8, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
+  else if constexpr (MB == 1)
+    // each wave streams its column block over the whole K, 8 k-steps per batch
+    launch(L, k_skinny<A_BF16, 1, 1, 3, 1, EPI_UQQR, 8>, dim3(nt, 1, 1), dim3(64 * 3), 0, g6);
   else
     skinny<A_BF16, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
 }
+// A8 stages a head's q^C (K = D <= 16 k-steps) in LDS once per workgroup.
+constexpr int A8_LDS_STEPS = 16;
 template <int MB>
 void skinny_a8(const GemmParams& g8, int nheads, bool quant, const Launch& L) {
   constexpr int NW = a8_nw<MB>();
   const unsigned nt = static_cast<unsigned>((g8.N0 + 32 * NW - 1) / (32 * NW));
+  const dim3 grid(nt, 1, static_cast<unsigned>(nheads));
   if (quant)
-    skinny<A_F32SPLIT, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), L);
+    skinny<A_F32SPLIT, MB, 1, NW, 1, EPI_UK>(g8, grid, L);
+  else if (MB == 1 && g8.K / 16 <= A8_LDS_STEPS && g8.a_frag)
+    launch(L, k_skinny<A_BF16, 1, 1, NW, 1, EPI_UK, 4, ALDS_FRAG, A8_LDS_STEPS>, grid,
+           dim3(64 * NW), 0, g8);
   else
-    skinny<A_BF16, MB, 1, NW, 1, EPI_UK>(g8, dim3(nt, 1, nheads), L);
+    skinny<A_BF16, MB, 1, NW, 1, EPI_UK>(g8, grid, L);
 }
 
 }  // namespace
