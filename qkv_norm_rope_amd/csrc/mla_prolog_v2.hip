@@ -278,9 +278,12 @@ constexpr int A_LDS_STEPS = 64;
 // stream.
 enum { ALDS_NONE = 0, ALDS_ROWMAJOR = 1, ALDS_FRAG = 2 };
 
+// One tile of the skinny GEMM: tile bx (column tiles of B0 then of B1),
+// split by, batch bz; run by a 64*NW*KW-thread workgroup.
 template <int AK, int MB, int NB, int NW, int KW, int EPI,
           int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS>
-__global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
+__device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, const int by,
+                                            const int bz) {
   typedef typename AccT<AK>::type Acc;
   constexpr int KSTEP = (AK == A_I8) ? 32 : 16;  // k per MFMA
   constexpr int G = (AK == A_I8) ? 16 : 8;       // k per 16-byte chunk
@@ -301,26 +304,26 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
   const int kw = wave / NW;
   const int g = lane >> 5;
   const int li = lane & 31;
-  const int z = blockIdx.z;
+  const int z = bz;
 
   const uint4* B;
   int64_t N, n0, ocol0;
-  if (static_cast<int>(blockIdx.x) < p.ntiles0) {
+  if (bx < p.ntiles0) {
     B = p.B0;
     N = p.N0;
-    n0 = static_cast<int64_t>(blockIdx.x) * TN;
+    n0 = static_cast<int64_t>(bx) * TN;
     ocol0 = 0;
   } else {
     B = p.B1;
     N = p.N1;
-    n0 = static_cast<int64_t>(blockIdx.x - p.ntiles0) * TN;
+    n0 = static_cast<int64_t>(bx - p.ntiles0) * TN;
     ocol0 = p.N0;
   }
   B += static_cast<int64_t>(z) * p.b_bstride;
   const int KC = static_cast<int>(p.K / G);  // 16-byte chunk rows per column
 
   const int nsteps = static_cast<int>(p.K / KSTEP);
-  const int s_lo = static_cast<int>(blockIdx.y * p.steps_per_split);
+  const int s_lo = static_cast<int>(by * p.steps_per_split);
   const int s_hi = min(s_lo + static_cast<int>(p.steps_per_split), nsteps);
   const int cnt = s_hi > s_lo ? s_hi - s_lo : 0;
   const int w_lo = s_lo + cnt * kw / KW;
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
 
   // Epilogue: 8-column groups of the (MB*32) x TN tile.
   GemmParams pe = p;
-  if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(blockIdx.y) * p.M * p.part_ld;
+  if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(by) * p.M * p.part_ld;
   for (int it = threadIdx.x; it < GROUPS; it += 64 * NW * KW) {
     const int row = it / (TN / 8);
     const int c0 = (it % (TN / 8)) * 8;
@@ -593,6 +596,14 @@ __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
     }
     Epi::apply(pe, m, gcol, ocol0 + gcol, z, raw, rawp, pre);
   }
+}
+
+template <int AK, int MB, int NB, int NW, int KW, int EPI,
+          int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS>
+__global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
+  skinny_tile<AK, MB, NB, NW, KW, EPI, P, ALDS, ACAP>(p, static_cast<int>(blockIdx.x),
+                                                     static_cast<int>(blockIdx.y),
+                                                     static_cast<int>(blockIdx.z));
 }
 
 // ---------------------------------------------------------------------------

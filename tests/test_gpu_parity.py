@@ -193,7 +193,7 @@ def test_mla_prefill_partial_quant_tiled_path():
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
-@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3])
+@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3, "mla_dec_t13"])
 def test_mla_deterministic(key):
     w = make_workload(key)
     gh.announce(f"mla determinism {w.cfg.name}")
@@ -240,8 +240,9 @@ def test_mla_T0_and_no_slots():
 
 
 # decode-sized shapes beyond the small list: a ragged T = 21 (one partial
-# 32-row block) and wider N / Hckv than one pass of 256 workgroups covers
-DECODE_CASES = ["mla_ragged_t21", "mla_wide"]
+# 32-row block), wider N / Hckv than one pass of 256 workgroups covers, and
+# two head-dim-128 shapes with partial tiles and batches
+DECODE_CASES = ["mla_ragged_t21", "mla_wide", "mla_dec_t13", "mla_dec_hckv96"]
 
 
 def _decode_case(key):

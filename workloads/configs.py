@@ -135,6 +135,17 @@ CONFIGS = {
                                 Hcq=512, N=160, D=128, Hckv=1024, Dr=64,
                                 block_num=2, block_size=64, n_skip=1,
                                 seed=2005),
+    # decode shapes with head dim 128: a partial row block, 2 W^UK column
+    # blocks per wave and half a 64-column q^R tile
+    "mla_dec_t13": MlaConfig("mla_dec_T13", B=13, S=1, He=512, Hcq=384,
+                             N=7, D=128, Hckv=256, Dr=32, block_num=3,
+                             block_size=16, n_skip=2, seed=2012),
+    # Hcq of 10 k-steps (a partial register batch) and Hckv of 3 column
+    # blocks
+    "mla_dec_hckv96": MlaConfig("mla_dec_hckv96_T32", B=32, S=1, He=256,
+                                Hcq=160, N=3, D=128, Hckv=96, Dr=64,
+                                block_num=2, block_size=32, n_skip=1,
+                                seed=2013),
     # prefill-sized T with no dimension a multiple of the 256x256 GEMM tile
     "mla_prefill_ragged": MlaConfig("mla_prefill_ragged_T300", B=3, S=100,
                                     He=512, Hcq=320, N=5, D=64, Hckv=96,
