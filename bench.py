@@ -315,14 +315,23 @@ def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
     for i in range(warmup):
         call(sets[i % 2])
     torch.cuda.synchronize()
+    # host cost of one call (argument marshalling), to hold the GPU for the
+    # whole enqueue of the timed region: no host gaps inside it
+    h0 = time.perf_counter()
+    for i in range(warmup):
+        call(sets[i % 2])
+    host_ms = (time.perf_counter() - h0) * 1e3 / max(1, warmup)
+    torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    _hold_gpu(torch, 5.0)
+    _hold_gpu(torch, 5.0 + 2.0 * host_ms * steps)
+    h0 = time.perf_counter()
     t0.record(s)
     for i in range(steps):
         call(sets[i % 2])
     t1.record(s)
+    enqueue_ms = (time.perf_counter() - h0) * 1e3
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     n_valid = int((w.arrays["index"] >= 0).sum())
@@ -330,7 +339,8 @@ def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": cfg.name, "tokens_per_s": cfg.T / (ms * 1e-3),
             "ms_per_step": ms, "algorithmic_bytes": nbytes,
-            "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+            "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "host_enqueue_ms": enqueue_ms}
 
 
 def cpu_baseline(w, seconds):
