@@ -1302,6 +1302,7 @@ struct FinishParams {
 
 constexpr int FIN_MAX_THREADS = 1024;
 constexpr int FIN_MAXSPLIT = 8;
+constexpr int FIN_SPLIT_SMALL = 4;  // the large-T plan's split-K bound
 
 // Workgroup size of the finish kernel for ntot columns: one thread per
 // 8-column chunk, whole waves, at most FIN_MAX_THREADS (more chunks loop).
@@ -1342,7 +1343,9 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
 }
 
 // QM: 0 none, 1 partial with bf16 caches, 2 partial with int8 caches.
-template <int QM>
+// MAXS: most splits summed (ksplit <= MAXS); fewer keep more workgroups
+// resident (the large-T plan splits at most 4 ways).
+template <int QM, int MAXS = FIN_MAXSPLIT>
 __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p) {
   extern __shared__ float row[];  // Hcq + Hckv + Dr summed values
   __shared__ float2 red[FIN_MAX_THREADS / 64];
@@ -1380,14 +1383,14 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
   for (int j = threadIdx.x; j < nch; j += blockDim.x) {
     const int c0 = 8 * j;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float v[FIN_MAXSPLIT][8];
+    float v[MAXS][8];
 #pragma unroll
-    for (int s = 0; s < FIN_MAXSPLIT; ++s) {
+    for (int s = 0; s < MAXS; ++s) {
       const int se = s < p.ksplit ? s : p.ksplit - 1;
       ld8f(p.part + (static_cast<int64_t>(se) * p.T + t) * ntot + c0, v[s]);
     }
 #pragma unroll
-    for (int s = 0; s < FIN_MAXSPLIT; ++s)
+    for (int s = 0; s < MAXS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += s < p.ksplit ? v[s][e] : 0.f;
 #pragma unroll
@@ -1936,7 +1939,10 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
 
   auto finish = [&]() {
     const dim3 grid(static_cast<unsigned>(T));
-    if (qm == 0)
+    if (qm == 0 && pl.ksplit <= FIN_SPLIT_SMALL)
+      launch(Lf, k_down_finish<0, FIN_SPLIT_SMALL>, grid, fin_block,
+             static_cast<uint32_t>(fin_smem), f);
+    else if (qm == 0)
       launch(Lf, k_down_finish<0>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
     else if (qm == 1)
       launch(Lf, k_down_finish<1>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
