@@ -75,3 +75,44 @@ def test_mla_graph_replays_match_eager(key):
         np.testing.assert_array_equal(gh.raw_bits(d["kv_cache"]), ref["kv"])
         np.testing.assert_array_equal(gh.raw_bits(d["kr_cache"]), ref["kr"])
     del g
+
+
+@pytest.mark.parametrize("key", [4, "qkv_ragged_asym"])
+def test_qkv_graph_replays_match_eager(key):
+    w = make_workload(key)
+    cfg = w.cfg
+    gh.announce(f"graph replay {cfg.name}")
+    d = gh.upload(w)
+    kc0, vc0 = d["k_cache"].clone(), d["v_cache"].clone()
+    q = torch.empty((cfg.T, cfg.Nq, cfg.D), dtype=d["qkv"].dtype, device="cuda")
+
+    def call(dd, out):
+        qn.qkv_rmsnorm_rope_cache(
+            dd["qkv"], dd["gamma_q"], dd["gamma_k"], dd["cos"], dd["sin"],
+            dd["index"], dd["k_cache"], dd["v_cache"], Nq=cfg.Nq, Nk=cfg.Nk,
+            Nv=cfg.Nv, quant_mode=cfg.quant_mode, epsilon=cfg.eps,
+            k_scale=dd.get("k_scale"), v_scale=dd.get("v_scale"),
+            k_offset=dd.get("k_offset"), v_offset=dd.get("v_offset"),
+            q_out=out, B=cfg.B, S=cfg.S)
+
+    call(d, q)
+    torch.cuda.synchronize()
+    ref = {"q": gh.raw_bits(q), "k": gh.raw_bits(d["k_cache"]),
+           "v": gh.raw_bits(d["v_cache"])}
+    d2 = gh.upload(w)
+    q2 = torch.empty_like(q)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(d, q)
+    for rep in range(3):
+        q.zero_()
+        d["k_cache"].copy_(kc0)
+        d["v_cache"].copy_(vc0)
+        call(d2, q2)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gh.raw_bits(q), ref["q"], err_msg=f"rep {rep}")
+        np.testing.assert_array_equal(gh.raw_bits(d["k_cache"]), ref["k"])
+        np.testing.assert_array_equal(gh.raw_bits(d["v_cache"]), ref["v"])
+    del g
