@@ -834,6 +834,13 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
 // them.
 // ---------------------------------------------------------------------------
 constexpr int G_TN = 256;
+// 128-row tiles (three stage buffers, 72 KB of LDS, at most 181 VGPRs) let
+// two workgroups share a CU, so one's epilogue stores overlap the other's
+// main loop; the prefill q^R and down-projection GEMMs use them (14% and 4%
+// faster than 256-row tiles at T = 4096).  The fused q^C + W^UK tiles stay
+// 256 rows: each tile loads its two heads' W^UK, and 128-row tiles double
+// that traffic (437 vs 320 us).
+constexpr int G_TM_HALF = 128;
 
 // One wave's 16-byte-per-lane buffer -> LDS load (buffer_load_dwordx4 ...
 // lds): lane l's 16 bytes land at lds + 16*l.  Issued from inline assembly
@@ -853,11 +860,15 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, co
                : "memory");
 }
 
-// Wait until at most N of this wave's loads are in flight, then barrier.
-// The "memory" clobber keeps LDS accesses on their side of it.
+// Wait until at most N of this wave's loads are in flight and all of its
+// LDS reads have returned, then barrier.  The "memory" clobber keeps LDS
+// accesses on their side of it; lgkmcnt(0) also covers reads whose
+// consumers (MFMAs, which touch no memory) the compiler placed after the
+// barrier: once every wave has passed it, a buffer may be refilled by
+// buffer->LDS loads while such a read would still be pending.
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear id;
@@ -1081,14 +1092,16 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
         qc[i][k] = make_uint4(pack_bf16x2(c[o], c[o + 1]), pack_bf16x2(c[o + 2], c[o + 3]),
                               pack_bf16x2(c[o + 4], c[o + 5]), pack_bf16x2(c[o + 6], c[o + 7]));
       }
-    // The tile's two heads (wn = 0, 1) run the W^UK product over 64-column
-    // passes of Hckv (4 m-blocks x 2 column blocks of accumulators: the rest
-    // of the AGPRs and the VGPRs hold qc).  A pass's W^UK operands (2 heads x
-    // 8 k-steps x 2 column blocks of 1 KB) are loaded into LDS by
-    // buffer->LDS loads one pass ahead: pass buffer b is stage b's arrays,
-    // sa<b> for the pass's first column block and sb<b> for its second
-    // (16 KB each), as [head*8 + k-step][lane].
+    // The tile's two heads (wn = 0, 1) run the W^UK product over passes of
+    // PB = 2 column blocks (32 columns each) of Hckv (MI m-blocks x PB
+    // column blocks of accumulators: the rest of the AGPRs and the VGPRs
+    // hold qc).  A pass's W^UK operands (2 heads x 8 k-steps x PB column
+    // blocks of 1 KB) are loaded into LDS by buffer->LDS loads one pass
+    // ahead, as [head*8 + k-step][lane] per column block: pass buffer b is
+    // stage b's arrays, sa<b> for the first column block and sb<b> for the
+    // second (16 KB each).
     constexpr int PB = 2;
+    constexpr int SPP = MI * 2 * PB;  // stores per wave per full pass
     const int KC2 = DH / 8;
     const int64_t nblk2 = (p.uk_N + 31) / 32;
     const int npass = static_cast<int>((nblk2 + PB - 1) / PB);
@@ -1096,13 +1109,16 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
     const int hs = w >> 1, kw = 4 * (w & 1);  // this wave's load share: head hs, k-steps kw..kw+3
     const rsrc_t ruk = make_rsrc(p.Buk + (head0 + hs) * p.uk_bstride,
                                  static_cast<uint32_t>(nblk2 * KC2 * 512));
+    auto pbuf = [&](auto bc, int jb) -> uint4* {
+      return jb == 0 ? &SA(bc)[0][0][0] : &SB(bc)[0][0][0];
+    };
     auto issue_uk = [&](auto bc, int pp) {
 #pragma unroll
       for (int jb = 0; jb < PB; ++jb) {
         int64_t nb2 = PB * pp + jb;
         nb2 = nb2 < nblk2 ? nb2 : nblk2 - 1;  // clamped blocks are never stored
         const uint32_t vo = lane * 16u + static_cast<uint32_t>(nb2 * KC2) * 512u;
-        uint4* dst = jb == 0 ? &SA(bc)[0][0][0] : &SB(bc)[0][0][0];  // jb is static
+        uint4* dst = pbuf(bc, jb);  // jb is static
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4)
           dma16(ruk, vo, static_cast<uint32_t>(kw + k4) * 1024u, dst + (hs * 8 + kw + k4) * 64);
@@ -1112,8 +1128,8 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
     // Output staging: a 4 KB slice per wave of its own array.
     __shared__ uint4 qn_stage[4][256];
     char* stg = reinterpret_cast<char*>(&qn_stage[w][0]);
-    const bool rows_in = m0 + 128 * wm + 127 < p.M;  // all of this wave's tokens are rows
-    // Returns whether the pass issued exactly 16 stores (all in range).
+    const bool rows_in = m0 + (TM / 2) * wm + TM / 2 - 1 < p.M;  // all of this wave's tokens are rows
+    // Returns whether the pass issued exactly SPP stores (all in range).
     auto pass_uk = [&](auto bc, int pp) -> bool {
       f32x16_t o[MI][PB];
 #pragma unroll
@@ -1124,8 +1140,7 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
       for (int ks = 0; ks < 8; ++ks) {
         uint4 wf[PB];
 #pragma unroll
-        for (int jb = 0; jb < PB; ++jb)
-          wf[jb] = (jb == 0 ? &SA(bc)[0][0][0] : &SB(bc)[0][0][0])[(wn * 8 + ks) * 64 + lane];
+        for (int jb = 0; jb < PB; ++jb) wf[jb] = pbuf(bc, jb)[(wn * 8 + ks) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1133,30 +1148,32 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
             o[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[jb]), as_bf16x8(qc[i][ks]),
                                                                 o[i][jb], 0, 0, 0);
       }
-      // o[i][jb]: lane l holds token 32*(4wm+i) + l%32, registers r the
+      // o[i][jb]: lane l holds token 32*(MI*wm+i) + l%32, registers r the
       // output columns 32*(PB*pp+jb) + 8(r/4) + 4g + r%4.  Transpose each
-      // m-block through the wave's 4 KB staging slice (32 tokens x 64 columns
-      // bf16, 16-byte chunk c of row t stored at chunk c ^ (t & 7)); then
-      // each store instruction writes 8 whole 128-byte rows.
-      const int cc = lane & 7;
-      const int64_t nc = 64 * pp + 8 * cc;
-      const bool full = rows_in && 64 * (pp + 1) <= p.uk_N;  // uniform per wave
+      // m-block through the wave's staging slice (32 tokens x 32*PB columns
+      // bf16: CPR 16-byte chunks per row, chunk c of row t stored at chunk
+      // c ^ (t % CPR)); then each store instruction writes 64/CPR whole rows.
+      constexpr int CPR = 4 * PB;
+      const int cc = lane & (CPR - 1);
+      const int64_t nc = 32 * PB * pp + 8 * cc;
+      const bool full = rows_in && 32 * PB * (pp + 1) <= p.uk_N;  // uniform per wave
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int jb = 0; jb < PB; ++jb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int c = (4 * jb + q) ^ (li & 7);
-            *reinterpret_cast<uint2*>(stg + li * 128 + c * 16 + g * 8) =
+            const int c = (4 * jb + q) ^ (li & (CPR - 1));
+            *reinterpret_cast<uint2*>(stg + li * (16 * CPR) + c * 16 + g * 8) =
                 make_uint2(pack_bf16x2(o[i][jb][4 * q], o[i][jb][4 * q + 1]),
                            pack_bf16x2(o[i][jb][4 * q + 2], o[i][jb][4 * q + 3]));
           }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int tr = 8 * k + (lane >> 3);
-          const uint4 v = *reinterpret_cast<const uint4*>(stg + tr * 128 + ((cc ^ (tr & 7)) * 16));
-          const int64_t m = m0 + 128 * wm + 32 * i + tr;
+        for (int k = 0; k < 2 * PB; ++k) {
+          const int tr = (64 / CPR) * k + lane / CPR;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + tr * (16 * CPR) +
+                                                          ((cc ^ (tr & (CPR - 1))) * 16));
+          const int64_t m = m0 + (TM / 2) * wm + 32 * i + tr;
           if (full || (m < p.M && nc < p.uk_N))
             st16(p.q_out + m * p.q_ld + head * p.q_bstride + nc, v);
         }
@@ -1166,13 +1183,13 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     // Each step: wait for this wave's loads of the pass -- only the previous
-    // pass's 16 stores were issued after them when that pass was full, so
+    // pass's SPP stores were issued after them when that pass was full, so
     // those stay in flight -- then a barrier (everybody's loads landed,
     // everybody done with the other buffer), start the next pass's loads,
     // compute and store.
     auto wait_pass = [&](bool prev_full) {
       if (prev_full)
-        vm_barrier<16>();
+        vm_barrier<SPP>();
       else
         vm_barrier<0>();
     };
@@ -1711,16 +1728,17 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
   const int64_t steps = a->He / 16;
   if (pl.gemm256) {
-    // Split the down projection over K so that the 256x256 tiles times the
-    // splits fill whole rounds of the 256 CUs best: minimise
-    // ceil(tiles * ks / 256) / ks over ks <= 4 (more splits cost partial-sum
-    // traffic), with steps per split even (32-k pipeline stages).
-    const int64_t tiles = (T + 255) / 256 *
+    // Split the down projection over K so that its 128x256 tiles (two
+    // workgroups per CU) times the splits fill whole rounds of the 512
+    // workgroup slots best: minimise ceil(tiles * ks / 512) / ks over ks <= 4
+    // (more splits cost partial-sum traffic), with steps per split even
+    // (32-k pipeline stages).
+    const int64_t tiles = (T + G_TM_HALF - 1) / G_TM_HALF *
                           ((a->Hcq + G_TN - 1) / G_TN + (a->Hckv + a->Dr + G_TN - 1) / G_TN);
     int64_t best = 1;
     double best_cost = 1e30;
     for (int64_t ks = 1; ks <= 4; ++ks) {
-      const double cost = static_cast<double>((tiles * ks + 255) / 256) / static_cast<double>(ks);
+      const double cost = static_cast<double>((tiles * ks + 511) / 512) / static_cast<double>(ks);
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = ks;
@@ -1984,14 +2002,14 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     g1.A = ws + pl.off_xfrag;
     g1.a_frag = 1;
     g1.a_mbs = a->He * 64;
-    // A1 and A6: 256x256 tiles, four stage buffers.  A8 (K = D, a short
-    // loop and a large bf16 output): 128x256 tiles and three buffers, two
-    // workgroups per CU so one's stores overlap the other's loads.
-    const unsigned mt = static_cast<unsigned>((T + 255) / 256);
+    // A1 and A6's q^R columns: 128x256 tiles and three buffers, two
+    // workgroups per CU so one's epilogue stores overlap the other's main
+    // loop.  The fused q^C + W^UK tiles: 256x256, four buffers.
+    const unsigned mt2 = static_cast<unsigned>((T + G_TM_HALF - 1) / G_TM_HALF);
     g1.ntiles0 = static_cast<int>((g1.N0 + G_TN - 1) / G_TN);
     const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + G_TN - 1) / G_TN);
-    launch(L1, k_gemm<EPI_PARTIAL, 256, 4>, dim3(nt1, mt, static_cast<unsigned>(pl.ksplit)),
-           dim3(256), 0, g1);
+    launch(L1, k_gemm<EPI_PARTIAL, G_TM_HALF, 3>,
+           dim3(nt1, mt2, static_cast<unsigned>(pl.ksplit)), dim3(256), 0, g1);
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
@@ -2003,8 +2021,8 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gr.B0 = wuqqr + (ND / 32) * (a->Hcq / 8) * 32;
       gr.N0 = a->N * a->Dr;
       gr.ND = 0;
-      launch(L6, k_gemm<EPI_UQQR, 256, 4>,
-             dim3(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt, 1), dim3(256), 0, gr);
+      launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>,
+             dim3(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt2, 1), dim3(256), 0, gr);
       mark(MLA_PHASE_AFTER_UQQR);
       // q^C tiles with the W^UK product in the epilogue.
       GemmParams gq = g6;
@@ -2015,11 +2033,12 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gq.q_out = g8.q_out;
       gq.q_ld = g8.q_ld;
       gq.q_bstride = g8.q_bstride;
+      const unsigned mt = static_cast<unsigned>((T + 255) / 256);
       launch(L8, k_gemm<EPI_QN, 256, 4, 128>, dim3(static_cast<unsigned>(ND / G_TN), mt, 1),
              dim3(256), 0, gq);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
-      launch(L6, k_gemm<EPI_UQQR, 256, 4>, dim3(nt6, mt, 1), dim3(256), 0, g6);
+      launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, dim3(nt6, mt2, 1), dim3(256), 0, g6);
       mark(MLA_PHASE_AFTER_UQQR);
       const unsigned nt8 = static_cast<unsigned>((g8.N0 + G_TN - 1) / G_TN);
       launch(L8, k_gemm<EPI_UK, 128, 3>,
