@@ -972,17 +972,23 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
 
   // B: the tile's 8 column blocks; blocks past N read as zeros.  Wave w
   // loads blocks 2w and 2w+1 of each k-step.
+  // (Both resources span this tile only, so their byte ranges fit 32 bits.)
   const int64_t nblk = (N + 31) / 32;
   const int64_t nb0 = n0 / 32;
-  const rsrc_t rb = make_rsrc(B + nb0 * KC * 32, static_cast<uint32_t>((nblk - nb0) * KC * 512));
+  const int64_t nbt = nblk - nb0 < 8 ? nblk - nb0 : 8;
+  const rsrc_t rb = make_rsrc(B + nb0 * KC * 32, static_cast<uint32_t>(nbt * KC * 512));
   uint32_t vb[2], va[AW];
 #pragma unroll
   for (int j = 0; j < 2; ++j) vb[j] = lane * 16u + static_cast<uint32_t>((2 * w + j) * KC) * 512u;
   // A in fragment layout (1 KB per 32-row block and k-step); wave w loads
   // blocks AW*w .. AW*w+AW-1.  Blocks past the buffer read as zeros.
+  // (Gathering row-major A with the same loads, 32 rows per load, made the
+  // T = 4096 down projection 38 us slower: more than the 21 us repack into
+  // this layout.)
   const int64_t mb0 = m0 / 32, mbt = (p.M + 31) / 32;
+  const int64_t nmb = mbt - mb0 < MA ? mbt - mb0 : MA;
   const rsrc_t ra = make_rsrc(static_cast<const char*>(p.A) + zb * p.a_zs + mb0 * p.a_mbs,
-                              static_cast<uint32_t>((mbt - mb0) * p.a_mbs));
+                              static_cast<uint32_t>(nmb * p.a_mbs));
 #pragma unroll
   for (int j = 0; j < AW; ++j) va[j] = lane * 16u + static_cast<uint32_t>((AW * w + j) * p.a_mbs);
 
