@@ -107,6 +107,16 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
   const u32x4_t w = {v.x, v.y, v.z, v.w};
   *(QKVNR_GLOBAL u32x4_t*)p = w;
 }
+// Streaming stores for outputs that no later kernel of the call reads:
+// nontemporal, so they do not displace reused lines from the caches.
+__device__ __forceinline__ void st16_nt(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (QKVNR_GLOBAL u32x4_t*)p);
+}
+__device__ __forceinline__ void st8_nt(void* p, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, (QKVNR_GLOBAL u32x2_t*)p);
+}
 __device__ __forceinline__ void st8(void* p, uint2 v) {
   const u32x2_t w = {v.x, v.y};
   *(QKVNR_GLOBAL u32x2_t*)p = w;

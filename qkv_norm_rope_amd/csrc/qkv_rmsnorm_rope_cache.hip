@@ -141,31 +141,31 @@ __global__ __launch_bounds__(256) void k_qkv_rmsnorm_rope_cache(QkvParams p) {
         const uint4 packed = pack8<ET>(y);
         if (is_q) {
           const int64_t o = (t * p.Nq + h) * kD + 8 * j;
-          st16(p.q_out + o, packed);
-          if (p.qbq) st16(p.qbq + o, packed);
+          st16_nt(p.q_out + o, packed);
+          if (p.qbq) st16_nt(p.qbq + o, packed);
         } else {
           const int hk = h - p.Nq;
-          if (p.kbq) st16(p.kbq + (t * p.Nk + hk) * kD + 8 * j, packed);
+          if (p.kbq) st16_nt(p.kbq + (t * p.Nk + hk) * kD + 8 * j, packed);
           if (write_cache) {
             const int64_t o = (slot * p.Nk + hk) * kD + 8 * j;
             if (QM == 0) {
-              st16(static_cast<uint16_t*>(p.kc) + o, packed);
+              st16_nt(static_cast<uint16_t*>(p.kc) + o, packed);
             } else {
               const uint2 q8 = quant8<QM>(y, p.ks + hk * kD + 8 * j, p.ko + hk * kD + 8 * j);
-              st8(static_cast<int8_t*>(p.kc) + o, q8);
+              st8_nt(static_cast<int8_t*>(p.kc) + o, q8);
             }
           }
         }
       } else {
         const int hv = h - p.Nq - p.Nk;
-        if (p.vbq) st16(p.vbq + (t * p.Nv + hv) * kD + 8 * j, raw[c]);
+        if (p.vbq) st16_nt(p.vbq + (t * p.Nv + hv) * kD + 8 * j, raw[c]);
         if (write_cache) {
           const int64_t o = (slot * p.Nv + hv) * kD + 8 * j;
           if (QM == 0) {
-            st16(static_cast<uint16_t*>(p.vc) + o, raw[c]);
+            st16_nt(static_cast<uint16_t*>(p.vc) + o, raw[c]);
           } else {
             const uint2 q8 = quant8<QM>(x, p.vs + hv * kD + 8 * j, p.vo + hv * kD + 8 * j);
-            st8(static_cast<int8_t*>(p.vc) + o, q8);
+            st8_nt(static_cast<int8_t*>(p.vc) + o, q8);
           }
         }
       }
