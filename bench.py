@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--rotate", type=int, default=4,
+    ap.add_argument("--rotate", type=int, default=12,
                     help="independent input sets cycled by the decode steps")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")

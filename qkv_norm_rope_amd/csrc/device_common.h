@@ -169,5 +169,11 @@ __device__ __forceinline__ uint4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
                                                           static_cast<int>(soff), 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// Streaming variant (nontemporal: cache policy bit 1) for data read once.
+__device__ __forceinline__ uint4 bld16_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                          static_cast<int>(soff), 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 }  // namespace qkvnr

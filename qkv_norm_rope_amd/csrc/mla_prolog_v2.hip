@@ -410,7 +410,14 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
       int s = (s0 + u) < s_last ? (s0 + u) : s_last;
       s = s > 0 ? s : 0;  // a wave with an empty range still loads in bounds
 #pragma unroll
-      for (int b = 0; b < NB; ++b) x.b[u][b] = bld16(rb[b], vb, static_cast<uint32_t>(s) * 1024u);
+      for (int b = 0; b < NB; ++b) {
+        // streaming loads for the up projections' weights (A6 15.3 vs 16.0
+        // us); the down projection measured faster with cached loads
+        if constexpr (EPI == EPI_PARTIAL)
+          x.b[u][b] = bld16(rb[b], vb, static_cast<uint32_t>(s) * 1024u);
+        else
+          x.b[u][b] = bld16_nt(rb[b], vb, static_cast<uint32_t>(s) * 1024u);
+      }
     }
   };
   auto load_a = [&](Batch& x, int s0) {
