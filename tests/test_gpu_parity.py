@@ -193,7 +193,9 @@ def test_mla_prefill_partial_quant_tiled_path():
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
-@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3, "mla_dec_t13"])
+# config 2 (prefill T = 4096): every GEMM tile shape at full occupancy,
+# where a stage-buffer race shows up as run-to-run differences
+@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3, "mla_dec_t13", 2])
 def test_mla_deterministic(key):
     w = make_workload(key)
     gh.announce(f"mla determinism {w.cfg.name}")
