@@ -334,21 +334,24 @@ def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
     enqueue_ms = (time.perf_counter() - h0) * 1e3
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / steps
-    # HIP-graph replay of the two calls (no launch gaps), as decode is timed
+    # HIP-graph replay (no launch gaps), as decode is timed: one graph of
+    # `per_graph` calls alternating the two sets (a serving step launches
+    # many layers' calls per graph)
+    per_graph = 20
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        call(sets[0])
-        call(sets[1])
+        for i in range(per_graph):
+            call(sets[i % 2])
     g.replay()
     torch.cuda.synchronize()
-    reps = max(1, steps // 2)
+    reps = max(1, steps // per_graph)
     _hold_gpu(torch, 2.0)
     t0.record(s)
     for _ in range(reps):
         g.replay()
     t1.record(s)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / (2 * reps)
+    ms = t0.elapsed_time(t1) / (per_graph * reps)
     del g
     n_valid = int((w.arrays["index"] >= 0).sum())
     nbytes = qkv_bytes(cfg, n_valid)
