@@ -1674,7 +1674,8 @@ constexpr int a6_kw() { return MB >= 4 ? 1 : 2; }
 constexpr int kA6Cols = 96;  // A6 tile: three waves across, one column block each
 template <int MB>
 constexpr int a8_nw() { return 4; }
-constexpr int kA1Cols = 64;  // A1 tile width (two column blocks per wave)
+constexpr int kA1Cols = 64;  // A1 tile width: two column blocks (one per wave across when x
+                             // is staged in LDS, both in each wave otherwise)
 
 // A1 reads x row-major: with one 32-row block each workgroup stages its
 // split of x in LDS (fragment order), otherwise lanes load rows directly.
