@@ -226,9 +226,9 @@ def _hold_gpu(torch, ms=20.0):
 def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     """Time `steps` calls cycling over the sets.
 
-    Returns (ms per step under HIP-graph replay, or eager when graph is
-    False; per-phase ms from the eager region; eager ms per step; per-kernel
-    ms).  The eager region records, on every step, the library's phase
+    Returns (ms per step under HIP-graph replay, or in a second eager region
+    without instrumentation when graph is False; per-phase ms from the
+    instrumented eager region; its ms per step; per-kernel ms).  The eager region records, on every step, the library's phase
     events (device-scope release, between its launches) and its per-kernel
     start/stop events (taken by each main kernel's own dispatch), with the
     GPU held until the whole region is enqueued.
@@ -273,6 +273,16 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
         for e in row:
             he.destroy(e)
     ms_step = ms_eager
+    if not graph:
+        # the same steps again without the instrumentation (the phase
+        # events' device-scope releases cost time between the launches)
+        _hold_gpu(torch, 5.0 + 0.1 * steps)
+        he.record(t0, stream)
+        for i in range(steps):
+            calls[i % len(calls)]()
+        he.record(t1, stream)
+        torch.cuda.synchronize()
+        ms_step = he.elapsed_ms(t0, t1) / steps
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
