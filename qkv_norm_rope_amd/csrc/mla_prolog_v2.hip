@@ -1540,23 +1540,25 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
 // Activation packing for the 256-tile GEMM: bf16 rows (M, K) into the MFMA
 // fragment layout, where chunk (32-row block mb, k-step s, lane (g, i))
 // holds row 32*mb + i, k in [16s + 8g, 16s + 8g + 8).  One workgroup moves a
-// 32-row x 256-k block through LDS: thread c reads 16 bytes at (row c/32,
-// chunk c%32) -- 512 contiguous bytes per row -- into LDS slot
-// (chunk)*32 + row, which is exactly the block's fragment order, so the
-// writes are 16 KB contiguous.  Rows past M are zeros.
+// 32-row x (16*PA_STEPS)-k block through LDS: thread c reads 16 bytes at
+// (row c/CPR, chunk c%CPR), CPR = 2*PA_STEPS chunks of contiguous row bytes,
+// into LDS slot (chunk)*32 + row, which is exactly the block's fragment
+// order, so the writes are contiguous.  Rows past M are zeros.
 // ---------------------------------------------------------------------------
-constexpr int PA_STEPS = 16;  // k-steps per workgroup (256 k)
+constexpr int PA_STEPS = 32;  // k-steps per workgroup (512 k)
 __global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src,
                                                 uint4* __restrict__ dst, int64_t M, int64_t K) {
+  constexpr int CPR = 2 * PA_STEPS;       // 16-byte chunks per row of the block
+  constexpr int PER = 32 * CPR / 256;     // chunks per thread
   __shared__ uint4 blk[PA_STEPS * 64];
   const int64_t steps = K / 16;
   const int64_t mb = blockIdx.y;
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * PA_STEPS;
   const int ns = static_cast<int>(min<int64_t>(PA_STEPS, steps - s0));
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < PER; ++u) {
     const int c = threadIdx.x + 256 * u;
-    const int row = c >> 5, q = c & 31;
+    const int row = c / CPR, q = c % CPR;
     const int64_t m = mb * 32 + row;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (q < 2 * ns && m < M) {  // x is read once: streaming loads (10 us faster at T = 4096)
@@ -1569,7 +1571,7 @@ __global__ __launch_bounds__(256) void k_pack_a(const uint16_t* __restrict__ src
   __syncthreads();
   uint4* out = dst + (mb * steps + s0) * 64;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < PER; ++u) {
     const int o = threadIdx.x + 256 * u;
     if (o < ns * 64) st16(out + o, blk[o]);
   }
