@@ -1667,7 +1667,7 @@ void tiled(const GemmParams& p, dim3 grid, const Launch& L) {
 // waves across take one column block each.  A6: 96-column tiles, three waves
 // across with one column block each (256 tiles for the DeepSeek-V3 shape:
 // one per CU); with one row block each wave streams the whole K in batches
-// of 8 k-steps, otherwise K is split over waves.  A8: 4 waves on different
+// of 4 k-steps, otherwise K is split over waves.  A8: 4 waves on different
 // column blocks of one head, the head's q^C staged in LDS.
 template <int MB>
 constexpr int a1_kw() { return MB >= 4 ? 2 : (MB == 2 ? 4 : 8); }
@@ -1702,8 +1702,8 @@ void skinny_a6(const GemmParams& g6, bool quant, const Launch& L) {
   if (quant)
     skinny<A_I8, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
   else if constexpr (MB == 1)
-    // each wave streams its column block over the whole K, 8 k-steps per batch
-    launch(L, k_skinny<A_BF16, 1, 1, 3, 1, EPI_UQQR, 8>, dim3(nt, 1, 1), dim3(64 * 3), 0, g6);
+    // each wave streams its column block over the whole K, 4 k-steps per batch
+    launch(L, k_skinny<A_BF16, 1, 1, 3, 1, EPI_UQQR, 4>, dim3(nt, 1, 1), dim3(64 * 3), 0, g6);
   else
     skinny<A_BF16, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
 }
