@@ -254,6 +254,28 @@ def _decode_case(key):
     return make_workload(key)
 
 
+# token counts at each plan boundary: one token, the skinny plan with one,
+# two and four 32-row blocks, and the first large-T shapes (ragged tile)
+TOKEN_CASES = [("mla_ragged", 1), ("mla_ragged", 33), ("mla_ragged", 64),
+               ("mla_ragged", 100), ("mla_ragged", 129), ("mla_mid_dsv3", 1),
+               ("mla_mid_dsv3", 128), ("mla_mid_dsv3", 257)]
+
+
+@pytest.mark.parametrize("key,T", TOKEN_CASES)
+def test_mla_token_counts(key, T):
+    cfg = get_config(key)
+    blocks = max(cfg.block_num, -(-(T + 8) // cfg.block_size))
+    w = make_workload(cfg.replace(B=T, S=1, block_num=blocks,
+                                  n_skip=min(cfg.n_skip, max(0, T - 1)),
+                                  seed=3000 + T))
+    gh.announce(f"mla {w.cfg.name} T={w.cfg.T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
 @pytest.mark.parametrize("key", DECODE_CASES)
 def test_mla_decode_shapes(key):
     w = _decode_case(key)
@@ -280,6 +302,19 @@ def test_mla_packed_equals_nd():
 @pytest.mark.parametrize("key", ["qkv_ragged", "qkv_ragged_none", "qkv_ragged_asym", 4])
 def test_qkv_parity(key):
     w = make_workload(key)
+    gh.announce(f"qkv {w.cfg.name} T={w.cfg.T} quant={w.cfg.quant_mode}")
+    dev = gh.upload(w)
+    before = _before(dev, ["k_cache", "v_cache"])
+    out = gh.run_qkv_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_qkv(w, out, before)}")
+
+
+@pytest.mark.parametrize("key,T", [("qkv_ragged", 1), ("qkv_ragged_none", 1),
+                                   ("qkv_ragged_asym", 7), ("qkv_ragged", 191)])
+def test_qkv_token_counts(key, T):
+    cfg = get_config(key)
+    w = make_workload(cfg.replace(B=1, S=T, seed=3100 + T))
     gh.announce(f"qkv {w.cfg.name} T={w.cfg.T} quant={w.cfg.quant_mode}")
     dev = gh.upload(w)
     before = _before(dev, ["k_cache", "v_cache"])
