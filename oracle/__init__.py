@@ -32,6 +32,7 @@ from .common import (
     check_index,
 )
 from .mla_prolog_v2 import mla_prolog_v2, mla_query_from_quantized
+from .mla_prolog_v2 import quant_query_per_head as mla_prolog_v2_quant_query
 from .qkv_rmsnorm_rope_cache import qkv_rmsnorm_rope_cache
 
 __all__ = [
@@ -45,5 +46,6 @@ __all__ = [
     "check_index",
     "mla_prolog_v2",
     "mla_query_from_quantized",
+    "mla_prolog_v2_quant_query",
     "qkv_rmsnorm_rope_cache",
 ]

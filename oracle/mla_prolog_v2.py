@@ -12,8 +12,14 @@ formulas section:
 
 Quantisation modes follow the constraints section's scenario table:
 "none" (everything bf16), "partial_kv_bf16" (int8 weight_uq_qr with a
-per-channel dequant scale and a dynamically quantised c^Q; bf16 caches) and
-"partial_kv_int8" (the same plus int8 caches with per-channel quant scales).
+per-channel dequant scale and a dynamically quantised c^Q; bf16 caches),
+"partial_kv_int8" (the same plus int8 caches with per-channel quant scales),
+and the two full-quantisation rows: "full_kv_bf16" (also int8 token_x with
+a per-token dequant scale and int8 weight_dq / weight_dkv_kr with
+per-channel dequant scales; bf16 caches and outputs) and "full_kv_int8" (the
+same with an int8 kv_cache, a bf16 kr_cache and an int8 query quantised per
+(token, head), its scales returned as dequant_scale_q_nope), per the
+dtype/shape table of the constraints section.
 
 Readings where the page is silent (each also listed in the design notes):
 
@@ -26,6 +32,14 @@ Readings where the page is silent (each also listed in the design notes):
 * int8 GEMM dequant: y = (sum_k c8 * w8) * s_token * dq_channel.
 * Cache quantisation divides by the per-channel scale (as formula (4) of
   aclnnQkvRmsNormRopeCache does), rounds half to even and saturates.
+* Full quantisation dequantises the down projections the same way as the
+  up projection: h = (sum_k x8 * w8) * dequant_scale_x[t] *
+  dequant_scale_w[j].  Its int8 kv_cache scale is taken per channel,
+  shape (1, Hckv), as the dtype/shape table gives it (the scenario table
+  calls it per-tensor; a per-tensor scale is the case of equal entries).
+  The int8 query is quantised per (token, head) like c^Q: scale =
+  max|q^N| / 127 over the head's Hckv values, codes round half to even in
+  [-127, 127]; dequant_scale_q_nope holds the scale (query ~ code * scale).
 """
 
 from __future__ import annotations
@@ -42,7 +56,8 @@ from .common import (
     scatter_slots,
 )
 
-QUANT_MODES = ("none", "partial_kv_bf16", "partial_kv_int8")
+QUANT_MODES = ("none", "partial_kv_bf16", "partial_kv_int8", "full_kv_bf16",
+               "full_kv_int8")
 
 
 def _split_query(Y: np.ndarray, N: int, D: int, Dr: int):
@@ -74,6 +89,20 @@ def mla_query_from_quantized(c8, s, w8, dq, wuk, cos, sin, N, D, Dr):
     query = _per_head_uk(qc, wuk)
     query_rope = rope_half(qr_pre, cos[:, None, :], sin[:, None, :])
     return query, query_rope
+
+
+def quant_query_per_head(query: np.ndarray):
+    """int8 query per (token, head), the full_kv_int8 output.
+
+    MlaPrologV2 README, scenario table: the query is returned quantised per
+    token and head; dtype/shape table: dequant_scale_q_nope is (T, N, 1).
+    Each head's Hckv values are quantised like c^Q's dynamic quantisation
+    (without a smooth factor): scale = max|q| / 127, codes round half to
+    even in [-127, 127], an all-zero row gets scale 0 and zero codes.
+    Returns the codes (T, N, Hckv) and the scales (T, N).
+    """
+    q = np.asarray(query, np.float64)
+    return dynamic_quant_int8(q, np.ones(q.shape[-1]))
 
 
 def mla_prolog_v2(arrays: dict, dtypes: dict, dims: dict,
@@ -110,8 +139,21 @@ def mla_prolog_v2(arrays: dict, dtypes: dict, dims: dict,
     kr_cache = decode(arrays["kr_cache"], kr_dt)
 
     out = {}
+    full = quant_mode.startswith("full")
+    if full:
+        # int8 x (per token) and int8 down-projection weights (per channel):
+        # the exact integer products, dequantised per token and per channel.
+        sx = decode(arrays["dequant_scale_x"], dtypes["dequant_scale_x"]).reshape(T)
+        sw_dq = decode(arrays["dequant_scale_w_dq"], dtypes["dequant_scale_w_dq"])
+        sw_dkv = decode(arrays["dequant_scale_w_dkv_kr"],
+                        dtypes["dequant_scale_w_dkv_kr"])
+        H = int_matmul_exact(X, Wdq).astype(np.float64) * sx[:, None] * sw_dq[None, :]
+        G = int_matmul_exact(X, Wdkvkr).astype(np.float64) * sx[:, None] \
+            * sw_dkv[None, :]
+    else:
+        H = X @ Wdq
+        G = X @ Wdkvkr
     # Query path.  c^Q = RmsNorm(x . W^DQ).
-    H = X @ Wdq
     cq = rmsnorm(H, g_cq, eps_cq)
     out["cq"] = cq
     if quant_mode == "none":
@@ -129,11 +171,13 @@ def mla_prolog_v2(arrays: dict, dtypes: dict, dims: dict,
         out["cq_int8"], out["cq_scale"] = c8, s
         query, query_rope = mla_query_from_quantized(
             c8, s, Wuqqr.astype(np.int64), dq, Wuk, cos, sin, N, D, Dr)
+    if quant_mode == "full_kv_int8":
+        out["query_f64"] = query
+        query, out["dequant_scale_q_nope"] = quant_query_per_head(query)
     out["query"] = query
     out["query_rope"] = query_rope
 
     # Key path.  c^KV = RmsNorm(x . W^DKV) and k^R = RoPE(x . W^KR).
-    G = X @ Wdkvkr
     ckv = rmsnorm(G[:, :Hckv], g_ckv, eps_ckv)
     kr = rope_half(G[:, Hckv:], cos, sin)
     out["ckv"], out["kr"] = ckv, kr
@@ -142,6 +186,10 @@ def mla_prolog_v2(arrays: dict, dtypes: dict, dims: dict,
         qs_ckr = decode(arrays["quant_scale_ckr"], dtypes["quant_scale_ckr"])
         kv_rows = quant_int8(ckv, qs_ckv)
         kr_rows = quant_int8(kr, qs_ckr)
+    elif quant_mode == "full_kv_int8":
+        qs_ckv = decode(arrays["quant_scale_ckv"], dtypes["quant_scale_ckv"])
+        kv_rows = quant_int8(ckv, qs_ckv)
+        kr_rows = kr
     else:
         kv_rows, kr_rows = ckv, kr
     out["kv_rows"], out["kr_rows"] = kv_rows, kr_rows

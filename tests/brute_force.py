@@ -51,15 +51,18 @@ def _q8(v, scale, offset=0.0):
 
 def mla_prolog_brute(x, Wdq, Wdkvkr, Wuqqr, Wuk, g_cq, g_ckv, cos, sin,
                      dims, eps_cq, eps_ckv, quant=None):
-    """Per-token loops.  quant: None or dict(smooth, dq, qs_ckv, qs_ckr).
+    """Per-token loops.  quant: None or dict(smooth, dq[, qs_ckv, qs_ckr,
+    query_int8]).
 
     Returns per-token lists: query[t][n][j], query_rope[t][n][j], kv_row[t],
-    kr_row[t] (codes when qs_ckv is given), and c8/s when quantised.
+    kr_row[t] (codes when qs_ckv / qs_ckr is given), and c8/s when
+    quantised.  With query_int8 the query rows are int8 codes of a per-row
+    scale max|row| / 127 (returned in q_scale[t][n]).
     """
     He, Hcq, N, D, Hckv, Dr = (dims[k] for k in ("He", "Hcq", "N", "D",
                                                   "Hckv", "Dr"))
     res = {"query": [], "query_rope": [], "kv_row": [], "kr_row": [],
-           "c8": [], "s": []}
+           "c8": [], "s": [], "q_scale": []}
     for t in range(len(x)):
         h = _matvec_rows(x[t], Wdq, Hcq)
         cq = _rms_norm(h, g_cq, eps_cq)
@@ -88,6 +91,15 @@ def mla_prolog_brute(x, Wdq, Wdkvkr, Wuqqr, Wuk, g_cq, g_ckv, cos, sin,
             qn.append(row)
             pre = y[N * D + n * Dr: N * D + (n + 1) * Dr]
             qr.append(_rope(pre, cos[t], sin[t]))
+        if quant is not None and quant.get("query_int8"):
+            scales = []
+            for n in range(N):
+                amax = max(abs(v) for v in qn[n])
+                sc = amax / 127.0
+                qn[n] = [max(-127, min(127, int(round(v / sc)))) if sc > 0 else 0
+                         for v in qn[n]]
+                scales.append(sc)
+            res["q_scale"].append(scales)
         res["query"].append(qn)
         res["query_rope"].append(qr)
         g = _matvec_rows(x[t], Wdkvkr, Hckv + Dr)
@@ -95,6 +107,7 @@ def mla_prolog_brute(x, Wdq, Wdkvkr, Wuqqr, Wuk, g_cq, g_ckv, cos, sin,
         kr = _rope(g[Hckv:], cos[t], sin[t])
         if quant is not None and quant.get("qs_ckv") is not None:
             ckv = [_q8(ckv[j], quant["qs_ckv"][j]) for j in range(Hckv)]
+        if quant is not None and quant.get("qs_ckr") is not None:
             kr = [_q8(kr[j], quant["qs_ckr"][j]) for j in range(Dr)]
         res["kv_row"].append(ckv)
         res["kr_row"].append(kr)

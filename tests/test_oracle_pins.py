@@ -360,6 +360,75 @@ def test_mla_quant_matches_brute_force_with_int8_caches():
     np.testing.assert_array_equal(ref["kr_rows"], np.array(bres["kr_row"]))
 
 
+@pytest.mark.parametrize("mode", ["full_kv_bf16", "full_kv_int8"])
+def test_mla_full_quant_matches_brute_force_on_dequantised_inputs(mode):
+    """Full quantisation against the brute-force loops fed the dequantised
+    int8 inputs: x8[t, k] * dequant_scale_x[t] and w8[k, j] *
+    dequant_scale_w[j] (exact in float64: 8-bit times 24-bit mantissas).
+    Equality pins where each scale multiplies (per token, per channel, which
+    weight's scale), the rest of the partial-quant path, the int8 kv_cache
+    with a bf16 kr_cache, and the per-(token, head) int8 query."""
+    cfg = get_config("mla_full_kvbf16").replace(
+        B=3, He=128, Hcq=64, N=2, D=32, Hckv=64, Dr=16, n_skip=1,
+        quant_mode=mode)
+    w = make_workload(cfg)
+    ref = _run_mla(w)
+    x8, sx = _dec(w, "token_x"), _dec(w, "dequant_scale_x")
+    wdq8, swdq = _dec(w, "weight_dq"), _dec(w, "dequant_scale_w_dq")
+    wkv8, swkv = _dec(w, "weight_dkv_kr"), _dec(w, "dequant_scale_w_dkv_kr")
+    x = [[float(x8[t, k]) * float(sx[t]) for k in range(cfg.He)]
+         for t in range(cfg.T)]
+    wdq = [[float(wdq8[k, j]) * float(swdq[j]) for j in range(cfg.Hcq)]
+           for k in range(cfg.He)]
+    wkv = [[float(wkv8[k, j]) * float(swkv[j])
+            for j in range(cfg.Hckv + cfg.Dr)] for k in range(cfg.He)]
+    quant = dict(smooth=_dec(w, "smooth_scales_cq").tolist(),
+                 dq=_dec(w, "dequant_scale_w_uq_qr").tolist())
+    if mode == "full_kv_int8":
+        quant.update(qs_ckv=_dec(w, "quant_scale_ckv").tolist(),
+                     query_int8=True)
+    bres = bf.mla_prolog_brute(
+        x, wdq, wkv, _dec(w, "weight_uq_qr").tolist(),
+        _dec(w, "weight_uk").tolist(), _dec(w, "rmsnorm_gamma_cq").tolist(),
+        _dec(w, "rmsnorm_gamma_ckv").tolist(), _dec(w, "rope_cos").tolist(),
+        _dec(w, "rope_sin").tolist(), _dims(cfg), cfg.eps_cq, cfg.eps_ckv,
+        quant)
+    np.testing.assert_array_equal(ref["cq_int8"], np.array(bres["c8"]))
+    np.testing.assert_allclose(ref["query_rope"], np.array(bres["query_rope"]),
+                               rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(ref["kr_rows"], np.array(bres["kr_row"]),
+                               rtol=1e-12, atol=1e-12)
+    if mode == "full_kv_bf16":
+        np.testing.assert_allclose(ref["query"], np.array(bres["query"]),
+                                   rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(ref["kv_rows"], np.array(bres["kv_row"]),
+                                   rtol=1e-12, atol=1e-12)
+        assert "dequant_scale_q_nope" not in ref
+    else:
+        np.testing.assert_array_equal(ref["query"], np.array(bres["query"]))
+        np.testing.assert_allclose(ref["dequant_scale_q_nope"],
+                                   np.array(bres["q_scale"]), rtol=1e-12)
+        np.testing.assert_array_equal(ref["kv_rows"], np.array(bres["kv_row"]))
+        assert ref["query"].dtype == np.int64
+
+
+def test_query_quant_per_head_worked_example():
+    """Per-(token, head) int8 query, by hand: the row (0.5, -1.0, 0.25, 0)
+    has max |q| = 1, scale 1/127; 0.5 * 127 = 63.5 rounds half to even to
+    64, 0.25 * 127 = 31.75 to 32; a zero row gets scale 0 and zero codes;
+    the largest magnitude always maps to +/-127."""
+    q = np.zeros((1, 2, 4))
+    q[0, 0] = [0.5, -1.0, 0.25, 0.0]
+    codes, scale = oracle.mla_prolog_v2_quant_query(q)
+    np.testing.assert_array_equal(codes[0, 0], [64, -127, 32, 0])
+    np.testing.assert_array_equal(codes[0, 1], [0, 0, 0, 0])
+    assert scale[0, 0] == 1.0 / 127.0 and scale[0, 1] == 0.0
+    r = np.random.default_rng(7).standard_normal((3, 4, 64))
+    c, s = oracle.mla_prolog_v2_quant_query(r)
+    assert np.all(np.abs(c).max(axis=-1) == 127)
+    assert np.all(np.abs(c * s[..., None] - r) <= s[..., None] / 2 + 1e-15)
+
+
 def test_mla_associativity():
     # c^Q . (W^UQ_n . W^UK_n) equals the staged (c^Q . W^UQ_n) . W^UK_n
     w = make_workload("mla_ragged")

@@ -146,6 +146,22 @@ CONFIGS = {
                                 Hcq=160, N=3, D=128, Hckv=96, Dr=64,
                                 block_num=2, block_size=32, n_skip=1,
                                 seed=2013),
+    # full quantisation (int8 x and down-projection weights): a one-block
+    # decode shape with bf16 caches, a two-block one with the int8 kv_cache
+    # and int8 query, and a large-T shape on the tiled plan
+    "mla_full_kvbf16": MlaConfig("mla_full_kvbf16_T21", B=21, S=1, He=512,
+                                 Hcq=256, N=5, D=64, Hckv=128, Dr=32,
+                                 block_num=4, block_size=16, n_skip=2,
+                                 quant_mode="full_kv_bf16", seed=2014),
+    "mla_full_kvint8": MlaConfig("mla_full_kvint8_T37", B=37, S=1, He=384,
+                                 Hcq=192, N=6, D=128, Hckv=96, Dr=64,
+                                 block_num=3, block_size=32, n_skip=3,
+                                 quant_mode="full_kv_int8", seed=2015),
+    "mla_full_kvint8_large": MlaConfig("mla_full_kvint8_T150", B=3, S=50,
+                                       He=256, Hcq=128, N=3, D=32, Hckv=64,
+                                       Dr=16, block_num=2, block_size=128,
+                                       n_skip=4, quant_mode="full_kv_int8",
+                                       seed=2016, layout="BSH"),
     # prefill-sized T with no dimension a multiple of the 256x256 GEMM tile
     "mla_prefill_ragged": MlaConfig("mla_prefill_ragged_T300", B=3, S=100,
                                     He=512, Hcq=320, N=5, D=64, Hckv=96,

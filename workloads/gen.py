@@ -105,12 +105,26 @@ def make_mla_workload(cfg: MlaConfig) -> Workload:
         A[name] = arr
         Ty[name] = dt
 
-    put("token_x", _store(rng.standard_normal((T, He)), "bf16"), "bf16")
-    put("weight_dq",
-        _store(rng.standard_normal((He, Hcq)) / np.sqrt(He), "bf16"), "bf16")
-    put("weight_dkv_kr",
-        _store(rng.standard_normal((He, Hckv + Dr)) / np.sqrt(He), "bf16"),
-        "bf16")
+    full = quant.startswith("full")
+    if full:
+        # int8 x and down-projection weights, uniform on [-127, 127]; their
+        # dequant scales (drawn last) bring them to the bf16 workloads'
+        # magnitudes
+        put("token_x", rng.integers(-127, 128, size=(T, He)).astype(np.int8),
+            "int8")
+        put("weight_dq",
+            rng.integers(-127, 128, size=(He, Hcq)).astype(np.int8), "int8")
+        put("weight_dkv_kr",
+            rng.integers(-127, 128, size=(He, Hckv + Dr)).astype(np.int8),
+            "int8")
+    else:
+        put("token_x", _store(rng.standard_normal((T, He)), "bf16"), "bf16")
+        put("weight_dq",
+            _store(rng.standard_normal((He, Hcq)) / np.sqrt(He), "bf16"),
+            "bf16")
+        put("weight_dkv_kr",
+            _store(rng.standard_normal((He, Hckv + Dr)) / np.sqrt(He), "bf16"),
+            "bf16")
     if quant == "none":
         put("weight_uq_qr",
             _store(rng.standard_normal((Hcq, N * (D + Dr))) / np.sqrt(Hcq),
@@ -137,6 +151,11 @@ def make_mla_workload(cfg: MlaConfig) -> Workload:
             "int8")
         put("kr_cache", rng.integers(-128, 128, size=kr_shape).astype(np.int8),
             "int8")
+    elif quant == "full_kv_int8":
+        # the full-quantisation int8 row keeps kr_cache in bf16
+        put("kv_cache", rng.integers(-128, 128, size=kv_shape).astype(np.int8),
+            "int8")
+        put("kr_cache", _store(rng.standard_normal(kr_shape), "bf16"), "bf16")
     else:
         put("kv_cache", _store(rng.standard_normal(kv_shape), "bf16"), "bf16")
         put("kr_cache", _store(rng.standard_normal(kr_shape), "bf16"), "bf16")
@@ -146,11 +165,25 @@ def make_mla_workload(cfg: MlaConfig) -> Workload:
             _store(rng.uniform(0.001, 0.01, N * (D + Dr)), "fp32"), "fp32")
         put("smooth_scales_cq", _store(rng.uniform(0.5, 1.5, Hcq), "fp32"),
             "fp32")
-    if quant == "partial_kv_int8":
+    if quant in ("partial_kv_int8", "full_kv_int8"):
         put("quant_scale_ckv", _store(rng.uniform(0.01, 0.05, Hckv), "fp32"),
             "fp32")
+    if quant == "partial_kv_int8":
         put("quant_scale_ckr", _store(rng.uniform(0.01, 0.05, Dr), "fp32"),
             "fp32")
+    if full:
+        # per-token x scale ~ U(0.01, 0.02): x8 * s has a standard deviation
+        # near 1; per-channel weight scales U(0.5, 1.5) / (73 sqrt(He)): a
+        # dequantised weight's standard deviation near 1/sqrt(He) (73 is
+        # the standard deviation of the uniform int8 draw)
+        put("dequant_scale_x", _store(rng.uniform(0.01, 0.02, T), "fp32"),
+            "fp32")
+        put("dequant_scale_w_dq",
+            _store(rng.uniform(0.5, 1.5, Hcq) / (73.0 * np.sqrt(He)), "fp32"),
+            "fp32")
+        put("dequant_scale_w_dkv_kr",
+            _store(rng.uniform(0.5, 1.5, Hckv + Dr) / (73.0 * np.sqrt(He)),
+                   "fp32"), "fp32")
     return w
 
 
