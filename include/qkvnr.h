@@ -92,8 +92,18 @@ const char* qkvnr_version(void);
  * PARTIAL_KV_INT8: as PARTIAL_KV_BF16, plus int8 kv_cache / kr_cache
  *   quantised per channel by quant_scale_ckv / quant_scale_ckr
  *   (code = saturate(round_half_even(value / scale))).
- * FULL_KV_BF16, FULL_KV_INT8: the full-quantisation rows; rejected with
- *   QKVNR_ERR_UNSUPPORTED. */
+ * FULL_KV_BF16: as PARTIAL_KV_BF16, plus int8 token_x with a per-token
+ *   fp32 dequant scale (dequant_scale_x) and int8 weight_dq / weight_dkv_kr
+ *   with per-channel fp32 dequant scales (dequant_scale_w_dq,
+ *   dequant_scale_w_dkv_kr): h = (sum_k x8 * w8) * dequant_scale_x[t] *
+ *   dequant_scale_w[j].  Caches and outputs bf16.
+ * FULL_KV_INT8: as FULL_KV_BF16 with an int8 kv_cache quantised per channel
+ *   by quant_scale_ckv (the README's dtype/shape table gives it shape
+ *   (1, Hckv); its scenario table's "per-tensor" is the case of equal
+ *   entries), a bf16 kr_cache, and an int8 query quantised per (token,
+ *   head): dequant_scale_q_nope[t, n] = max_j |q^N[t, n, j]| / 127 and
+ *   query = round_half_even(q^N / that scale) in [-127, 127] (0 for an
+ *   all-zero head). */
 enum {
   MLA_QUANT_NONE = 0,
   MLA_QUANT_PARTIAL_KV_BF16 = 1,
@@ -137,7 +147,8 @@ typedef struct MlaPrologV2Args {
 
   /* Dimensions (MlaPrologV2 README, constraints).  T = B*S tokens; for the
    * (T, He) layout pass B = T, S = 1.  Requirements checked here:
-   * He, Hcq, D multiples of 32 (K dims of the MFMA tiles), Hckv a multiple
+   * He, Hcq, D multiples of 32 (K dims of the MFMA tiles; He of 64 in
+   * FULL_*, Hcq of 64 in PARTIAL_* and FULL_*), Hckv a multiple
    * of 16, Dr in {16, 32, 64} with (N*D) % Dr == 0, Nkv == 1, all > 0
    * except B, S (either may be 0: nothing is done) and block_num /
    * block_size (either 0: the caches are left untouched, queries are still
@@ -150,40 +161,44 @@ typedef struct MlaPrologV2Args {
                                   "PA_NZ" -> QKVNR_ERR_UNSUPPORTED */
 
   /* ---- inputs (device) ---- */
-  const void* token_x;         /* (T, He) bf16 */
-  const void* weight_dq;       /* (He, Hcq) bf16 */
+  const void* token_x;         /* (T, He) bf16, int8 in FULL_* */
+  const void* weight_dq;       /* (He, Hcq) bf16, int8 in FULL_* */
   const void* weight_uq_qr;    /* (Hcq, N*(D+Dr)): bf16 (NONE) or int8
-                                  (PARTIAL_*).  Columns [0, N*D) are W^UQ,
+                                  (PARTIAL_*, FULL_*).  Columns [0, N*D) are W^UQ,
                                   head n at n*D; columns [N*D, N*(D+Dr)) are
                                   W^QR, head n at N*D + n*Dr. */
   const void* weight_uk;       /* (N, D, Hckv) bf16 */
-  const void* weight_dkv_kr;   /* (He, Hckv+Dr) bf16: [W^DKV | W^KR] */
+  const void* weight_dkv_kr;   /* (He, Hckv+Dr): [W^DKV | W^KR], bf16,
+                                  int8 in FULL_* */
   const void* rmsnorm_gamma_cq;   /* (Hcq) bf16 */
   const void* rmsnorm_gamma_ckv;  /* (Hckv) bf16 */
   const void* rope_sin;        /* (T, Dr) bf16 */
   const void* rope_cos;        /* (T, Dr) bf16 */
   const int64_t* cache_index;  /* (T) flat slot ids, -1 = skip */
-  const float* dequant_scale_x;        /* reserved: must be NULL */
-  const float* dequant_scale_w_dq;     /* reserved: must be NULL */
-  const float* dequant_scale_w_uq_qr;  /* (N*(D+Dr)) fp32, PARTIAL_* only */
-  const float* dequant_scale_w_dkv_kr; /* reserved: must be NULL */
-  const float* quant_scale_ckv;        /* (Hckv) fp32, PARTIAL_KV_INT8 only */
+  /* Scales a scenario does not use must be NULL (else
+   * QKVNR_ERR_RESERVED_NONNULL). */
+  const float* dequant_scale_x;        /* (T) fp32, FULL_* only */
+  const float* dequant_scale_w_dq;     /* (Hcq) fp32, FULL_* only */
+  const float* dequant_scale_w_uq_qr;  /* (N*(D+Dr)) fp32, PARTIAL_*, FULL_* */
+  const float* dequant_scale_w_dkv_kr; /* (Hckv+Dr) fp32, FULL_* only */
+  const float* quant_scale_ckv;        /* (Hckv) fp32, PARTIAL_KV_INT8 and
+                                          FULL_KV_INT8 only */
   const float* quant_scale_ckr;        /* (Dr) fp32, PARTIAL_KV_INT8 only */
-  const float* smooth_scales_cq;       /* (Hcq) fp32, PARTIAL_* only */
+  const float* smooth_scales_cq;       /* (Hcq) fp32, PARTIAL_*, FULL_* */
 
   /* ---- in/out (device), updated in place at indexed slots only ---- */
   void* kv_cache;              /* (BlockNum, BlockSize, Nkv, Hckv): bf16, or
+                                  int8 in PARTIAL_KV_INT8 and FULL_KV_INT8 */
+  void* kr_cache;              /* (BlockNum, BlockSize, Nkv, Dr): bf16, or
                                   int8 in PARTIAL_KV_INT8 */
-  void* kr_cache;              /* (BlockNum, BlockSize, Nkv, Dr): same dtype
-                                  rule as kv_cache */
 
   /* ---- outputs (device), fully overwritten ---- */
-  void* query;                 /* (T, N, Hckv) bf16 */
+  void* query;                 /* (T, N, Hckv) bf16, int8 in FULL_KV_INT8 */
   void* query_rope;            /* (T, N, Dr) bf16 */
-  float* dequant_scale_q_nope; /* full quantisation only: must be NULL */
+  float* dequant_scale_q_nope; /* (T, N) fp32, FULL_KV_INT8 only */
 
   /* ---- optional diagnostics (device), NULL when not wanted ----
-   * PARTIAL_* only: the int8 codes of c^Q (T, Hcq) and their per-token
+   * PARTIAL_* and FULL_*: the int8 codes of c^Q (T, Hcq) and their per-token
    * scales (T) exactly as the up-projection consumed them. */
   int8_t* dbg_cq_int8;
   float* dbg_cq_scale;

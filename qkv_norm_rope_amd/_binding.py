@@ -239,6 +239,8 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
                        rmsnorm_epsilon_cq=1e-5, rmsnorm_epsilon_ckv=1e-5,
                        dequant_scale_w_uq_qr=None, quant_scale_ckv=None,
                        quant_scale_ckr=None, smooth_scales_cq=None,
+                       dequant_scale_x=None, dequant_scale_w_dq=None,
+                       dequant_scale_w_dkv_kr=None, dequant_scale_q_nope=None,
                        dbg_cq_int8=None, dbg_cq_scale=None, cache_mode=None,
                        B=None, S=None) -> MlaPrologV2Args:
     """Fill the C struct from tensors.  Dims come from the tensor shapes:
@@ -276,6 +278,8 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
         a.query_rope = _ptr(query_rope)
         a.dbg_cq_int8 = _ptr(dbg_cq_int8)
         a.dbg_cq_scale = _ptr(dbg_cq_scale)
+        a.dequant_scale_x = _ptr(dequant_scale_x)
+        a.dequant_scale_q_nope = _ptr(dequant_scale_q_nope)
     a.weight_dq = _ptr(weight_dq)
     a.weight_uq_qr = _ptr(weight_uq_qr)
     a.weight_uk = _ptr(weight_uk)
@@ -290,6 +294,8 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
     a.quant_scale_ckv = _ptr(quant_scale_ckv)
     a.quant_scale_ckr = _ptr(quant_scale_ckr)
     a.smooth_scales_cq = _ptr(smooth_scales_cq)
+    a.dequant_scale_w_dq = _ptr(dequant_scale_w_dq)
+    a.dequant_scale_w_dkv_kr = _ptr(dequant_scale_w_dkv_kr)
     return a
 
 
@@ -308,13 +314,16 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   rmsnorm_epsilon_cq=1e-5, rmsnorm_epsilon_ckv=1e-5,
                   dequant_scale_w_uq_qr=None, quant_scale_ckv=None,
                   quant_scale_ckr=None, smooth_scales_cq=None,
+                  dequant_scale_x=None, dequant_scale_w_dq=None,
+                  dequant_scale_w_dkv_kr=None, dequant_scale_q_nope=None,
                   query=None, query_rope=None, workspace=None,
                   return_cq_quant=False, cache_mode=None, stream=None,
                   phase_events=None, kernel_events=None):
     """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
 
-    Returns (query, query_rope), plus (cq_int8, cq_scale) when
-    return_cq_quant is set in a partial-quant mode.  phase_events: optional
+    Returns (query, query_rope), with dequant_scale_q_nope (T, N, 1) after
+    them in "full_kv_int8" (int8 query), plus (cq_int8, cq_scale) when
+    return_cq_quant is set in a partial- or full-quant mode.  phase_events: optional
     list of recorded torch.cuda.Event(enable_timing=True) objects, recorded
     again by the library at the MLA_PHASES boundaries.
     """
@@ -326,8 +335,14 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
     Hckv = rmsnorm_gamma_ckv.shape[-1]
     Dr = rope_sin.shape[-1]
     dev = token_x.device
+    q8 = quant_mode in ("full_kv_int8", MLA_QUANT["full_kv_int8"])
     if query is None:
-        query = torch.empty(lead + (N, Hckv), dtype=torch.bfloat16, device=dev)
+        query = torch.empty(lead + (N, Hckv),
+                            dtype=torch.int8 if q8 else torch.bfloat16,
+                            device=dev)
+    if q8 and dequant_scale_q_nope is None:
+        dequant_scale_q_nope = torch.empty(lead + (N, 1), dtype=torch.float32,
+                                           device=dev)
     if query_rope is None:
         query_rope = torch.empty(lead + (N, Dr), dtype=torch.bfloat16,
                                  device=dev)
@@ -344,7 +359,11 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
         rmsnorm_epsilon_ckv=rmsnorm_epsilon_ckv,
         dequant_scale_w_uq_qr=dequant_scale_w_uq_qr,
         quant_scale_ckv=quant_scale_ckv, quant_scale_ckr=quant_scale_ckr,
-        smooth_scales_cq=smooth_scales_cq, dbg_cq_int8=dbg8, dbg_cq_scale=dbgs,
+        smooth_scales_cq=smooth_scales_cq, dequant_scale_x=dequant_scale_x,
+        dequant_scale_w_dq=dequant_scale_w_dq,
+        dequant_scale_w_dkv_kr=dequant_scale_w_dkv_kr,
+        dequant_scale_q_nope=dequant_scale_q_nope if q8 else None,
+        dbg_cq_int8=dbg8, dbg_cq_scale=dbgs,
         cache_mode=cache_mode,
         B=lead[0] if len(lead) == 2 else None,
         S=lead[1] if len(lead) == 2 else None)
@@ -363,9 +382,10 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
     _check(lib.mla_prolog_v2(ctypes.byref(a), _ptr(workspace),
                              workspace.numel() * workspace.element_size(),
                              _stream(stream)), "mla_prolog_v2")
+    out = (query, query_rope) + ((dequant_scale_q_nope,) if q8 else ())
     if return_cq_quant:
-        return query, query_rope, dbg8, dbgs
-    return query, query_rope
+        return out + (dbg8, dbgs)
+    return out
 
 
 class PreparedMlaPrologV2:

@@ -33,9 +33,7 @@ int validate_mla(const MlaPrologV2Args* a) {
     return QKVNR_ERR_NULL_ARG;
   if (a->n_kernel_events < 0 || (a->n_kernel_events > 0 && a->kernel_events == nullptr))
     return QKVNR_ERR_NULL_ARG;
-  if (a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8)
-    return QKVNR_ERR_UNSUPPORTED;
-  if (a->quant_mode < MLA_QUANT_NONE || a->quant_mode > MLA_QUANT_PARTIAL_KV_INT8)
+  if (a->quant_mode < MLA_QUANT_NONE || a->quant_mode > MLA_QUANT_FULL_KV_INT8)
     return QKVNR_ERR_BAD_MODE;
   if (a->weight_layout != MLA_WEIGHT_ND && a->weight_layout != MLA_WEIGHT_PACKED_K16)
     return QKVNR_ERR_BAD_MODE;
@@ -58,7 +56,11 @@ int validate_mla(const MlaPrologV2Args* a) {
   // Limits of the kernels built here.
   if (a->Nkv != 1) return QKVNR_ERR_UNSUPPORTED;
   const bool quant = a->quant_mode != MLA_QUANT_NONE;
-  if (a->He % 32 || a->Hcq % (quant ? 64 : 32) || a->D % 32 || a->Hckv % 16)
+  const bool full =
+      a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8;
+  const bool kv8 =
+      a->quant_mode == MLA_QUANT_PARTIAL_KV_INT8 || a->quant_mode == MLA_QUANT_FULL_KV_INT8;
+  if (a->He % (full ? 64 : 32) || a->Hcq % (quant ? 64 : 32) || a->D % 32 || a->Hckv % 16)
     return QKVNR_ERR_UNSUPPORTED;
   if (!(a->Dr == 16 || a->Dr == 32 || a->Dr == 64) || (a->N * a->D) % a->Dr != 0)
     return QKVNR_ERR_UNSUPPORTED;
@@ -71,10 +73,16 @@ int validate_mla(const MlaPrologV2Args* a) {
   if (!good_eps(a->rmsnorm_epsilon_cq) || !good_eps(a->rmsnorm_epsilon_ckv))
     return QKVNR_ERR_BAD_EPS;
 
-  // Reserved parameters (README parameter table) must be NULL; the
-  // query dequant scale only exists in full quantisation.
-  if (a->dequant_scale_x || a->dequant_scale_w_dq || a->dequant_scale_w_dkv_kr ||
-      a->dequant_scale_q_nope)
+  // Parameters a scenario does not use (README dtype/shape table: "no
+  // value needed") must be NULL: the x and down-projection dequant scales
+  // outside full quantisation, the query's dequant scale outside
+  // FULL_KV_INT8, the cache quant scales where the caches are bf16, and
+  // the kr_cache scale in full quantisation (its kr_cache stays bf16).
+  if (!full && (a->dequant_scale_x || a->dequant_scale_w_dq || a->dequant_scale_w_dkv_kr))
+    return QKVNR_ERR_RESERVED_NONNULL;
+  if (a->quant_mode != MLA_QUANT_FULL_KV_INT8 && a->dequant_scale_q_nope)
+    return QKVNR_ERR_RESERVED_NONNULL;
+  if ((!kv8 && a->quant_scale_ckv) || (full && a->quant_scale_ckr))
     return QKVNR_ERR_RESERVED_NONNULL;
 
   if (T == 0) return QKVNR_OK;  // empty tensors are allowed; nothing runs
@@ -90,6 +98,12 @@ int validate_mla(const MlaPrologV2Args* a) {
   if (a->quant_mode == MLA_QUANT_PARTIAL_KV_INT8 &&
       (a->quant_scale_ckv == nullptr || a->quant_scale_ckr == nullptr))
     return QKVNR_ERR_NULL_ARG;
+  if (full && (a->dequant_scale_x == nullptr || a->dequant_scale_w_dq == nullptr ||
+               a->dequant_scale_w_dkv_kr == nullptr))
+    return QKVNR_ERR_NULL_ARG;
+  if (a->quant_mode == MLA_QUANT_FULL_KV_INT8 &&
+      (a->quant_scale_ckv == nullptr || a->dequant_scale_q_nope == nullptr))
+    return QKVNR_ERR_NULL_ARG;
 
   const void* al16[] = {a->token_x,   a->weight_dq,       a->weight_uq_qr,      a->weight_uk,
                         a->weight_dkv_kr, a->rmsnorm_gamma_cq, a->rmsnorm_gamma_ckv, a->rope_sin,
@@ -102,6 +116,13 @@ int validate_mla(const MlaPrologV2Args* a) {
   if (slots && (!aligned16(a->kv_cache) || !aligned16(a->kr_cache))) return QKVNR_ERR_BAD_ALIGNMENT;
   if (a->quant_mode == MLA_QUANT_PARTIAL_KV_INT8 &&
       (!aligned16(a->quant_scale_ckv) || !aligned16(a->quant_scale_ckr)))
+    return QKVNR_ERR_BAD_ALIGNMENT;
+  if (full && ((reinterpret_cast<uintptr_t>(a->dequant_scale_x) & 3u) ||
+               !aligned16(a->dequant_scale_w_dq) ||
+               !aligned16(a->dequant_scale_w_dkv_kr)))
+    return QKVNR_ERR_BAD_ALIGNMENT;
+  if (a->quant_mode == MLA_QUANT_FULL_KV_INT8 &&
+      (!aligned16(a->quant_scale_ckv) || (reinterpret_cast<uintptr_t>(a->dequant_scale_q_nope) & 3u)))
     return QKVNR_ERR_BAD_ALIGNMENT;
   if ((a->dbg_cq_int8 && !aligned8(a->dbg_cq_int8)) ||
       (a->dbg_cq_scale && (reinterpret_cast<uintptr_t>(a->dbg_cq_scale) & 3u)))

@@ -35,6 +35,7 @@ struct MlaPlan {
   // workspace offsets (bytes) and total size
   size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
   size_t off_part, off_cq, off_cq_scale, off_qc;
+  size_t off_qn;      // FULL_KV_INT8: q^N in fp32 before its per-head quant
   size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
   int64_t rows;       // token rows padded to the plan's 32-row blocks
   size_t total;

@@ -79,6 +79,7 @@ struct GemmParams {
   int64_t qr_ld;     // N*Dr
   // EPI_UK (and EPI_QN's output)
   uint16_t* q_out;  // (T, N, Hckv)
+  float* q_f32;     // when set, q^N goes here in fp32 instead (same indexing)
   int64_t q_ld;     // N*Hckv
   int64_t q_bstride;  // Hckv (per head)
   // EPI_QN: q^C never leaves registers; the W^UK product runs in the
@@ -179,9 +180,13 @@ struct Epilogue {
     if constexpr (EPI == EPI_PARTIAL) {
       st8f(p.part + m * p.part_ld + ocol, v);
     } else if constexpr (EPI == EPI_UK) {
-      uint16_t* dst = p.q_out + m * p.q_ld + static_cast<int64_t>(z) * p.q_bstride + gcol;
-      st16_nt(dst, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+      const int64_t o = m * p.q_ld + static_cast<int64_t>(z) * p.q_bstride + gcol;
+      if (p.q_f32 != nullptr) {
+        st8f(p.q_f32 + o, v);  // full quantisation: quantised per (token, head) next
+      } else {
+        st16_nt(p.q_out + o, make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])));
+      }
     } else {  // EPI_UQQR
       if (gcol < p.ND) {
         dequant(pre.cs, pre.d, v);
@@ -1329,6 +1334,12 @@ struct FinishParams {
   float* cq_scale;
   int8_t* dbg_cq_i8;
   float* dbg_cq_scale;
+  // Full quantisation: the partials are int8 x int8 sums, dequantised per
+  // token (sx) and per channel (sw_dq for c^Q's columns, sw_dkv for the
+  // c^KV / k^R columns) once the splits are summed.  NULL otherwise.
+  const float* sx;
+  const float* sw_dq;
+  const float* sw_dkv;
 };
 
 constexpr int FIN_MAX_THREADS = 1024;
@@ -1373,7 +1384,9 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
   }
 }
 
-// QM: 0 none, 1 partial with bf16 caches, 2 partial with int8 caches.
+// QM: 0 none, 1 c^Q quantised with bf16 caches (partial or full
+// quantisation), 2 c^Q quantised with int8 kv and kr caches (partial),
+// 3 c^Q quantised with an int8 kv cache and a bf16 kr cache (full).
 // MAXS: most splits summed (ksplit <= MAXS); fewer keep more workgroups
 // resident (the large-T plan splits at most 4 ways).
 template <int QM, int MAXS = FIN_MAXSPLIT>
@@ -1400,7 +1413,7 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
     pb = ld16(p.sinb + t * p.Dr + i0);
     if (QM != 0) {
       const float* f = p.smooth + (cq ? c0 : 0);
-      if (QM == 2 && ckv) f = p.qs_ckv + (c0 - p.Hcq);
+      if ((QM == 2 || QM == 3) && ckv) f = p.qs_ckv + (c0 - p.Hcq);
       if (QM == 2 && !cq && !ckv) f = p.qs_ckr + i0;
       ld8f(f, pf);
     }
@@ -1424,6 +1437,15 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
     for (int s = 0; s < MAXS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += s < p.ksplit ? v[s][e] : 0.f;
+    if (QM != 0 && p.sx != nullptr) {
+      // full quantisation: integer sums times the token's and the
+      // channels' dequant scales
+      float sw[8];
+      ld8f(c0 < p.Hcq ? p.sw_dq + c0 : p.sw_dkv + (c0 - p.Hcq), sw);
+      const float sxt = gld(p.sx + t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * sxt * sw[e];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       row[c0 + e] = acc[e];
@@ -1479,7 +1501,7 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
       unpack_bf16x8(pa, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = x[e] * rkv * g[e];
-      if (QM == 2) {
+      if (QM == 2 || QM == 3) {
         int q[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) q[e] = sat_rne(o[e] / pf[e], -128, 127);
@@ -1534,6 +1556,42 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
     gst(p.cq_scale + t, sc);
     if (p.dbg_cq_scale) gst(p.dbg_cq_scale + t, sc);
   }
+}
+
+// ---------------------------------------------------------------------------
+// int8 query per (token, head) for full quantisation with an int8 kv_cache
+// (MlaPrologV2 README: query quantised per token and head, its scales in
+// dequant_scale_q_nope (T, N, 1)).  One wave per row of H = Hckv fp32 q^N
+// values: scale = max|q| / 127, codes round half to even in [-127, 127];
+// an all-zero row gets scale 0 and zero codes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_query(const float* __restrict__ qn,
+                                                     int8_t* __restrict__ q8,
+                                                     float* __restrict__ qscale, int64_t rows,
+                                                     int H) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole wave leaves together
+  const float* src = qn + r * H;
+  float amax = 0.f;
+  for (int c = 8 * lane; c < H; c += 512) {
+    float v[8];
+    ld8f(src + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = group_max<64>(amax);
+  const float sc = amax / 127.0f;
+  for (int c = 8 * lane; c < H; c += 512) {
+    float v[8];
+    ld8f(src + c, v);
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = sc > 0.f ? sat_rne(v[e] / sc, -127, 127) : 0;
+    st8(q8 + r * H + c,
+        make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])));
+  }
+  if (lane == 0) gst(qscale + r, sc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1682,10 +1740,15 @@ constexpr int kA1Cols = 64;  // A1 tile width: two column blocks (one per wave a
 // A1 reads x row-major: with one 32-row block each workgroup stages its
 // split of x in LDS (fragment order), otherwise lanes load rows directly.
 template <int MB>
-void skinny_a1(const GemmParams& g1, const MlaPlan& pl, const Launch& L) {
+void skinny_a1(const GemmParams& g1, const MlaPlan& pl, bool xq, const Launch& L) {
   const dim3 grid(static_cast<unsigned>(g1.ntiles0 + (g1.N1 + kA1Cols - 1) / kA1Cols),
                   static_cast<unsigned>(pl.ksplit), 1);
   constexpr int KW = a1_kw<MB>();
+  if (xq) {
+    // full quantisation: int8 x . int8 weights (32-k steps), int32 sums
+    skinny<A_I8, MB, 2, 1, KW, EPI_PARTIAL>(g1, grid, L);
+    return;
+  }
   if constexpr (MB == 1) {
     if (pl.steps_per_split <= A_LDS_STEPS) {
       // one column block per wave, two waves across, K over 8 waves
@@ -1743,11 +1806,13 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   MlaPlan pl{};
   const int64_t T = a->B * a->S;
   const bool quant = a->quant_mode != MLA_QUANT_NONE;
+  const bool xq = a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8;
   const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
   pl.skinny = T <= 128;
   pl.gemm256 = !pl.skinny && !quant;
   pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
-  const int64_t steps = a->He / 16;
+  // k-steps of the down projection: 16 k (bf16) or 32 k (int8 x)
+  const int64_t steps = a->He / (xq ? 32 : 16);
   if (pl.gemm256) {
     // Split the down projection over K so that its 128x256 tiles (two
     // workgroups per CU) times the splits fill whole rounds of the 512
@@ -1797,9 +1862,9 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     const size_t eb_uq = quant ? 1 : 2;
     auto pad32 = [](int64_t n) { return static_cast<size_t>((n + 31) / 32 * 32); };
     pl.off_wdq = off;
-    off += align256(static_cast<size_t>(a->He) * pad32(a->Hcq) * 2);
+    off += align256(static_cast<size_t>(a->He) * pad32(a->Hcq) * (xq ? 1 : 2));
     pl.off_wdkvkr = off;
-    off += align256(static_cast<size_t>(a->He) * pad32(a->Hckv + a->Dr) * 2);
+    off += align256(static_cast<size_t>(a->He) * pad32(a->Hckv + a->Dr) * (xq ? 1 : 2));
     pl.off_wuqqr = off;
     off += align256(static_cast<size_t>(a->Hcq) * pad32(a->N * (a->D + a->Dr)) * eb_uq);
     pl.off_wuk = off;
@@ -1813,6 +1878,9 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   off += align256(static_cast<size_t>(T) * 4);
   pl.off_qc = off;
   off += align256(static_cast<size_t>(pl.rows * a->N * a->D) * (quant ? 4 : 2));
+  pl.off_qn = off;
+  if (a->quant_mode == MLA_QUANT_FULL_KV_INT8)
+    off += align256(static_cast<size_t>(T * a->N * a->Hckv) * sizeof(float));
   pl.off_xfrag = off;
   if (pl.gemm256) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
   pl.total = T > 0 ? off : 0;
@@ -1824,16 +1892,25 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   const int64_t T = a->B * a->S;
   if (T == 0) return QKVNR_OK;
   const bool quant = a->quant_mode != MLA_QUANT_NONE;
-  const int qm = a->quant_mode;  // 0, 1, 2
+  const bool xq = a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8;
+  const bool q8out = a->quant_mode == MLA_QUANT_FULL_KV_INT8;
+  // finish variant: 0 none, 1 c^Q quant + bf16 caches, 2 + int8 kv / kr,
+  // 3 + int8 kv and bf16 kr (k_down_finish's QM)
+  const int qm = a->quant_mode == MLA_QUANT_FULL_KV_BF16 ? 1
+                 : a->quant_mode == MLA_QUANT_FULL_KV_INT8 ? 3
+                                                           : a->quant_mode;
   char* ws = static_cast<char*>(workspace);
   const int64_t NDR = a->N * (a->D + a->Dr);
   const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
 
   const uint4 *wdq, *wdkvkr, *wuqqr, *wuk;
   if (a->weight_layout == MLA_WEIGHT_ND) {
-    int rc = launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, 2, a->Hcq, 0, st);
+    const int eb_down = xq ? 1 : 2;
+    int rc = launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, eb_down, a->Hcq,
+                                0, st);
     if (rc == QKVNR_OK)
-      rc = launch_pack_weight(a->weight_dkv_kr, ws + pl.off_wdkvkr, 1, a->He, a->Hckv + a->Dr, 2,
+      rc = launch_pack_weight(a->weight_dkv_kr, ws + pl.off_wdkvkr, 1, a->He, a->Hckv + a->Dr,
+                              eb_down,
                               a->Hckv + a->Dr, 0, st);
     if (rc == QKVNR_OK)
       rc = launch_pack_weight(a->weight_uq_qr, ws + pl.off_wuqqr, 1, a->Hcq, NDR, quant ? 1 : 2,
@@ -1925,6 +2002,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   g8.q_out = static_cast<uint16_t*>(a->query);
   g8.q_ld = a->N * a->Hckv;
   g8.q_bstride = a->Hckv;
+  if (q8out) g8.q_f32 = reinterpret_cast<float*>(ws + pl.off_qn);
   if (frag) {
     g8.a_frag = 1;
     g8.a_mbs = a->D * (quant ? 128 : 64);  // 32 rows x D fp32 / bf16
@@ -1958,6 +2036,11 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   f.cq_frag = frag ? 1 : 0;
   f.dbg_cq_i8 = a->dbg_cq_int8;
   f.dbg_cq_scale = a->dbg_cq_scale;
+  if (xq) {
+    f.sx = a->dequant_scale_x;
+    f.sw_dq = a->dequant_scale_w_dq;
+    f.sw_dkv = a->dequant_scale_w_dkv_kr;
+  }
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
   const dim3 fin_block(static_cast<unsigned>(fin_threads(ntot)));
 
@@ -1985,8 +2068,10 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       launch(Lf, k_down_finish<0>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
     else if (qm == 1)
       launch(Lf, k_down_finish<1>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
-    else
+    else if (qm == 2)
       launch(Lf, k_down_finish<2>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
+    else
+      launch(Lf, k_down_finish<3>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
   };
 
   const int nh = static_cast<int>(a->N);
@@ -1994,9 +2079,9 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   if (pl.skinny) {
     g1.ntiles0 = static_cast<int>((g1.N0 + kA1Cols - 1) / kA1Cols);
     switch (pl.mb) {
-      case 1: skinny_a1<1>(g1, pl, L1); break;
-      case 2: skinny_a1<2>(g1, pl, L1); break;
-      default: skinny_a1<4>(g1, pl, L1); break;
+      case 1: skinny_a1<1>(g1, pl, xq, L1); break;
+      case 2: skinny_a1<2>(g1, pl, xq, L1); break;
+      default: skinny_a1<4>(g1, pl, xq, L1); break;
     }
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
@@ -2070,7 +2155,10 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     const unsigned mt = static_cast<unsigned>((T + TBM - 1) / TBM);
     g1.ntiles0 = static_cast<int>((g1.N0 + TBN - 1) / TBN);
     const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + TBN - 1) / TBN);
-    tiled<A_BF16, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), L1);
+    if (xq)
+      tiled<A_I8, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), L1);
+    else
+      tiled<A_BF16, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), L1);
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
@@ -2085,6 +2173,12 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       tiled<A_F32SPLIT, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
     else
       tiled<A_BF16, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
+  }
+  if (q8out) {
+    const int64_t rows = T * a->N;
+    launch(L0, k_quant_query, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
+           static_cast<const float*>(g8.q_f32), static_cast<int8_t*>(a->query),
+           a->dequant_scale_q_nope, rows, static_cast<int>(a->Hckv));
   }
   mark(MLA_PHASE_AFTER_UK);
   return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;

@@ -145,11 +145,16 @@ def run_mla_gpu(w, dev=None, layout="packed", bsh=False, workspace=None):
         quant_scale_ckv=d.get("quant_scale_ckv"),
         quant_scale_ckr=d.get("quant_scale_ckr"),
         smooth_scales_cq=d.get("smooth_scales_cq"),
+        dequant_scale_x=d.get("dequant_scale_x"),
+        dequant_scale_w_dq=d.get("dequant_scale_w_dq"),
+        dequant_scale_w_dkv_kr=d.get("dequant_scale_w_dkv_kr"),
         return_cq_quant=quant != "none", workspace=workspace)
     out = {"query": res[0], "query_rope": res[1], "kv_cache": d["kv_cache"],
            "kr_cache": d["kr_cache"]}
+    if quant == "full_kv_int8":
+        out["dequant_scale_q_nope"] = res[2]
     if quant != "none":
-        out["cq_int8"], out["cq_scale"] = res[2], res[3]
+        out["cq_int8"], out["cq_scale"] = res[-2], res[-1]
     return out
 
 
@@ -185,15 +190,16 @@ def check_mla(w, out, before, tokens=None):
                                            "query_rope")
     else:
         stats.update(check_quant_conditioned(ww, ref, out, q, qr, tokens))
-    int8 = cfg.quant_mode == "partial_kv_int8"
+    kv8 = cfg.quant_mode in ("partial_kv_int8", "full_kv_int8")
+    kr8 = cfg.quant_mode == "partial_kv_int8"
     index = w.arrays["cache_index"].reshape(-1)
     if cfg.slots > 0:
         tok = None if tokens is None else np.asarray(tokens)
         stats["kv_cache"] = check_cache(before["kv_cache"], out["kv_cache"],
-                                        index, ref["kv_rows"], int8,
+                                        index, ref["kv_rows"], kv8,
                                         "kv_cache", tok)
         stats["kr_cache"] = check_cache(before["kr_cache"], out["kr_cache"],
-                                        index, ref["kr_rows"], int8,
+                                        index, ref["kr_rows"], kr8,
                                         "kr_cache", tok)
     return stats
 
@@ -227,9 +233,22 @@ def check_quant_conditioned(ww, ref, out, q, qr, tokens):
     sin = decode(ww.arrays["rope_sin"], "bf16").reshape(-1, cfg.Dr)
     rq, rqr = oracle.mla_query_from_quantized(c8, s, W8, dq, Wuk, cos, sin,
                                               cfg.N, cfg.D, cfg.Dr)
-    return {"code_flips": int(diff.sum()),
-            "query": assert_close(dev_to_f64(q), rq, "query"),
-            "query_rope": assert_close(dev_to_f64(qr), rqr, "query_rope")}
+    stats = {"code_flips": int(diff.sum()),
+             "query_rope": assert_close(dev_to_f64(qr), rqr, "query_rope")}
+    if cfg.quant_mode != "full_kv_int8":
+        stats["query"] = assert_close(dev_to_f64(q), rq, "query")
+        return stats
+    # int8 query per (token, head): the oracle's quantisation of the re-run
+    # q^N; scales to 1e-3 relative, codes within +/-1
+    codes, scale = oracle.mla_prolog_v2_quant_query(rq)
+    sg = out["dequant_scale_q_nope"].reshape(-1, cfg.N).cpu().numpy().astype(np.float64)
+    if tokens is not None:
+        sg = sg[tokens]
+    np.testing.assert_allclose(sg, scale, rtol=1e-3, atol=1e-12)
+    qg = q.cpu().numpy().astype(np.int64)
+    assert_codes(qg, codes, "query")
+    stats["query_code_mismatch"] = int((qg != codes).sum())
+    return stats
 
 
 # ---------------------------------------------------------------------------

@@ -75,6 +75,13 @@ def mla_args(T=32, quant="none", He=7168, Hcq=1536, N=128, D=128, Hckv=512,
     if quant == "partial_kv_int8":
         a.quant_scale_ckv = fake()
         a.quant_scale_ckr = fake()
+    if quant.startswith("full"):
+        a.dequant_scale_x = fake()
+        a.dequant_scale_w_dq = fake()
+        a.dequant_scale_w_dkv_kr = fake()
+    if quant == "full_kv_int8":
+        a.quant_scale_ckv = fake()
+        a.dequant_scale_q_nope = fake()
     return a
 
 
@@ -83,7 +90,8 @@ def mla_validate(a):
 
 
 def test_mla_valid_args_pass():
-    for q in ("none", "partial_kv_bf16", "partial_kv_int8"):
+    for q in ("none", "partial_kv_bf16", "partial_kv_int8", "full_kv_bf16",
+              "full_kv_int8"):
         assert mla_validate(mla_args(quant=q)) == 0
     assert mla_validate(mla_args(T=4, He=256, Hcq=128, N=4, D=32, Hckv=64,
                                  Dr=16, bn=4, bs=16)) == 0
@@ -92,8 +100,8 @@ def test_mla_valid_args_pass():
 @pytest.mark.parametrize("mutate,code", [
     (lambda a: setattr(a, "struct_size", 8), -8),
     (lambda a: setattr(a, "reserved0", 1), -8),
-    (lambda a: setattr(a, "quant_mode", 3), -4),   # full quant, kv bf16
-    (lambda a: setattr(a, "quant_mode", 4), -4),   # full quant, kv int8
+    (lambda a: setattr(a, "quant_mode", 3), -1),   # full quant without its scales
+    (lambda a: setattr(a, "quant_mode", 4), -1),
     (lambda a: setattr(a, "quant_mode", 9), -3),
     (lambda a: setattr(a, "weight_layout", 7), -3),
     (lambda a: setattr(a, "cache_mode", b"PA_NZ"), -4),
@@ -133,6 +141,39 @@ def test_mla_quant_mode_needs_its_scales():
     assert mla_validate(a) == -1
     # Hcq must be a multiple of 64 for the int8 up-projection
     assert mla_validate(mla_args(quant="partial_kv_bf16", Hcq=1568)) == -4
+
+
+def test_mla_full_quant_scales():
+    """Full quantisation needs the x and down-projection dequant scales (and,
+    with the int8 kv_cache, its quant scale and the query's output scale);
+    scales its scenario does not use must be NULL; He must be a multiple of
+    64 (int8 K steps of the tiled down projection)."""
+    for q in ("full_kv_bf16", "full_kv_int8"):
+        for f in ("dequant_scale_x", "dequant_scale_w_dq",
+                  "dequant_scale_w_dkv_kr", "dequant_scale_w_uq_qr",
+                  "smooth_scales_cq"):
+            a = mla_args(quant=q)
+            setattr(a, f, None)
+            assert mla_validate(a) == -1, (q, f)
+        a = mla_args(quant=q)
+        a.quant_scale_ckr = fake()          # kr_cache stays bf16
+        assert mla_validate(a) == -5
+        assert mla_validate(mla_args(quant=q, He=7136)) == -4
+    a = mla_args(quant="full_kv_int8")
+    a.dequant_scale_q_nope = None
+    assert mla_validate(a) == -1
+    a = mla_args(quant="full_kv_int8")
+    a.quant_scale_ckv = None
+    assert mla_validate(a) == -1
+    a = mla_args(quant="full_kv_bf16")
+    a.dequant_scale_q_nope = fake()         # bf16 query: no output scale
+    assert mla_validate(a) == -5
+    a = mla_args(quant="full_kv_bf16")
+    a.quant_scale_ckv = fake()              # bf16 kv_cache
+    assert mla_validate(a) == -5
+    a = mla_args(quant="partial_kv_bf16")
+    a.dequant_scale_x = fake()              # x stays bf16
+    assert mla_validate(a) == -5
 
 
 def test_mla_empty_cases():

@@ -125,7 +125,8 @@ def test_pack_weight_uk_bit_exact(N, D, H):
 # ---- MLA prolog --------------------------------------------------------------
 
 MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3",
-             "mla_prefill_ragged"]
+             "mla_prefill_ragged", "mla_full_kvbf16", "mla_full_kvint8",
+             "mla_full_kvint8_large"]
 
 
 @pytest.mark.parametrize("key", MLA_SMALL)
@@ -195,7 +196,8 @@ def test_mla_prefill_partial_quant_tiled_path():
 
 # config 2 (prefill T = 4096): every GEMM tile shape at full occupancy,
 # where a stage-buffer race shows up as run-to-run differences
-@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3, "mla_dec_t13", 2])
+@pytest.mark.parametrize("key", [0, "mla_mid_dsv3", 3, "mla_dec_t13", 2,
+                                 "mla_full_kvint8"])
 def test_mla_deterministic(key):
     w = make_workload(key)
     gh.announce(f"mla determinism {w.cfg.name}")
@@ -207,6 +209,20 @@ def test_mla_deterministic(key):
         outs.append({k: gh.raw_bits(v) for k, v in o.items()})
     for k in outs[0]:
         np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
+
+
+@pytest.mark.parametrize("mode,T", [("full_kv_int8", 32), ("full_kv_bf16", 64)])
+def test_mla_full_quant_dsv3_dims(mode, T):
+    """Full quantisation at the DeepSeek-V3 dims with 32 heads (the
+    partially quantised workload's shape): the one- and two-block decode
+    plans."""
+    w = make_workload(get_config(3).replace(B=T, quant_mode=mode, seed=2017))
+    gh.announce(f"mla {w.cfg.name} {mode} T={T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
 def test_mla_T0_and_no_slots():
