@@ -47,6 +47,7 @@ def parse():
                     help="independent input sets cycled by the decode steps")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
+    ap.add_argument("--no-full-quant", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -67,6 +68,20 @@ def mla_bytes(c, wb_uq=2, cache_b=2):
     per_tok = (c.He * 2 + 2 * c.Dr * 2 + 8 + c.N * c.Hckv * 2
                + c.N * c.Dr * 2 + (c.Hckv + c.Dr) * cache_b)
     return weights + gammas + T * per_tok
+
+
+def mla_full_bytes(c):
+    """Full quantisation with the int8 kv_cache: int8 x, down-projection
+    and up-projection weights, bf16 W^UK, fp32 scales; int8 query with a
+    per-(token, head) scale, bf16 query_rope and kr_cache, int8 kv_cache."""
+    T = c.T
+    weights = c.He * (c.Hcq + c.Hckv + c.Dr) + c.Hcq * c.N * (c.D + c.Dr) \
+        + c.N * c.D * c.Hckv * 2
+    scales = (c.Hcq + (c.Hckv + c.Dr) + c.N * (c.D + c.Dr) + c.Hcq
+              + c.Hckv) * 4 + (c.Hcq + c.Hckv) * 2
+    per_tok = (c.He + 4 + 2 * c.Dr * 2 + 8 + c.N * c.Hckv + c.N * 4
+               + c.N * c.Dr * 2 + c.Hckv + c.Dr * 2)
+    return weights + scales + T * per_tok
 
 
 def mla_flops(c):
@@ -146,6 +161,12 @@ def calibrate_copy(torch, mb):
     del src, dst
 
 
+# scale tensors of the quantised scenarios, passed by name when present
+MLA_SCALES = ("dequant_scale_w_uq_qr", "smooth_scales_cq", "quant_scale_ckv",
+              "quant_scale_ckr", "dequant_scale_x", "dequant_scale_w_dq",
+              "dequant_scale_w_dkv_kr", "dequant_scale_q_nope")
+
+
 def prepare_mla_sets(w, n_sets, torch, qn, gh):
     """Upload one seeded workload, pack its weights, and clone it n_sets-1
     times into distinct allocations."""
@@ -160,16 +181,22 @@ def prepare_mla_sets(w, n_sets, torch, qn, gh):
         "weight_uk": qn.mla_pack_weight_uk(d["weight_uk"]),
     }
     for k in ("rmsnorm_gamma_cq", "rmsnorm_gamma_ckv", "rope_sin", "rope_cos",
-              "cache_index", "kv_cache", "kr_cache"):
-        base[k] = d[k]
+              "cache_index", "kv_cache", "kr_cache") + MLA_SCALES:
+        if k in d:
+            base[k] = d[k]
     sets = [base]
     for _ in range(1, n_sets):
         sets.append({k: v.clone() for k, v in base.items()})
+    q8 = cfg.quant_mode == "full_kv_int8"
     for s in sets:
         s["query"] = torch.empty((cfg.B, cfg.S, cfg.N, cfg.Hckv),
-                                 dtype=torch.bfloat16, device="cuda")
+                                 dtype=torch.int8 if q8 else torch.bfloat16,
+                                 device="cuda")
         s["query_rope"] = torch.empty((cfg.B, cfg.S, cfg.N, cfg.Dr),
                                       dtype=torch.bfloat16, device="cuda")
+        if q8:
+            s["dequant_scale_q_nope"] = torch.empty(
+                (cfg.B, cfg.S, cfg.N, 1), dtype=torch.float32, device="cuda")
     return sets
 
 
@@ -241,11 +268,13 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
              "weight_dkv_kr", "rmsnorm_gamma_cq", "rmsnorm_gamma_ckv",
              "rope_sin", "rope_cos", "cache_index", "kv_cache", "kr_cache",
              "query", "query_rope")
-    calls = [qn.PreparedMlaPrologV2(*[s[k] for k in names], **kw)
+    def scales(s):
+        return {k: s[k] for k in MLA_SCALES if k in s}
+    calls = [qn.PreparedMlaPrologV2(*[s[k] for k in names], **kw, **scales(s))
              for s in sets[:1]]
     ws = calls[0].workspace
     calls += [qn.PreparedMlaPrologV2(*[s[k] for k in names], workspace=ws,
-                                     **kw) for s in sets[1:]]
+                                     **kw, **scales(s)) for s in sets[1:]]
     stream = torch.cuda.current_stream()
     he = HipEvents()
     ev = [[he.create() for _ in range(nph)] for _ in range(steps)]
@@ -510,6 +539,29 @@ def main():
                          "traffic": None},
         }
         del psets
+        torch.cuda.empty_cache()
+
+    # ---- full quantisation (int8 kv_cache and query), T = 32 -------------
+    if not args.no_full_quant:
+        wf = make_workload(cfg.replace(quant_mode="full_kv_int8", seed=1101))
+        fc = wf.cfg
+        fsets = prepare_mla_sets(wf, args.rotate, torch, qn, gh)
+        fms, _, _, fk = run_mla(fc, fsets, max(20, args.steps // 2),
+                                max(5, args.warmup // 2), torch, qn)
+        fb = mla_full_bytes(fc)
+        out["full_quant_decode"] = {
+            "workload": fc.name + "_full_kv_int8",
+            "quant_mode": "full_kv_int8",
+            "tokens_per_s": fc.T / (fms * 1e-3), "ms_per_step": fms,
+            "algorithmic_bytes": fb,
+            "achieved_GBps": fb / (fms * 1e-3) / 1e9,
+            "hbm_frac": fb / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_us": dict(zip(qn.MLA_KERNELS, [k * 1e3 for k in fk])),
+            "timing": "HIP-graph replay of the prepared calls over "
+                      f"{args.rotate} rotating input sets; int8 x, weights "
+                      "(W^UK bf16), kv_cache and query",
+        }
+        del fsets
         torch.cuda.empty_cache()
 
     if not args.no_qkv:
