@@ -80,6 +80,10 @@ struct GemmParams {
   // EPI_UK (and EPI_QN's output)
   uint16_t* q_out;  // (T, N, Hckv)
   float* q_f32;     // when set, q^N goes here in fp32 instead (same indexing)
+  // EPI_UK with the per-(token, head) int8 quantisation fused (QH): codes
+  // (T, N, Hckv) and scales (T, N), one workgroup covering a head's Hckv
+  int8_t* q8_out;
+  float* q8_scale;
   int64_t q_ld;     // N*Hckv
   int64_t q_bstride;  // Hckv (per head)
   // EPI_QN: q^C never leaves registers; the W^UK product runs in the
@@ -286,7 +290,8 @@ enum { ALDS_NONE = 0, ALDS_ROWMAJOR = 1, ALDS_FRAG = 2 };
 // One tile of the skinny GEMM: tile bx (column tiles of B0 then of B1),
 // split by, batch bz; run by a 64*NW*KW-thread workgroup.
 template <int AK, int MB, int NB, int NW, int KW, int EPI,
-          int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS>
+          int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS,
+          bool QH = false>
 __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, const int by,
                                             const int bz) {
   typedef typename AccT<AK>::type Acc;
@@ -571,6 +576,48 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   }
   __syncthreads();
 
+  if constexpr (QH) {
+    // int8 query per (token, head): the tile is the head's whole Hckv
+    // (N <= TN, one column tile).  TPR threads per row, each over 8-column
+    // chunks c0 = 8*(part + TPR*i); the row's max |q^N| is a butterfly over
+    // its TPR lanes (aligned, inside one wave); scale = max / 127, codes
+    // round half to even in [-127, 127], 0 for an all-zero row.
+    static_assert(EPI == EPI_UK && MB == 1 && KW == 1, "QH: one row block, whole-K waves");
+    constexpr int NT = 64 * NW;
+    constexpr int TPR = NT / 32;
+    static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0, "QH: rows inside one wave");
+    constexpr int CH = TN / 8 / TPR;  // chunks per thread
+    const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c0 = 8 * (part + TPR * i);
+      if (c0 < N) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(__uint_as_float(lds[0][row][c0 + e])));
+      }
+    }
+    amax = group_max<TPR>(amax);
+    const float sc = amax / 127.0f;
+    if (row < p.M) {
+      const int64_t ob = static_cast<int64_t>(row) * p.q_ld + static_cast<int64_t>(bz) * p.q_bstride;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c0 = 8 * (part + TPR * i);
+        if (c0 < N) {
+          int q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            q[e] = sc > 0.f ? sat_rne(__uint_as_float(lds[0][row][c0 + e]) / sc, -127, 127) : 0;
+          st8(p.q8_out + ob + c0,
+              make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7])));
+        }
+      }
+      if (part == 0) gst(p.q8_scale + static_cast<int64_t>(row) * (p.q_ld / p.q_bstride) + bz, sc);
+    }
+    return;
+  }
+
   // Epilogue: 8-column groups of the (MB*32) x TN tile.
   GemmParams pe = p;
   if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(by) * p.M * p.part_ld;
@@ -611,9 +658,10 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
 }
 
 template <int AK, int MB, int NB, int NW, int KW, int EPI,
-          int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS>
+          int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS,
+          bool QH = false>
 __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
-  skinny_tile<AK, MB, NB, NW, KW, EPI, P, ALDS, ACAP>(p, static_cast<int>(blockIdx.x),
+  skinny_tile<AK, MB, NB, NW, KW, EPI, P, ALDS, ACAP, QH>(p, static_cast<int>(blockIdx.x),
                                                      static_cast<int>(blockIdx.y),
                                                      static_cast<int>(blockIdx.z));
 }
@@ -2002,7 +2050,15 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   g8.q_out = static_cast<uint16_t*>(a->query);
   g8.q_ld = a->N * a->Hckv;
   g8.q_bstride = a->Hckv;
-  if (q8out) g8.q_f32 = reinterpret_cast<float*>(ws + pl.off_qn);
+  // FULL_KV_INT8: one workgroup per head quantises the query in its
+  // epilogue when a head's Hckv fits one tile of at most 16 waves and T fits
+  // one row block; otherwise q^N goes out in fp32 for k_quant_query.
+  const bool qh = q8out && pl.skinny && pl.mb == 1 && a->Hckv <= 512;
+  if (q8out && !qh) g8.q_f32 = reinterpret_cast<float*>(ws + pl.off_qn);
+  if (qh) {
+    g8.q8_out = static_cast<int8_t*>(a->query);
+    g8.q8_scale = a->dequant_scale_q_nope;
+  }
   if (frag) {
     g8.a_frag = 1;
     g8.a_mbs = a->D * (quant ? 128 : 64);  // 32 rows x D fp32 / bf16
@@ -2092,10 +2148,23 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       default: skinny_a6<4>(g6, quant, L6); break;
     }
     mark(MLA_PHASE_AFTER_UQQR);
-    switch (pl.mb) {
-      case 1: skinny_a8<1>(g8, nh, quant, L8); break;
-      case 2: skinny_a8<2>(g8, nh, quant, L8); break;
-      default: skinny_a8<4>(g8, nh, quant, L8); break;
+    if (qh) {
+      const dim3 grid(1, 1, static_cast<unsigned>(nh));
+      if (a->Hckv <= 128)
+        launch(L8, k_skinny<A_F32SPLIT, 1, 1, 4, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,
+               grid, dim3(64 * 4), 0, g8);
+      else if (a->Hckv <= 256)
+        launch(L8, k_skinny<A_F32SPLIT, 1, 1, 8, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,
+               grid, dim3(64 * 8), 0, g8);
+      else
+        launch(L8, k_skinny<A_F32SPLIT, 1, 1, 16, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,
+               grid, dim3(64 * 16), 0, g8);
+    } else {
+      switch (pl.mb) {
+        case 1: skinny_a8<1>(g8, nh, quant, L8); break;
+        case 2: skinny_a8<2>(g8, nh, quant, L8); break;
+        default: skinny_a8<4>(g8, nh, quant, L8); break;
+      }
     }
   } else if (pl.gemm256) {
     // x into fragment layout first: the GEMM's A loads are then 1 KB
@@ -2174,7 +2243,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     else
       tiled<A_BF16, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
   }
-  if (q8out) {
+  if (q8out && !qh) {
     const int64_t rows = T * a->N;
     launch(L0, k_quant_query, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0,
            static_cast<const float*>(g8.q_f32), static_cast<int8_t*>(a->query),

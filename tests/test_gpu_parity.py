@@ -211,6 +211,23 @@ def test_mla_deterministic(key):
         np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
 
 
+@pytest.mark.parametrize("Hckv,T", [(96, 21), (256, 9), (64, 1)])
+def test_mla_full_quant_query_in_epilogue(Hckv, T):
+    """FULL_KV_INT8 with one row block: the W^UK product quantises the query
+    per (token, head) in its epilogue, one workgroup per head of 4, 8 or 16
+    waves (Hckv up to 128, 256, 512)."""
+    cfg = get_config("mla_full_kvint8").replace(B=T, Hckv=Hckv,
+                                                n_skip=min(2, T - 1),
+                                                seed=2018 + Hckv)
+    w = make_workload(cfg)
+    gh.announce(f"mla {w.cfg.name} Hckv={Hckv} T={T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
 @pytest.mark.parametrize("mode,T", [("full_kv_int8", 32), ("full_kv_bf16", 64)])
 def test_mla_full_quant_dsv3_dims(mode, T):
     """Full quantisation at the DeepSeek-V3 dims with 32 heads (the
