@@ -10,7 +10,7 @@ import torch
 
 import qkv_norm_rope_amd as qn
 from tests import gpu_helpers as gh
-from workloads import make_workload
+from workloads import get_config, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -26,8 +26,9 @@ def _prepared(w, d):
     d["weight_uk"] = qn.mla_pack_weight_uk(d["weight_uk"])
     d["weight_uq_qr"] = qn.mla_pack_weight_uq_qr(d["weight_uq_qr"], cfg.N,
                                                  cfg.D, cfg.Dr)
-    q = torch.empty((cfg.T, cfg.N, cfg.Hckv), dtype=torch.bfloat16,
-                    device="cuda")
+    q8 = cfg.quant_mode == "full_kv_int8"
+    q = torch.empty((cfg.T, cfg.N, cfg.Hckv),
+                    dtype=torch.int8 if q8 else torch.bfloat16, device="cuda")
     qr = torch.empty((cfg.T, cfg.N, cfg.Dr), dtype=torch.bfloat16,
                      device="cuda")
     kw = {}
@@ -37,15 +38,29 @@ def _prepared(w, d):
     if cfg.quant_mode == "partial_kv_int8":
         kw.update(quant_scale_ckv=d["quant_scale_ckv"],
                   quant_scale_ckr=d["quant_scale_ckr"])
+    if cfg.quant_mode.startswith("full"):
+        kw.update(dequant_scale_x=d["dequant_scale_x"],
+                  dequant_scale_w_dq=d["dequant_scale_w_dq"],
+                  dequant_scale_w_dkv_kr=d["dequant_scale_w_dkv_kr"])
+    if q8:
+        d["dequant_scale_q_nope"] = torch.empty((cfg.T, cfg.N, 1),
+                                                dtype=torch.float32,
+                                                device="cuda")
+        kw.update(quant_scale_ckv=d["quant_scale_ckv"],
+                  dequant_scale_q_nope=d["dequant_scale_q_nope"])
     return qn.PreparedMlaPrologV2(*[d[k] for k in NAMES], q, qr,
                                   quant_mode=cfg.quant_mode,
                                   rmsnorm_epsilon_cq=cfg.eps_cq,
                                   rmsnorm_epsilon_ckv=cfg.eps_ckv, **kw)
 
 
-@pytest.mark.parametrize("key", [1, 3, "mla_mid_dsv3"])
+@pytest.mark.parametrize("key", [1, 3, "mla_mid_dsv3", "mla_full_kvint8",
+                                 "mla_full_kvint8_small_t"])
 def test_mla_graph_replays_match_eager(key):
-    w = make_workload(key)
+    if key == "mla_full_kvint8_small_t":  # the query quantised in A8's epilogue
+        w = make_workload(get_config("mla_full_kvint8").replace(B=21, n_skip=2))
+    else:
+        w = make_workload(key)
     gh.announce(f"graph replay {w.cfg.name}")
     d = gh.upload(w)
     kv0, kr0 = d["kv_cache"].clone(), d["kr_cache"].clone()
@@ -54,6 +69,9 @@ def test_mla_graph_replays_match_eager(key):
     torch.cuda.synchronize()
     ref = {"q": gh.raw_bits(q), "qr": gh.raw_bits(qr),
            "kv": gh.raw_bits(d["kv_cache"]), "kr": gh.raw_bits(d["kr_cache"])}
+    qs = d.get("dequant_scale_q_nope")  # full quantisation with an int8 query
+    if qs is not None:
+        ref["qs"] = gh.raw_bits(qs)
     # a second, independent eager call used as eager work between replays
     d2 = gh.upload(w)
     other = _prepared(w, d2)
@@ -64,6 +82,8 @@ def test_mla_graph_replays_match_eager(key):
     for rep in range(3):
         q.zero_()
         qr.zero_()
+        if qs is not None:
+            qs.zero_()
         d["kv_cache"].copy_(kv0)
         d["kr_cache"].copy_(kr0)
         other()
@@ -74,6 +94,8 @@ def test_mla_graph_replays_match_eager(key):
         np.testing.assert_array_equal(gh.raw_bits(qr), ref["qr"], err_msg=f"rep {rep}")
         np.testing.assert_array_equal(gh.raw_bits(d["kv_cache"]), ref["kv"])
         np.testing.assert_array_equal(gh.raw_bits(d["kr_cache"]), ref["kr"])
+        if qs is not None:
+            np.testing.assert_array_equal(gh.raw_bits(qs), ref["qs"])
     del g
 
 
