@@ -432,8 +432,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the prolog shards by token or head with no "
-              "collective in this build)", file=sys.stderr)
+              "supported (the prolog would shard by token or by head; the "
+              "library implements no collective)", file=sys.stderr)
         return 2
     import torch
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
