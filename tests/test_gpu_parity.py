@@ -242,6 +242,28 @@ def test_mla_full_quant_dsv3_dims(mode, T):
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
+@pytest.mark.parametrize("key", ["mla_ragged_q", "mla_full_kvbf16",
+                                 "mla_full_kvint8", "mla_dec_t13"])
+def test_mla_zero_tokens(key):
+    """All-zero tokens: c^Q = 0, so the dynamic quantisation's scale is 0
+    with zero codes, the int8 query's per-head scale is 0, and the norms see
+    a zero row (their epsilon keeps them finite).  The tokens around them
+    are ordinary."""
+    w = make_workload(key)
+    x = w.arrays["token_x"].reshape(w.cfg.T, -1)
+    x[[0, w.cfg.T // 2]] = 0
+    gh.announce(f"mla zero tokens {w.cfg.name} {w.cfg.quant_mode}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+    if w.cfg.quant_mode != "none":
+        s = out["cq_scale"].cpu().numpy()
+        assert s[0] == 0 and s[w.cfg.T // 2] == 0
+        assert not out["cq_int8"][0].any()
+
+
 def test_mla_T0_and_no_slots():
     w = make_workload(0)
     cfg = w.cfg
