@@ -237,6 +237,7 @@ class HipEvents:
         ms = self.ct.c_float()
         if self.hip.hipEventElapsedTime(self.ct.byref(ms), a.cuda_event,
                                         b.cuda_event) != 0:
+            self.hip.hipGetLastError()  # do not leave the error to torch
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
 
@@ -297,7 +298,14 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     kernel_ms = [0.0] * nk
     for row in kev:
         for k in range(nk):
-            kernel_ms[k] += he.elapsed_ms(row[2 * k], row[2 * k + 1]) / steps
+            if kernel_ms[k] is None:
+                continue
+            try:
+                kernel_ms[k] += he.elapsed_ms(row[2 * k], row[2 * k + 1]) / steps
+            except RuntimeError:
+                # events never recorded: this plan launches no such kernel
+                # (decode runs the finish inside the up projection's launch)
+                kernel_ms[k] = None
     for row in ev + kev:
         for e in row:
             he.destroy(e)
@@ -489,7 +497,8 @@ def main():
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes,
                           "achieved": step_gbs, "peak": HBM_PEAK_GBS,
                           "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS},
-        "kernel_us": dict(zip(qn.MLA_KERNELS, [k * 1e3 for k in kernel_ms])),
+        "kernel_us": dict(zip(qn.MLA_KERNELS, [None if k is None else k * 1e3
+                                               for k in kernel_ms])),
         "phase_us": dict(zip(("down", "norm_cache", "up_qr", "uk"),
                              [p * 1e3 for p in phase_ms])),
         "timing": "value and ms_per_step: HIP-graph replay of the prepared "
@@ -525,7 +534,8 @@ def main():
             "step_TFLOPs": fl / (pms * 1e-3) / 1e12,
             "mfma_frac": fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "kernel_us": dict(zip(("down", "norm", "up_qr_rope",
-                                   "up_qc_uk"), [k * 1e3 for k in pk])),
+                                   "up_qc_uk"),
+                                  [None if k is None else k * 1e3 for k in pk])),
             "phase_us": dict(zip(("down", "norm_cache", "up_qr_rope",
                                   "up_qc_uk"),
                                  [p * 1e3 for p in pph])),
@@ -556,7 +566,8 @@ def main():
             "algorithmic_bytes": fb,
             "achieved_GBps": fb / (fms * 1e-3) / 1e9,
             "hbm_frac": fb / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_us": dict(zip(qn.MLA_KERNELS, [k * 1e3 for k in fk])),
+            "kernel_us": dict(zip(qn.MLA_KERNELS, [None if k is None else k * 1e3
+                                                   for k in fk])),
             "timing": "HIP-graph replay of the prepared calls over "
                       f"{args.rotate} rotating input sets; int8 x, weights "
                       "(W^UK bf16), kv_cache and query",
