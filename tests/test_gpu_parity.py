@@ -228,11 +228,15 @@ def test_mla_full_quant_query_in_epilogue(Hckv, T):
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
-@pytest.mark.parametrize("mode,T", [("full_kv_int8", 32), ("full_kv_bf16", 64)])
+@pytest.mark.parametrize("mode,T", [("full_kv_int8", 32), ("full_kv_bf16", 64),
+                                    ("full_kv_bf16", 32), ("full_kv_int8", 64),
+                                    ("partial_kv_bf16", 64),
+                                    ("partial_kv_bf16", 32)])
 def test_mla_full_quant_dsv3_dims(mode, T):
-    """Full quantisation at the DeepSeek-V3 dims with 32 heads (the
-    partially quantised workload's shape): the one- and two-block decode
-    plans."""
+    """The quantised scenarios at the DeepSeek-V3 dims with 32 heads (the
+    partially quantised workload's shape), on the one- and two-block decode
+    plans: both full-quantisation rows and the partial one with bf16
+    caches."""
     w = make_workload(get_config(3).replace(B=T, quant_mode=mode, seed=2017))
     gh.announce(f"mla {w.cfg.name} {mode} T={T}")
     dev = gh.upload(w)
