@@ -211,11 +211,12 @@ def test_mla_deterministic(key):
         np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
 
 
-@pytest.mark.parametrize("Hckv,T", [(96, 21), (256, 9), (64, 1)])
+@pytest.mark.parametrize("Hckv,T", [(96, 21), (256, 9), (64, 1), (1024, 8)])
 def test_mla_full_quant_query_in_epilogue(Hckv, T):
     """FULL_KV_INT8 with one row block: the W^UK product quantises the query
     per (token, head) in its epilogue, one workgroup per head of 4, 8 or 16
-    waves (Hckv up to 128, 256, 512)."""
+    waves (Hckv up to 128, 256, 512); a wider head (Hckv = 1024) takes the
+    fp32 q^N + k_quant_query path."""
     cfg = get_config("mla_full_kvint8").replace(B=T, Hckv=Hckv,
                                                 n_skip=min(2, T - 1),
                                                 seed=2018 + Hckv)
