@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-qkv", action="store_true")
     ap.add_argument("--no-full-quant", action="store_true")
+    ap.add_argument("--no-partial-quant", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -68,6 +69,20 @@ def mla_bytes(c, wb_uq=2, cache_b=2):
     per_tok = (c.He * 2 + 2 * c.Dr * 2 + 8 + c.N * c.Hckv * 2
                + c.N * c.Dr * 2 + (c.Hckv + c.Dr) * cache_b)
     return weights + gammas + T * per_tok
+
+
+def mla_partial_bytes(c):
+    """Partial quantisation with int8 caches: bf16 x and down-projection
+    weights, int8 W^UQ_QR, bf16 W^UK, fp32 scales; bf16 query and query_rope,
+    int8 kv / kr cache rows."""
+    T = c.T
+    weights = c.He * (c.Hcq + c.Hckv + c.Dr) * 2 + c.Hcq * c.N * (c.D + c.Dr) \
+        + c.N * c.D * c.Hckv * 2
+    scales = (c.N * (c.D + c.Dr) + c.Hcq + c.Hckv + c.Dr) * 4 \
+        + (c.Hcq + c.Hckv) * 2
+    per_tok = (c.He * 2 + 2 * c.Dr * 2 + 8 + c.N * c.Hckv * 2
+               + c.N * c.Dr * 2 + c.Hckv + c.Dr)
+    return weights + scales + T * per_tok
 
 
 def mla_full_bytes(c):
@@ -549,6 +564,28 @@ def main():
                          "traffic": None},
         }
         del psets
+        torch.cuda.empty_cache()
+
+    # ---- partial quantisation, int8 caches: T = 64, 32 heads -------------
+    if not args.no_partial_quant:
+        wq = make_workload(3)
+        qc = wq.cfg
+        qsets = prepare_mla_sets(wq, args.rotate, torch, qn, gh)
+        qms, _, _, qk = run_mla(qc, qsets, max(20, args.steps // 2),
+                                max(5, args.warmup // 2), torch, qn)
+        qb = mla_partial_bytes(qc)
+        out["partial_quant"] = {
+            "workload": qc.name, "quant_mode": qc.quant_mode,
+            "tokens_per_s": qc.T / (qms * 1e-3), "ms_per_step": qms,
+            "algorithmic_bytes": qb,
+            "achieved_GBps": qb / (qms * 1e-3) / 1e9,
+            "hbm_frac": qb / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_us": dict(zip(qn.MLA_KERNELS, [None if k is None else k * 1e3
+                                                   for k in qk])),
+            "timing": "HIP-graph replay of the prepared calls over "
+                      f"{args.rotate} rotating input sets",
+        }
+        del qsets
         torch.cuda.empty_cache()
 
     # ---- full quantisation (int8 kv_cache and query), T = 32 -------------
