@@ -61,8 +61,8 @@ enum {
                                        shape rule */
   QKVNR_ERR_BAD_MODE = -3,          /* unknown quant mode, dtype or layout */
   QKVNR_ERR_UNSUPPORTED = -4,       /* valid on the pages, not built here
-                                       (full quantisation, PA_NZ caches,
-                                       Nkv != 1, ...) */
+                                       (PA_NZ caches, Nkv != 1, dims off
+                                       the kernels' multiples, ...) */
   QKVNR_ERR_RESERVED_NONNULL = -5,  /* a reserved pointer is not NULL */
   QKVNR_ERR_WORKSPACE_TOO_SMALL = -6,
   QKVNR_ERR_BAD_EPS = -7,           /* epsilon negative or not finite */
@@ -71,7 +71,9 @@ enum {
                                        (cache_index and dbg_cq_int8: 8,
                                        dbg_cq_scale: 4) */
   QKVNR_ERR_LAUNCH_FAILED = -10,    /* hipGetLastError after a launch */
-  QKVNR_ERR_BAD_INDEX = -11         /* host index check (debug flag) */
+  QKVNR_ERR_BAD_INDEX = -11         /* reserved: no entry point returns it
+                                       (indexes are checked on the device,
+                                       see "Cache updates" above) */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -263,7 +265,9 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
  * `elem_bytes` = 2 (bf16/fp16) or 1 (int8), batches contiguous) into the
  * MLA_WEIGHT_PACKED_K16 layout at dst, a distinct buffer of
  * batch * K * ceil(N/32)*32 elements.  K must be a multiple of
- * 16 / elem_bytes.  Device pointers; enqueued on `stream`. */
+ * 16 / elem_bytes.  batch <= 65535, K and N <= 2^30 and the packed
+ * element count <= 2^46, else QKVNR_ERR_BAD_SHAPE (the same bounds hold for
+ * the two packers below).  Device pointers; enqueued on `stream`. */
 int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K,
                     int64_t N, int32_t elem_bytes, void* stream);
 

@@ -26,6 +26,14 @@ int check_cache_mode(const char* m) {
 constexpr int64_t kDimCap = int64_t(1) << 30;
 constexpr int64_t kKCap = int64_t(1) << 22;
 
+// The packers' bounds: batch (or heads) <= 65535, each dim <= 2^30 and at
+// most 2^46 packed elements, so no size product below overflows int64.
+bool pack_dims_ok(int64_t batch, int64_t K, int64_t N) {
+  if (batch < 0 || K < 0 || N < 0 || batch > 65535 || K > kDimCap || N > kDimCap) return false;
+  const int64_t per = K * ((N + 31) / 32) * 32;  // < 2^61
+  return batch == 0 || per <= (int64_t(1) << 46) / batch;
+}
+
 int validate_mla(const MlaPrologV2Args* a) {
   if (a == nullptr) return QKVNR_ERR_NULL_ARG;
   if (a->struct_size != sizeof(MlaPrologV2Args) || a->reserved0 != 0) return QKVNR_ERR_BAD_STRUCT;
@@ -229,7 +237,7 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace, size_t workspace
 int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
                     int32_t elem_bytes, void* stream) {
   if (elem_bytes != 1 && elem_bytes != 2) return QKVNR_ERR_BAD_MODE;
-  if (batch < 0 || K < 0 || N < 0 || K % (16 / elem_bytes) != 0) return QKVNR_ERR_BAD_SHAPE;
+  if (!pack_dims_ok(batch, K, N) || K % (16 / elem_bytes) != 0) return QKVNR_ERR_BAD_SHAPE;
   if (batch * K * N == 0) return QKVNR_OK;
   if (src == nullptr || dst == nullptr) return QKVNR_ERR_NULL_ARG;
   if (!aligned16(dst) || (elem_bytes == 2 && (reinterpret_cast<uintptr_t>(src) & 1u)))
@@ -240,8 +248,7 @@ int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_
 
 int mla_pack_weight_uk(const void* src, void* dst, int64_t N, int64_t D, int64_t Hckv,
                        void* stream) {
-  if (N < 0 || D < 0 || Hckv < 0 || N > 65535 || D > kDimCap || Hckv > kDimCap || D % 16 != 0)
-    return QKVNR_ERR_BAD_SHAPE;
+  if (!pack_dims_ok(N, D, Hckv) || D % 16 != 0) return QKVNR_ERR_BAD_SHAPE;
   if (N * D * Hckv == 0) return QKVNR_OK;
   if (src == nullptr || dst == nullptr) return QKVNR_ERR_NULL_ARG;
   if (!aligned16(dst) || (reinterpret_cast<uintptr_t>(src) & 1u)) return QKVNR_ERR_BAD_ALIGNMENT;
@@ -253,7 +260,7 @@ int mla_pack_weight_uq_qr(const void* src, void* dst, int64_t Hcq, int64_t N, in
                           int64_t Dr, int32_t elem_bytes, void* stream) {
   if (elem_bytes != 1 && elem_bytes != 2) return QKVNR_ERR_BAD_MODE;
   if (Hcq < 0 || N < 0 || D < 0 || Dr < 0 || Hcq > kDimCap || N > 65535 || D > kDimCap ||
-      Dr > kDimCap || Hcq % (16 / elem_bytes) != 0)
+      Dr > kDimCap || !pack_dims_ok(1, Hcq, N * (D + Dr)) || Hcq % (16 / elem_bytes) != 0)
     return QKVNR_ERR_BAD_SHAPE;
   if (Hcq * N == 0) return QKVNR_OK;
   if (D % 32 != 0 || !(Dr == 16 || Dr == 32 || Dr == 64)) return QKVNR_ERR_UNSUPPORTED;

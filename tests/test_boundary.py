@@ -223,6 +223,11 @@ def test_pack_weight_validation():
     assert lib.mla_pack_weight(None, None, 1, 24, 8, 1, None) == -2
     assert lib.mla_pack_weight(None, None, 0, 16, 8, 2, None) == 0
     assert lib.mla_pack_weight(None, None, 1, 16, 8, 2, None) == -1
+    # sizes whose products would overflow int64 are rejected before use
+    big = 1 << 40
+    assert lib.mla_pack_weight(None, None, big, big, big, 2, None) == -2
+    assert lib.mla_pack_weight(None, None, 1, 1 << 30, 1 << 30, 2, None) == -2
+    assert lib.mla_pack_weight(None, None, 65536, 16, 32, 2, None) == -2
     assert lib.mla_pack_weight(ctypes.c_void_p(fake()),
                                ctypes.c_void_p(fake() + 8), 1, 16, 8, 2,
                                None) == -9
@@ -235,6 +240,7 @@ def test_pack_weight_uk_validation():
     assert f(None, None, -1, 32, 32, None) == -2
     assert f(None, None, 0, 32, 32, None) == 0         # empty: nothing
     assert f(None, None, 2, 32, 32, None) == -1
+    assert f(None, None, 65535, 1 << 30, 1 << 30, None) == -2   # too large
     assert f(ctypes.c_void_p(fake()), ctypes.c_void_p(fake() + 8), 2, 32, 32,
              None) == -9
 
@@ -250,6 +256,7 @@ def test_pack_weight_uq_qr_validation():
     assert f(None, None, 64, 4, 48, 64, 2, None) == -4       # D % 32
     assert f(None, None, 64, 4, 32, 48, 2, None) == -4       # Dr not 16/32/64
     assert f(None, None, 64, 4, 32, 64, 2, None) == -1
+    assert f(None, None, 1 << 30, 65535, 1 << 30, 64, 2, None) == -2  # too large
     assert f(ctypes.c_void_p(fake()), ctypes.c_void_p(fake() + 8), 64, 4, 32,
              64, 2, None) == -9
 
