@@ -216,6 +216,15 @@ def test_mla_workspace_size_and_too_small():
     assert n.value == 0
 
 
+def test_mla_row_width_limit():
+    # the down projection's row (Hcq + Hckv + Dr fp32 values) is staged in
+    # 64 KB of LDS: 16384 values pass, 16 more do not
+    assert mla_validate(mla_args(T=13, He=64, Hcq=12288, N=2, D=32,
+                                 Hckv=4032, Dr=64)) == 0
+    assert mla_validate(mla_args(T=13, He=64, Hcq=12288, N=2, D=32,
+                                 Hckv=4048, Dr=64)) == -4
+
+
 def test_pack_weight_validation():
     lib = b.load_library()
     assert lib.mla_pack_weight(None, None, 1, 16, 8, 3, None) == -3

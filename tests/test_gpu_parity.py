@@ -347,6 +347,26 @@ def test_mla_decode_shapes(key):
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
+# the largest row the validator accepts ((Hcq + Hckv + Dr) * 4 = 64 KB) on
+# the decode and large-T plans, unquantised, partially and fully quantised
+@pytest.mark.parametrize("mode,T", [("none", 13), ("none", 130),
+                                    ("partial_kv_int8", 13),
+                                    ("partial_kv_int8", 130),
+                                    ("full_kv_int8", 13),
+                                    ("full_kv_bf16", 130)])
+def test_mla_max_row_width(mode, T):
+    cfg = get_config("mla_max_row")
+    blocks = max(cfg.block_num, -(-(T + 8) // cfg.block_size))
+    w = make_workload(cfg.replace(B=T, quant_mode=mode, block_num=blocks,
+                                  seed=cfg.seed + T))
+    gh.announce(f"mla max row {mode} T={T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
 def test_mla_packed_equals_nd():
     w = make_workload("mla_ragged")
     gh.announce("mla packed vs ND layouts")

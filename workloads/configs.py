@@ -162,6 +162,12 @@ CONFIGS = {
                                        Dr=16, block_num=2, block_size=128,
                                        n_skip=4, quant_mode="full_kv_int8",
                                        seed=2016, layout="BSH"),
+    # the widest down-projection row the kernels accept: Hcq + Hckv + Dr =
+    # 16384 fp32 values (64 KB, the finish kernel's staged row), with a
+    # kv row (4032) that is no multiple of 32 columns
+    "mla_max_row": MlaConfig("mla_max_row_T13", B=13, S=1, He=64, Hcq=12288,
+                             N=2, D=32, Hckv=4032, Dr=64, block_num=2,
+                             block_size=16, n_skip=1, seed=2017),
     # prefill-sized T with no dimension a multiple of the 256x256 GEMM tile
     "mla_prefill_ragged": MlaConfig("mla_prefill_ragged_T300", B=3, S=100,
                                     He=512, Hcq=320, N=5, D=64, Hckv=96,
