@@ -125,8 +125,8 @@ def test_pack_weight_uk_bit_exact(N, D, H):
 # ---- MLA prolog --------------------------------------------------------------
 
 MLA_SMALL = [0, "mla_ragged", "mla_ragged_q", "mla_ragged_qb", "mla_mid_dsv3",
-             "mla_prefill_ragged", "mla_full_kvbf16", "mla_full_kvint8",
-             "mla_full_kvint8_large"]
+             "mla_prefill_ragged", "mla_fused_ragged", "mla_full_kvbf16",
+             "mla_full_kvint8", "mla_full_kvint8_large"]
 
 
 @pytest.mark.parametrize("key", MLA_SMALL)
@@ -318,7 +318,8 @@ def _decode_case(key):
 # two and four 32-row blocks, and the first large-T shapes (ragged tile)
 TOKEN_CASES = [("mla_ragged", 1), ("mla_ragged", 33), ("mla_ragged", 64),
                ("mla_ragged", 100), ("mla_ragged", 129), ("mla_mid_dsv3", 1),
-               ("mla_mid_dsv3", 128), ("mla_mid_dsv3", 257)]
+               ("mla_mid_dsv3", 128), ("mla_mid_dsv3", 257),
+               ("mla_fused_ragged", 150)]
 
 
 @pytest.mark.parametrize("key,T", TOKEN_CASES)

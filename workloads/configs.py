@@ -168,6 +168,13 @@ CONFIGS = {
     "mla_max_row": MlaConfig("mla_max_row_T13", B=13, S=1, He=64, Hcq=12288,
                              N=2, D=32, Hckv=4032, Dr=64, block_num=2,
                              block_size=16, n_skip=1, seed=2017),
+    # the fused q^C + W^UK prefill path (D = 128, N*D a multiple of 256)
+    # with a W^UK width (224) that ends in half a 64-column pass and a
+    # ragged second row tile
+    "mla_fused_ragged": MlaConfig("mla_fused_ragged_T300", B=3, S=100,
+                                  He=256, Hcq=160, N=4, D=128, Hckv=224,
+                                  Dr=64, block_num=4, block_size=128,
+                                  n_skip=5, seed=2018, layout="BSH"),
     # prefill-sized T with no dimension a multiple of the 256x256 GEMM tile
     "mla_prefill_ragged": MlaConfig("mla_prefill_ragged_T300", B=3, S=100,
                                     He=512, Hcq=320, N=5, D=64, Hckv=96,
