@@ -80,3 +80,14 @@ def test_flops_match_the_gemm_shapes(key):
     # the prefill workload has the decode weights and T = 4096 tokens
     if key == 1:
         assert bench.mla_flops(get_config(2)) == 2 * 4096 * kn == 501_974_302_720
+
+
+def test_up_projection_bytes_match_the_workload_tensors():
+    # the decode up projection as launched: W^UQ_QR and the cos/sin rows
+    # read, q^R written, and the bf16 c^Q it reads and q^C it writes
+    # (intermediates of T x Hcq and T x N*D in the workspace)
+    w = make_workload(1)
+    c, a = w.cfg, w.arrays
+    expect = (a["weight_uq_qr"].nbytes + a["rope_cos"].nbytes + a["rope_sin"].nbytes
+              + c.T * c.N * c.Dr * 2 + c.T * c.Hcq * 2 + c.T * c.N * c.D * 2)
+    assert bench.uqqr_bytes(c) == expect == 77_176_832
