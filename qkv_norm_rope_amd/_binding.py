@@ -170,6 +170,100 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _pad32(n: int) -> int:
+    return (n + 31) // 32 * 32
+
+
+def _expect(t, dtype, numel: int, name: str):
+    """The library takes raw pointers and cannot see tensor sizes, so each
+    tensor's element type and element count are checked here, before a
+    kernel could read or write past it.  An absent tensor is left to the
+    library's own NULL checks."""
+    if t is None:
+        return
+    _need(t, dtype, name)
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements for these "
+                         f"dimensions, got {t.numel()} (shape {tuple(t.shape)})")
+
+
+def _validate_mla(a: "MlaPrologV2Args", t: dict):
+    """Element types and counts of the MlaPrologV2 tensors for the
+    dimensions and quant mode in `a` (the dtype/shape table of
+    include/qkvnr.h; packed weights hold whole 32-column blocks)."""
+    m = a.quant_mode
+    full, quant = m in (3, 4), m != 0
+    kv8, kr8, q8 = m in (2, 4), m == 2, m == 4
+    T = a.B * a.S
+    bf, i8, f32 = torch.bfloat16, torch.int8, torch.float32
+    cols = _pad32 if a.weight_layout == MLA_WEIGHT_PACKED_K16 else int
+    down = i8 if full else bf
+    slots = a.block_num * a.block_size * a.Nkv
+    _expect(t.get("token_x"), down, T * a.He, "token_x")
+    _expect(t.get("weight_dq"), down, a.He * cols(a.Hcq), "weight_dq")
+    _expect(t.get("weight_dkv_kr"), down, a.He * cols(a.Hckv + a.Dr),
+            "weight_dkv_kr")
+    _expect(t.get("weight_uq_qr"), i8 if quant else bf,
+            a.Hcq * cols(a.N * (a.D + a.Dr)), "weight_uq_qr")
+    _expect(t.get("weight_uk"), bf, a.N * a.D * cols(a.Hckv), "weight_uk")
+    _expect(t.get("rmsnorm_gamma_cq"), bf, a.Hcq, "rmsnorm_gamma_cq")
+    _expect(t.get("rmsnorm_gamma_ckv"), bf, a.Hckv, "rmsnorm_gamma_ckv")
+    _expect(t.get("rope_sin"), bf, T * a.Dr, "rope_sin")
+    _expect(t.get("rope_cos"), bf, T * a.Dr, "rope_cos")
+    _expect(t.get("cache_index"), torch.int64, T, "cache_index")
+    _expect(t.get("kv_cache"), i8 if kv8 else bf, slots * a.Hckv, "kv_cache")
+    _expect(t.get("kr_cache"), i8 if kr8 else bf, slots * a.Dr, "kr_cache")
+    _expect(t.get("query"), i8 if q8 else bf, T * a.N * a.Hckv, "query")
+    _expect(t.get("query_rope"), bf, T * a.N * a.Dr, "query_rope")
+    if quant:
+        _expect(t.get("dequant_scale_w_uq_qr"), f32, a.N * (a.D + a.Dr),
+                "dequant_scale_w_uq_qr")
+        _expect(t.get("smooth_scales_cq"), f32, a.Hcq, "smooth_scales_cq")
+        _expect(t.get("dbg_cq_int8"), i8, T * a.Hcq, "cq_int8")
+        _expect(t.get("dbg_cq_scale"), f32, T, "cq_scale")
+    if kv8:
+        _expect(t.get("quant_scale_ckv"), f32, a.Hckv, "quant_scale_ckv")
+    if kr8:
+        _expect(t.get("quant_scale_ckr"), f32, a.Dr, "quant_scale_ckr")
+    if full:
+        _expect(t.get("dequant_scale_x"), f32, T, "dequant_scale_x")
+        _expect(t.get("dequant_scale_w_dq"), f32, a.Hcq, "dequant_scale_w_dq")
+        _expect(t.get("dequant_scale_w_dkv_kr"), f32, a.Hckv + a.Dr,
+                "dequant_scale_w_dkv_kr")
+    if q8:
+        _expect(t.get("dequant_scale_q_nope"), f32, T * a.N,
+                "dequant_scale_q_nope")
+
+
+def _validate_qkv(a: "QkvRmsNormRopeCacheArgs", t: dict):
+    """Element types and counts of the QkvRmsNormRopeCache tensors for the
+    dimensions and quant mode in `a`."""
+    dt = {0: torch.float16, 1: torch.bfloat16}.get(a.dtype)
+    if dt is None:
+        raise TypeError("qkv must be float16 or bfloat16")
+    T, D = a.B * a.S, a.D
+    cache = dt if a.quant_mode == QKV_QUANT["none"] else torch.int8
+    slots = a.block_num * a.block_size
+    _expect(t.get("qkv"), dt, T * (a.Nq + a.Nk + a.Nv) * D, "qkv")
+    _expect(t.get("gamma_q"), dt, D, "gamma_q")
+    _expect(t.get("gamma_k"), dt, D, "gamma_k")
+    _expect(t.get("cos"), dt, T * D, "cos")
+    _expect(t.get("sin"), dt, T * D, "sin")
+    _expect(t.get("index"), torch.int64, T, "index")
+    _expect(t.get("k_cache"), cache, slots * a.Nk * D, "k_cache")
+    _expect(t.get("v_cache"), cache, slots * a.Nv * D, "v_cache")
+    _expect(t.get("q_out"), dt, T * a.Nq * D, "q_out")
+    _expect(t.get("q_before_quant"), dt, T * a.Nq * D, "q_before_quant")
+    _expect(t.get("k_before_quant"), dt, T * a.Nk * D, "k_before_quant")
+    _expect(t.get("v_before_quant"), dt, T * a.Nv * D, "v_before_quant")
+    if a.quant_mode != QKV_QUANT["none"]:
+        _expect(t.get("k_scale"), torch.float32, a.Nk * D, "k_scale")
+        _expect(t.get("v_scale"), torch.float32, a.Nv * D, "v_scale")
+    if a.quant_mode == QKV_QUANT["asymmetric"]:
+        _expect(t.get("k_offset"), torch.float32, a.Nk * D, "k_offset")
+        _expect(t.get("v_offset"), torch.float32, a.Nv * D, "v_offset")
+
+
 # ---------------------------------------------------------------------------
 # weight packing
 # ---------------------------------------------------------------------------
@@ -367,6 +461,19 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
         cache_mode=cache_mode,
         B=lead[0] if len(lead) == 2 else None,
         S=lead[1] if len(lead) == 2 else None)
+    _validate_mla(a, dict(
+        token_x=token_x, weight_dq=weight_dq, weight_uq_qr=weight_uq_qr,
+        weight_uk=weight_uk, weight_dkv_kr=weight_dkv_kr,
+        rmsnorm_gamma_cq=rmsnorm_gamma_cq, rmsnorm_gamma_ckv=rmsnorm_gamma_ckv,
+        rope_sin=rope_sin, rope_cos=rope_cos, cache_index=cache_index,
+        kv_cache=kv_cache, kr_cache=kr_cache, query=query,
+        query_rope=query_rope, dequant_scale_w_uq_qr=dequant_scale_w_uq_qr,
+        quant_scale_ckv=quant_scale_ckv, quant_scale_ckr=quant_scale_ckr,
+        smooth_scales_cq=smooth_scales_cq, dequant_scale_x=dequant_scale_x,
+        dequant_scale_w_dq=dequant_scale_w_dq,
+        dequant_scale_w_dkv_kr=dequant_scale_w_dkv_kr,
+        dequant_scale_q_nope=dequant_scale_q_nope, dbg_cq_int8=dbg8,
+        dbg_cq_scale=dbgs))
     if phase_events:
         handles = (_vp * len(phase_events))(*[e.cuda_event for e in phase_events])
         a.phase_events = ctypes.cast(handles, ctypes.POINTER(_vp))
@@ -411,6 +518,13 @@ class PreparedMlaPrologV2:
             cache_index, kv_cache, kr_cache, query, query_rope,
             B=lead[0] if len(lead) == 2 else None,
             S=lead[1] if len(lead) == 2 else None, **kw)
+        _validate_mla(self.args, dict(
+            kw, token_x=token_x, weight_dq=weight_dq,
+            weight_uq_qr=weight_uq_qr, weight_uk=weight_uk,
+            weight_dkv_kr=weight_dkv_kr, rmsnorm_gamma_cq=rmsnorm_gamma_cq,
+            rmsnorm_gamma_ckv=rmsnorm_gamma_ckv, rope_sin=rope_sin,
+            rope_cos=rope_cos, cache_index=cache_index, kv_cache=kv_cache,
+            kr_cache=kr_cache, query=query, query_rope=query_rope))
         nbytes = mla_prolog_v2_workspace_size(self.args)
         if workspace is None or \
                 workspace.numel() * workspace.element_size() < nbytes:
@@ -524,6 +638,12 @@ def qkv_rmsnorm_rope_cache(qkv, gamma_q, gamma_k, cos, sin, index, k_cache,
         v_offset=v_offset, q_before_quant=qb, k_before_quant=kb,
         v_before_quant=vb, B=B, S=S, cache_mode=cache_mode)
     a.D = int(D)
+    _validate_qkv(a, dict(
+        qkv=qkv3, gamma_q=gamma_q, gamma_k=gamma_k, cos=cos, sin=sin,
+        index=index, k_cache=k_cache, v_cache=v_cache, q_out=q_out,
+        q_before_quant=qb, k_before_quant=kb, v_before_quant=vb,
+        k_scale=k_scale, v_scale=v_scale, k_offset=k_offset,
+        v_offset=v_offset))
     _check(lib.qkv_rmsnorm_rope_cache(ctypes.byref(a), _stream(stream)),
            "qkv_rmsnorm_rope_cache")
     if before_quant:

@@ -337,3 +337,97 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(16, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         qn.mla_pack_weight(w)
+
+
+# ---- the binding's tensor checks (metadata only; CPU tensors) ------------
+
+def _mla_tensors(T, He, Hcq, N, D, Hckv, Dr, bn, bs, quant, packed):
+    import torch
+    bf, i8, f32 = torch.bfloat16, torch.int8, torch.float32
+    full, q = quant.startswith("full"), quant != "none"
+    kv8, kr8 = quant in ("partial_kv_int8", "full_kv_int8"), quant == "partial_kv_int8"
+    p = (lambda n: (n + 31) // 32 * 32) if packed else (lambda n: n)
+    e = torch.empty
+    t = dict(token_x=e(T, He, dtype=i8 if full else bf),
+             weight_dq=e(He, p(Hcq), dtype=i8 if full else bf),
+             weight_dkv_kr=e(He, p(Hckv + Dr), dtype=i8 if full else bf),
+             weight_uq_qr=e(Hcq, p(N * (D + Dr)), dtype=i8 if q else bf),
+             weight_uk=e(N, D, p(Hckv), dtype=bf),
+             rmsnorm_gamma_cq=e(Hcq, dtype=bf), rmsnorm_gamma_ckv=e(Hckv, dtype=bf),
+             rope_sin=e(T, Dr, dtype=bf), rope_cos=e(T, Dr, dtype=bf),
+             cache_index=e(T, dtype=torch.int64),
+             kv_cache=e(bn, bs, 1, Hckv, dtype=i8 if kv8 else bf),
+             kr_cache=e(bn, bs, 1, Dr, dtype=i8 if kr8 else bf),
+             query=e(T, N, Hckv, dtype=i8 if quant == "full_kv_int8" else bf),
+             query_rope=e(T, N, Dr, dtype=bf))
+    if q:
+        t.update(dequant_scale_w_uq_qr=e(N * (D + Dr), dtype=f32),
+                 smooth_scales_cq=e(Hcq, dtype=f32))
+    if kv8:
+        t["quant_scale_ckv"] = e(Hckv, dtype=f32)
+    if kr8:
+        t["quant_scale_ckr"] = e(Dr, dtype=f32)
+    if full:
+        t.update(dequant_scale_x=e(T, dtype=f32), dequant_scale_w_dq=e(Hcq, dtype=f32),
+                 dequant_scale_w_dkv_kr=e(Hckv + Dr, dtype=f32))
+    if quant == "full_kv_int8":
+        t["dequant_scale_q_nope"] = e(T, N, 1, dtype=f32)
+    return t
+
+
+@pytest.mark.parametrize("quant", list(b.MLA_QUANT))
+@pytest.mark.parametrize("packed", [True, False])
+def test_binding_checks_mla_tensor_types_and_sizes(quant, packed):
+    import torch
+    dims = dict(T=5, He=256, Hcq=128, N=3, D=32, Hckv=80, Dr=16, bn=2, bs=16)
+    lay = b.MLA_WEIGHT_PACKED_K16 if packed else b.MLA_WEIGHT_ND
+    a = mla_args(T=5, quant=quant, He=256, Hcq=128, N=3, D=32, Hckv=80, Dr=16,
+                 bn=2, bs=16, layout=lay)
+    t = _mla_tensors(quant=quant, packed=packed, **dims)
+    b._validate_mla(a, t)  # consistent tensors pass
+    # a wrong element type, a short weight, an unpadded packed weight, a
+    # cache of the other type, a short scale: each is refused
+    with pytest.raises(TypeError):
+        b._validate_mla(a, dict(t, rope_cos=t["rope_cos"].float()))
+    with pytest.raises(ValueError):
+        b._validate_mla(a, dict(t, weight_uk=t["weight_uk"][:, :, :16]))
+    with pytest.raises(TypeError):
+        b._validate_mla(a, dict(t, kv_cache=torch.empty(
+            2, 16, 1, 80, dtype=torch.bfloat16 if t["kv_cache"].dtype == torch.int8
+            else torch.int8)))
+    with pytest.raises(ValueError):
+        b._validate_mla(a, dict(t, cache_index=t["cache_index"][:4]))
+    if packed:
+        with pytest.raises(ValueError):  # Hckv = 80 packs to 96 columns
+            b._validate_mla(a, dict(t, weight_uk=t["weight_uk"][:, :, :80].contiguous()))
+    if quant != "none":
+        with pytest.raises(ValueError):
+            b._validate_mla(a, dict(t, smooth_scales_cq=t["smooth_scales_cq"][:64]))
+
+
+@pytest.mark.parametrize("quant", list(b.QKV_QUANT))
+def test_binding_checks_qkv_tensor_types_and_sizes(quant):
+    import torch
+    h, f32, i8 = torch.float16, torch.float32, torch.int8
+    T, bn, bs = 6, 2, 16
+    a = qkv_args(B=2, S=3, quant=quant, bn=bn, bs=bs)
+    e = torch.empty
+    cache = h if quant == "none" else i8
+    t = dict(qkv=e(T, 48, 128, dtype=h), gamma_q=e(128, dtype=h),
+             gamma_k=e(128, dtype=h), cos=e(T, 128, dtype=h), sin=e(T, 128, dtype=h),
+             index=e(T, dtype=torch.int64), k_cache=e(bn, bs, 8, 128, dtype=cache),
+             v_cache=e(bn, bs, 8, 128, dtype=cache), q_out=e(T, 32, 128, dtype=h))
+    if quant != "none":
+        t.update(k_scale=e(1024, dtype=f32), v_scale=e(1024, dtype=f32))
+    if quant == "asymmetric":
+        t.update(k_offset=e(1024, dtype=f32), v_offset=e(1024, dtype=f32))
+    b._validate_qkv(a, t)
+    with pytest.raises(TypeError):
+        b._validate_qkv(a, dict(t, gamma_k=t["gamma_k"].to(torch.bfloat16)))
+    with pytest.raises(ValueError):
+        b._validate_qkv(a, dict(t, index=t["index"][:5]))
+    with pytest.raises(ValueError):
+        b._validate_qkv(a, dict(t, q_out=e(T, 8, 128, dtype=h)))
+    if quant != "none":
+        with pytest.raises(ValueError):
+            b._validate_qkv(a, dict(t, v_scale=e(128, dtype=f32)))
