@@ -162,22 +162,17 @@ def test_mla_parity_partial_quant_T64():
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
-def test_mla_parity_prefill_T4096_sampled():
-    # Full-size run; the oracle checks a sample of tokens spread over every
-    # 128-row tile, and the whole cache for placement.
+def test_mla_parity_prefill_T4096():
+    # Full-size run; every one of the 4096 tokens is compared with the
+    # oracle (run on 512-token pieces), and the whole cache for placement.
     w = make_workload(2)
     gh.announce(f"mla {w.cfg.name} full size")
     dev = gh.upload(w)
     before = _before(dev, ["kv_cache", "kr_cache"])
     out = gh.run_mla_gpu(w, dev, bsh=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(77)
-    tokens = np.sort(np.concatenate([
-        np.arange(0, w.cfg.T, 128) + rng.integers(0, 128, w.cfg.T // 128),
-        [0, w.cfg.T - 1]]))
-    tokens = np.unique(tokens)
-    gh.announce(f"  checking {tokens.size} sampled tokens")
-    gh.announce(f"  ok {gh.check_mla(w, out, before, tokens=tokens)}")
+    gh.announce(f"  checking all {w.cfg.T} tokens in 512-token pieces")
+    gh.announce(f"  ok (worst err/tol) {gh.check_mla(w, out, before, chunk=512)}")
 
 
 def test_mla_prefill_partial_quant_tiled_path():

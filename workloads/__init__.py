@@ -15,6 +15,7 @@ from .gen import (
     make_mla_workload,
     make_qkv_workload,
     bf16_bits_from_f64,
+    sub_workload,
 )
 
 __all__ = [
@@ -27,4 +28,5 @@ __all__ = [
     "make_mla_workload",
     "make_qkv_workload",
     "bf16_bits_from_f64",
+    "sub_workload",
 ]

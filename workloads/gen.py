@@ -232,3 +232,19 @@ def make_workload(key) -> Workload:
     if isinstance(cfg, MlaConfig):
         return make_mla_workload(cfg)
     return make_qkv_workload(cfg)
+
+
+def sub_workload(w: Workload, tokens) -> Workload:
+    """The same MLA workload restricted to some tokens (in the given
+    order).  Tokens are independent: each output row depends only on its
+    own x, RoPE row and index, so the restriction is a valid workload of
+    len(tokens) tokens with the same weights and caches."""
+    import copy
+    tokens = np.asarray(tokens)
+    s = copy.copy(w)
+    s.arrays = dict(w.arrays)
+    for k in ("token_x", "rope_cos", "rope_sin", "cache_index"):
+        s.arrays[k] = w.arrays[k].reshape(w.cfg.T, -1)[tokens].reshape(
+            (len(tokens),) + w.arrays[k].shape[1:])
+    s.cfg = w.cfg.replace(B=len(tokens), S=1)
+    return s
