@@ -39,7 +39,11 @@
  *  - Cache updates: a token whose index is -1 writes nothing.  Indexes must
  *    lie in [-1, BlockNum*BlockSize) and must not repeat (both operators'
  *    index restrictions).  The kernels skip any index outside that range
- *    (memory safety); a repeated slot gets an unspecified winner.
+ *    (memory safety); a repeated slot gets an unspecified winner.  The
+ *    opt-in debug flags (MLA_FLAG_CHECK_INDEX, QKV_FLAG_CHECK_INPUTS) copy
+ *    the index to the host first, synchronising the stream, and refuse a
+ *    violation with QKVNR_ERR_BAD_INDEX before anything is launched; a
+ *    call with a debug flag must not be captured into a HIP graph.
  */
 #ifndef QKVNR_H
 #define QKVNR_H
@@ -59,7 +63,8 @@ enum {
   QKVNR_ERR_NULL_ARG = -1,          /* a required pointer is NULL */
   QKVNR_ERR_BAD_SHAPE = -2,         /* a dimension is negative or breaks a
                                        shape rule */
-  QKVNR_ERR_BAD_MODE = -3,          /* unknown quant mode, dtype or layout */
+  QKVNR_ERR_BAD_MODE = -3,          /* unknown quant mode, dtype, layout,
+                                       cache mode or flag bit */
   QKVNR_ERR_UNSUPPORTED = -4,       /* valid on the pages, not built here
                                        (PA_NZ caches, Nkv != 1, dims off
                                        the kernels' multiples, ...) */
@@ -70,17 +75,32 @@ enum {
   QKVNR_ERR_BAD_ALIGNMENT = -9,     /* a pointer is not 16-byte aligned
                                        (cache_index and dbg_cq_int8: 8,
                                        dbg_cq_scale: 4) */
-  QKVNR_ERR_LAUNCH_FAILED = -10,    /* hipGetLastError after a launch */
-  QKVNR_ERR_BAD_INDEX = -11         /* reserved: no entry point returns it
-                                       (indexes are checked on the device,
-                                       see "Cache updates" above) */
+  QKVNR_ERR_LAUNCH_FAILED = -10,    /* a HIP call failed (hipGetLastError
+                                       after a launch, or the debug checks'
+                                       copy) */
+  QKVNR_ERR_BAD_INDEX = -11,        /* an index outside [-1, BlockNum *
+                                       BlockSize) or a repeated one: only
+                                       from mla_check_cache_index and the
+                                       opt-in debug checks (MLA_FLAG_CHECK_
+                                       INDEX, QKV_FLAG_CHECK_INPUTS) */
+  QKVNR_ERR_BAD_SCALE = -12         /* a zero quant scale: only from the
+                                       opt-in QKV_FLAG_CHECK_INPUTS check */
 };
 
-/* Human-readable name of a status code (static storage, never NULL). */
-const char* qkvnr_status_string(int status);
+/* Human-readable name of a status code (static storage, never NULL; an
+ * unknown code gives "unknown status").  Errors: none. */
+const char* mla_status_string(int status);
 
-/* Library version, QKVNR_VERSION_STRING. */
-const char* qkvnr_version(void);
+/* Library version, QKVNR_VERSION_STRING (static storage).  Errors: none. */
+const char* mla_lib_version(void);
+
+/* Both operators' index restriction (aclnnQkvRmsNormRopeCache, other
+ * restrictions; the MlaPrologV2 cache_index follows the same rule): every
+ * index[i], i < n, lies in [-1, slots) and no non-negative value repeats.
+ * `index` is HOST memory (may be NULL when n == 0); nothing is launched.
+ * Returns QKVNR_OK, QKVNR_ERR_BAD_INDEX, QKVNR_ERR_BAD_SHAPE (n < 0 or
+ * slots < 0) or QKVNR_ERR_NULL_ARG. */
+int mla_check_cache_index(const int64_t* index, int64_t n, int64_t slots);
 
 /* ======================================================================= */
 /* MlaPrologV2                                                              */
@@ -141,11 +161,20 @@ enum {
  *   natural order already has that property and is kept. */
 enum { MLA_WEIGHT_ND = 0, MLA_WEIGHT_PACKED_K16 = 1 };
 
+/* Debug flags of MlaPrologV2Args.flags.  MLA_FLAG_CHECK_INDEX: before
+ * launching, copy cache_index to the host (synchronises `stream`) and
+ * return QKVNR_ERR_BAD_INDEX if an index lies outside [-1, BlockNum *
+ * BlockSize) or repeats.  Unknown bits: QKVNR_ERR_BAD_MODE. */
+enum { MLA_FLAG_CHECK_INDEX = 1 };
+
+/* Arguments of one MlaPrologV2 call: the tensors of the MlaPrologV2 README
+ * parameter table, with the shapes and dtypes of its constraints section
+ * (shape rules and dtype/shape table). */
 typedef struct MlaPrologV2Args {
   uint32_t struct_size;      /* = sizeof(MlaPrologV2Args) */
   int32_t quant_mode;        /* MLA_QUANT_* */
   int32_t weight_layout;     /* MLA_WEIGHT_* */
-  int32_t reserved0;         /* must be 0 */
+  int32_t flags;             /* MLA_FLAG_* (0 in production) */
 
   /* Dimensions (MlaPrologV2 README, constraints).  T = B*S tokens; for the
    * (T, He) layout pass B = T, S = 1.  Requirements checked here:
@@ -246,22 +275,41 @@ enum {
 };
 
 /* Bytes of device workspace mla_prolog_v2() needs for these arguments
- * (depends on the dims, T, quant mode and weight layout).  Writes *bytes
- * and returns QKVNR_OK, or a validation error (then *bytes is 0). */
+ * (depends on the dims, T, quant mode and weight layout; the pages' first
+ * phase, which sizes the workspace, as one call).  Writes *bytes and
+ * returns QKVNR_OK, or a validation error (then *bytes is 0).  The size
+ * comes back through a pointer so that an error is never mistaken for a
+ * zero-byte workspace.  Host only, no HIP call. */
 int mla_prolog_v2_workspace_size(const MlaPrologV2Args* args, size_t* bytes);
 
-/* Host-only validation of args (the checks mla_prolog_v2 runs first).
- * Makes no HIP call. */
+/* Host-only validation of args against the MlaPrologV2 README constraints
+ * (shape rules, scenario and dtype/shape tables) and this library's kernel
+ * limits: the checks mla_prolog_v2 runs first.  Makes no HIP call.
+ * Returns QKVNR_OK or the first failing check's QKVNR_ERR_* code. */
 int mla_prolog_v2_validate(const MlaPrologV2Args* args);
 
-/* Run the prolog.  workspace: device scratch of at least
- * mla_prolog_v2_workspace_size() bytes, 256-byte aligned, owned by the
- * caller, contents undefined on entry and exit (may be NULL when the size
- * is 0).  Enqueues on `stream` and returns without synchronising. */
+/* Which main kernels (bit i = MLA_KERNEL_i) a call with these args
+ * launches, and so which kernel_events pairs it records.  Writes *mask and
+ * returns QKVNR_OK, or a validation error (then *mask is 0).  Host only. */
+int mla_prolog_v2_kernels(const MlaPrologV2Args* args, uint32_t* mask);
+
+/* Run the prolog: the five formulas of the MlaPrologV2 README function
+ * description (c^Q, q^N, q^R, c^KV -> kv_cache, k^R -> kr_cache) in the
+ * quantisation scenario args->quant_mode.  workspace: device scratch of at
+ * least mla_prolog_v2_workspace_size() bytes, 256-byte aligned, owned by
+ * the caller, contents undefined on entry and exit (may be NULL when the
+ * size is 0).  Enqueues on `stream` and returns without synchronising
+ * (except under MLA_FLAG_CHECK_INDEX).  Errors: any validation code,
+ * QKVNR_ERR_WORKSPACE_TOO_SMALL, QKVNR_ERR_BAD_INDEX (debug flag),
+ * QKVNR_ERR_LAUNCH_FAILED; nothing is launched on a validation error. */
 int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
                   size_t workspace_bytes, void* stream);
 
-/* Pack `batch` row-major (K, N) matrices (each K*N elements of
+/* Weight packing: the MFMA-native counterpart of the MlaPrologV2 pages'
+ * FRACTAL_NZ weight format (MLA_WEIGHT_PACKED_K16 above); done once per
+ * weight, outside the per-token path.
+ *
+ * Pack `batch` row-major (K, N) matrices (each K*N elements of
  * `elem_bytes` = 2 (bf16/fp16) or 1 (int8), batches contiguous) into the
  * MLA_WEIGHT_PACKED_K16 layout at dst, a distinct buffer of
  * batch * K * ceil(N/32)*32 elements.  K must be a multiple of
@@ -303,11 +351,23 @@ enum { QKV_QUANT_NONE = 0, QKV_QUANT_SYMMETRIC = 1, QKV_QUANT_ASYMMETRIC = 2 };
  * (and of the caches in QKV_QUANT_NONE). */
 enum { QKV_DTYPE_FP16 = 0, QKV_DTYPE_BF16 = 1 };
 
+/* Debug flags of QkvRmsNormRopeCacheArgs.flags.  QKV_FLAG_CHECK_INPUTS:
+ * before launching, copy the index (and, quantised, k_scale / v_scale) to
+ * the host (synchronises `stream`) and return QKVNR_ERR_BAD_INDEX for an
+ * index outside [-1, BlockNum * BlockSize) or a repeated one, or
+ * QKVNR_ERR_BAD_SCALE for a zero scale (the page's other restrictions).
+ * Unknown bits: QKVNR_ERR_BAD_MODE. */
+enum { QKV_FLAG_CHECK_INPUTS = 1 };
+
+/* Arguments of one QkvRmsNormRopeCache call.  The page's parameter tables
+ * did not survive extraction; the tensors below are rebuilt from its
+ * function description, formulas (1)-(4) and the requireMemory sum of its
+ * other restrictions. */
 typedef struct QkvRmsNormRopeCacheArgs {
   uint32_t struct_size;      /* = sizeof(QkvRmsNormRopeCacheArgs) */
   int32_t quant_mode;        /* QKV_QUANT_* */
   int32_t dtype;             /* QKV_DTYPE_* */
-  int32_t reserved0;         /* must be 0 */
+  int32_t flags;             /* QKV_FLAG_* (0 in production) */
 
   /* Dimensions (aclnnQkvRmsNormRopeCache, input shape restrictions):
    * D == 128; Nk == Nv; Nq, Nk >= 1; block_num >= ceil(S / block_size) * B
@@ -339,12 +399,41 @@ typedef struct QkvRmsNormRopeCacheArgs {
   void* v_before_quant;      /* optional (B*S, Nv, D): v as split */
 } QkvRmsNormRopeCacheArgs;
 
-/* Host-only validation (makes no HIP call). */
+/* Host-only validation against the aclnnQkvRmsNormRopeCache input shape
+ * restrictions and this library's kernel limits (makes no HIP call).
+ * Returns QKVNR_OK or the first failing check's QKVNR_ERR_* code. */
 int qkv_rmsnorm_rope_cache_validate(const QkvRmsNormRopeCacheArgs* args);
 
-/* Run the fused op: one pass over qkv, no workspace.  Enqueues on `stream`
- * and returns without synchronising. */
+/* Run the fused op, aclnnQkvRmsNormRopeCache formulas (1) SplitVD, (2)
+ * RmsNorm of q and k, (3) half-and-half RoPE of q and k, (4) quant of k
+ * and v, then q_out and the paged scatter: one pass over qkv, no
+ * workspace.  Enqueues on `stream` and returns without synchronising
+ * (except under QKV_FLAG_CHECK_INPUTS).  Errors: any validation code,
+ * QKVNR_ERR_BAD_INDEX / QKVNR_ERR_BAD_SCALE (debug flag),
+ * QKVNR_ERR_LAUNCH_FAILED; nothing is launched on a validation error. */
 int qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* args, void* stream);
+
+/* ======================================================================= */
+/* Measurement probes                                                       */
+/* ======================================================================= */
+
+/* Not part of either operator: reference points for the roofline figures a
+ * benchmark reports beside the published peaks (HBM bandwidth, dense bf16
+ * MFMA rate).  Both enqueue one kernel on `stream` and return without
+ * synchronising; time them with events.
+ *
+ * mla_probe_read: stream `bytes` (a multiple of 16, src 16-byte aligned)
+ * of device memory once with nontemporal loads.  `sink`: a device word,
+ * written only in a case that does not happen in practice (it keeps the
+ * loads from being optimised away).  Errors: QKVNR_ERR_NULL_ARG,
+ * QKVNR_ERR_BAD_SHAPE, QKVNR_ERR_BAD_ALIGNMENT, QKVNR_ERR_LAUNCH_FAILED.
+ *
+ * mla_probe_mfma_bf16: 512 workgroups x 4 waves, each wave `iters` steps
+ * of four independent v_mfma_f32_32x32x16_bf16 chains: 2^28 * iters flop,
+ * no memory traffic in the loop.  `sink` as above.  iters in [1, 2^31],
+ * else QKVNR_ERR_BAD_SHAPE. */
+int mla_probe_read(const void* src, size_t bytes, void* sink, void* stream);
+int mla_probe_mfma_bf16(int64_t iters, void* sink, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

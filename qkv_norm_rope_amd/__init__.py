@@ -18,22 +18,28 @@ All work runs in the HIP library ``lib/libqkvnr.so``; build it with
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    MLA_FLAG_CHECK_INDEX,
     MLA_KERNELS,
     MLA_PHASES,
     MLA_QUANT,
     MLA_WEIGHT_ND,
     MLA_WEIGHT_PACKED_K16,
+    QKV_FLAG_CHECK_INPUTS,
     QKV_QUANT,
     MlaPrologV2Args,
     PreparedMlaPrologV2,
     QkvRmsNormRopeCacheArgs,
     QkvnrError,
     load_library,
+    mla_check_cache_index,
     mla_pack_weight,
+    mla_probe_mfma_bf16,
+    mla_probe_read,
     mla_pack_weight_uk,
     mla_pack_weight_uq_qr,
     mla_prolog_v2,
     mla_prolog_v2_args,
+    mla_prolog_v2_kernels,
     mla_prolog_v2_workspace_size,
     qkv_rmsnorm_rope_cache,
     qkv_rmsnorm_rope_cache_args,

@@ -25,8 +25,10 @@ STATUS_NAMES = {
     -5: "QKVNR_ERR_RESERVED_NONNULL", -6: "QKVNR_ERR_WORKSPACE_TOO_SMALL",
     -7: "QKVNR_ERR_BAD_EPS", -8: "QKVNR_ERR_BAD_STRUCT",
     -9: "QKVNR_ERR_BAD_ALIGNMENT", -10: "QKVNR_ERR_LAUNCH_FAILED",
-    -11: "QKVNR_ERR_BAD_INDEX",
+    -11: "QKVNR_ERR_BAD_INDEX", -12: "QKVNR_ERR_BAD_SCALE",
 }
+MLA_FLAG_CHECK_INDEX = 1
+QKV_FLAG_CHECK_INPUTS = 1
 MLA_QUANT = {"none": 0, "partial_kv_bf16": 1, "partial_kv_int8": 2,
              "full_kv_bf16": 3, "full_kv_int8": 4}
 MLA_WEIGHT_ND, MLA_WEIGHT_PACKED_K16 = 0, 1
@@ -36,10 +38,12 @@ QKV_QUANT = {"none": 0, "symmetric": 1, "asymmetric": 2}
 QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
 
 EXPORTS = (
-    "qkvnr_status_string", "qkvnr_version", "mla_prolog_v2_workspace_size",
-    "mla_prolog_v2_validate", "mla_prolog_v2", "mla_pack_weight",
+    "mla_status_string", "mla_lib_version", "mla_check_cache_index",
+    "mla_prolog_v2_workspace_size", "mla_prolog_v2_validate",
+    "mla_prolog_v2_kernels", "mla_prolog_v2", "mla_pack_weight",
     "mla_pack_weight_uq_qr", "mla_pack_weight_uk",
     "qkv_rmsnorm_rope_cache_validate", "qkv_rmsnorm_rope_cache",
+    "mla_probe_read", "mla_probe_mfma_bf16",
 )
 
 _vp = ctypes.c_void_p
@@ -49,7 +53,7 @@ _i64 = ctypes.c_int64
 class MlaPrologV2Args(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32), ("quant_mode", ctypes.c_int32),
-        ("weight_layout", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("B", _i64), ("S", _i64), ("He", _i64), ("Hcq", _i64), ("N", _i64),
         ("D", _i64), ("Hckv", _i64), ("Dr", _i64), ("Nkv", _i64),
         ("block_num", _i64), ("block_size", _i64),
@@ -75,7 +79,7 @@ class MlaPrologV2Args(ctypes.Structure):
 class QkvRmsNormRopeCacheArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", ctypes.c_uint32), ("quant_mode", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("B", _i64), ("S", _i64), ("Nq", _i64), ("Nk", _i64), ("Nv", _i64),
         ("D", _i64), ("block_num", _i64), ("block_size", _i64),
         ("epsilon", ctypes.c_double), ("cache_mode", ctypes.c_char_p),
@@ -97,20 +101,33 @@ class QkvnrError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libqkvnr.so once; raise if it has not been built."""
+def load_library(path: str = None) -> ctypes.CDLL:
+    """Load libqkvnr.so once; raise if it has not been built.
+
+    QKVNR_LIBRARY overrides the path (the host sanitizer test points it at
+    an address/undefined-behaviour-sanitized build of the C ABI layer)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("QKVNR_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m qkv_norm_rope_amd.build`"
             " (there is no non-HIP fallback)")
     lib = ctypes.CDLL(path)
-    lib.qkvnr_status_string.restype = ctypes.c_char_p
-    lib.qkvnr_status_string.argtypes = [ctypes.c_int]
-    lib.qkvnr_version.restype = ctypes.c_char_p
-    lib.qkvnr_version.argtypes = []
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_lib_version.restype = ctypes.c_char_p
+    lib.mla_lib_version.argtypes = []
+    lib.mla_check_cache_index.restype = ctypes.c_int
+    lib.mla_check_cache_index.argtypes = [_vp, _i64, _i64]
+    lib.mla_probe_read.restype = ctypes.c_int
+    lib.mla_probe_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+    lib.mla_probe_mfma_bf16.restype = ctypes.c_int
+    lib.mla_probe_mfma_bf16.argtypes = [_i64, _vp, _vp]
+    lib.mla_prolog_v2_kernels.restype = ctypes.c_int
+    lib.mla_prolog_v2_kernels.argtypes = [
+        ctypes.POINTER(MlaPrologV2Args), ctypes.POINTER(ctypes.c_uint32)]
     lib.mla_prolog_v2_workspace_size.restype = ctypes.c_int
     lib.mla_prolog_v2_workspace_size.argtypes = [
         ctypes.POINTER(MlaPrologV2Args), ctypes.POINTER(ctypes.c_size_t)]
@@ -138,11 +155,24 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 def status_string(status: int) -> str:
-    return load_library().qkvnr_status_string(status).decode()
+    return load_library().mla_status_string(status).decode()
 
 
 def version() -> str:
-    return load_library().qkvnr_version().decode()
+    return load_library().mla_lib_version().decode()
+
+
+def mla_check_cache_index(index, slots: int) -> int:
+    """The index restriction checked on the host: returns the library's
+    status for `index` (a CPU int64 tensor or array) against `slots`
+    (QKVNR_OK, or QKVNR_ERR_BAD_INDEX for an out-of-range or repeated
+    index)."""
+    import numpy as np
+    a = np.ascontiguousarray(
+        index.cpu().numpy() if isinstance(index, torch.Tensor) else index,
+        dtype=np.int64).reshape(-1)
+    return load_library().mla_check_cache_index(
+        a.ctypes.data if a.size else None, a.size, int(slots))
 
 
 def _check(status: int, what: str):
@@ -265,6 +295,26 @@ def _validate_qkv(a: "QkvRmsNormRopeCacheArgs", t: dict):
 
 
 # ---------------------------------------------------------------------------
+# measurement probes
+# ---------------------------------------------------------------------------
+
+def mla_probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Enqueue one streaming read of src (device, contiguous, a multiple of
+    16 bytes); sink is a device tensor of at least 4 bytes."""
+    _check(load_library().mla_probe_read(
+        _ptr(src), src.numel() * src.element_size(), _ptr(sink),
+        _stream(stream)), "mla_probe_read")
+
+
+def mla_probe_mfma_bf16(iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Enqueue the dense bf16 MFMA loop; returns its flop count."""
+    _check(load_library().mla_probe_mfma_bf16(int(iters), _ptr(sink),
+                                              _stream(stream)),
+           "mla_probe_mfma_bf16")
+    return (1 << 28) * int(iters)
+
+
+# ---------------------------------------------------------------------------
 # weight packing
 # ---------------------------------------------------------------------------
 
@@ -336,7 +386,7 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
                        dequant_scale_x=None, dequant_scale_w_dq=None,
                        dequant_scale_w_dkv_kr=None, dequant_scale_q_nope=None,
                        dbg_cq_int8=None, dbg_cq_scale=None, cache_mode=None,
-                       B=None, S=None) -> MlaPrologV2Args:
+                       B=None, S=None, flags=0) -> MlaPrologV2Args:
     """Fill the C struct from tensors.  Dims come from the tensor shapes:
     token_x (T, He) or (B, S, He); weight_dq (He, Hcq); weight_uk
     (N, D, Hckv); rope tables (T, Dr); caches (BlockNum, BlockSize, Nkv, H).
@@ -346,6 +396,7 @@ def mla_prolog_v2_args(token_x, weight_dq, weight_uq_qr, weight_uk,
     a.quant_mode = MLA_QUANT[quant_mode] if isinstance(quant_mode, str) \
         else int(quant_mode)
     a.weight_layout = int(weight_layout)
+    a.flags = int(flags)
     He = token_x.shape[-1]
     T = token_x.numel() // He if He else 0
     if B is None:
@@ -401,6 +452,16 @@ def mla_prolog_v2_workspace_size(args: MlaPrologV2Args) -> int:
     return n.value
 
 
+def mla_prolog_v2_kernels(args: MlaPrologV2Args) -> tuple:
+    """Names (from MLA_KERNELS) of the main kernels a call with these args
+    launches, i.e. whose kernel_events it records."""
+    m = ctypes.c_uint32(0)
+    _check(load_library().mla_prolog_v2_kernels(ctypes.byref(args),
+                                                ctypes.byref(m)),
+           "mla_prolog_v2_kernels")
+    return tuple(k for i, k in enumerate(MLA_KERNELS) if m.value >> i & 1)
+
+
 def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   rmsnorm_gamma_cq, rmsnorm_gamma_ckv, rope_sin, rope_cos,
                   cache_index, kv_cache, kr_cache, *, quant_mode="none",
@@ -412,8 +473,13 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   dequant_scale_w_dkv_kr=None, dequant_scale_q_nope=None,
                   query=None, query_rope=None, workspace=None,
                   return_cq_quant=False, cache_mode=None, stream=None,
-                  phase_events=None, kernel_events=None):
+                  phase_events=None, kernel_events=None,
+                  debug_check_index=False):
     """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
+
+    debug_check_index: the library copies cache_index to the host first
+    (synchronising the stream) and refuses an out-of-range or repeated index
+    with QKVNR_ERR_BAD_INDEX before launching anything.
 
     Returns (query, query_rope), with dequant_scale_q_nope (T, N, 1) after
     them in "full_kv_int8" (int8 query), plus (cq_int8, cq_scale) when
@@ -460,7 +526,8 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
         dbg_cq_int8=dbg8, dbg_cq_scale=dbgs,
         cache_mode=cache_mode,
         B=lead[0] if len(lead) == 2 else None,
-        S=lead[1] if len(lead) == 2 else None)
+        S=lead[1] if len(lead) == 2 else None,
+        flags=MLA_FLAG_CHECK_INDEX if debug_check_index else 0)
     _validate_mla(a, dict(
         token_x=token_x, weight_dq=weight_dq, weight_uq_qr=weight_uq_qr,
         weight_uk=weight_uk, weight_dkv_kr=weight_dkv_kr,
@@ -577,9 +644,10 @@ def qkv_rmsnorm_rope_cache_args(qkv, gamma_q, gamma_k, cos, sin, index,
                                 k_scale=None, v_scale=None, k_offset=None,
                                 v_offset=None, q_before_quant=None,
                                 k_before_quant=None, v_before_quant=None,
-                                B=None, S=None, cache_mode=None):
+                                B=None, S=None, cache_mode=None, flags=0):
     a = QkvRmsNormRopeCacheArgs()
     a.struct_size = ctypes.sizeof(QkvRmsNormRopeCacheArgs)
+    a.flags = int(flags)
     a.quant_mode = QKV_QUANT[quant_mode] if isinstance(quant_mode, str) \
         else int(quant_mode)
     a.dtype = QKV_DTYPE.get(qkv.dtype, -1)
@@ -611,8 +679,14 @@ def qkv_rmsnorm_rope_cache(qkv, gamma_q, gamma_k, cos, sin, index, k_cache,
                            epsilon=1e-6, k_scale=None, v_scale=None,
                            k_offset=None, v_offset=None, q_out=None,
                            before_quant=False, B=None, S=None,
-                           cache_mode=None, stream=None):
+                           cache_mode=None, stream=None,
+                           debug_check_inputs=False):
     """Run QkvRmsNormRopeCache; k_cache and v_cache are updated in place.
+
+    debug_check_inputs: the library copies the index (and the quant scales)
+    to the host first, synchronising the stream, and refuses an
+    out-of-range or repeated index (QKVNR_ERR_BAD_INDEX) or a zero scale
+    (QKVNR_ERR_BAD_SCALE) before launching anything.
 
     qkv: (T, Nq+Nk+Nv, D) or (B, S, (Nq+Nk+Nv)*D).  Returns q_out (T, Nq, D),
     plus (q_before_quant, k_before_quant, v_before_quant) when
@@ -636,7 +710,8 @@ def qkv_rmsnorm_rope_cache(qkv, gamma_q, gamma_k, cos, sin, index, k_cache,
         Nq=Nq, Nk=Nk, Nv=Nv, quant_mode=quant_mode, epsilon=epsilon,
         k_scale=k_scale, v_scale=v_scale, k_offset=k_offset,
         v_offset=v_offset, q_before_quant=qb, k_before_quant=kb,
-        v_before_quant=vb, B=B, S=S, cache_mode=cache_mode)
+        v_before_quant=vb, B=B, S=S, cache_mode=cache_mode,
+        flags=QKV_FLAG_CHECK_INPUTS if debug_check_inputs else 0)
     a.D = int(D)
     _validate_qkv(a, dict(
         qkv=qkv3, gamma_q=gamma_q, gamma_k=gamma_k, cos=cos, sin=sin,

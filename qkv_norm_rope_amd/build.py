@@ -3,8 +3,10 @@
     python -m qkv_norm_rope_amd.build          # build in-tree
     python -m qkv_norm_rope_amd.build --print  # show the commands only
 
-Each .hip source compiles to an object under qkv_norm_rope_amd/_build/, then
-one shared library links them: qkv_norm_rope_amd/lib/libqkvnr.so.
+Each .hip source compiles (hipcc, gfx950) and the host-only C ABI layer
+host.cpp compiles (the host C++ compiler) to an object under
+qkv_norm_rope_amd/_build/, then one shared library links them:
+qkv_norm_rope_amd/lib/libqkvnr.so.
 """
 
 from __future__ import annotations
@@ -23,7 +25,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqkvnr.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["capi.hip", "qkv_rmsnorm_rope_cache.hip", "mla_prolog_v2.hip"]
+SOURCES = ["runtime.hip", "qkv_rmsnorm_rope_cache.hip", "mla_prolog_v2.hip"]
+HOST_SOURCES = ["host.cpp"]  # plain C++: no HIP, also built under sanitizers
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every device compile.
@@ -40,6 +43,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build)")
 
 
+HOST_CFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}"]
+
+
+def host_cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and shutil.which(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler (g++) found")
+
+
 def commands():
     cc = hipcc()
     objs, cmds = [], []
@@ -47,6 +60,11 @@ def commands():
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    cxx = host_cxx()
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".cpp", ".host.o"))
+        objs.append(obj)
+        cmds.append([cxx, *HOST_CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o",
             LIB + ".tmp"]
     return cmds, link

@@ -1,17 +1,18 @@
-// Internal interface between the C-ABI layer (capi.hip) and the kernel
-// launchers.  Not installed; the public header is include/qkvnr.h.
+// Internal interface between the C-ABI layer (host.cpp, plain C++) and the
+// HIP launchers.  Not installed; the public header is include/qkvnr.h.
+// Streams are hipStream_t passed as void*, so this header needs no HIP.
 #pragma once
 
-#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
+#include "plan.h"
 #include "qkvnr.h"
 
 namespace qkvnr {
 
 // Launch the fused qkv kernel; arguments already validated.
-int launch_qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* a, hipStream_t stream);
+int launch_qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* a, void* stream);
 
 // Pack (batch, K, N) row-major weights into the K16 blocked layout; columns
 // from rope_col0 on are rope heads of rope_dim columns, reordered into the
@@ -19,32 +20,22 @@ int launch_qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* a, hipStream_t 
 // kperm (bf16, K % 16 == 0): within each 16-k step the two 8-k chunks hold
 // k offsets {0-3, 8-11} and {4-7, 12-15}.
 int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
-                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream,
+                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, void* stream,
                        bool kperm = false);
-
-// Execution plan of one MlaPrologV2 call: which kernel family runs, the
-// split-K factor of the down projection and the workspace carve-up.  A pure
-// function of the arguments, so workspace sizing and execution agree.
-struct MlaPlan {
-  bool skinny;        // decode-sized T: weight-streaming kernels
-  bool gemm256;       // large T, bf16: 256x256-tile MFMA GEMMs
-  bool fuse_uk;       // gemm256 with the W^UK product fused into A6's q^C tiles
-  int mb;             // 32-row blocks held per wave (skinny only)
-  int ksplit;         // down-projection split-K factor
-  int64_t steps_per_split;
-  // workspace offsets (bytes) and total size
-  size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
-  size_t off_part, off_cq, off_cq_scale, off_qc;
-  size_t off_qn;      // FULL_KV_INT8: q^N in fp32 before its per-head quant
-  size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
-  int64_t rows;       // token rows padded to the plan's 32-row blocks
-  size_t total;
-};
-
-MlaPlan make_mla_plan(const MlaPrologV2Args* a);
 
 // Launch the prolog; arguments validated, workspace large enough.
 int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& plan, void* workspace,
-                         hipStream_t stream);
+                         void* stream);
+
+// Copy `bytes` of device memory to host memory in stream order and wait for
+// the copy (the debug checks only).  QKVNR_OK or QKVNR_ERR_LAUNCH_FAILED.
+int copy_to_host_sync(void* host_dst, const void* dev_src, size_t bytes, void* stream);
+
+// Measurement probes (runtime.hip): a streaming read of `bytes` (a multiple
+// of 16) from device memory, and a dense bf16 MFMA loop of `iters` steps per
+// chain over 512 workgroups x 4 waves x 4 chains.  `sink` is a device word
+// that is written only in a case that does not happen.
+int probe_read(const void* src, size_t bytes, void* sink, void* stream);
+int probe_mfma(int64_t iters, void* sink, void* stream);
 
 }  // namespace qkvnr

@@ -893,14 +893,13 @@ __global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
 // waits only for its own loads of it, then one barrier publishes all of
 // them.
 // ---------------------------------------------------------------------------
-constexpr int G_TN = 256;
+// (G_TN = 256 columns, plan.h.)
 // 128-row tiles (three stage buffers, 72 KB of LDS, at most 181 VGPRs) let
 // two workgroups share a CU, so one's epilogue stores overlap the other's
 // main loop; the prefill q^R and down-projection GEMMs use them (14% and 4%
 // faster than 256-row tiles at T = 4096).  The fused q^C + W^UK tiles stay
 // 256 rows: each tile loads its two heads' W^UK, and 128-row tiles double
-// that traffic (437 vs 320 us).
-constexpr int G_TM_HALF = 128;
+// that traffic (437 vs 320 us).  (G_TM_HALF = 128, plan.h.)
 
 // One wave's 16-byte-per-lane buffer -> LDS load (buffer_load_dwordx4 ...
 // lds): lane l's 16 bytes land at lds + 16*l.  Issued from inline assembly
@@ -1391,8 +1390,7 @@ struct FinishParams {
 };
 
 constexpr int FIN_MAX_THREADS = 1024;
-constexpr int FIN_MAXSPLIT = 8;
-constexpr int FIN_SPLIT_SMALL = 4;  // the large-T plan's split-K bound
+// (FIN_MAXSPLIT and FIN_SPLIT_SMALL, the split-K bounds, are in plan.h.)
 
 // Workgroup size of the finish kernel for ntot columns: one thread per
 // 8-column chunk, whole waves, at most FIN_MAX_THREADS (more chunks loop).
@@ -1737,8 +1735,6 @@ __global__ __launch_bounds__(256) void k_pack(const char* __restrict__ src, uint
   }
 }
 
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
 // One launch: the stream and, when the caller asked for per-kernel timing,
 // the start and stop events (hipExtLaunchKernel takes them at the kernel's
 // own dispatch, so they bracket exactly its execution).
@@ -1782,8 +1778,8 @@ constexpr int a6_kw() { return MB >= 4 ? 1 : 2; }
 constexpr int kA6Cols = 96;  // A6 tile: three waves across, one column block each
 template <int MB>
 constexpr int a8_nw() { return 4; }
-constexpr int kA1Cols = 64;  // A1 tile width: two column blocks (one per wave across when x
-                             // is staged in LDS, both in each wave otherwise)
+// A1 tiles are kA1Cols = 64 columns wide (plan.h): two column blocks, one
+// per wave across when x is staged in LDS, both in each wave otherwise.
 
 // A1 reads x row-major: with one 32-row block each workgroup stages its
 // split of x in LDS (fragment order), otherwise lanes load rows directly.
@@ -1847,8 +1843,9 @@ void skinny_a8(const GemmParams& g8, int nheads, bool quant, const Launch& L) {
 }  // namespace
 
 int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,
-                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, hipStream_t stream,
+                       int elem_bytes, int64_t rope_col0, int64_t rope_dim, void* stream_v,
                        bool kperm) {
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
   const int G = 16 / elem_bytes;
   const int64_t total = batch * (K / G) * ((N + 31) / 32) * 32;
   if (total == 0) return QKVNR_OK;
@@ -1860,93 +1857,9 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
   return hipGetLastError() == hipSuccess ? QKVNR_OK : QKVNR_ERR_LAUNCH_FAILED;
 }
 
-MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
-  MlaPlan pl{};
-  const int64_t T = a->B * a->S;
-  const bool quant = a->quant_mode != MLA_QUANT_NONE;
-  const bool xq = a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8;
-  const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
-  pl.skinny = T <= 128;
-  pl.gemm256 = !pl.skinny && !quant;
-  pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
-  // k-steps of the down projection: 16 k (bf16) or 32 k (int8 x)
-  const int64_t steps = a->He / (xq ? 32 : 16);
-  if (pl.gemm256) {
-    // Split the down projection over K so that its 128x256 tiles (two
-    // workgroups per CU) times the splits fill whole rounds of the 512
-    // workgroup slots best: minimise ceil(tiles * ks / 512) / ks over ks <= 4
-    // (more splits cost partial-sum traffic), with steps per split even
-    // (32-k pipeline stages).
-    const int64_t tiles = (T + G_TM_HALF - 1) / G_TM_HALF *
-                          ((a->Hcq + G_TN - 1) / G_TN + (a->Hckv + a->Dr + G_TN - 1) / G_TN);
-    int64_t best = 1;
-    double best_cost = 1e30;
-    for (int64_t ks = 1; ks <= 4; ++ks) {
-      const double cost = static_cast<double>((tiles * ks + 511) / 512) / static_cast<double>(ks);
-      if (cost < best_cost - 1e-9) {
-        best_cost = cost;
-        best = ks;
-      }
-    }
-    int64_t sps = (steps + best - 1) / best;
-    sps += sps & 1;
-    pl.steps_per_split = sps;
-    pl.ksplit = static_cast<int>((steps + sps - 1) / sps);
-  } else if (pl.skinny) {
-    // Split the down projection over K so that (64-column tiles x splits)
-    // stays within one wave of workgroups over the 256 CUs (no tail round),
-    // at most FIN_MAXSPLIT splits (the finish kernel sums them) and at least
-    // one k-step per wave.
-    const int kw = pl.mb >= 4 ? 2 : (pl.mb == 2 ? 4 : 8);
-    const int64_t ntiles = (a->Hcq + kA1Cols - 1) / kA1Cols + (a->Hckv + a->Dr + kA1Cols - 1) / kA1Cols;
-    int64_t ks = 256 / (ntiles > 0 ? ntiles : 1);
-    if (ks > FIN_MAXSPLIT) ks = FIN_MAXSPLIT;
-    if (ks > steps / kw) ks = steps / kw;
-    if (ks < 1) ks = 1;
-    pl.steps_per_split = (steps + ks - 1) / ks;
-    pl.ksplit = static_cast<int>((steps + pl.steps_per_split - 1) / pl.steps_per_split);
-  } else {
-    pl.steps_per_split = steps;
-    pl.ksplit = 1;
-  }
-  pl.rows = pl.skinny ? 32 * pl.mb : (pl.gemm256 ? (T + 31) / 32 * 32 : T);
-  // Prefill fuses the W^UK product into the q^C tiles of A6 when a wave's
-  // 128 q^C columns are exactly one head (D = 128) and the q^C columns end
-  // on a tile boundary.
-  pl.fuse_uk = pl.gemm256 && a->D == 128 && (a->N * a->D) % G_TN == 0;
-  size_t off = 0;
-  if (a->weight_layout == MLA_WEIGHT_ND) {
-    // packed copies: columns padded to whole 32-column blocks
-    const size_t eb_uq = quant ? 1 : 2;
-    auto pad32 = [](int64_t n) { return static_cast<size_t>((n + 31) / 32 * 32); };
-    pl.off_wdq = off;
-    off += align256(static_cast<size_t>(a->He) * pad32(a->Hcq) * (xq ? 1 : 2));
-    pl.off_wdkvkr = off;
-    off += align256(static_cast<size_t>(a->He) * pad32(a->Hckv + a->Dr) * (xq ? 1 : 2));
-    pl.off_wuqqr = off;
-    off += align256(static_cast<size_t>(a->Hcq) * pad32(a->N * (a->D + a->Dr)) * eb_uq);
-    pl.off_wuk = off;
-    off += align256(static_cast<size_t>(a->N * a->D) * pad32(a->Hckv) * 2);
-  }
-  pl.off_part = off;
-  off += align256(static_cast<size_t>(pl.ksplit) * T * ntot * 4);
-  pl.off_cq = off;
-  off += align256(static_cast<size_t>(pl.rows * a->Hcq) * (quant ? 1 : 2));
-  pl.off_cq_scale = off;
-  off += align256(static_cast<size_t>(T) * 4);
-  pl.off_qc = off;
-  off += align256(static_cast<size_t>(pl.rows * a->N * a->D) * (quant ? 4 : 2));
-  pl.off_qn = off;
-  if (a->quant_mode == MLA_QUANT_FULL_KV_INT8)
-    off += align256(static_cast<size_t>(T * a->N * a->Hckv) * sizeof(float));
-  pl.off_xfrag = off;
-  if (pl.gemm256) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
-  pl.total = T > 0 ? off : 0;
-  return pl;
-}
-
 int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* workspace,
-                         hipStream_t st) {
+                         void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t T = a->B * a->S;
   if (T == 0) return QKVNR_OK;
   const bool quant = a->quant_mode != MLA_QUANT_NONE;

@@ -1,0 +1,45 @@
+// Execution plan of one MlaPrologV2 call and the launch-shape constants it
+// is computed from.  Host-only C++ (no HIP): the entry points in host.cpp
+// size the workspace from it and the launchers in mla_prolog_v2.hip execute
+// it, so sizing and execution always agree.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qkvnr.h"
+
+namespace qkvnr {
+
+// Prefill GEMM tile width (columns) and the height of its two-per-CU tiles.
+constexpr int G_TN = 256;
+constexpr int G_TM_HALF = 128;
+// Most split-K partials the down-projection finish sums, and the bound of
+// the large-T plan's split factor (its finish is instantiated for it).
+constexpr int FIN_MAXSPLIT = 8;
+constexpr int FIN_SPLIT_SMALL = 4;
+// Decode down-projection tile width: two 32-column blocks.
+constexpr int kA1Cols = 64;
+
+// Which kernel family runs, the split-K factor of the down projection and
+// the workspace carve-up.  A pure function of the arguments.
+struct MlaPlan {
+  bool skinny;        // decode-sized T: weight-streaming kernels
+  bool gemm256;       // large T, bf16: 256x256-tile MFMA GEMMs
+  bool fuse_uk;       // gemm256 with the W^UK product fused into A6's q^C tiles
+  int mb;             // 32-row blocks held per wave (skinny only)
+  int ksplit;         // down-projection split-K factor
+  int64_t steps_per_split;
+  // workspace offsets (bytes) and total size
+  size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
+  size_t off_part, off_cq, off_cq_scale, off_qc;
+  size_t off_qn;      // FULL_KV_INT8: q^N in fp32 before its per-head quant
+  size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
+  int64_t rows;       // token rows padded to the plan's 32-row blocks
+  size_t total;
+};
+
+// Arguments must have passed validation.
+MlaPlan make_mla_plan(const MlaPrologV2Args* a);
+
+}  // namespace qkvnr

@@ -181,7 +181,8 @@ void launch_t(const QkvParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int launch_qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* a, hipStream_t stream) {
+int launch_qkv_rmsnorm_rope_cache(const QkvRmsNormRopeCacheArgs* a, void* stream_v) {
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
   QkvParams p;
   p.qkv = static_cast<const uint16_t*>(a->qkv);
   p.gq = static_cast<const uint16_t*>(a->gamma_q);

@@ -43,6 +43,38 @@ def test_library_exports_every_header_symbol():
     assert qn.status_string(0) == "ok"
     assert qn.status_string(-4) == "unsupported configuration"
     assert qn.status_string(12345) == "unknown status"
+    assert qn.status_string(-11) == "cache index out of range or repeated"
+    assert qn.status_string(-12) == "a quant scale is zero"
+
+
+# ---- host index check (both operators' index restriction) -----------------
+
+@pytest.mark.parametrize("index,slots,code", [
+    ([], 0, 0),
+    ([-1, -1], 0, 0),                 # -1 skips; no slot needed
+    ([0, 5, -1, 3], 6, 0),
+    ([5, 0, 5], 6, -11),              # repeated slot
+    ([-1, 2, -1, 2], 3, -11),
+    ([0, 6], 6, -11),                 # past BlockNum * BlockSize
+    ([0, -2], 6, -11),                # below -1
+    ([2**62], 6, -11),
+    ([0], -1, -2),                    # negative slot count
+])
+def test_check_cache_index(index, slots, code):
+    assert qn.mla_check_cache_index(index, slots) == code
+
+
+def test_check_cache_index_large_and_null():
+    import numpy as np
+    rng = np.random.default_rng(5)
+    idx = rng.permutation(1 << 20).astype(np.int64)
+    idx[rng.integers(0, idx.size, 1000)] = -1
+    assert qn.mla_check_cache_index(idx, 1 << 20) == 0
+    idx[7] = idx[9] = 1234567 % (1 << 20)
+    assert qn.mla_check_cache_index(idx, 1 << 20) == -11
+    lib = b.load_library()
+    assert lib.mla_check_cache_index(None, 3, 10) == -1
+    assert lib.mla_check_cache_index(None, -1, 10) == -2
 
 
 # ---- fake device pointers: validation never dereferences them -------------
@@ -97,9 +129,26 @@ def test_mla_valid_args_pass():
                                  Dr=16, bn=4, bs=16)) == 0
 
 
+def test_mla_kernels_mask():
+    # every plan launches the four main kernels once when there are tokens
+    for T in (1, 32, 64, 128, 129, 4096):
+        for q in ("none", "partial_kv_int8", "full_kv_int8"):
+            assert qn.mla_prolog_v2_kernels(mla_args(T=T, quant=q)) == \
+                qn.MLA_KERNELS
+    e = mla_args(T=0)
+    assert qn.mla_prolog_v2_kernels(e) == ()
+    bad = mla_args()
+    bad.He = 7000
+    with pytest.raises(qn.QkvnrError):
+        qn.mla_prolog_v2_kernels(bad)
+    lib = b.load_library()
+    assert lib.mla_prolog_v2_kernels(ctypes.byref(mla_args()), None) == -1
+
+
 @pytest.mark.parametrize("mutate,code", [
     (lambda a: setattr(a, "struct_size", 8), -8),
-    (lambda a: setattr(a, "reserved0", 1), -8),
+    (lambda a: setattr(a, "flags", 2), -3),        # unknown debug flag bit
+    (lambda a: setattr(a, "flags", -1), -3),
     (lambda a: setattr(a, "quant_mode", 3), -1),   # full quant without its scales
     (lambda a: setattr(a, "quant_mode", 4), -1),
     (lambda a: setattr(a, "quant_mode", 9), -3),
@@ -301,6 +350,7 @@ def test_qkv_valid_args_pass():
 
 @pytest.mark.parametrize("mutate,code", [
     (lambda a: setattr(a, "struct_size", 4), -8),
+    (lambda a: setattr(a, "flags", 4), -3),        # unknown debug flag bit
     (lambda a: setattr(a, "quant_mode", 3), -3),
     (lambda a: setattr(a, "dtype", 2), -3),
     (lambda a: setattr(a, "cache_mode", b"PA_NZ"), -4),
@@ -431,3 +481,42 @@ def test_binding_checks_qkv_tensor_types_and_sizes(quant):
     if quant != "none":
         with pytest.raises(ValueError):
             b._validate_qkv(a, dict(t, v_scale=e(128, dtype=f32)))
+
+
+def test_mla_fuzzed_args_validate_size_and_plan_consistently():
+    # Random dims (up to and past the validator's caps), modes, layouts and
+    # pointer patterns: validate, workspace sizing and the kernel mask must
+    # agree and return documented codes.  Under the host sanitizer build
+    # (tests/test_host_sanitizers.py) an overflow or bad access in the
+    # validation or plan arithmetic aborts the run.
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    lib = b.load_library()
+    codes = set(b.STATUS_NAMES)
+    dims = ("B", "S", "He", "Hcq", "N", "D", "Hckv", "Dr", "Nkv", "block_num",
+            "block_size")
+    choices = [0, 1, 2, 15, 16, 32, 48, 64, 96, 128, 512, 1536, 7168, 16384,
+               1 << 22, (1 << 22) + 32, 1 << 23, 1 << 30, (1 << 30) + 1,
+               1 << 40, -1]
+    for it in range(3000):
+        q = list(b.MLA_QUANT)[int(rng.integers(0, 5))]
+        a = mla_args(quant=q, layout=int(rng.integers(0, 2)))
+        for d in dims:
+            if rng.random() < 0.3:
+                setattr(a, d, int(rng.choice(choices)))
+        if rng.random() < 0.1:
+            a.flags = int(rng.integers(0, 3))
+        if rng.random() < 0.1:
+            a.cache_index = None
+        rc = mla_validate(a)
+        assert rc in codes, (it, rc)
+        n = ctypes.c_size_t(123)
+        rs = lib.mla_prolog_v2_workspace_size(ctypes.byref(a), ctypes.byref(n))
+        m = ctypes.c_uint32(7)
+        rk = lib.mla_prolog_v2_kernels(ctypes.byref(a), ctypes.byref(m))
+        assert rs == rc and rk == rc, (it, rc, rs, rk)
+        if rc != 0:
+            assert n.value == 0 and m.value == 0
+        else:
+            T = a.B * a.S
+            assert (n.value > 0) == (T > 0) and m.value == (15 if T else 0)
