@@ -34,6 +34,8 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+DECODE_TARGET_FRAC = 0.60      # decode T=32: fraction of HBM peak on bytes moved
+PREFILL_TARGET_FRAC = 0.50     # prefill T=4096: fraction of bf16 MFMA peak
 METRIC = ("MLA-prolog tokens/s at decode T=32 & prefill T=4096; "
           "%HBM BW / %MFMA peak")
 
@@ -50,6 +52,10 @@ def parse():
     ap.add_argument("--no-full-quant", action="store_true")
     ap.add_argument("--no-partial-quant", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--regions", type=int, default=5,
+                    help="separately timed regions of --steps calls each "
+                         "(the value is their median)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="first run a plain device copy of MB megabytes "
@@ -105,10 +111,18 @@ def mla_flops(c):
 
 
 def uqqr_bytes(c):
-    """Up projection as launched: W^UQ_QR, c^Q in, q^C out (bf16), q^R out,
-    cos/sin rows."""
+    """Algorithmic bytes of the up-projection launch: its share of the
+    call's algorithmic bytes (W^UQ_QR, the cos/sin rows its RoPE reads, the
+    query_rope rows it writes).  c^Q in and q^C out are workspace traffic
+    between the library's own kernels, counted in uqqr_workspace_bytes."""
     return c.Hcq * c.N * (c.D + c.Dr) * 2 + c.T * (
-        c.Hcq * 2 + c.N * c.D * 2 + c.N * c.Dr * 2 + 2 * c.Dr * 2)
+        2 * c.Dr * 2 + c.N * c.Dr * 2)
+
+
+def uqqr_workspace_bytes(c):
+    """Workspace bytes the up-projection launch also moves: c^Q (bf16) in,
+    q^C (bf16) out."""
+    return c.T * (c.Hcq * 2 + c.N * c.D * 2)
 
 
 def uqqr_flops(c):
@@ -266,15 +280,26 @@ def _hold_gpu(torch, ms=20.0):
     torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
 
 
-def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
-    """Time `steps` calls cycling over the sets.
+def _spread(ms_list):
+    xs = sorted(ms_list)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return med, xs[0], xs[-1]
 
-    Returns (ms per step under HIP-graph replay, or in a second eager region
-    without instrumentation when graph is False; per-phase ms from the
-    instrumented eager region; its ms per step; per-kernel ms).  The eager region records, on every step, the library's phase
-    events (device-scope release, between its launches) and its per-kernel
-    start/stop events (taken by each main kernel's own dispatch), with the
-    GPU held until the whole region is enqueued.
+
+def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True, regions=5):
+    """Time `steps` calls cycling over the sets, in `regions` separately
+    timed regions of exactly `steps` calls each.
+
+    Returns a dict: ms (median ms per call over the regions), ms_min,
+    ms_max, regions, steps; phase_ms and kernel_ms (per-call averages from
+    an instrumented eager region of the same `steps` calls: the library's
+    phase events between its launches and each main kernel's own start/stop
+    events, read only for the kernels the library reports it launches);
+    ms_eager (that region's ms per call).  The timed regions are HIP-graph
+    replays of one graph holding the `steps` calls (graph=True), or eager
+    launches of them (graph=False), each bracketed by a device
+    synchronisation on both sides.
     """
     nph = len(qn.MLA_PHASES)
     nk = len(qn.MLA_KERNELS)
@@ -291,6 +316,9 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     ws = calls[0].workspace
     calls += [qn.PreparedMlaPrologV2(*[s[k] for k in names], workspace=ws,
                                      **kw, **scales(s)) for s in sets[1:]]
+    seq = [calls[i % len(calls)] for i in range(steps)]
+    # the kernels whose start/stop events a call records
+    launched = qn.mla_prolog_v2_kernels(calls[0].args)
     stream = torch.cuda.current_stream()
     he = HipEvents()
     ev = [[he.create() for _ in range(nph)] for _ in range(steps)]
@@ -301,8 +329,8 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     t0, t1 = he.create(), he.create()
     _hold_gpu(torch, 5.0 + 0.1 * steps)
     he.record(t0, stream)
-    for i in range(steps):
-        calls[i % len(calls)](phase_events=ev[i], kernel_events=kev[i])
+    for i, c in enumerate(seq):
+        c(phase_events=ev[i], kernel_events=kev[i])
     he.record(t1, stream)
     torch.cuda.synchronize()
     ms_eager = he.elapsed_ms(t0, t1) / steps
@@ -310,53 +338,48 @@ def run_mla(cfg, sets, steps, warmup, torch, qn, graph=True):
     for row in ev:
         for p in range(nph - 1):
             phase_ms[p] += he.elapsed_ms(row[p], row[p + 1]) / steps
-    kernel_ms = [0.0] * nk
-    for row in kev:
-        for k in range(nk):
-            if kernel_ms[k] is None:
-                continue
-            try:
-                kernel_ms[k] += he.elapsed_ms(row[2 * k], row[2 * k + 1]) / steps
-            except RuntimeError:
-                # events never recorded: this plan launches no such kernel
-                # (decode runs the finish inside the up projection's launch)
-                kernel_ms[k] = None
+    kernel_ms = [None] * nk
+    for k, name in enumerate(qn.MLA_KERNELS):
+        if name in launched:
+            kernel_ms[k] = sum(he.elapsed_ms(row[2 * k], row[2 * k + 1])
+                               for row in kev) / steps
     for row in ev + kev:
         for e in row:
             he.destroy(e)
-    ms_step = ms_eager
-    if not graph:
-        # the same steps again without the instrumentation (the phase
-        # events' device-scope releases cost time between the launches)
-        _hold_gpu(torch, 5.0 + 0.1 * steps)
-        he.record(t0, stream)
-        for i in range(steps):
-            calls[i % len(calls)]()
-        he.record(t1, stream)
-        torch.cuda.synchronize()
-        ms_step = he.elapsed_ms(t0, t1) / steps
+    g = None
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for c in calls:
+            for c in seq:
                 c()
-        reps = max(1, steps // len(calls))
-        g.replay()
+        g.replay()  # untimed: first replay
         torch.cuda.synchronize()
-        _hold_gpu(torch, 2.0)
+    times = []
+    for _ in range(regions):
+        torch.cuda.synchronize()
+        _hold_gpu(torch, 2.0 if graph else 5.0 + 0.1 * steps)
         he.record(t0, stream)
-        for _ in range(reps):
+        if graph:
             g.replay()
+        else:
+            for c in seq:
+                c()
         he.record(t1, stream)
         torch.cuda.synchronize()
-        ms_step = he.elapsed_ms(t0, t1) / (reps * len(calls))
-        del g
+        times.append(he.elapsed_ms(t0, t1) / steps)
+    del g
     he.destroy(t0)
     he.destroy(t1)
-    return ms_step, phase_ms, ms_eager, kernel_ms
+    med, lo, hi = _spread(times)
+    return {"ms": med, "ms_min": lo, "ms_max": hi, "regions": regions,
+            "steps": steps, "phase_ms": phase_ms, "kernel_ms": kernel_ms,
+            "ms_eager": ms_eager}
 
 
-def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
+def bench_qkv(steps, warmup, torch, qn, gh, make_workload, regions=5):
+    """The qkv op on its (B=64, S=128) workload: `regions` HIP-graph
+    replays, each of one graph holding `steps` calls alternating two input
+    sets, timed separately; median, min and max ms per call."""
     w = make_workload(4)
     cfg = w.cfg
     sets = []
@@ -377,78 +400,163 @@ def bench_qkv(steps, warmup, torch, qn, gh, make_workload):
     for i in range(warmup):
         call(sets[i % 2])
     torch.cuda.synchronize()
-    # host cost of one call (argument marshalling), to hold the GPU for the
-    # whole enqueue of the timed region: no host gaps inside it
-    h0 = time.perf_counter()
-    for i in range(warmup):
-        call(sets[i % 2])
-    host_ms = (time.perf_counter() - h0) * 1e3 / max(1, warmup)
-    torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    _hold_gpu(torch, 5.0 + 2.0 * host_ms * steps)
-    h0 = time.perf_counter()
-    t0.record(s)
-    for i in range(steps):
-        call(sets[i % 2])
-    t1.record(s)
-    enqueue_ms = (time.perf_counter() - h0) * 1e3
-    torch.cuda.synchronize()
-    ms_eager = t0.elapsed_time(t1) / steps
-    # HIP-graph replay (no launch gaps), as decode is timed: one graph of
-    # `per_graph` calls alternating the two sets (a serving step launches
-    # many layers' calls per graph)
-    per_graph = 20
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(per_graph):
+        for i in range(steps):
             call(sets[i % 2])
     g.replay()
     torch.cuda.synchronize()
-    reps = max(1, steps // per_graph)
-    _hold_gpu(torch, 2.0)
-    t0.record(s)
-    for _ in range(reps):
+    times = []
+    for _ in range(regions):
+        torch.cuda.synchronize()
+        _hold_gpu(torch, 2.0)
+        t0.record(s)
         g.replay()
-    t1.record(s)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / (per_graph * reps)
+        t1.record(s)
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) / steps)
     del g
+    ms, lo, hi = _spread(times)
     n_valid = int((w.arrays["index"] >= 0).sum())
     nbytes = qkv_bytes(cfg, n_valid)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"workload": cfg.name, "tokens_per_s": cfg.T / (ms * 1e-3),
-            "ms_per_step": ms, "algorithmic_bytes": nbytes,
+            "ms_per_step": ms, "ms_min": lo, "ms_max": hi, "steps": steps,
+            "regions": regions, "algorithmic_bytes": nbytes,
             "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-            "timing": "HIP-graph replay; eager launches in eager_ms_per_step",
-            "eager_ms_per_step": ms_eager, "host_enqueue_ms": enqueue_ms}
+            "timing": f"median of {regions} HIP-graph replays of {steps} "
+                      "calls each"}
+
+
+def measure_peaks(torch, qn, mib=1024):
+    """Achievable rates on this GPU: a streaming read (the library's read
+    probe) and a plain device copy (read + write) of `mib` MiB, and the
+    library's MFMA-only bf16 loop; best of 5 event-timed runs each."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(5):
+            t0.record(s)
+            fn()
+            t1.record(s)
+            torch.cuda.synchronize()
+            out.append(t0.elapsed_time(t1))
+        return min(out)
+    read_ms = best(lambda: qn.mla_probe_read(src, sink))
+    copy_ms = best(lambda: dst.copy_(src))
+    iters = 20000
+    flop = qn.mla_probe_mfma_bf16(iters, sink)  # warm-up call; returns the flop count
+    torch.cuda.synchronize()
+    mfma_ms = best(lambda: qn.mla_probe_mfma_bf16(iters, sink))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"read_GBps": n / (read_ms * 1e-3) / 1e9,
+            "copy_GBps": 2 * n / (copy_ms * 1e-3) / 1e9,
+            "mfma_bf16_TFLOPs": flop / (mfma_ms * 1e-3) / 1e12,
+            "how": f"streaming read and device copy of {mib} MiB (copy "
+                   "counts read + write bytes); dense bf16 MFMA loop with no "
+                   "memory traffic; best of 5"}
+
+
+def _blas_info():
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {})
+        return f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:  # pragma: no cover - older numpy
+        return "unknown"
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return len(os.sched_getaffinity(0))
+
+
+def _time_oracle(fn, seconds, reps=3):
+    """Median wall time of fn over at least `reps` runs, stopping once
+    `seconds` have passed after the third."""
+    ts = []
+    t_start = time.perf_counter()
+    while len(ts) < reps or time.perf_counter() - t_start < seconds:
+        t = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t)
+        if len(ts) >= reps and time.perf_counter() - t_start >= seconds:
+            break
+    ts.sort()
+    return ts[len(ts) // 2], len(ts)
 
 
 def cpu_baseline(w, seconds):
-    import numpy as np  # noqa: F401
+    """The float64 NumPy oracle on the host cores: whole T = 32 decode
+    calls for about `seconds`; tokens/s from the median call time."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        cores = len(os.sched_getaffinity(0))
     cfg = w.cfg
     dims = dict(He=cfg.He, Hcq=cfg.Hcq, N=cfg.N, D=cfg.D, Hckv=cfg.Hckv,
                 Dr=cfg.Dr)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.mla_prolog_v2(w.arrays, w.dtypes, dims, cfg.quant_mode,
-                             cfg.eps_cq, cfg.eps_ckv)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{n} float64 NumPy oracle calls of the full T={cfg.T} "
-                      f"decode workload ({el:.1f} s)"}
+    med, n = _time_oracle(lambda: oracle.mla_prolog_v2(
+        w.arrays, w.dtypes, dims, cfg.quant_mode, cfg.eps_cq, cfg.eps_ckv),
+        seconds)
+    return {"value": cfg.T / med, "unit": "tokens/s",
+            "cores": int(_blas_threads()), "kind": "oracle",
+            "blas": _blas_info(),
+            "sample": f"median of {n} float64 NumPy oracle calls of the full "
+                      f"T={cfg.T} decode workload"}
+
+
+def cpu_baseline_other(make_workload, seconds):
+    """The oracle on the other workloads, median of 3 calls each: tiny
+    (config 0) whole; partial quant (config 3) on its first 16 tokens and
+    prefill (config 2) on its first 512 (tokens are independent; the
+    oracle's exact int64 product makes a whole config-3 call take seconds);
+    the qkv op (config 4) whole.  tokens/s each."""
+    import numpy as np
+    import oracle
+    from workloads import sub_workload
+    out = {}
+    for key, sample in ((0, None), (3, 16), (2, 512)):
+        w = make_workload(key)
+        cfg = w.cfg
+        if sample:
+            w = sub_workload(w, np.arange(sample))
+        dims = dict(He=cfg.He, Hcq=cfg.Hcq, N=cfg.N, D=cfg.D, Hckv=cfg.Hckv,
+                    Dr=cfg.Dr)
+        ww = w
+        med, n = _time_oracle(lambda: oracle.mla_prolog_v2(
+            ww.arrays, ww.dtypes, dims, cfg.quant_mode, cfg.eps_cq,
+            cfg.eps_ckv), 0.0)
+        T = ww.cfg.T
+        out[cfg.name] = {"tokens_per_s": T / med, "median_s": med,
+                         "calls": n, "tokens_per_call": T}
+    w = make_workload(4)
+    cfg = w.cfg
+    med, n = _time_oracle(lambda: oracle.qkv_rmsnorm_rope_cache(
+        w.arrays, w.dtypes, dict(Nq=cfg.Nq, Nk=cfg.Nk, Nv=cfg.Nv, D=cfg.D),
+        cfg.quant_mode, cfg.eps), 0.0)
+    out[cfg.name] = {"tokens_per_s": cfg.T / med, "median_s": med,
+                     "calls": n, "tokens_per_call": cfg.T}
+    return out
+
+
+def progress(msg):
+    """One line on stderr per finished section (the JSON line is stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -474,8 +582,10 @@ def main():
     w = make_workload(1)
     cfg = w.cfg
     sets = prepare_mla_sets(w, args.rotate, torch, qn, gh)
-    ms, phase_ms, ms_eager, kernel_ms = run_mla(cfg, sets, args.steps,
-                                                args.warmup, torch, qn)
+    r = run_mla(cfg, sets, args.steps, args.warmup, torch, qn,
+                regions=args.regions)
+    ms = r["ms"]
+    kernel_ms = r["kernel_ms"]
     step_bytes = mla_bytes(cfg)
     a6_ms = kernel_ms[2]  # the up projection's own start/stop events
     a6_bytes = uqqr_bytes(cfg)
@@ -504,56 +614,78 @@ def main():
                    "block_size": cfg.block_size, "quant_mode": cfg.quant_mode,
                    "weight_layout": "packed_k16",
                    "rotating_input_sets": args.rotate},
+        "timing": {"value": f"median over {r['regions']} separately timed "
+                            f"regions, each one HIP-graph replay of exactly "
+                            f"{args.steps} prepared calls (steps) cycling "
+                            f"over {args.rotate} input sets, device "
+                            "synchronised before and after each region",
+                   "ms_per_step_min": r["ms_min"],
+                   "ms_per_step_max": r["ms_max"],
+                   "regions": r["regions"],
+                   "calls_per_region": args.steps,
+                   "kernel_us": "start/stop events taken by each main "
+                                "kernel's own dispatch (hipExtLaunchKernel, "
+                                "on the launch stream) in an eager region "
+                                "of the same calls",
+                   "phase_us": "events recorded between the launches "
+                               "(kernel plus dispatch)"},
         "roofline": {"kernel": "up projection c^Q.[W^UQ|W^QR] + RoPE q^R",
                      "bound": "hbm", "achieved": a6_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": a6_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": a6_bytes,
-                     "avg_launch_us": a6_ms * 1e3},
+                     "workspace_bytes": uqqr_workspace_bytes(cfg),
+                     "avg_launch_us": a6_ms * 1e3,
+                     "duration": "average over the eager region's calls of "
+                                 "the kernel's own start/stop events"},
         "step_roofline": {"bound": "hbm", "algorithmic_bytes": step_bytes,
                           "achieved": step_gbs, "peak": HBM_PEAK_GBS,
-                          "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS},
+                          "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
+                          "target_frac": DECODE_TARGET_FRAC,
+                          "gap_to_target": DECODE_TARGET_FRAC
+                          - step_gbs / HBM_PEAK_GBS},
         "kernel_us": dict(zip(qn.MLA_KERNELS, [None if k is None else k * 1e3
                                                for k in kernel_ms])),
         "phase_us": dict(zip(("down", "norm_cache", "up_qr", "uk"),
-                             [p * 1e3 for p in phase_ms])),
-        "timing": "value and ms_per_step: HIP-graph replay of the prepared "
-                  "calls; kernel_us and roofline: start/stop events taken "
-                  "by each main kernel's own dispatch (hipExtLaunchKernel, "
-                  "on the launch stream) in an eager region of the same "
-                  "steps; phase_us: events recorded between the launches "
-                  "(kernel plus dispatch)",
-        "eager": {"ms_per_step": ms_eager,
-                  "tokens_per_s": cfg.T / (ms_eager * 1e-3)},
+                             [p * 1e3 for p in r["phase_ms"]])),
+        "eager": {"ms_per_step": r["ms_eager"],
+                  "tokens_per_s": cfg.T / (r["ms_eager"] * 1e-3)},
     }
     del sets
     torch.cuda.empty_cache()
+    progress(f"decode T=32: {ms * 1e3:.2f} us/step")
 
     # ---- prefill, T = 4096 ------------------------------------------------
     if not args.no_prefill:
         wp = make_workload(2)
         pc = wp.cfg
         psets = prepare_mla_sets(wp, 1, torch, qn, gh)
-        psteps = max(3, args.steps // 20)
-        pms, pph, _, pk = run_mla(pc, psets, psteps,
-                                  max(2, args.warmup // 10), torch, qn,
-                                  graph=False)
+        psteps = max(10, args.steps // 2)
+        pr = run_mla(pc, psets, psteps, max(2, args.warmup // 2), torch, qn,
+                     graph=False, regions=3)
+        pms, pk = pr["ms"], pr["kernel_ms"]
         fl = mla_flops(pc)
         # The prefill plan fuses q^C.W^UK into the q^C tiles of the up
         # projection: the two launches after the norm phase (q^R tiles, then
         # q^C tiles with the W^UK product) are one roofline unit.
         upf = uqqr_flops(pc) + uk_flops(pc)
         up_ms = pk[2] + pk[3]
+        frac = fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
         out["prefill"] = {
             "workload": pc.name, "tokens_per_s": pc.T / (pms * 1e-3),
-            "ms_per_step": pms, "steps": psteps, "algorithmic_flops": fl,
+            "ms_per_step": pms, "ms_min": pr["ms_min"], "ms_max": pr["ms_max"],
+            "steps": psteps, "regions": pr["regions"],
+            "timing": f"median of {pr['regions']} eager regions of {psteps} "
+                      "calls each",
+            "algorithmic_flops": fl,
             "step_TFLOPs": fl / (pms * 1e-3) / 1e12,
-            "mfma_frac": fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "mfma_frac": frac, "target_mfma_frac": PREFILL_TARGET_FRAC,
+            "gap_to_target": PREFILL_TARGET_FRAC - frac,
             "kernel_us": dict(zip(("down", "norm", "up_qr_rope",
                                    "up_qc_uk"),
                                   [None if k is None else k * 1e3 for k in pk])),
             "phase_us": dict(zip(("down", "norm_cache", "up_qr_rope",
                                   "up_qc_uk"),
-                                 [p * 1e3 for p in pph])),
+                                 [p * 1e3 for p in pr["phase_ms"]])),
             "roofline": {"kernel": "up projections c^Q.[W^UQ|W^QR] with "
                                    "RoPE q^R and the fused per-head "
                                    "q^C.W^UK",
@@ -561,64 +693,82 @@ def main():
                          "achieved": upf / (up_ms * 1e-3) / 1e12,
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": upf / (up_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                         "traffic": None},
+                         "algorithmic_flops": upf, "traffic": None},
         }
         del psets
         torch.cuda.empty_cache()
+        progress(f"prefill T=4096: {pms * 1e3:.1f} us/step")
 
     # ---- partial quantisation, int8 caches: T = 64, 32 heads -------------
     if not args.no_partial_quant:
         wq = make_workload(3)
         qc = wq.cfg
         qsets = prepare_mla_sets(wq, args.rotate, torch, qn, gh)
-        qms, _, _, qk = run_mla(qc, qsets, max(20, args.steps // 2),
-                                max(5, args.warmup // 2), torch, qn)
+        qr = run_mla(qc, qsets, args.steps, max(5, args.warmup // 2), torch,
+                     qn, regions=args.regions)
+        qms, qk = qr["ms"], qr["kernel_ms"]
         qb = mla_partial_bytes(qc)
         out["partial_quant"] = {
             "workload": qc.name, "quant_mode": qc.quant_mode,
             "tokens_per_s": qc.T / (qms * 1e-3), "ms_per_step": qms,
+            "ms_min": qr["ms_min"], "ms_max": qr["ms_max"],
             "algorithmic_bytes": qb,
             "achieved_GBps": qb / (qms * 1e-3) / 1e9,
             "hbm_frac": qb / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernel_us": dict(zip(qn.MLA_KERNELS, [None if k is None else k * 1e3
                                                    for k in qk])),
-            "timing": "HIP-graph replay of the prepared calls over "
-                      f"{args.rotate} rotating input sets",
+            "timing": f"median of {qr['regions']} HIP-graph replays of "
+                      f"{args.steps} calls over {args.rotate} rotating "
+                      "input sets",
         }
         del qsets
         torch.cuda.empty_cache()
+        progress(f"partial quant T=64: {qms * 1e3:.2f} us/step")
 
     # ---- full quantisation (int8 kv_cache and query), T = 32 -------------
     if not args.no_full_quant:
         wf = make_workload(cfg.replace(quant_mode="full_kv_int8", seed=1101))
         fc = wf.cfg
         fsets = prepare_mla_sets(wf, args.rotate, torch, qn, gh)
-        fms, _, _, fk = run_mla(fc, fsets, max(20, args.steps // 2),
-                                max(5, args.warmup // 2), torch, qn)
+        fr = run_mla(fc, fsets, args.steps, max(5, args.warmup // 2), torch,
+                     qn, regions=args.regions)
+        fms, fk = fr["ms"], fr["kernel_ms"]
         fb = mla_full_bytes(fc)
         out["full_quant_decode"] = {
             "workload": fc.name + "_full_kv_int8",
             "quant_mode": "full_kv_int8",
             "tokens_per_s": fc.T / (fms * 1e-3), "ms_per_step": fms,
+            "ms_min": fr["ms_min"], "ms_max": fr["ms_max"],
             "algorithmic_bytes": fb,
             "achieved_GBps": fb / (fms * 1e-3) / 1e9,
             "hbm_frac": fb / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernel_us": dict(zip(qn.MLA_KERNELS, [None if k is None else k * 1e3
                                                    for k in fk])),
-            "timing": "HIP-graph replay of the prepared calls over "
-                      f"{args.rotate} rotating input sets; int8 x, weights "
-                      "(W^UK bf16), kv_cache and query",
+            "timing": f"median of {fr['regions']} HIP-graph replays of "
+                      f"{args.steps} calls over {args.rotate} rotating input "
+                      "sets; int8 x, weights (W^UK bf16), kv_cache and query",
         }
         del fsets
         torch.cuda.empty_cache()
+        progress(f"full quant T=32: {fms * 1e3:.2f} us/step")
 
     if not args.no_qkv:
         out["qkv_rmsnorm_rope_cache"] = bench_qkv(
-            max(10, args.steps // 2), max(3, args.warmup // 2), torch, qn, gh,
-            make_workload)
+            max(20, args.steps), max(3, args.warmup // 2), torch, qn, gh,
+            make_workload, regions=args.regions)
+        progress("qkv op: %.2f us/step"
+                 % (out["qkv_rmsnorm_rope_cache"]["ms_per_step"] * 1e3))
+
+    if not args.no_peaks:
+        out["achievable_peaks"] = measure_peaks(torch, qn)
+        progress(f"achievable peaks: {out['achievable_peaks']}")
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        progress("cpu baseline (decode) done")
+        out["cpu_baseline_other_workloads"] = cpu_baseline_other(
+            make_workload, args.cpu_seconds)
+        progress("cpu baseline (other workloads) done")
     print(json.dumps(out), flush=True)
     return 0
 
