@@ -83,8 +83,11 @@ enum {
                                        from mla_check_cache_index and the
                                        opt-in debug checks (MLA_FLAG_CHECK_
                                        INDEX, QKV_FLAG_CHECK_INPUTS) */
-  QKVNR_ERR_BAD_SCALE = -12         /* a zero quant scale: only from the
+  QKVNR_ERR_BAD_SCALE = -12,        /* a zero quant scale: only from the
                                        opt-in QKV_FLAG_CHECK_INPUTS check */
+  QKVNR_ERR_SCRATCH_TOO_SMALL = -13  /* mla_prolog_v2_no_alloc: the call
+                                        needs more workspace than
+                                        MLA_NO_ALLOC_SCRATCH_BYTES */
 };
 
 /* Human-readable name of a status code (static storage, never NULL; an
@@ -304,6 +307,24 @@ int mla_prolog_v2_kernels(const MlaPrologV2Args* args, uint32_t* mask);
  * QKVNR_ERR_LAUNCH_FAILED; nothing is launched on a validation error. */
 int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* Size of the fixed per-device scratch array of mla_prolog_v2_no_alloc. */
+#define MLA_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* mla_prolog_v2 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from a
+ * 16 MiB array the library holds on each GPU it runs on (allocated with
+ * the code object, kept until the process ends) instead of a caller buffer.
+ * The call itself allocates nothing.  It needs nothing cleared.  Calls that
+ * overlap in time on one GPU share that array and race: order them on one
+ * stream.  Limit: calls whose mla_prolog_v2_workspace_size exceeds
+ * MLA_NO_ALLOC_SCRATCH_BYTES are refused with QKVNR_ERR_SCRATCH_TOO_SMALL
+ * (at the DeepSeek-V3 dims every decode-sized call with T <= 128 fits,
+ * except FULL_KV_INT8 above T = 32; ND-layout weights, packed into the
+ * workspace, need far more).  MLA_FLAG_CHECK_INDEX is refused
+ * (QKVNR_ERR_BAD_MODE).  Other errors as mla_prolog_v2. */
+int mla_prolog_v2_no_alloc(const MlaPrologV2Args* args, void* stream);
 
 /* Weight packing: the MFMA-native counterpart of the MlaPrologV2 pages'
  * FRACTAL_NZ weight format (MLA_WEIGHT_PACKED_K16 above); done once per

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     MLA_FLAG_CHECK_INDEX,
     MLA_KERNELS,
+    MLA_NO_ALLOC_SCRATCH_BYTES,
     MLA_PHASES,
     MLA_QUANT,
     MLA_WEIGHT_ND,
@@ -40,6 +41,7 @@ from ._binding import (  # noqa: F401
     mla_prolog_v2,
     mla_prolog_v2_args,
     mla_prolog_v2_kernels,
+    mla_prolog_v2_no_alloc,
     mla_prolog_v2_workspace_size,
     qkv_rmsnorm_rope_cache,
     qkv_rmsnorm_rope_cache_args,

@@ -26,7 +26,9 @@ STATUS_NAMES = {
     -7: "QKVNR_ERR_BAD_EPS", -8: "QKVNR_ERR_BAD_STRUCT",
     -9: "QKVNR_ERR_BAD_ALIGNMENT", -10: "QKVNR_ERR_LAUNCH_FAILED",
     -11: "QKVNR_ERR_BAD_INDEX", -12: "QKVNR_ERR_BAD_SCALE",
+    -13: "QKVNR_ERR_SCRATCH_TOO_SMALL",
 }
+MLA_NO_ALLOC_SCRATCH_BYTES = 16 << 20
 MLA_FLAG_CHECK_INDEX = 1
 QKV_FLAG_CHECK_INPUTS = 1
 MLA_QUANT = {"none": 0, "partial_kv_bf16": 1, "partial_kv_int8": 2,
@@ -40,7 +42,8 @@ QKV_DTYPE = {torch.float16: 0, torch.bfloat16: 1}
 EXPORTS = (
     "mla_status_string", "mla_lib_version", "mla_check_cache_index",
     "mla_prolog_v2_workspace_size", "mla_prolog_v2_validate",
-    "mla_prolog_v2_kernels", "mla_prolog_v2", "mla_pack_weight",
+    "mla_prolog_v2_kernels", "mla_prolog_v2", "mla_prolog_v2_no_alloc",
+    "mla_pack_weight",
     "mla_pack_weight_uq_qr", "mla_pack_weight_uk",
     "qkv_rmsnorm_rope_cache_validate", "qkv_rmsnorm_rope_cache",
     "mla_probe_read", "mla_probe_mfma_bf16",
@@ -133,6 +136,8 @@ def load_library(path: str = None) -> ctypes.CDLL:
         ctypes.POINTER(MlaPrologV2Args), ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_prolog_v2_validate.restype = ctypes.c_int
     lib.mla_prolog_v2_validate.argtypes = [ctypes.POINTER(MlaPrologV2Args)]
+    lib.mla_prolog_v2_no_alloc.restype = ctypes.c_int
+    lib.mla_prolog_v2_no_alloc.argtypes = [ctypes.POINTER(MlaPrologV2Args), _vp]
     lib.mla_prolog_v2.restype = ctypes.c_int
     lib.mla_prolog_v2.argtypes = [ctypes.POINTER(MlaPrologV2Args), _vp,
                                   ctypes.c_size_t, _vp]
@@ -474,8 +479,11 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
                   query=None, query_rope=None, workspace=None,
                   return_cq_quant=False, cache_mode=None, stream=None,
                   phase_events=None, kernel_events=None,
-                  debug_check_index=False):
+                  debug_check_index=False, no_alloc=False):
     """Run MlaPrologV2; kv_cache and kr_cache are updated in place.
+
+    no_alloc: run mla_prolog_v2_no_alloc (the library's fixed per-device
+    scratch instead of a workspace; `workspace` is ignored).
 
     debug_check_index: the library copies cache_index to the host first
     (synchronising the stream) and refuses an out-of-range or repeated index
@@ -550,16 +558,30 @@ def mla_prolog_v2(token_x, weight_dq, weight_uq_qr, weight_uk, weight_dkv_kr,
             *[e.cuda_event for e in kernel_events])
         a.kernel_events = ctypes.cast(khandles, ctypes.POINTER(_vp))
         a.n_kernel_events = len(kernel_events)
-    nbytes = mla_prolog_v2_workspace_size(a)
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    _check(lib.mla_prolog_v2(ctypes.byref(a), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(),
-                             _stream(stream)), "mla_prolog_v2")
+    if no_alloc:
+        _check(lib.mla_prolog_v2_no_alloc(ctypes.byref(a), _stream(stream)),
+               "mla_prolog_v2_no_alloc")
+    else:
+        nbytes = mla_prolog_v2_workspace_size(a)
+        if workspace is None or \
+                workspace.numel() * workspace.element_size() < nbytes:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8,
+                                    device=dev)
+        _check(lib.mla_prolog_v2(ctypes.byref(a), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "mla_prolog_v2")
     out = (query, query_rope) + ((dequant_scale_q_nope,) if q8 else ())
     if return_cq_quant:
         return out + (dbg8, dbgs)
     return out
+
+
+def mla_prolog_v2_no_alloc(*args, **kw):
+    """mla_prolog_v2 through the no-allocation entry point: the workspace is
+    the library's fixed per-device scratch (MLA_NO_ALLOC_SCRATCH_BYTES); the
+    outputs are allocated here unless passed in (query=, query_rope=)."""
+    kw.pop("workspace", None)
+    return mla_prolog_v2(*args, no_alloc=True, **kw)
 
 
 class PreparedMlaPrologV2:

@@ -25,7 +25,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqkvnr.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["runtime.hip", "qkv_rmsnorm_rope_cache.hip", "mla_prolog_v2.hip"]
+SOURCES = ["runtime.hip", "no_alloc.hip", "qkv_rmsnorm_rope_cache.hip",
+           "mla_prolog_v2.hip"]
 HOST_SOURCES = ["host.cpp"]  # plain C++: no HIP, also built under sanitizers
 
 ARCH = "gfx950"

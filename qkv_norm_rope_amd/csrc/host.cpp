@@ -357,6 +357,8 @@ const char* mla_status_string(int s) {
     case QKVNR_ERR_LAUNCH_FAILED: return "kernel launch failed";
     case QKVNR_ERR_BAD_INDEX: return "cache index out of range or repeated";
     case QKVNR_ERR_BAD_SCALE: return "a quant scale is zero";
+    case QKVNR_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more than the no-allocation entry point's fixed scratch";
     default: return "unknown status";
   }
 }
@@ -404,6 +406,17 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace, size_t workspace
     if (rc != QKVNR_OK) return rc;
   }
   return launch_mla_prolog_v2(args, plan, workspace, stream);
+}
+
+int mla_prolog_v2_no_alloc(const MlaPrologV2Args* args, void* stream) {
+  const int rc = validate_mla(args);
+  if (rc != QKVNR_OK) return rc;
+  // the debug copy would allocate host memory and synchronise
+  if (args->flags & MLA_FLAG_CHECK_INDEX) return QKVNR_ERR_BAD_MODE;
+  if (args->B * args->S == 0) return QKVNR_OK;
+  const MlaPlan plan = make_mla_plan(args);
+  if (plan.total > MLA_NO_ALLOC_SCRATCH_BYTES) return QKVNR_ERR_SCRATCH_TOO_SMALL;
+  return launch_mla_prolog_v2_no_alloc(args, plan, stream);
 }
 
 int mla_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int64_t N,

@@ -27,6 +27,10 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
 int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& plan, void* workspace,
                          void* stream);
 
+// The same on this library's fixed per-device scratch array (no_alloc.hip);
+// plan.total <= MLA_NO_ALLOC_SCRATCH_BYTES already checked.
+int launch_mla_prolog_v2_no_alloc(const MlaPrologV2Args* a, const MlaPlan& plan, void* stream);
+
 // Copy `bytes` of device memory to host memory in stream order and wait for
 // the copy (the debug checks only).  QKVNR_OK or QKVNR_ERR_LAUNCH_FAILED.
 int copy_to_host_sync(void* host_dst, const void* dev_src, size_t bytes, void* stream);

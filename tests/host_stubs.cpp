@@ -18,6 +18,10 @@ int launch_mla_prolog_v2(const MlaPrologV2Args*, const MlaPlan&, void*, void*) {
   return QKVNR_ERR_LAUNCH_FAILED;
 }
 
+int launch_mla_prolog_v2_no_alloc(const MlaPrologV2Args*, const MlaPlan&, void*) {
+  return QKVNR_ERR_LAUNCH_FAILED;
+}
+
 int copy_to_host_sync(void*, const void*, size_t, void*) { return QKVNR_ERR_LAUNCH_FAILED; }
 
 int probe_read(const void*, size_t, void*, void*) { return QKVNR_ERR_LAUNCH_FAILED; }

@@ -520,3 +520,30 @@ def test_mla_fuzzed_args_validate_size_and_plan_consistently():
         else:
             T = a.B * a.S
             assert (n.value > 0) == (T > 0) and m.value == (15 if T else 0)
+
+
+def test_no_alloc_entry_point_host_checks():
+    # refusals happen on the host before any launch (no GPU needed)
+    lib = b.load_library()
+    src = open(HEADER).read()
+    m = re.search(r"#define MLA_NO_ALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == qn.MLA_NO_ALLOC_SCRATCH_BYTES
+    big = mla_args(T=4096)
+    assert qn.mla_prolog_v2_workspace_size(big) > qn.MLA_NO_ALLOC_SCRATCH_BYTES
+    assert lib.mla_prolog_v2_no_alloc(ctypes.byref(big), None) == -13
+    nd = mla_args(T=32, layout=b.MLA_WEIGHT_ND)  # packs weights into scratch
+    assert lib.mla_prolog_v2_no_alloc(ctypes.byref(nd), None) == -13
+    dbg = mla_args(T=32)
+    dbg.flags = b.MLA_FLAG_CHECK_INDEX
+    assert lib.mla_prolog_v2_no_alloc(ctypes.byref(dbg), None) == -3
+    e = mla_args(T=0)
+    assert lib.mla_prolog_v2_no_alloc(ctypes.byref(e), None) == 0
+    bad = mla_args(T=32)
+    bad.He = 7000
+    assert lib.mla_prolog_v2_no_alloc(ctypes.byref(bad), None) == -4
+    # the decode shapes it is for fit
+    for q, T in (("none", 128), ("partial_kv_int8", 128), ("full_kv_bf16", 128),
+                 ("full_kv_int8", 32)):
+        assert qn.mla_prolog_v2_workspace_size(mla_args(T=T, quant=q)) <= \
+            qn.MLA_NO_ALLOC_SCRATCH_BYTES, (q, T)
+    assert qn.status_string(-13).startswith("the call needs more than")
