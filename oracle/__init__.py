@@ -15,6 +15,8 @@ Sources (each function cites the section it follows):
 * "aclnnQkvRmsNormRopeCache" (CANN API reference): formulas (1) SplitVD,
   (2) RmsNorm, (3) RoPE half-and-half, (4) Quant, and the input-shape and
   other restrictions.
+* "aclnnMlaPreprocessV2" (CANN API reference): the interface function
+  bullets (the order of the steps) and the RmsNormQuant formula block.
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 library special cases, brute force on tiny inputs, invariants).  End-to-end
@@ -34,6 +36,12 @@ from .common import (
 from .mla_prolog_v2 import mla_prolog_v2, mla_query_from_quantized
 from .mla_prolog_v2 import quant_query_per_head as mla_prolog_v2_quant_query
 from .qkv_rmsnorm_rope_cache import qkv_rmsnorm_rope_cache
+from .mla_preprocess_v2 import (
+    mla_preprocess_v2,
+    preprocess_query_from_codes,
+    rmsnorm_quant,
+    rmsnorm_quant_values,
+)
 
 __all__ = [
     "decode",
@@ -48,4 +56,8 @@ __all__ = [
     "mla_query_from_quantized",
     "mla_prolog_v2_quant_query",
     "qkv_rmsnorm_rope_cache",
+    "mla_preprocess_v2",
+    "preprocess_query_from_codes",
+    "rmsnorm_quant",
+    "rmsnorm_quant_values",
 ]

@@ -144,3 +144,63 @@ def qkv_brute(qkv, gq, gk, cos, sin, dims, eps, scales=None):
         k_rows.append(kt)
         v_rows.append(vt)
     return q_out, k_rows, v_rows
+
+
+def _rmsnorm_quant(row, gamma, bias, scale, eps):
+    v = _rms_norm(row, gamma, eps)
+    out = []
+    for i in range(len(v)):
+        q = round((v[i] + bias[i]) * scale)  # half to even
+        out.append(max(-128, min(127, int(q))))
+    return out
+
+
+def preprocess_brute(x, W1, W2, Wuk, g_x, g_cq, g_ckv, b_x, b_cq, s_x, s_cq,
+                     d1, d2, cos, sin, dims, eps):
+    """MlaPreprocessV2 per token, in the bullets' order: RmsNormQuant of x,
+    the int8 product with W^DQKV (exact Python ints) and its per-channel
+    dequant, the split, RmsNormQuant of the query latent, the int8 product
+    with [W^UQ | W^QR], W^UK per head, RoPE, and the key latent's RmsNorm
+    and RoPE.  Returns per-token lists: query[t][n][j], query_rope[t][n][j],
+    kv_row[t], kr_row[t], x8[t], c8[t]."""
+    He, Hcq, N, D, Hckv, Dr = (dims[k] for k in ("He", "Hcq", "N", "D",
+                                                  "Hckv", "Dr"))
+    ntot = Hcq + Hckv + Dr
+    res = {"query": [], "query_rope": [], "kv_row": [], "kr_row": [],
+           "x8": [], "c8": []}
+    for t in range(len(x)):
+        x8 = _rmsnorm_quant(x[t], g_x, b_x, s_x, eps)
+        y1 = []
+        for j in range(ntot):
+            acc = 0
+            for k in range(He):
+                acc += x8[k] * W1[k][j]
+            y1.append(acc * d1[j])
+        h, gkv, gr = y1[:Hcq], y1[Hcq:Hcq + Hckv], y1[Hcq + Hckv:]
+        c8 = _rmsnorm_quant(h, g_cq, b_cq, s_cq, eps)
+        ncol = N * (D + Dr)
+        y2 = []
+        for j in range(ncol):
+            acc = 0
+            for k in range(Hcq):
+                acc += c8[k] * W2[k][j]
+            y2.append(acc * d2[j])
+        q_t, qr_t = [], []
+        for n in range(N):
+            qc = y2[n * D:(n + 1) * D]
+            row = []
+            for j in range(Hckv):
+                s = 0.0
+                for d in range(D):
+                    s += qc[d] * Wuk[n][d][j]
+                row.append(s)
+            q_t.append(row)
+            qr_t.append(_rope(y2[N * D + n * Dr:N * D + (n + 1) * Dr],
+                              cos[t], sin[t]))
+        res["query"].append(q_t)
+        res["query_rope"].append(qr_t)
+        res["kv_row"].append(_rms_norm(gkv, g_ckv, eps))
+        res["kr_row"].append(_rope(gr, cos[t], sin[t]))
+        res["x8"].append(x8)
+        res["c8"].append(c8)
+    return res

@@ -8,11 +8,12 @@ round-to-nearest-even; the rounded values are the inputs both the oracle and
 the HIP library consume.
 """
 
-from .configs import CONFIGS, MlaConfig, QkvConfig, get_config
+from .configs import CONFIGS, MlaConfig, PreConfig, QkvConfig, get_config
 from .gen import (
     Workload,
     make_workload,
     make_mla_workload,
+    make_preprocess_workload,
     make_qkv_workload,
     bf16_bits_from_f64,
     sub_workload,
@@ -21,11 +22,13 @@ from .gen import (
 __all__ = [
     "CONFIGS",
     "MlaConfig",
+    "PreConfig",
     "QkvConfig",
     "get_config",
     "Workload",
     "make_workload",
     "make_mla_workload",
+    "make_preprocess_workload",
     "make_qkv_workload",
     "bf16_bits_from_f64",
     "sub_workload",

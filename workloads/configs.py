@@ -99,6 +99,41 @@ class QkvConfig:
         return dataclasses.replace(self, **kw)
 
 
+@dataclass(frozen=True)
+class PreConfig:
+    """An MlaPreprocessV2 workload (aclnnMlaPreprocessV2): the same latent
+    dimensions as the MLA prolog, int8 W^DQKV and W^UQ_QR, and one RmsNorm
+    epsilon for its three norms."""
+    name: str
+    B: int
+    S: int
+    He: int
+    Hcq: int
+    N: int
+    D: int
+    Hckv: int
+    Dr: int
+    block_num: int
+    block_size: int
+    eps: float = 1e-6
+    n_skip: int = 0
+    seed: int = 0
+    layout: str = "TND"
+
+    kind = "pre"
+
+    @property
+    def T(self) -> int:
+        return self.B * self.S
+
+    @property
+    def slots(self) -> int:
+        return self.block_num * self.block_size
+
+    def replace(self, **kw) -> "PreConfig":
+        return dataclasses.replace(self, **kw)
+
+
 _DSV3 = dict(He=7168, Hcq=1536, N=128, D=128, Hckv=512, Dr=64)
 
 CONFIGS = {
@@ -180,6 +215,21 @@ CONFIGS = {
                                     He=512, Hcq=320, N=5, D=64, Hckv=96,
                                     Dr=32, block_num=4, block_size=128,
                                     n_skip=7, seed=2006, layout="BSH"),
+    # MlaPreprocessV2: tiny, ragged decode, DeepSeek-V3 dims with 32 heads
+    # (decode), and a T above the decode plan's limit (tiled kernels)
+    "pre_tiny": PreConfig("pre_tiny_T4", B=4, S=1, He=256, Hcq=128, N=4, D=32,
+                          Hckv=64, Dr=16, block_num=4, block_size=16,
+                          n_skip=1, seed=3001),
+    "pre_ragged": PreConfig("pre_ragged_T37", B=37, S=1, He=384, Hcq=192,
+                            N=6, D=64, Hckv=128, Dr=32, block_num=5,
+                            block_size=16, n_skip=3, seed=3002),
+    "pre_dsv3": PreConfig("pre_decode_T32_dsv3_N32", B=32, S=1,
+                          block_num=192, block_size=128, seed=3003,
+                          **{**_DSV3, "N": 32}),
+    "pre_large": PreConfig("pre_large_T300", B=3, S=100, He=512, Hcq=256,
+                           N=5, D=64, Hckv=96, Dr=32, block_num=4,
+                           block_size=128, n_skip=7, seed=3004,
+                           layout="BSH"),
     "qkv_ragged": QkvConfig("qkv_ragged_B3_S50", B=3, S=50, Nq=4, Nk=2, Nv=2,
                             D=128, block_num=3, block_size=64,
                             quant_mode="symmetric", seed=2101),

@@ -35,7 +35,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .configs import MlaConfig, QkvConfig, get_config
+from .configs import MlaConfig, PreConfig, QkvConfig, get_config
 
 
 def bf16_bits_from_f64(a) -> np.ndarray:
@@ -227,10 +227,73 @@ def make_qkv_workload(cfg: QkvConfig) -> Workload:
     return w
 
 
+def make_preprocess_workload(cfg: PreConfig) -> Workload:
+    """MlaPreprocessV2 inputs.  Draw order: x, W^DQKV, W^UQ_QR, W^UK, the
+    three gammas, the two biases, the two quant scales, the two dequant
+    scales, positions, index, cache pre-fill.
+
+    x ~ N(0, 1) bf16; int8 weights uniform on [-127, 127]; gammas
+    U(0.5, 1.5) bf16; biases U(-0.1, 0.1) fp32; each quant scale one fp32
+    value U(20, 30), so the normalised rows (|v| up to ~5) span most of the
+    int8 range and saturate only in the far tails; per-channel dequant
+    scales U(0.5, 1.5) / (quant scale * 73 * sqrt(K)) (73 is the standard
+    deviation of the uniform int8 draw), which brings the dequantised
+    products to unit size; W^UK ~ N(0, 1/sqrt(D)) bf16; caches pre-filled
+    N(0, 1) bf16.
+    """
+    rng = np.random.default_rng(cfg.seed)
+    T, He, Hcq, N, D, Hckv, Dr = (cfg.T, cfg.He, cfg.Hcq, cfg.N, cfg.D,
+                                  cfg.Hckv, cfg.Dr)
+    w = Workload(cfg)
+    A, Ty = w.arrays, w.dtypes
+
+    def put(name, arr, dt):
+        A[name] = arr
+        Ty[name] = dt
+
+    ntot = Hcq + Hckv + Dr
+    put("token_x", _store(rng.standard_normal((T, He)), "bf16"), "bf16")
+    put("weight_dqkv", rng.integers(-127, 128, size=(He, ntot)).astype(np.int8),
+        "int8")
+    put("weight_uq_qr",
+        rng.integers(-127, 128, size=(Hcq, N * (D + Dr))).astype(np.int8),
+        "int8")
+    put("weight_uk",
+        _store(rng.standard_normal((N, D, Hckv)) / np.sqrt(D), "bf16"), "bf16")
+    put("gamma_x", _store(rng.uniform(0.5, 1.5, He), "bf16"), "bf16")
+    put("gamma_cq", _store(rng.uniform(0.5, 1.5, Hcq), "bf16"), "bf16")
+    put("gamma_ckv", _store(rng.uniform(0.5, 1.5, Hckv), "bf16"), "bf16")
+    put("bias_x", _store(rng.uniform(-0.1, 0.1, He), "fp32"), "fp32")
+    put("bias_cq", _store(rng.uniform(-0.1, 0.1, Hcq), "fp32"), "fp32")
+    qsx = _store(rng.uniform(20.0, 30.0, 1), "fp32")
+    qsc = _store(rng.uniform(20.0, 30.0, 1), "fp32")
+    put("quant_scale_x", qsx, "fp32")
+    put("quant_scale_cq", qsc, "fp32")
+    put("dequant_scale_dqkv",
+        _store(rng.uniform(0.5, 1.5, ntot)
+               / (float(qsx[0]) * 73.0 * np.sqrt(He)), "fp32"), "fp32")
+    put("dequant_scale_uq_qr",
+        _store(rng.uniform(0.5, 1.5, N * (D + Dr))
+               / (float(qsc[0]) * 73.0 * np.sqrt(Hcq)), "fp32"), "fp32")
+    pos, cos, sin = _rope_tables(rng, T, Dr, "bf16")
+    w.extra["positions"] = pos
+    put("rope_cos", cos, "bf16")
+    put("rope_sin", sin, "bf16")
+    put("cache_index", _index(rng, T, cfg.slots, cfg.n_skip), "int64")
+    put("kv_cache", _store(rng.standard_normal(
+        (cfg.block_num, cfg.block_size, 1, Hckv)), "bf16"), "bf16")
+    put("kr_cache", _store(rng.standard_normal(
+        (cfg.block_num, cfg.block_size, 1, Dr)), "bf16"), "bf16")
+    return w
+
+
 def make_workload(key) -> Workload:
-    cfg = key if isinstance(key, (MlaConfig, QkvConfig)) else get_config(key)
+    cfg = key if isinstance(key, (MlaConfig, QkvConfig, PreConfig)) \
+        else get_config(key)
     if isinstance(cfg, MlaConfig):
         return make_mla_workload(cfg)
+    if isinstance(cfg, PreConfig):
+        return make_preprocess_workload(cfg)
     return make_qkv_workload(cfg)
 
 
