@@ -360,6 +360,89 @@ int mla_pack_weight_uq_qr(const void* src, void* dst, int64_t Hcq, int64_t N,
                           void* stream);
 
 /* ======================================================================= */
+/* MlaPreprocessV2                                                          */
+/* ======================================================================= */
+
+/* aclnnMlaPreprocessV2 (CANN API reference: interface function bullets,
+ * formula block).  Per token t, in the bullets' order:
+ *     x8 = RmsNormQuant(x)               (He: gamma_x, bias_x, quant_scale_x)
+ *     [h | g_kv | g_r] = x8 . W^DQKV     (int8 product, dequant per channel)
+ *     path 1: c8 = RmsNormQuant(h)       (Hcq: gamma_cq, bias_cq, quant_scale_cq)
+ *             y  = c8 . [W^UQ | W^QR]    (int8 product, dequant per channel)
+ *             path 3: query = y's q^C . W^UK per head
+ *             path 4: query_rope = RoPE(y's rope block)
+ *     path 2: path 5: RmsNorm(g_kv) (gamma_ckv) -> kv_cache[cache_index[t]]
+ *             path 6: RoPE(g_r)                   -> kr_cache[cache_index[t]]
+ * RmsNormQuant(v) = (gamma * v / RMS(v) + bias) * quant_scale as the
+ * formula block prints it, then rounded half to even and saturated to
+ * [-128, 127]; RMS(v) = sqrt(mean(v^2) + epsilon), one epsilon for all
+ * three norms.  The int8 products are exact integer sums times a
+ * per-output-channel fp32 dequant scale.  The page's parameter tables did
+ * not survive extraction: the names below are this library's.  Shapes as
+ * MlaPrologV2 (T = B*S tokens, Nkv = 1); He and Hcq multiples of 64, D of
+ * 32, Hckv of 16, Dr in {16, 32, 64}.  The page's ranges (B <= 256, He in
+ * [2048, 10240], N in {16, 32, 64, 128}, BlockNum 192, BlockSize 128)
+ * describe its own kernels; any shape above is accepted. */
+typedef struct MlaPreprocessV2Args {
+  uint32_t struct_size;      /* = sizeof(MlaPreprocessV2Args) */
+  int32_t weight_layout;     /* MLA_WEIGHT_* for weight_dqkv, weight_uq_qr,
+                                weight_uk (packed: mla_pack_weight for
+                                weight_dqkv, mla_pack_weight_uq_qr,
+                                mla_pack_weight_uk) */
+  int32_t flags;             /* MLA_FLAG_CHECK_INDEX, else 0 */
+  int32_t reserved0;         /* must be 0 */
+  int64_t B, S, He, Hcq, N, D, Hckv, Dr, block_num, block_size;
+  double epsilon;            /* RmsNorm epsilon, >= 0 */
+  float quant_scale_x;       /* RmsNormQuant scale of x (finite) */
+  float quant_scale_cq;      /* RmsNormQuant scale of the query latent */
+  const char* cache_mode;    /* NULL, "" or "PA_ND" */
+
+  /* ---- inputs (device) ---- */
+  const void* token_x;       /* (T, He) bf16 */
+  const void* gamma_x;       /* (He) bf16 */
+  const float* bias_x;       /* (He) fp32 */
+  const void* weight_dqkv;   /* (He, Hcq+Hckv+Dr) int8: [W^DQ | W^DKV | W^KR] */
+  const float* dequant_scale_dqkv;   /* (Hcq+Hckv+Dr) fp32 */
+  const void* gamma_cq;      /* (Hcq) bf16 */
+  const float* bias_cq;      /* (Hcq) fp32 */
+  const void* weight_uq_qr;  /* (Hcq, N*(D+Dr)) int8, column order as
+                                MlaPrologV2's weight_uq_qr */
+  const float* dequant_scale_uq_qr;  /* (N*(D+Dr)) fp32 */
+  const void* weight_uk;     /* (N, D, Hckv) bf16 */
+  const void* gamma_ckv;     /* (Hckv) bf16 */
+  const void* rope_sin;      /* (T, Dr) bf16 */
+  const void* rope_cos;      /* (T, Dr) bf16 */
+  const int64_t* cache_index;  /* (T) flat slot ids, -1 = skip */
+
+  /* ---- in/out (device) ---- */
+  void* kv_cache;            /* (BlockNum, BlockSize, 1, Hckv) bf16 */
+  void* kr_cache;            /* (BlockNum, BlockSize, 1, Dr) bf16 */
+  /* ---- outputs (device) ---- */
+  void* query;               /* (T, N, Hckv) bf16: q^N */
+  void* query_rope;          /* (T, N, Dr) bf16: q^R */
+  /* ---- optional diagnostics (device), NULL when not wanted: the int8
+   * codes of the two RmsNormQuant steps, (T, He) and (T, Hcq) ---- */
+  int8_t* dbg_x_int8;
+  int8_t* dbg_cq_int8;
+} MlaPreprocessV2Args;
+
+/* Host-only validation (no HIP call): QKVNR_OK or the first failing
+ * check's code (a non-finite quant scale: QKVNR_ERR_BAD_SCALE). */
+int mla_preprocess_v2_validate(const MlaPreprocessV2Args* args);
+
+/* Bytes of device workspace mla_preprocess_v2() needs; as
+ * mla_prolog_v2_workspace_size.  Host only. */
+int mla_preprocess_v2_workspace_size(const MlaPreprocessV2Args* args,
+                                     size_t* bytes);
+
+/* Run MlaPreprocessV2 on `stream` (workspace as mla_prolog_v2).  Errors:
+ * any validation code, QKVNR_ERR_WORKSPACE_TOO_SMALL, QKVNR_ERR_BAD_INDEX
+ * (MLA_FLAG_CHECK_INDEX), QKVNR_ERR_LAUNCH_FAILED; nothing is launched on
+ * a validation error. */
+int mla_preprocess_v2(const MlaPreprocessV2Args* args, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ======================================================================= */
 /* QkvRmsNormRopeCache                                                      */
 /* ======================================================================= */
 

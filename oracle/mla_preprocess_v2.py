@@ -67,7 +67,7 @@ def preprocess_query_from_codes(c8, w8_uqqr, dq_uqqr, wuk, cos, sin, N, D, Dr):
 
 
 def mla_preprocess_v2(arrays: dict, dtypes: dict, dims: dict,
-                      eps: float = 1e-6) -> dict:
+                      eps: float = 1e-6, x_int8=None, cq_int8=None) -> dict:
     """Run the whole operator on stored inputs (named as in the library's
     MlaPreprocessV2Args).  dims: He, Hcq, N, D, Hckv, Dr.
 
@@ -75,6 +75,13 @@ def mla_preprocess_v2(arrays: dict, dtypes: dict, dims: dict,
     updated kv_cache / kr_cache, the per-token cache rows, the int8 codes of
     both RmsNormQuant steps (x_int8, cq_int8) and the values they round
     (x_q, cq_q).
+
+    x_int8 / cq_int8, when given, replace the codes of the corresponding
+    RmsNormQuant step (the values it rounds are still computed and
+    returned), and the rest of the chain runs from them.  A code whose value
+    sits within rounding error of a .5 tie can legitimately round either
+    way in a lower precision; the GPU parity check re-runs the chain from
+    the GPU's own codes after checking that they differ only there.
     """
     He, Hcq, N, D, Hckv, Dr = (dims[k] for k in ("He", "Hcq", "N", "D",
                                                   "Hckv", "Dr"))
@@ -101,7 +108,8 @@ def mla_preprocess_v2(arrays: dict, dtypes: dict, dims: dict,
     out = {}
     # x -> RmsNormQuant -> x W^DQKV (downsampling)
     out["x_q"] = rmsnorm_quant_values(X, g_x, b_x, s_x, eps)
-    x8 = rmsnorm_quant(X, g_x, b_x, s_x, eps)
+    x8 = rmsnorm_quant(X, g_x, b_x, s_x, eps) if x_int8 is None \
+        else np.asarray(x_int8, np.int64).reshape(T, He)
     out["x_int8"] = x8
     Y1 = int_matmul_exact(x8, W1).astype(np.float64) * d1[None, :]
     # split into path 1 (query latent) and path 2 (key latent)
@@ -109,7 +117,8 @@ def mla_preprocess_v2(arrays: dict, dtypes: dict, dims: dict,
     g_kv, g_r = Y1[:, Hcq:Hcq + Hckv], Y1[:, Hcq + Hckv:]
     # path 1: RmsNormQuant -> W^UQ -> paths 3 (W^UK) and 4 (RoPE)
     out["cq_q"] = rmsnorm_quant_values(h, g_cq, b_cq, s_cq, eps)
-    c8 = rmsnorm_quant(h, g_cq, b_cq, s_cq, eps)
+    c8 = rmsnorm_quant(h, g_cq, b_cq, s_cq, eps) if cq_int8 is None \
+        else np.asarray(cq_int8, np.int64).reshape(T, Hcq)
     out["cq_int8"] = c8
     out["query"], out["query_rope"] = preprocess_query_from_codes(
         c8, W2, d2, Wuk, cos, sin, N, D, Dr)

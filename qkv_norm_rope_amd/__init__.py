@@ -9,7 +9,9 @@ Python names mirror the C ABI in include/qkvnr.h:
   packing of a (K, N) weight into the MFMA-native K16 blocked layout the
   prolog streams;
 * :func:`qkv_rmsnorm_rope_cache` - the fused qkv split / RmsNorm / RoPE /
-  quant / scatter op.
+  quant / scatter op;
+* :func:`mla_preprocess_v2` - MlaPreprocessV2 (RmsNormQuant of x, int8
+  W^DQKV, RmsNormQuant of the query latent, int8 W^UQ, W^UK, RoPE, caches).
 
 All work runs in the HIP library ``lib/libqkvnr.so``; build it with
 ``python -m qkv_norm_rope_amd.build``.
@@ -27,6 +29,7 @@ from ._binding import (  # noqa: F401
     MLA_WEIGHT_PACKED_K16,
     QKV_FLAG_CHECK_INPUTS,
     QKV_QUANT,
+    MlaPreprocessV2Args,
     MlaPrologV2Args,
     PreparedMlaPrologV2,
     QkvRmsNormRopeCacheArgs,
@@ -38,6 +41,7 @@ from ._binding import (  # noqa: F401
     mla_probe_read,
     mla_pack_weight_uk,
     mla_pack_weight_uq_qr,
+    mla_preprocess_v2,
     mla_prolog_v2,
     mla_prolog_v2_args,
     mla_prolog_v2_kernels,

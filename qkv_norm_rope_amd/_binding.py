@@ -47,6 +47,8 @@ EXPORTS = (
     "mla_pack_weight_uq_qr", "mla_pack_weight_uk",
     "qkv_rmsnorm_rope_cache_validate", "qkv_rmsnorm_rope_cache",
     "mla_probe_read", "mla_probe_mfma_bf16",
+    "mla_preprocess_v2_validate", "mla_preprocess_v2_workspace_size",
+    "mla_preprocess_v2",
 )
 
 _vp = ctypes.c_void_p
@@ -94,6 +96,25 @@ class QkvRmsNormRopeCacheArgs(ctypes.Structure):
     ]
 
 
+class MlaPreprocessV2Args(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32), ("weight_layout", ctypes.c_int32),
+        ("flags", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("B", _i64), ("S", _i64), ("He", _i64), ("Hcq", _i64), ("N", _i64),
+        ("D", _i64), ("Hckv", _i64), ("Dr", _i64), ("block_num", _i64),
+        ("block_size", _i64), ("epsilon", ctypes.c_double),
+        ("quant_scale_x", ctypes.c_float), ("quant_scale_cq", ctypes.c_float),
+        ("cache_mode", ctypes.c_char_p),
+        ("token_x", _vp), ("gamma_x", _vp), ("bias_x", _vp),
+        ("weight_dqkv", _vp), ("dequant_scale_dqkv", _vp),
+        ("gamma_cq", _vp), ("bias_cq", _vp), ("weight_uq_qr", _vp),
+        ("dequant_scale_uq_qr", _vp), ("weight_uk", _vp), ("gamma_ckv", _vp),
+        ("rope_sin", _vp), ("rope_cos", _vp), ("cache_index", _vp),
+        ("kv_cache", _vp), ("kr_cache", _vp), ("query", _vp),
+        ("query_rope", _vp), ("dbg_x_int8", _vp), ("dbg_cq_int8", _vp),
+    ]
+
+
 class QkvnrError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -136,6 +157,14 @@ def load_library(path: str = None) -> ctypes.CDLL:
         ctypes.POINTER(MlaPrologV2Args), ctypes.POINTER(ctypes.c_size_t)]
     lib.mla_prolog_v2_validate.restype = ctypes.c_int
     lib.mla_prolog_v2_validate.argtypes = [ctypes.POINTER(MlaPrologV2Args)]
+    lib.mla_preprocess_v2_validate.restype = ctypes.c_int
+    lib.mla_preprocess_v2_validate.argtypes = [ctypes.POINTER(MlaPreprocessV2Args)]
+    lib.mla_preprocess_v2_workspace_size.restype = ctypes.c_int
+    lib.mla_preprocess_v2_workspace_size.argtypes = [
+        ctypes.POINTER(MlaPreprocessV2Args), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_preprocess_v2.restype = ctypes.c_int
+    lib.mla_preprocess_v2.argtypes = [ctypes.POINTER(MlaPreprocessV2Args), _vp,
+                                      ctypes.c_size_t, _vp]
     lib.mla_prolog_v2_no_alloc.restype = ctypes.c_int
     lib.mla_prolog_v2_no_alloc.argtypes = [ctypes.POINTER(MlaPrologV2Args), _vp]
     lib.mla_prolog_v2.restype = ctypes.c_int
@@ -654,6 +683,130 @@ class PreparedMlaPrologV2:
                                      _stream(stream))
         _check(rc, "mla_prolog_v2")
         return self.query, self.query_rope
+
+
+# ---------------------------------------------------------------------------
+# MlaPreprocessV2
+# ---------------------------------------------------------------------------
+
+def _validate_pre(a: "MlaPreprocessV2Args", t: dict):
+    """Element types and counts of the MlaPreprocessV2 tensors for the
+    dimensions in `a` (include/qkvnr.h; packed weights hold whole
+    32-column blocks)."""
+    T = a.B * a.S
+    bf, i8, f32 = torch.bfloat16, torch.int8, torch.float32
+    cols = _pad32 if a.weight_layout == MLA_WEIGHT_PACKED_K16 else int
+    ntot = a.Hcq + a.Hckv + a.Dr
+    slots = a.block_num * a.block_size
+    _expect(t.get("token_x"), bf, T * a.He, "token_x")
+    _expect(t.get("gamma_x"), bf, a.He, "gamma_x")
+    _expect(t.get("bias_x"), f32, a.He, "bias_x")
+    _expect(t.get("weight_dqkv"), i8, a.He * cols(ntot), "weight_dqkv")
+    _expect(t.get("dequant_scale_dqkv"), f32, ntot, "dequant_scale_dqkv")
+    _expect(t.get("gamma_cq"), bf, a.Hcq, "gamma_cq")
+    _expect(t.get("bias_cq"), f32, a.Hcq, "bias_cq")
+    _expect(t.get("weight_uq_qr"), i8, a.Hcq * cols(a.N * (a.D + a.Dr)),
+            "weight_uq_qr")
+    _expect(t.get("dequant_scale_uq_qr"), f32, a.N * (a.D + a.Dr),
+            "dequant_scale_uq_qr")
+    _expect(t.get("weight_uk"), bf, a.N * a.D * cols(a.Hckv), "weight_uk")
+    _expect(t.get("gamma_ckv"), bf, a.Hckv, "gamma_ckv")
+    _expect(t.get("rope_sin"), bf, T * a.Dr, "rope_sin")
+    _expect(t.get("rope_cos"), bf, T * a.Dr, "rope_cos")
+    _expect(t.get("cache_index"), torch.int64, T, "cache_index")
+    _expect(t.get("kv_cache"), bf, slots * a.Hckv, "kv_cache")
+    _expect(t.get("kr_cache"), bf, slots * a.Dr, "kr_cache")
+    _expect(t.get("query"), bf, T * a.N * a.Hckv, "query")
+    _expect(t.get("query_rope"), bf, T * a.N * a.Dr, "query_rope")
+    _expect(t.get("dbg_x_int8"), i8, T * a.He, "x_int8")
+    _expect(t.get("dbg_cq_int8"), i8, T * a.Hcq, "cq_int8")
+
+
+def mla_preprocess_v2(token_x, gamma_x, bias_x, quant_scale_x, weight_dqkv,
+                      dequant_scale_dqkv, gamma_cq, bias_cq, quant_scale_cq,
+                      weight_uq_qr, dequant_scale_uq_qr, weight_uk, gamma_ckv,
+                      rope_sin, rope_cos, cache_index, kv_cache, kr_cache, *,
+                      epsilon=1e-6, weight_layout=MLA_WEIGHT_PACKED_K16,
+                      query=None, query_rope=None, workspace=None,
+                      return_codes=False, debug_check_index=False,
+                      cache_mode=None, stream=None):
+    """Run MlaPreprocessV2; kv_cache and kr_cache are updated in place.
+
+    token_x (T, He) or (B, S, He) bf16; weight_dqkv (He, Hcq+Hckv+Dr) int8
+    (packed with mla_pack_weight unless weight_layout is MLA_WEIGHT_ND);
+    weight_uq_qr (Hcq, N*(D+Dr)) int8 (mla_pack_weight_uq_qr); weight_uk
+    (N, D, Hckv) bf16 (mla_pack_weight_uk); quant_scale_x / quant_scale_cq
+    Python floats.  Returns (query, query_rope), plus the int8 codes of the
+    two RmsNormQuant steps, (T, He) and (T, Hcq), when return_codes is set.
+    """
+    lib = load_library()
+    He = token_x.shape[-1]
+    lead = tuple(token_x.shape[:-1])
+    T = token_x.numel() // He if He else 0
+    N, D = weight_uk.shape[0], weight_uk.shape[1]
+    Hcq, Hckv = gamma_cq.shape[-1], gamma_ckv.shape[-1]
+    Dr = rope_sin.shape[-1]
+    dev = token_x.device
+    if query is None:
+        query = torch.empty(lead + (N, Hckv), dtype=torch.bfloat16, device=dev)
+    if query_rope is None:
+        query_rope = torch.empty(lead + (N, Dr), dtype=torch.bfloat16,
+                                 device=dev)
+    dx = dc = None
+    if return_codes:
+        dx = torch.empty((T, He), dtype=torch.int8, device=dev)
+        dc = torch.empty((T, Hcq), dtype=torch.int8, device=dev)
+    a = MlaPreprocessV2Args()
+    a.struct_size = ctypes.sizeof(MlaPreprocessV2Args)
+    a.weight_layout = int(weight_layout)
+    a.flags = MLA_FLAG_CHECK_INDEX if debug_check_index else 0
+    B, S = (lead[0], lead[1]) if len(lead) == 2 else (T, 1)
+    a.B, a.S, a.He, a.Hcq, a.N, a.D = int(B), int(S), int(He), int(Hcq), \
+        int(N), int(D)
+    a.Hckv, a.Dr = int(Hckv), int(Dr)
+    a.block_num, a.block_size = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    a.epsilon = float(epsilon)
+    a.quant_scale_x, a.quant_scale_cq = float(quant_scale_x), \
+        float(quant_scale_cq)
+    a.cache_mode = cache_mode.encode() if cache_mode else None
+    if T > 0:
+        a.token_x, a.rope_sin, a.rope_cos = _ptr(token_x), _ptr(rope_sin), \
+            _ptr(rope_cos)
+        a.cache_index, a.query = _ptr(cache_index), _ptr(query)
+        a.query_rope = _ptr(query_rope)
+        a.dbg_x_int8, a.dbg_cq_int8 = _ptr(dx), _ptr(dc)
+    a.gamma_x, a.bias_x = _ptr(gamma_x), _ptr(bias_x)
+    a.weight_dqkv, a.dequant_scale_dqkv = _ptr(weight_dqkv), \
+        _ptr(dequant_scale_dqkv)
+    a.gamma_cq, a.bias_cq = _ptr(gamma_cq), _ptr(bias_cq)
+    a.weight_uq_qr, a.dequant_scale_uq_qr = _ptr(weight_uq_qr), \
+        _ptr(dequant_scale_uq_qr)
+    a.weight_uk, a.gamma_ckv = _ptr(weight_uk), _ptr(gamma_ckv)
+    if kv_cache.numel():
+        a.kv_cache = _ptr(kv_cache)
+    if kr_cache.numel():
+        a.kr_cache = _ptr(kr_cache)
+    _validate_pre(a, dict(
+        token_x=token_x, gamma_x=gamma_x, bias_x=bias_x,
+        weight_dqkv=weight_dqkv, dequant_scale_dqkv=dequant_scale_dqkv,
+        gamma_cq=gamma_cq, bias_cq=bias_cq, weight_uq_qr=weight_uq_qr,
+        dequant_scale_uq_qr=dequant_scale_uq_qr, weight_uk=weight_uk,
+        gamma_ckv=gamma_ckv, rope_sin=rope_sin, rope_cos=rope_cos,
+        cache_index=cache_index, kv_cache=kv_cache, kr_cache=kr_cache,
+        query=query, query_rope=query_rope, dbg_x_int8=dx, dbg_cq_int8=dc))
+    n = ctypes.c_size_t(0)
+    _check(lib.mla_preprocess_v2_workspace_size(ctypes.byref(a),
+                                                 ctypes.byref(n)),
+           "mla_preprocess_v2_workspace_size")
+    if workspace is None or \
+            workspace.numel() * workspace.element_size() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    _check(lib.mla_preprocess_v2(ctypes.byref(a), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "mla_preprocess_v2")
+    if return_codes:
+        return query, query_rope, dx, dc
+    return query, query_rope
 
 
 # ---------------------------------------------------------------------------

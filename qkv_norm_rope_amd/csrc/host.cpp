@@ -102,6 +102,19 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   return pl;
 }
 
+MlaPlan make_preprocess_plan(const MlaPrologV2Args* m) {
+  MlaPlan pl = make_mla_plan(m);
+  const int64_t T = m->B * m->S;
+  if (T == 0) return pl;
+  size_t off = pl.total;
+  pl.off_prex8 = off;
+  off += align256(static_cast<size_t>(T) * static_cast<size_t>(m->He));
+  pl.off_presx = off;
+  off += align256(static_cast<size_t>(T) * sizeof(float));
+  pl.total = off;
+  return pl;
+}
+
 }  // namespace qkvnr
 
 namespace {
@@ -288,6 +301,76 @@ int validate_qkv(const QkvRmsNormRopeCacheArgs* a) {
 }
 
 
+// MlaPreprocessV2 as the equivalent prolog arguments: full quantisation
+// with bf16 caches, W^DQKV as weight_dq (the launcher splits it), the c^Q
+// bias in smooth_scales_cq, and placeholders (never read) where the
+// launcher substitutes workspace regions (x's codes and their unit token
+// scales).
+MlaPrologV2Args preprocess_as_prolog(const MlaPreprocessV2Args* a) {
+  MlaPrologV2Args m{};
+  m.struct_size = sizeof(MlaPrologV2Args);
+  m.quant_mode = MLA_QUANT_FULL_KV_BF16;
+  m.weight_layout = a->weight_layout;
+  m.flags = a->flags;
+  m.B = a->B;
+  m.S = a->S;
+  m.He = a->He;
+  m.Hcq = a->Hcq;
+  m.N = a->N;
+  m.D = a->D;
+  m.Hckv = a->Hckv;
+  m.Dr = a->Dr;
+  m.Nkv = 1;
+  m.block_num = a->block_num;
+  m.block_size = a->block_size;
+  m.rmsnorm_epsilon_cq = a->epsilon;
+  m.rmsnorm_epsilon_ckv = a->epsilon;
+  m.cache_mode = a->cache_mode;
+  m.token_x = a->token_x;
+  m.weight_dq = a->weight_dqkv;
+  m.weight_dkv_kr = a->weight_dqkv;
+  m.weight_uq_qr = a->weight_uq_qr;
+  m.weight_uk = a->weight_uk;
+  m.rmsnorm_gamma_cq = a->gamma_cq;
+  m.rmsnorm_gamma_ckv = a->gamma_ckv;
+  m.rope_sin = a->rope_sin;
+  m.rope_cos = a->rope_cos;
+  m.cache_index = a->cache_index;
+  m.dequant_scale_x = a->dequant_scale_dqkv;  // placeholder: unit scales
+  m.dequant_scale_w_dq = a->dequant_scale_dqkv;
+  // the W^DKV | W^KR part of the scales (an out-of-range Hcq is refused by
+  // the validation; the pointer is then not formed)
+  m.dequant_scale_w_dkv_kr = a->dequant_scale_dqkv != nullptr && a->Hcq > 0 && a->Hcq <= kDimCap
+                                 ? a->dequant_scale_dqkv + a->Hcq
+                                 : a->dequant_scale_dqkv;
+  m.dequant_scale_w_uq_qr = a->dequant_scale_uq_qr;
+  m.smooth_scales_cq = a->bias_cq;
+  m.kv_cache = a->kv_cache;
+  m.kr_cache = a->kr_cache;
+  m.query = a->query;
+  m.query_rope = a->query_rope;
+  m.dbg_cq_int8 = a->dbg_cq_int8;
+  return m;
+}
+
+int validate_pre(const MlaPreprocessV2Args* a) {
+  if (a == nullptr) return QKVNR_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(MlaPreprocessV2Args) || a->reserved0 != 0)
+    return QKVNR_ERR_BAD_STRUCT;
+  if (a->flags & ~MLA_FLAG_CHECK_INDEX) return QKVNR_ERR_BAD_MODE;
+  if (!isfinite(a->quant_scale_x) || !isfinite(a->quant_scale_cq)) return QKVNR_ERR_BAD_SCALE;
+  const MlaPrologV2Args m = preprocess_as_prolog(a);
+  const int rc = validate_mla(&m);
+  if (rc != QKVNR_OK || a->B * a->S == 0) return rc;
+  if (a->gamma_x == nullptr || a->bias_x == nullptr || a->bias_cq == nullptr ||
+      a->dequant_scale_dqkv == nullptr)
+    return QKVNR_ERR_NULL_ARG;
+  if (!aligned16(a->gamma_x) || !aligned16(a->bias_x) || !aligned16(a->bias_cq) ||
+      (a->dbg_x_int8 && !aligned8(a->dbg_x_int8)))
+    return QKVNR_ERR_BAD_ALIGNMENT;
+  return QKVNR_OK;
+}
+
 // Host copy of a device array of n elements (debug checks only).
 template <typename V>
 int fetch(std::vector<V>& out, const V* dev, int64_t n, void* stream) {
@@ -406,6 +489,37 @@ int mla_prolog_v2(const MlaPrologV2Args* args, void* workspace, size_t workspace
     if (rc != QKVNR_OK) return rc;
   }
   return launch_mla_prolog_v2(args, plan, workspace, stream);
+}
+
+int mla_preprocess_v2_validate(const MlaPreprocessV2Args* args) { return validate_pre(args); }
+
+int mla_preprocess_v2_workspace_size(const MlaPreprocessV2Args* args, size_t* bytes) {
+  if (bytes == nullptr) return QKVNR_ERR_NULL_ARG;
+  *bytes = 0;
+  const int rc = validate_pre(args);
+  if (rc != QKVNR_OK) return rc;
+  const MlaPrologV2Args m = preprocess_as_prolog(args);
+  *bytes = make_preprocess_plan(&m).total;
+  return QKVNR_OK;
+}
+
+int mla_preprocess_v2(const MlaPreprocessV2Args* args, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int rc = validate_pre(args);
+  if (rc != QKVNR_OK) return rc;
+  if (args->B * args->S == 0) return QKVNR_OK;
+  const MlaPrologV2Args m = preprocess_as_prolog(args);
+  const MlaPlan plan = make_preprocess_plan(&m);
+  if (workspace_bytes < plan.total) return QKVNR_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return QKVNR_ERR_NULL_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QKVNR_ERR_BAD_ALIGNMENT;
+  if (args->flags & MLA_FLAG_CHECK_INDEX) {
+    rc = debug_check_mla(&m, stream);
+    if (rc != QKVNR_OK) return rc;
+  }
+  const PreprocessExtra pre{args->gamma_x, args->bias_x, args->quant_scale_x,
+                            args->quant_scale_cq, args->dbg_x_int8};
+  return launch_mla_prolog_v2(&m, plan, workspace, stream, &pre);
 }
 
 int mla_prolog_v2_no_alloc(const MlaPrologV2Args* args, void* stream) {

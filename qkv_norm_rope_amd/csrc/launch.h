@@ -23,9 +23,22 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
                        int elem_bytes, int64_t rope_col0, int64_t rope_dim, void* stream,
                        bool kperm = false);
 
-// Launch the prolog; arguments validated, workspace large enough.
+// MlaPreprocessV2 on the prolog's full-quantisation kernels: RmsNormQuant of
+// x first (into the workspace), then the int8 path with the static c^Q
+// quant finish.  `a` then holds the equivalent prolog arguments: token_x
+// the bf16 x, weight_dq the whole packed (or ND) W^DQKV, smooth_scales_cq
+// the c^Q bias.
+struct PreprocessExtra {
+  const void* gamma_x;  // (He) bf16
+  const float* bias_x;  // (He) fp32
+  float qs_x, qs_cq;    // the two RmsNormQuant scales
+  int8_t* dbg_x_int8;   // optional (T, He) copy of x's codes
+};
+
+// Launch the prolog (pre == nullptr) or MlaPreprocessV2; arguments
+// validated, workspace large enough.
 int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& plan, void* workspace,
-                         void* stream);
+                         void* stream, const PreprocessExtra* pre = nullptr);
 
 // The same on this library's fixed per-device scratch array (no_alloc.hip);
 // plan.total <= MLA_NO_ALLOC_SCRATCH_BYTES already checked.

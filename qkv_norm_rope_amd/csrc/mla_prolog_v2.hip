@@ -1387,6 +1387,10 @@ struct FinishParams {
   const float* sx;
   const float* sw_dq;
   const float* sw_dkv;
+  // MlaPreprocessV2 (QM = 4): c^Q codes = sat(rne((RmsNorm(h) + bias) * qs_cq))
+  // with the bias in `smooth`; the per-token scale the up projection applies
+  // is 1.
+  float qs_cq;
 };
 
 constexpr int FIN_MAX_THREADS = 1024;
@@ -1432,7 +1436,9 @@ __device__ __forceinline__ void unpack_bf16x8(uint4 w, float* f) {
 
 // QM: 0 none, 1 c^Q quantised with bf16 caches (partial or full
 // quantisation), 2 c^Q quantised with int8 kv and kr caches (partial),
-// 3 c^Q quantised with an int8 kv cache and a bf16 kr cache (full).
+// 3 c^Q quantised with an int8 kv cache and a bf16 kr cache (full),
+// 4 c^Q quantised statically (MlaPreprocessV2's RmsNormQuant: bias, then
+// one per-tensor scale) with bf16 caches.
 // MAXS: most splits summed (ksplit <= MAXS); fewer keep more workgroups
 // resident (the large-T plan splits at most 4 ways).
 template <int QM, int MAXS = FIN_MAXSPLIT>
@@ -1526,7 +1532,15 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
     if (c0 < p.Hcq) {
       float g[8];
       unpack_bf16x8(pa, g);
-      if (QM == 0) {
+      if (QM == 4) {
+        // aclnnMlaPreprocessV2 RmsNormQuant: (RmsNorm(h) + bias) * scale
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = sat_rne((x[e] * rq * g[e] + pf[e]) * p.qs_cq, -128, 127);
+        const uint2 w = make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
+        st8(p.cq_i8 + cq_off(c0, 32), w);
+        if (p.dbg_cq_i8) st8(p.dbg_cq_i8 + t * p.Hcq + c0, w);
+      } else if (QM == 0) {
         st16(p.cq_bf16 + cq_off(c0, 16),
              make_uint4(pack_bf16x2(x[0] * rq * g[0], x[1] * rq * g[1]),
                         pack_bf16x2(x[2] * rq * g[2], x[3] * rq * g[3]),
@@ -1585,6 +1599,10 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
     }
   }
   if (QM == 0) return;
+  if (QM == 4) {
+    if (threadIdx.x == 0) gst(p.cq_scale + t, 1.0f);  // static quant: no per-token scale
+    return;
+  }
 
   // Partial quant: per-token dynamic int8 of the smoothed c^Q (max-abs/127).
   const float am = block_reduce2<1>(make_float2(amax, 0.f), red).x;
@@ -1602,6 +1620,49 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
     gst(p.cq_scale + t, sc);
     if (p.dbg_cq_scale) gst(p.dbg_cq_scale + t, sc);
   }
+}
+
+// ---------------------------------------------------------------------------
+// MlaPreprocessV2 first step (aclnnMlaPreprocessV2: x is processed by
+// RmsNormQuant before the W^DQKV product; formula block): per token,
+// codes = sat(rne((gamma * x / RMS(x) + bias) * scale)) in [-128, 127],
+// written row-major (T, He) for the int8 down projection, which reads the
+// token's dequant scale from sx: 1 here (the per-channel dequant scales of
+// W^DQKV carry the step).  One 256-thread workgroup per token, He a
+// multiple of 64; x is read twice (the second pass hits the cache).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm_quant_x(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ gamma,
+                                                         const float* __restrict__ bias,
+                                                         float qs, float eps, int He,
+                                                         int8_t* __restrict__ x8,
+                                                         float* __restrict__ sx,
+                                                         int8_t* __restrict__ dbg) {
+  __shared__ float2 red[4];
+  const int64_t t = blockIdx.x;
+  const uint16_t* row = x + t * He;
+  float ss = 0.f;
+  for (int c = 8 * static_cast<int>(threadIdx.x); c < He; c += 8 * 256) {
+    float v[8];
+    unpack_bf16x8(ld16(row + c), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+  }
+  const float tot = block_reduce2<0>(make_float2(ss, 0.f), red).x;
+  const float r = 1.0f / __builtin_sqrtf(tot / static_cast<float>(He) + eps);
+  for (int c = 8 * static_cast<int>(threadIdx.x); c < He; c += 8 * 256) {
+    float v[8], g[8], b[8];
+    unpack_bf16x8(ld16(row + c), v);
+    unpack_bf16x8(ld16(gamma + c), g);
+    ld8f(bias + c, b);
+    int q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = sat_rne((v[e] * r * g[e] + b[e]) * qs, -128, 127);
+    const uint2 w = make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
+    st8(x8 + t * He + c, w);
+    if (dbg) st8(dbg + t * He + c, w);
+  }
+  if (threadIdx.x == 0) gst(sx + t, 1.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -1858,7 +1919,7 @@ int launch_pack_weight(const void* src, void* dst, int64_t batch, int64_t K, int
 }
 
 int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* workspace,
-                         void* stream) {
+                         void* stream, const PreprocessExtra* pre) {
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t T = a->B * a->S;
   if (T == 0) return QKVNR_OK;
@@ -1867,7 +1928,8 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   const bool q8out = a->quant_mode == MLA_QUANT_FULL_KV_INT8;
   // finish variant: 0 none, 1 c^Q quant + bf16 caches, 2 + int8 kv / kr,
   // 3 + int8 kv and bf16 kr (k_down_finish's QM)
-  const int qm = a->quant_mode == MLA_QUANT_FULL_KV_BF16 ? 1
+  const int qm = pre != nullptr                              ? 4
+                 : a->quant_mode == MLA_QUANT_FULL_KV_BF16 ? 1
                  : a->quant_mode == MLA_QUANT_FULL_KV_INT8 ? 3
                                                            : a->quant_mode;
   char* ws = static_cast<char*>(workspace);
@@ -1875,11 +1937,17 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
 
   const uint4 *wdq, *wdkvkr, *wuqqr, *wuk;
+  // MlaPreprocessV2's merged W^DQKV packs as one matrix: with Hcq a whole
+  // number of 32-column blocks, its W^DKV | W^KR columns start at block
+  // Hcq / 32, the layout of two separately packed matrices back to back.
+  const int64_t dkv_chunks = (a->Hcq / 32) * (a->He / (xq ? 16 : 8)) * 32;
   if (a->weight_layout == MLA_WEIGHT_ND) {
     const int eb_down = xq ? 1 : 2;
-    int rc = launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, eb_down, a->Hcq,
-                                0, st);
-    if (rc == QKVNR_OK)
+    int rc = pre != nullptr
+                 ? launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, ntot, 1, ntot, 0, st)
+                 : launch_pack_weight(a->weight_dq, ws + pl.off_wdq, 1, a->He, a->Hcq, eb_down,
+                                      a->Hcq, 0, st);
+    if (rc == QKVNR_OK && pre == nullptr)
       rc = launch_pack_weight(a->weight_dkv_kr, ws + pl.off_wdkvkr, 1, a->He, a->Hckv + a->Dr,
                               eb_down,
                               a->Hckv + a->Dr, 0, st);
@@ -1891,12 +1959,12 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
                               st, /*kperm=*/true);
     if (rc != QKVNR_OK) return rc;
     wdq = reinterpret_cast<const uint4*>(ws + pl.off_wdq);
-    wdkvkr = reinterpret_cast<const uint4*>(ws + pl.off_wdkvkr);
+    wdkvkr = pre != nullptr ? wdq + dkv_chunks : reinterpret_cast<const uint4*>(ws + pl.off_wdkvkr);
     wuqqr = reinterpret_cast<const uint4*>(ws + pl.off_wuqqr);
     wuk = reinterpret_cast<const uint4*>(ws + pl.off_wuk);
   } else {
     wdq = static_cast<const uint4*>(a->weight_dq);
-    wdkvkr = static_cast<const uint4*>(a->weight_dkv_kr);
+    wdkvkr = pre != nullptr ? wdq + dkv_chunks : static_cast<const uint4*>(a->weight_dkv_kr);
     wuqqr = static_cast<const uint4*>(a->weight_uq_qr);
     wuk = static_cast<const uint4*>(a->weight_uk);
   }
@@ -1918,7 +1986,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   const bool frag = pl.skinny || pl.gemm256;
   const int64_t mblocks = pl.rows / 32;
   GemmParams g1{};
-  g1.A = a->token_x;
+  g1.A = pre != nullptr ? static_cast<const void*>(ws + pl.off_prex8) : a->token_x;
   g1.lda = a->He;
   g1.B0 = wdq;
   g1.N0 = a->Hcq;
@@ -2016,10 +2084,11 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   f.dbg_cq_i8 = a->dbg_cq_int8;
   f.dbg_cq_scale = a->dbg_cq_scale;
   if (xq) {
-    f.sx = a->dequant_scale_x;
+    f.sx = pre != nullptr ? reinterpret_cast<const float*>(ws + pl.off_presx) : a->dequant_scale_x;
     f.sw_dq = a->dequant_scale_w_dq;
     f.sw_dkv = a->dequant_scale_w_dkv_kr;
   }
+  if (pre != nullptr) f.qs_cq = pre->qs_cq;
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
   const dim3 fin_block(static_cast<unsigned>(fin_threads(ntot)));
 
@@ -2049,11 +2118,19 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       launch(Lf, k_down_finish<1>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
     else if (qm == 2)
       launch(Lf, k_down_finish<2>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
-    else
+    else if (qm == 3)
       launch(Lf, k_down_finish<3>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
+    else
+      launch(Lf, k_down_finish<4>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
   };
 
   const int nh = static_cast<int>(a->N);
+  if (pre != nullptr)  // RmsNormQuant of x: the down projection's int8 input
+    launch(L0, k_rmsnorm_quant_x, dim3(static_cast<unsigned>(T)), dim3(256), 0,
+           static_cast<const uint16_t*>(a->token_x), static_cast<const uint16_t*>(pre->gamma_x),
+           pre->bias_x, pre->qs_x, static_cast<float>(a->rmsnorm_epsilon_cq),
+           static_cast<int>(a->He), reinterpret_cast<int8_t*>(ws + pl.off_prex8),
+           reinterpret_cast<float*>(ws + pl.off_presx), pre->dbg_x_int8);
   mark(MLA_PHASE_START);
   if (pl.skinny) {
     g1.ntiles0 = static_cast<int>((g1.N0 + kA1Cols - 1) / kA1Cols);

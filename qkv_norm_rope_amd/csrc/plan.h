@@ -35,11 +35,17 @@ struct MlaPlan {
   size_t off_part, off_cq, off_cq_scale, off_qc;
   size_t off_qn;      // FULL_KV_INT8: q^N in fp32 before its per-head quant
   size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
+  size_t off_prex8, off_presx;  // MlaPreprocessV2: RmsNormQuant codes of x
+                                // (T, He) int8 and their unit token scales
   int64_t rows;       // token rows padded to the plan's 32-row blocks
   size_t total;
 };
 
 // Arguments must have passed validation.
 MlaPlan make_mla_plan(const MlaPrologV2Args* a);
+
+// MlaPreprocessV2 runs on the full-quantisation plan of the equivalent
+// prolog arguments `m`, plus room for the RmsNormQuant codes of x.
+MlaPlan make_preprocess_plan(const MlaPrologV2Args* m);
 
 }  // namespace qkvnr

@@ -316,3 +316,86 @@ def check_qkv(w, out, before):
     stats["v_cache"] = check_cache(before["v_cache"], out["v_cache"], index,
                                    ref["v_rows"], int8, "v_cache")
     return stats
+
+
+# ---------------------------------------------------------------------------
+# MlaPreprocessV2
+# ---------------------------------------------------------------------------
+
+def run_preprocess_gpu(w, dev=None, layout="packed", bsh=False):
+    """Run MlaPreprocessV2 on workload w; returns dict of device tensors
+    (query, query_rope, caches, and the two steps' int8 codes)."""
+    cfg = w.cfg
+    d = dev if dev is not None else upload(w)
+    if layout == "packed":
+        w1 = qn.mla_pack_weight(d["weight_dqkv"])
+        w2 = qn.mla_pack_weight_uq_qr(d["weight_uq_qr"], cfg.N, cfg.D, cfg.Dr)
+        wuk = qn.mla_pack_weight_uk(d["weight_uk"])
+        lay = qn.MLA_WEIGHT_PACKED_K16
+    else:
+        w1, w2, wuk = d["weight_dqkv"], d["weight_uq_qr"], d["weight_uk"]
+        lay = qn.MLA_WEIGHT_ND
+    x = d["token_x"]
+    if bsh:
+        x = x.view(cfg.B, cfg.S, cfg.He)
+    q, qr, x8, c8 = qn.mla_preprocess_v2(
+        x, d["gamma_x"], d["bias_x"], float(w.arrays["quant_scale_x"][0]), w1,
+        d["dequant_scale_dqkv"], d["gamma_cq"], d["bias_cq"],
+        float(w.arrays["quant_scale_cq"][0]), w2, d["dequant_scale_uq_qr"],
+        wuk, d["gamma_ckv"], d["rope_sin"], d["rope_cos"], d["cache_index"],
+        d["kv_cache"], d["kr_cache"], epsilon=cfg.eps, weight_layout=lay,
+        return_codes=True)
+    return {"query": q, "query_rope": qr, "kv_cache": d["kv_cache"],
+            "kr_cache": d["kr_cache"], "x_int8": x8, "cq_int8": c8}
+
+
+def _codes_near_ties(gpu, ref_codes, values, what, window=1e-2):
+    """GPU int8 codes within +/-1 of the oracle's, differing only where the
+    oracle's unrounded value sits within `window` of a .5 tie."""
+    diff = gpu != ref_codes
+    assert np.abs(gpu - ref_codes).max(initial=0) <= 1, f"{what}: code off by >1"
+    v = np.abs(values)
+    tie = np.abs(v - np.floor(v) - 0.5)
+    assert (tie[diff] < window).all(), f"{what}: a code flips away from a tie"
+    return int(diff.sum())
+
+
+def check_preprocess(w, out, before):
+    """MlaPreprocessV2 parity, conditioned on the GPU's own int8 codes (the
+    A-9 rule of the prolog, applied to both RmsNormQuant steps): (i) x's
+    codes within +/-1 of the oracle's, differing only near a rounding tie;
+    (ii) the query latent's codes likewise against the oracle re-run from
+    the GPU's x codes; (iii) query, query_rope and every cache row against
+    the oracle re-run from both of the GPU's code sets, under the
+    0.02 * max(1, |ref|) rule; placement as for the prolog."""
+    cfg = w.cfg
+    dims = mla_dims(cfg)
+    ref = oracle.mla_preprocess_v2(w.arrays, w.dtypes, dims, cfg.eps)
+    x8 = out["x_int8"].cpu().numpy().astype(np.int64)
+    stats = {"x_code_flips": _codes_near_ties(x8, ref["x_int8"], ref["x_q"],
+                                              "x codes")}
+    if stats["x_code_flips"]:
+        ref = oracle.mla_preprocess_v2(w.arrays, w.dtypes, dims, cfg.eps,
+                                       x_int8=x8)
+    c8 = out["cq_int8"].cpu().numpy().astype(np.int64)
+    stats["cq_code_flips"] = _codes_near_ties(c8, ref["cq_int8"], ref["cq_q"],
+                                              "c^Q codes")
+    if stats["cq_code_flips"]:
+        ref = oracle.mla_preprocess_v2(w.arrays, w.dtypes, dims, cfg.eps,
+                                       x_int8=x8, cq_int8=c8)
+    T = cfg.T
+    stats["query"] = assert_close(
+        dev_to_f64(out["query"].reshape(T, cfg.N, cfg.Hckv)), ref["query"],
+        "query")
+    stats["query_rope"] = assert_close(
+        dev_to_f64(out["query_rope"].reshape(T, cfg.N, cfg.Dr)),
+        ref["query_rope"], "query_rope")
+    index = w.arrays["cache_index"].reshape(-1)
+    if cfg.slots > 0:
+        stats["kv_cache"] = check_cache(before["kv_cache"], out["kv_cache"],
+                                        index, ref["kv_rows"], False,
+                                        "kv_cache")
+        stats["kr_cache"] = check_cache(before["kr_cache"], out["kr_cache"],
+                                        index, ref["kr_rows"], False,
+                                        "kr_cache")
+    return stats

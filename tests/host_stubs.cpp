@@ -14,7 +14,8 @@ int launch_pack_weight(const void*, void*, int64_t, int64_t, int64_t, int, int64
   return QKVNR_ERR_LAUNCH_FAILED;
 }
 
-int launch_mla_prolog_v2(const MlaPrologV2Args*, const MlaPlan&, void*, void*) {
+int launch_mla_prolog_v2(const MlaPrologV2Args*, const MlaPlan&, void*, void*,
+                         const PreprocessExtra*) {
   return QKVNR_ERR_LAUNCH_FAILED;
 }
 

@@ -547,3 +547,85 @@ def test_no_alloc_entry_point_host_checks():
         assert qn.mla_prolog_v2_workspace_size(mla_args(T=T, quant=q)) <= \
             qn.MLA_NO_ALLOC_SCRATCH_BYTES, (q, T)
     assert qn.status_string(-13).startswith("the call needs more than")
+
+
+# ---- MlaPreprocessV2 -------------------------------------------------------
+
+def pre_args(T=32, He=7168, Hcq=1536, N=32, D=128, Hckv=512, Dr=64, bn=192,
+             bs=128, layout=b.MLA_WEIGHT_PACKED_K16):
+    a = b.MlaPreprocessV2Args()
+    a.struct_size = ctypes.sizeof(b.MlaPreprocessV2Args)
+    a.weight_layout = layout
+    a.B, a.S = T, 1
+    a.He, a.Hcq, a.N, a.D, a.Hckv, a.Dr = He, Hcq, N, D, Hckv, Dr
+    a.block_num, a.block_size = bn, bs
+    a.epsilon = 1e-6
+    a.quant_scale_x, a.quant_scale_cq = 25.0, 21.0
+    for f in ("token_x", "gamma_x", "bias_x", "weight_dqkv",
+              "dequant_scale_dqkv", "gamma_cq", "bias_cq", "weight_uq_qr",
+              "dequant_scale_uq_qr", "weight_uk", "gamma_ckv", "rope_sin",
+              "rope_cos", "cache_index", "kv_cache", "kr_cache", "query",
+              "query_rope"):
+        setattr(a, f, fake())
+    return a
+
+
+def pre_validate(a):
+    return b.load_library().mla_preprocess_v2_validate(ctypes.byref(a))
+
+
+def test_preprocess_valid_args_pass():
+    assert pre_validate(pre_args()) == 0
+    assert pre_validate(pre_args(T=4, He=256, Hcq=128, N=4, D=32, Hckv=64,
+                                 Dr=16, bn=4, bs=16)) == 0
+    assert pre_validate(pre_args(T=4096)) == 0
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "struct_size", 8), -8),
+    (lambda a: setattr(a, "reserved0", 1), -8),
+    (lambda a: setattr(a, "flags", 2), -3),
+    (lambda a: setattr(a, "quant_scale_x", float("inf")), -12),
+    (lambda a: setattr(a, "quant_scale_cq", float("nan")), -12),
+    (lambda a: setattr(a, "He", 7168 + 32), -4),    # int8 K: multiple of 64
+    (lambda a: setattr(a, "Hcq", 1536 + 32), -4),
+    (lambda a: setattr(a, "Hcq", -64), -2),
+    (lambda a: setattr(a, "Dr", 48), -4),
+    (lambda a: setattr(a, "epsilon", -1.0), -7),
+    (lambda a: setattr(a, "cache_mode", b"PA_NZ"), -4),
+    (lambda a: setattr(a, "gamma_x", None), -1),
+    (lambda a: setattr(a, "bias_x", None), -1),
+    (lambda a: setattr(a, "bias_cq", None), -1),
+    (lambda a: setattr(a, "dequant_scale_dqkv", None), -1),
+    (lambda a: setattr(a, "dequant_scale_uq_qr", None), -1),
+    (lambda a: setattr(a, "weight_dqkv", None), -1),
+    (lambda a: setattr(a, "kv_cache", None), -1),
+    (lambda a: setattr(a, "bias_x", fake() + 4), -9),
+    (lambda a: setattr(a, "token_x", fake() + 2), -9),
+])
+def test_preprocess_validation_errors(mutate, code):
+    a = pre_args()
+    mutate(a)
+    assert pre_validate(a) == code
+
+
+def test_preprocess_workspace_and_empty():
+    lib = b.load_library()
+    n = ctypes.c_size_t(0)
+    a = pre_args()
+    assert lib.mla_preprocess_v2_workspace_size(ctypes.byref(a),
+                                                ctypes.byref(n)) == 0
+    # at least the prolog's full-quantisation workspace plus x's codes
+    assert n.value >= 32 * 7168
+    small = ctypes.c_size_t(0)
+    a2 = pre_args(T=4, He=256, Hcq=128, N=4, D=32, Hckv=64, Dr=16, bn=4, bs=16)
+    lib.mla_preprocess_v2_workspace_size(ctypes.byref(a2), ctypes.byref(small))
+    assert 0 < small.value < n.value
+    assert lib.mla_preprocess_v2(ctypes.byref(a), fake(), n.value - 256,
+                                 None) == -6
+    e = pre_args(T=0)
+    for f in ("token_x", "rope_sin", "rope_cos", "cache_index", "query",
+              "query_rope"):
+        setattr(e, f, None)
+    assert pre_validate(e) == 0
+    assert lib.mla_preprocess_v2(ctypes.byref(e), None, 0, None) == 0
