@@ -20,6 +20,8 @@ Prints ONE JSON line.  Besides the headline value it carries:
 * step_roofline - the whole call's algorithmic bytes over the step time;
 * prefill - the same prolog at T = 4096 (bf16 MFMA-bound);
 * qkv_rmsnorm_rope_cache - the fused qkv op on its (B=64, S=128) workload;
+* preprocess_decode - MlaPreprocessV2 at the DeepSeek-V3 dims (32 heads),
+  decode T = 32;
 * cpu_baseline - the float64 NumPy oracle timed on this host on a bounded
   sample of the decode workload.
 """
@@ -53,6 +55,7 @@ def parse():
     ap.add_argument("--no-partial-quant", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--no-preprocess", action="store_true")
     ap.add_argument("--regions", type=int, default=5,
                     help="separately timed regions of --steps calls each "
                          "(the value is their median)")
@@ -131,6 +134,19 @@ def uqqr_flops(c):
 
 def uk_flops(c):
     return 2 * c.T * c.N * c.D * c.Hckv
+
+
+def preprocess_bytes(c):
+    """MlaPreprocessV2 algorithmic bytes: bf16 x, gammas, W^UK, cos/sin,
+    outputs and cache rows; int8 W^DQKV and W^UQ_QR; fp32 biases, dequant
+    scales and the two quant scales; int64 index."""
+    ntot = c.Hcq + c.Hckv + c.Dr
+    nuq = c.N * (c.D + c.Dr)
+    weights = c.He * ntot + c.Hcq * nuq + c.N * c.D * c.Hckv * 2
+    params = (c.He + c.Hcq + c.Hckv) * 2 + (c.He + c.Hcq + ntot + nuq + 2) * 4
+    per_tok = (c.He * 2 + 2 * c.Dr * 2 + 8 + c.N * c.Hckv * 2
+               + c.N * c.Dr * 2 + (c.Hckv + c.Dr) * 2)
+    return weights + params + c.T * per_tok
 
 
 def qkv_bytes(c, n_valid):
@@ -429,6 +445,75 @@ def bench_qkv(steps, warmup, torch, qn, gh, make_workload, regions=5):
             "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "timing": f"median of {regions} HIP-graph replays of {steps} "
                       "calls each"}
+
+
+def bench_preprocess(steps, warmup, rotate, torch, qn, gh, make_workload,
+                     regions=5):
+    """MlaPreprocessV2 at the DeepSeek-V3 dims with 32 heads, decode
+    T = 32: `regions` HIP-graph replays of one graph holding `steps` calls
+    over `rotate` independent input sets (packed weights); median, min and
+    max ms per call."""
+    w = make_workload("pre_dsv3")
+    cfg = w.cfg
+    d0 = gh.upload(w)
+    base = dict(d0)
+    base["weight_dqkv"] = qn.mla_pack_weight(d0["weight_dqkv"])
+    base["weight_uq_qr"] = qn.mla_pack_weight_uq_qr(d0["weight_uq_qr"], cfg.N,
+                                                    cfg.D, cfg.Dr)
+    base["weight_uk"] = qn.mla_pack_weight_uk(d0["weight_uk"])
+    del d0
+    sets = [base] + [{k: v.clone() for k, v in base.items()}
+                     for _ in range(rotate - 1)]
+    qsx = float(w.arrays["quant_scale_x"][0])
+    qsc = float(w.arrays["quant_scale_cq"][0])
+    for st in sets:
+        st["query"] = torch.empty((cfg.T, cfg.N, cfg.Hckv),
+                                  dtype=torch.bfloat16, device="cuda")
+        st["query_rope"] = torch.empty((cfg.T, cfg.N, cfg.Dr),
+                                       dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+
+    def call(st):
+        qn.mla_preprocess_v2(
+            st["token_x"], st["gamma_x"], st["bias_x"], qsx,
+            st["weight_dqkv"], st["dequant_scale_dqkv"], st["gamma_cq"],
+            st["bias_cq"], qsc, st["weight_uq_qr"], st["dequant_scale_uq_qr"],
+            st["weight_uk"], st["gamma_ckv"], st["rope_sin"], st["rope_cos"],
+            st["cache_index"], st["kv_cache"], st["kr_cache"],
+            epsilon=cfg.eps, query=st["query"], query_rope=st["query_rope"],
+            workspace=ws)
+
+    for i in range(warmup):
+        call(sets[i % rotate])
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            call(sets[i % rotate])
+    g.replay()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(regions):
+        torch.cuda.synchronize()
+        _hold_gpu(torch, 2.0)
+        t0.record(s)
+        g.replay()
+        t1.record(s)
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) / steps)
+    del g
+    ms, lo, hi = _spread(times)
+    nbytes = preprocess_bytes(cfg)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "tokens_per_s": cfg.T / (ms * 1e-3),
+            "ms_per_step": ms, "ms_min": lo, "ms_max": hi, "steps": steps,
+            "regions": regions, "algorithmic_bytes": nbytes,
+            "achieved_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "timing": f"median of {regions} HIP-graph replays of {steps} "
+                      f"calls over {rotate} rotating input sets"}
 
 
 def measure_peaks(torch, qn, mib=1024):
@@ -751,6 +836,14 @@ def main():
         del fsets
         torch.cuda.empty_cache()
         progress(f"full quant T=32: {fms * 1e3:.2f} us/step")
+
+    if not args.no_preprocess:
+        out["preprocess_decode"] = bench_preprocess(
+            args.steps, max(5, args.warmup // 2), args.rotate, torch, qn, gh,
+            make_workload, regions=args.regions)
+        progress("preprocess T=32: %.2f us/step"
+                 % (out["preprocess_decode"]["ms_per_step"] * 1e3))
+        torch.cuda.empty_cache()
 
     if not args.no_qkv:
         out["qkv_rmsnorm_rope_cache"] = bench_qkv(

@@ -93,3 +93,14 @@ def test_up_projection_bytes_match_the_workload_tensors():
               + c.T * c.N * c.Dr * 2)
     assert bench.uqqr_bytes(c) == expect == 76_029_952
     assert bench.uqqr_workspace_bytes(c) == c.T * c.Hcq * 2 + c.T * c.N * c.D * 2
+
+
+def test_preprocess_bytes_match_the_workload_tensors():
+    # every input read once (weights, parameters, x, cos/sin, index), the
+    # outputs written once, one bf16 cache row pair per token (all valid)
+    w = make_workload("pre_dsv3")
+    c, a = w.cfg, w.arrays
+    read = sum(a[k].nbytes for k in a if k not in ("kv_cache", "kr_cache"))
+    written = c.T * (c.N * c.Hckv * 2 + c.N * c.Dr * 2 + (c.Hckv + c.Dr) * 2)
+    assert (a["cache_index"] >= 0).all()
+    assert bench.preprocess_bytes(c) == read + written
