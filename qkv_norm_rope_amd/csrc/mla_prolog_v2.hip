@@ -960,16 +960,28 @@ __device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
 // bf16, registers 8h..8h+7 are then directly the token-side operand of a
 // 16-k step of the W^UK product -- in exactly the k order mla_pack_weight_uk
 // gives W^UK -- so q^C never leaves the registers.
+// Waves of a k_gemm workgroup: 2 x 2 of (TM/2) x 128, or for the fused
+// q^C + W^UK tiles 4 x 2 of 64 x 128 (two waves per SIMD: 128 accumulators
+// each, so one wave's MFMAs run while the other waits on LDS or a barrier).
+template <int EPI>
+constexpr int gemm_waves() { return EPI == EPI_QN ? 8 : 4; }
+
 template <int EPI, int TM, int NBUF, int DH = 0>
-__global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
   typedef Epilogue<A_BF16, EPI == EPI_QN ? EPI_UQQR : EPI> Epi;
   constexpr bool SWAP = EPI == EPI_QN;
   static_assert(!SWAP || (TM == 256 && DH == 128 && NBUF == 4),
                 "fused W^UK product: 256-row tiles, one 128-wide head per wave");
+  static_assert(TM != 256 || NBUF == 4, "256-row tiles: the double-buffered pipeline");
+  constexpr int NWV = gemm_waves<EPI>();  // waves per workgroup
+  constexpr int WR = NWV / 2;             // wave rows (two wave columns of 128)
+  constexpr int TPW = TM / WR;            // tokens (rows) per wave
   constexpr int MA = TM / 32;   // A blocks per k-step
-  constexpr int MI = TM / 64;   // m-blocks per wave
-  constexpr int AW = MA / 4;    // A blocks loaded per wave per k-step
-  constexpr int LPW = 2 * (AW + 2);  // loads per wave per stage
+  constexpr int MI = TPW / 32;  // m-blocks per wave
+  constexpr int AW = MA / NWV;  // A blocks loaded per wave per k-step
+  constexpr int BW = 8 / NWV;   // B blocks loaded per wave per k-step
+  static_assert(AW >= 1 && BW >= 1, "every wave loads A and B blocks");
+  constexpr int LPW = 2 * (AW + BW);  // loads per wave per stage
   static_assert(TM == 256 || TM == 128, "tile height");
   static_assert(NBUF >= 3 && NBUF <= 4, "stage buffers");
   // Stage t: A blocks in sa<t>, B blocks in sb<t>, per k-step.  (Separate
@@ -1030,15 +1042,15 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
   const int nst = s_hi > s_lo ? (s_hi - s_lo) / 2 : 0;
 
   // B: the tile's 8 column blocks; blocks past N read as zeros.  Wave w
-  // loads blocks 2w and 2w+1 of each k-step.
+  // loads blocks BW*w .. BW*w+BW-1 of each k-step.
   // (Both resources span this tile only, so their byte ranges fit 32 bits.)
   const int64_t nblk = (N + 31) / 32;
   const int64_t nb0 = n0 / 32;
   const int64_t nbt = nblk - nb0 < 8 ? nblk - nb0 : 8;
   const rsrc_t rb = make_rsrc(B + nb0 * KC * 32, static_cast<uint32_t>(nbt * KC * 512));
-  uint32_t vb[2], va[AW];
+  uint32_t vb[BW], va[AW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) vb[j] = lane * 16u + static_cast<uint32_t>((2 * w + j) * KC) * 512u;
+  for (int j = 0; j < BW; ++j) vb[j] = lane * 16u + static_cast<uint32_t>((BW * w + j) * KC) * 512u;
   // A in fragment layout (1 KB per 32-row block and k-step); wave w loads
   // blocks AW*w .. AW*w+AW-1.  Blocks past the buffer read as zeros.
   // (Gathering row-major A with the same loads, 32 rows per load, made the
@@ -1062,7 +1074,7 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < AW; ++j) dma16(ra, va[j], s * 1024u, &SA(bufc)[ks][AW * w + j][0]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) dma16(rb, vb[j], s * 1024u, &SB(bufc)[ks][2 * w + j][0]);
+      for (int j = 0; j < BW; ++j) dma16(rb, vb[j], s * 1024u, &SB(bufc)[ks][BW * w + j][0]);
     }
   };
 
@@ -1112,7 +1124,74 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
     compute(bufc);
   };
 
-  if (nst > 0) {
+  // 256-row tiles run one wave per SIMD, so nothing else hides the LDS
+  // read latency of a k-step's fragments or the stage barrier.  Their
+  // pipeline double-buffers the fragments: each step reads k-step 1 of its
+  // stage while k-step 0's MFMAs run, and its barrier sits between the two
+  // k-steps (after it, all of the stage's fragments are in registers, so
+  // the stage's buffer is refilled at once and the next stage's k-step 0
+  // fragments load under k-step 1's MFMAs).  One stage more is in flight:
+  // the buffer refilled at step t is stage t's own, with stage t + NBUF.
+  if constexpr (TM == 256) {
+    uint4 fa0[MI], fb0[4], fa1[MI], fb1[4];
+    auto rd = [&](auto bufc, int ks, uint4 (&fa)[MI], uint4 (&fb)[4]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) fa[i] = SA(bufc)[ks][MI * wm + i][lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = SB(bufc)[ks][4 * wn + j][lane];
+    };
+    auto mm = [&](const uint4 (&fa)[MI], const uint4 (&fb)[4]) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (SWAP)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[j]), as_bf16x8(fa[i]),
+                                                                 acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]),
+                                                                 acc[i][j], 0, 0, 0);
+        }
+    };
+    // Stage t in buffer BUF = t % NBUF; on entry fa0/fb0 hold its k-step 0.
+    // The barrier's vmcnt allows the NBUF - 2 stages issued after stage
+    // t + 1 to stay in flight; its lgkmcnt(0) also covers this stage's
+    // k-step 1 reads, so every wave is done with buffer BUF after it.
+    auto step2 = [&](auto bufc, int t) {
+      constexpr int BUF = decltype(bufc)::value;
+      // (sched_barrier pins each group in place: the compiler would sink
+      // the MFMAs, which touch no memory, below the barrier)
+      rd(bufc, 1, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fa0, fb0);
+      __builtin_amdgcn_sched_barrier(0);
+      vm_barrier<LPW*(NBUF - 2)>();
+      issue(bufc, t + NBUF);
+      rd(std::integral_constant<int, (BUF + 1) % NBUF>{}, 0, fa0, fb0);  // stage t + 1
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nst > 0) {
+      issue(C0{}, 0);
+      issue(C1{}, 1);
+      issue(C2{}, 2);
+      issue(C3{}, 3);
+      vm_barrier<LPW*(NBUF - 1)>();  // stage 0 landed
+      rd(C0{}, 0, fa0, fb0);
+      const int nstb = nst / NBUF * NBUF;
+      for (int t = 0; t < nstb; t += NBUF) {
+        step2(C0{}, t);
+        step2(C1{}, t + 1);
+        step2(C2{}, t + 2);
+        step2(C3{}, t + 3);
+      }
+      const int rem = nst - nstb;
+      if (rem >= 1) step2(C0{}, nstb);
+      if (rem >= 2) step2(C1{}, nstb + 1);
+      if (rem >= 3) step2(C2{}, nstb + 2);
+    }
+  } else if (nst > 0) {
     issue(C0{}, 0);
     issue(C1{}, 1);
     if constexpr (NBUF == 4) issue(C2{}, 2);
@@ -1171,7 +1250,9 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
     const int64_t nblk2 = (p.uk_N + 31) / 32;
     const int npass = static_cast<int>((nblk2 + PB - 1) / PB);
     const int64_t head0 = n0 / DH;
-    const int hs = w >> 1, kw = 4 * (w & 1);  // this wave's load share: head hs, k-steps kw..kw+3
+    // this wave's load share of a pass: head hs, k-steps kw .. kw+KPW-1
+    constexpr int KPW = 8 / (NWV / 2);
+    const int hs = w / (NWV / 2), kw = KPW * (w % (NWV / 2));
     const rsrc_t ruk = make_rsrc(p.Buk + (head0 + hs) * p.uk_bstride,
                                  static_cast<uint32_t>(nblk2 * KC2 * 512));
     auto pbuf = [&](auto bc, int jb) -> uint4* {
@@ -1185,15 +1266,17 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
         const uint32_t vo = lane * 16u + static_cast<uint32_t>(nb2 * KC2) * 512u;
         uint4* dst = pbuf(bc, jb);  // jb is static
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
+        for (int k4 = 0; k4 < KPW; ++k4)
           dma16(ruk, vo, static_cast<uint32_t>(kw + k4) * 1024u, dst + (hs * 8 + kw + k4) * 64);
       }
     };
     const int64_t head = head0 + wn;
-    // Output staging: a 4 KB slice per wave of its own array.
-    __shared__ uint4 qn_stage[4][256];
-    char* stg = reinterpret_cast<char*>(&qn_stage[w][0]);
-    const bool rows_in = m0 + (TM / 2) * wm + TM / 2 - 1 < p.M;  // all of this wave's tokens are rows
+    // Output staging: a 4 KB slice per wave of stage buffers 2 and 3's A
+    // arrays (the passes use buffers 0 and 1; every load into LDS has
+    // landed).
+    static_assert(sizeof(sa2) == 4 * 4096, "staging: four waves per A array");
+    char* stg = reinterpret_cast<char*>(w < 4 ? &sa2[0][0][0] : &sa3[0][0][0]) + (w & 3) * 4096;
+    const bool rows_in = m0 + TPW * wm + TPW - 1 < p.M;  // all of this wave's tokens are rows
     // Returns whether the pass issued exactly SPP stores (all in range).
     auto pass_uk = [&](auto bc, int pp) -> bool {
       f32x16_t o[MI][PB];
@@ -1238,7 +1321,7 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
           const int tr = (64 / CPR) * k + lane / CPR;
           const uint4 v = *reinterpret_cast<const uint4*>(stg + tr * (16 * CPR) +
                                                           ((cc ^ (tr & (CPR - 1))) * 16));
-          const int64_t m = m0 + (TM / 2) * wm + 32 * i + tr;
+          const int64_t m = m0 + TPW * wm + 32 * i + tr;
           if (full || (m < p.M && nc < p.uk_N))
             // plain stores: streaming ones measured 27 us slower here
             st16(p.q_out + m * p.q_ld + head * p.q_bstride + nc, v);
@@ -1323,7 +1406,7 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int it = lane + 64 * (k + u);
-        const int64_t m = m0 + (TM / 2) * wm + 32 * i + (it >> 4);
+        const int64_t m = m0 + TPW * wm + 32 * i + (it >> 4);
         const int64_t gcol = n0 + 128 * wn + (it & 15) * 8;
         pre[u] = typename Epi::Pre{};
         if (need_pre && m < p.M && gcol < N) pre[u] = Epi::prefetch(p, m, gcol);
@@ -1333,7 +1416,7 @@ __global__ __launch_bounds__(256, TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
         const int it = lane + 64 * (k + u);
         const int row = it >> 4;
         const int c0 = (it & 15) * 8;
-        const int64_t m = m0 + (TM / 2) * wm + 32 * i + row;
+        const int64_t m = m0 + TPW * wm + 32 * i + row;
         const int64_t gcol = n0 + 128 * wn + c0;
         if (m >= p.M || gcol >= N) continue;
         uint32_t raw[8], rawp[8];
@@ -2210,7 +2293,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gq.q_bstride = g8.q_bstride;
       const unsigned mt = static_cast<unsigned>((T + 255) / 256);
       launch(L8, k_gemm<EPI_QN, 256, 4, 128>, dim3(static_cast<unsigned>(ND / G_TN), mt, 1),
-             dim3(256), 0, gq);
+             dim3(64 * gemm_waves<EPI_QN>()), 0, gq);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
       launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, dim3(nt6, mt2, 1), dim3(256), 0, g6);
