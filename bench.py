@@ -36,6 +36,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, TOP/s
 DECODE_TARGET_FRAC = 0.60      # decode T=32: fraction of HBM peak on bytes moved
 PREFILL_TARGET_FRAC = 0.50     # prefill T=4096: fraction of bf16 MFMA peak
 METRIC = ("MLA-prolog tokens/s at decode T=32 & prefill T=4096; "
@@ -122,10 +123,17 @@ def uqqr_bytes(c):
         2 * c.Dr * 2 + c.N * c.Dr * 2)
 
 
-def uqqr_workspace_bytes(c):
+def uqqr_workspace_bytes(c, merged=False):
     """Workspace bytes the up-projection launch also moves: c^Q (bf16) in,
-    q^C (bf16) out."""
-    return c.T * (c.Hcq * 2 + c.N * c.D * 2)
+    q^C (bf16) out, and with the W^UK product in the same launch q^C read
+    back once per 128-column W^UK tile of each head."""
+    back = (c.Hckv + 127) // 128 * c.T * c.N * c.D * 2 if merged else 0
+    return c.T * (c.Hcq * 2 + c.N * c.D * 2) + back
+
+
+def uk_bytes(c):
+    """Algorithmic bytes of the W^UK product: W^UK in, the query out."""
+    return c.N * c.D * c.Hckv * 2 + c.T * c.N * c.Hckv * 2
 
 
 def uqqr_flops(c):
@@ -655,7 +663,7 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import qkv_norm_rope_amd as qn
     from workloads import device as gh
-    from workloads import make_workload
+    from workloads import get_config, make_workload
 
     qn.load_library()  # fail loudly without the HIP library
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -673,7 +681,9 @@ def main():
     kernel_ms = r["kernel_ms"]
     step_bytes = mla_bytes(cfg)
     a6_ms = kernel_ms[2]  # the up projection's own start/stop events
-    a6_bytes = uqqr_bytes(cfg)
+    # bf16 decode at T <= 32 runs the W^UK product inside the same launch
+    merged = kernel_ms[3] is None
+    a6_bytes = uqqr_bytes(cfg) + (uk_bytes(cfg) if merged else 0)
     a6_gbs = a6_bytes / (a6_ms * 1e-3) / 1e9
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
     rec = recorded_traffic()
@@ -714,11 +724,13 @@ def main():
                                 "of the same calls",
                    "phase_us": "events recorded between the launches "
                                "(kernel plus dispatch)"},
-        "roofline": {"kernel": "up projection c^Q.[W^UQ|W^QR] + RoPE q^R",
+        "roofline": {"kernel": "up projection c^Q.[W^UQ|W^QR] + RoPE q^R"
+                               + (" + per-head q^C.W^UK (one launch)"
+                                  if merged else ""),
                      "bound": "hbm", "achieved": a6_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": a6_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": a6_bytes,
-                     "workspace_bytes": uqqr_workspace_bytes(cfg),
+                     "workspace_bytes": uqqr_workspace_bytes(cfg, merged),
                      "avg_launch_us": a6_ms * 1e3,
                      "duration": "average over the eager region's calls of "
                                  "the kernel's own start/stop events"},
@@ -783,6 +795,41 @@ def main():
         del psets
         torch.cuda.empty_cache()
         progress(f"prefill T=4096: {pms * 1e3:.1f} us/step")
+
+    # ---- partial quantisation at prefill size: T = 4096 ---------------------
+    if not args.no_prefill and not args.no_partial_quant:
+        wpq = make_workload(get_config(2).replace(
+            name="mla_prefill_T4096_dsv3_partial_kv_int8",
+            quant_mode="partial_kv_int8", seed=1102))
+        pqc = wpq.cfg
+        pqsets = prepare_mla_sets(wpq, 1, torch, qn, gh)
+        psteps = max(10, args.steps // 2)
+        pqr = run_mla(pqc, pqsets, psteps, max(2, args.warmup // 2), torch, qn,
+                      graph=False, regions=3)
+        pqms = pqr["ms"]
+        # bf16 products (x.W^DQ_KR, q^C.W^UK) at the bf16 peak, the int8
+        # c^Q.W^UQ_QR at the int8 peak
+        t_peak = (2 * pqc.T * (pqc.He * (pqc.Hcq + pqc.Hckv + pqc.Dr)
+                               + pqc.N * pqc.D * pqc.Hckv)) / (BF16_PEAK_TFLOPS * 1e12) \
+            + uqqr_flops(pqc) / (INT8_PEAK_TOPS * 1e12)
+        out["prefill_partial_quant"] = {
+            "workload": pqc.name, "quant_mode": pqc.quant_mode,
+            "tokens_per_s": pqc.T / (pqms * 1e-3), "ms_per_step": pqms,
+            "ms_min": pqr["ms_min"], "ms_max": pqr["ms_max"],
+            "steps": psteps, "regions": pqr["regions"],
+            "algorithmic_ops": mla_flops(pqc),
+            "mixed_peak_frac": t_peak / (pqms * 1e-3),
+            "mixed_peak": "bf16 products at 2.5 PFLOP/s, the int8 up "
+                          "projection at 5.0 POP/s",
+            "kernel_us": dict(zip(qn.MLA_KERNELS,
+                                  [None if k is None else k * 1e3
+                                   for k in pqr["kernel_ms"]])),
+            "timing": f"median of {pqr['regions']} eager regions of {psteps} "
+                      "calls each",
+        }
+        del pqsets
+        torch.cuda.empty_cache()
+        progress(f"prefill partial quant T=4096: {pqms * 1e3:.1f} us/step")
 
     # ---- partial quantisation, int8 caches: T = 64, 32 heads -------------
     if not args.no_partial_quant:

@@ -257,7 +257,10 @@ typedef struct MlaPrologV2Args {
 
 /* The main kernels of one call, for kernel_events.  With the large-T plan
  * that fuses the W^UK product, MLA_KERNEL_UQQR is the q^R-column launch and
- * MLA_KERNEL_UK the q^C-column launch with the fused W^UK product. */
+ * MLA_KERNEL_UK the q^C-column launch with the fused W^UK product.  With
+ * the bf16 decode plan for T <= 32 and D <= 128, MLA_KERNEL_UQQR is one
+ * launch that runs the up projection and the W^UK product, and
+ * MLA_KERNEL_UK is not launched (mla_prolog_v2_kernels reports which). */
 enum {
   MLA_KERNEL_DOWN = 0,  /* x . [W^DQ | W^DKV_KR] */
   MLA_KERNEL_NORM = 1,  /* RmsNorms, c^Q quant, RoPE k^R, cache scatter */

@@ -176,4 +176,19 @@ __device__ __forceinline__ uint4 bld16_nt(rsrc_t r, uint32_t voff, uint32_t soff
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Device-scope accesses (cache policy bit 4, sc1) for data handed from one
+// workgroup to another within a launch: the store writes through to the
+// level shared by every XCD before it counts as complete, and the load is
+// served from that level, never from a stale copy in this XCD's L2.
+constexpr int kDeviceScope = 16;
+__device__ __forceinline__ uint4 bld16_dev(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                          static_cast<int>(soff), kDeviceScope);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void bst8_dev(rsrc_t r, uint32_t voff, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(voff), 0, kDeviceScope);
+}
+
 }  // namespace qkvnr

@@ -71,6 +71,10 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   // 128 q^C columns are exactly one head (D = 128) and the q^C columns end
   // on a tile boundary.
   pl.fuse_uk = pl.gemm256 && a->D == 128 && (a->N * a->D) % G_TN == 0;
+  // Decode with one row block in bf16 runs the up projection and the W^UK
+  // product as one launch when a head's q^C and W^UK slices fit a wave's
+  // registers (D <= 128).
+  pl.merge_uk = pl.skinny && pl.mb == 1 && !quant && a->D <= 128;
   size_t off = 0;
   if (a->weight_layout == MLA_WEIGHT_ND) {
     // packed copies: columns padded to whole 32-column blocks
@@ -98,6 +102,8 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
     off += align256(static_cast<size_t>(T * a->N * a->Hckv) * sizeof(float));
   pl.off_xfrag = off;
   if (pl.gemm256) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
+  pl.off_sync = off;
+  if (pl.merge_uk) off += static_cast<size_t>(a->N) * SYNC_STRIDE * 4;
   pl.total = T > 0 ? off : 0;
   return pl;
 }
@@ -470,8 +476,15 @@ int mla_prolog_v2_kernels(const MlaPrologV2Args* args, uint32_t* mask) {
   *mask = 0;
   const int rc = validate_mla(args);
   if (rc != QKVNR_OK) return rc;
-  // Every plan launches each of the main kernels once when there are tokens.
-  if (args->B * args->S > 0) *mask = (1u << MLA_KERNEL_COUNT) - 1u;
+  // Every plan launches each of the main kernels once when there are
+  // tokens, except that the merged decode launch runs the W^UK product
+  // inside the up projection's kernel.
+  if (args->B * args->S > 0) {
+    *mask = (1u << MLA_KERNEL_COUNT) - 1u;
+    const MlaPlan pl = make_mla_plan(args);
+    if (pl.merge_uk) *mask &= ~(1u << MLA_KERNEL_UK);
+
+  }
   return QKVNR_OK;
 }
 

@@ -75,6 +75,12 @@ struct GemmParams {
   int qc_frag;            // write q^C in per-head fragment layout
   int64_t qc_D;           // head dim D (fragment layout)
   int64_t qc_mblocks;     // 32-row blocks per head (fragment layout)
+  int qc_coherent;        // bf16 fragment q^C with device-scope stores, for a
+                          // consumer in the same launch (k_decode_tail)
+  // Handoff words of the merged decode launch that this launch zeroes
+  // first (workgroup 0), SYNC_STRIDE words apart; NULL: none.
+  unsigned* zero_words;
+  int zero_count;
   uint16_t* qr_out;  // (T, N, Dr)
   int64_t qr_ld;     // N*Dr
   // EPI_UK (and EPI_QN's output)
@@ -214,6 +220,11 @@ struct Epilogue {
               st16(static_cast<float*>(p.qc_out) + off,
                    make_uint4(__float_as_uint(v[4 * hh]), __float_as_uint(v[4 * hh + 1]),
                               __float_as_uint(v[4 * hh + 2]), __float_as_uint(v[4 * hh + 3])));
+            } else if (p.qc_coherent) {
+              // decode q^C (< 2^31 bytes): one resource over the buffer
+              bst8_dev(make_rsrc(p.qc_out, 0x7fffffffu), static_cast<uint32_t>(off) * 2u,
+                       make_uint2(pack_bf16x2(v[4 * hh], v[4 * hh + 1]),
+                                  pack_bf16x2(v[4 * hh + 2], v[4 * hh + 3])));
             } else {
               st8(static_cast<uint16_t*>(p.qc_out) + off,
                   make_uint2(pack_bf16x2(v[4 * hh], v[4 * hh + 1]),
@@ -276,6 +287,15 @@ struct SkinnyDepth {
   static constexpr int value = (8 / per_step) > 0 ? (8 / per_step) : 1;
 };
 
+// ---------------------------------------------------------------------------
+// Handoff counters between the workgroups of the merged decode launch
+// (k_decode_tail) sit in the workspace one per 256-byte line (SYNC_STRIDE
+// words apart, plan.h): hundreds of workgroups polling a few shared lines
+// measured 4 us slower than the same polls spread over lines.  The down
+// projection, the launch before, zeroes them.
+// ---------------------------------------------------------------------------
+constexpr uint32_t SYNC_SPIN_LIMIT = 1u << 18;  // polls before a wait gives up
+
 // A_LDS_STEPS: most k-steps of one split whose A operand (32 rows, bf16) a
 // workgroup stages in LDS by default (64 KB).
 constexpr int A_LDS_STEPS = 64;
@@ -288,12 +308,15 @@ constexpr int A_LDS_STEPS = 64;
 enum { ALDS_NONE = 0, ALDS_ROWMAJOR = 1, ALDS_FRAG = 2 };
 
 // One tile of the skinny GEMM: tile bx (column tiles of B0 then of B1),
-// split by, batch bz; run by a 64*NW*KW-thread workgroup.
+// split by, batch bz; run by a 64*NW*KW-thread workgroup, plus XW extra
+// waves that skip the main loop and share the epilogue.
 template <int AK, int MB, int NB, int NW, int KW, int EPI,
           int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS,
-          bool QH = false>
+          bool QH = false, int XW = 0>
 __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, const int by,
                                             const int bz) {
+  static_assert(XW == 0 || (ALDS == ALDS_NONE && !QH), "extra waves: plain tiles only");
+  constexpr int NALL = 64 * (NW * KW + XW);  // threads of the workgroup
   typedef typename AccT<AK>::type Acc;
   constexpr int KSTEP = (AK == A_I8) ? 32 : 16;  // k per MFMA
   constexpr int G = (AK == A_I8) ? 16 : 8;       // k per 16-byte chunk
@@ -310,8 +333,9 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   // Wave-level quantities live in SGPRs: the per-step load offsets below are
   // scalar, so the loop's address arithmetic costs no VGPRs.
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const bool active = wave < NW * KW;  // a streaming wave (wave-uniform)
   const int nw = wave % NW;
-  const int kw = wave / NW;
+  const int kw = active ? wave / NW : 0;
   const int g = lane >> 5;
   const int li = lane & 31;
   const int z = bz;
@@ -541,7 +565,7 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
     lds_barrier();  // keeps the first weight batch in flight
     if (w_lo < w_hi) load_a(X, w_lo);
   }
-  if (w_lo < w_hi) {
+  if (active && w_lo < w_hi) {
     int s = w_lo;
     if constexpr (ALDS == ALDS_NONE) load(X, s);
     for (;;) {
@@ -558,6 +582,7 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
 
   // Stage: 32x32 MFMA output, lane l / register r -> row 8*(r/4) + 4*(l/32)
   // + r%4, column l%32.
+  if (active)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -621,7 +646,7 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   // Epilogue: 8-column groups of the (MB*32) x TN tile.
   GemmParams pe = p;
   if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(by) * p.M * p.part_ld;
-  for (int it = threadIdx.x; it < GROUPS; it += 64 * NW * KW) {
+  for (int it = threadIdx.x; it < GROUPS; it += NALL) {
     const int row = it / (TN / 8);
     const int c0 = (it % (TN / 8)) * 8;
     const int64_t m = row;
@@ -661,9 +686,120 @@ template <int AK, int MB, int NB, int NW, int KW, int EPI,
           int P = SkinnyDepth<AK, MB, NB>::value, int ALDS = ALDS_NONE, int ACAP = A_LDS_STEPS,
           bool QH = false>
 __global__ __launch_bounds__(64 * NW * KW) void k_skinny(GemmParams p) {
+  if (p.zero_words != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < p.zero_count; i += blockDim.x)
+      gst(p.zero_words + i * SYNC_STRIDE, 0u);
   skinny_tile<AK, MB, NB, NW, KW, EPI, P, ALDS, ACAP, QH>(p, static_cast<int>(blockIdx.x),
                                                      static_cast<int>(blockIdx.y),
                                                      static_cast<int>(blockIdx.z));
+}
+
+// ---------------------------------------------------------------------------
+// W^UK tiles of the merged decode launch (k_decode_tail, after the finish
+// kernel below): head h, 128 columns of Hckv, one 32-column block per wave.
+// A tile loads its whole W^UK slice (D/16 k-steps, 16 bytes per lane each)
+// into registers as soon as it is dispatched, waits until every
+// up-projection tile covering head h's q^C columns has counted itself done,
+// reads the head's q^C once per workgroup into LDS (device-scope loads: the
+// producers wrote it through to the level every XCD shares, and these never
+// hit a stale copy in this XCD's L2), and ends with D/16 MFMAs and the q^N
+// stores.  Each XCD dispatches its workgroups in index order, so every
+// up-projection tile is dispatched before any W^UK tile of its XCD and never
+// waits itself: the wait always ends (it is bounded all the same).
+// ---------------------------------------------------------------------------
+constexpr int UK_TILE_COLS = 128;  // 4 waves x 32 columns of Hckv
+constexpr int UK_MAX_STEPS = 8;    // D <= 128
+constexpr int kA6Cols = 96;  // decode A6 tile: three waves across, one column block each
+
+// Up-projection tiles of kA6Cols columns that cover head h's q^C columns
+// [h*D, (h+1)*D): the count its W^UK tiles wait for.
+__device__ __forceinline__ unsigned up_tiles_of_head(int h, int D) {
+  return static_cast<unsigned>(((h + 1) * D - 1) / kA6Cols - (h * D) / kA6Cols + 1);
+}
+
+template <int KS>
+__device__ __forceinline__ void uk_tile_after_up(const GemmParams& p, const int h, const int ct,
+                                                 const unsigned* ready, const unsigned need) {
+  static_assert(KS <= UK_MAX_STEPS, "the W^UK slice is held in registers");
+  __shared__ uint32_t stage[32][UK_TILE_COLS + 4];
+  __shared__ uint4 qcs[UK_MAX_STEPS * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int li = lane & 31, g = lane >> 5;
+  const int KC = static_cast<int>(p.K / 8);  // 16-byte chunk rows per column block
+  const int64_t nblk = (p.N0 + 31) / 32;
+  int64_t nb = static_cast<int64_t>(ct) * (UK_TILE_COLS / 32) + wave;
+  nb = nb < nblk ? nb : nblk - 1;  // clamped blocks are computed, never stored
+  const rsrc_t rb = make_rsrc(p.B0 + static_cast<int64_t>(h) * p.b_bstride + nb * KC * 32,
+                              static_cast<uint32_t>(KC) * 512u);
+  const uint32_t vl = static_cast<uint32_t>(lane) * 16u;
+  uint4 w[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) w[s] = bld16_nt(rb, vl, static_cast<uint32_t>(s) * 1024u);
+
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need &&
+           ++n < SYNC_SPIN_LIMIT)
+      __builtin_amdgcn_s_sleep(4);
+  }
+  __syncthreads();
+
+  // Head h's q^C in fragment layout: k-step s is 64 lanes x 16 bytes at s KB.
+  const rsrc_t ra = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(h) * p.a_zs,
+                              static_cast<uint32_t>(KS) * 1024u);
+  constexpr int PER = (KS * 64 + 255) / 256;
+  uint4 q[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;
+    q[i] = bld16_dev(ra, static_cast<uint32_t>(c < KS * 64 ? c : KS * 64 - 1) * 16u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;
+    if (c < KS * 64) qcs[c] = q[i];
+  }
+  __syncthreads();
+  f32x16_t acc = {};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) mfma_step<A_BF16>(acc, qcs[s * 64 + lane], w[s]);
+
+  // 32x32 block -> LDS (row 8*(r/4) + 4*g + r%4, column li), then each
+  // thread stores 8 consecutive columns of one row.
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    stage[8 * (r >> 2) + 4 * g + (r & 3)][wave * 32 + li] = __float_as_uint(acc[r]);
+  __syncthreads();
+  for (int it = threadIdx.x; it < 32 * (UK_TILE_COLS / 8); it += 256) {
+    const int row = it / (UK_TILE_COLS / 8);
+    const int c0 = (it % (UK_TILE_COLS / 8)) * 8;
+    const int64_t gcol = static_cast<int64_t>(ct) * UK_TILE_COLS + c0;
+    if (row >= p.M || gcol >= p.N0) continue;
+    const uint32_t* v = &stage[row][c0];
+    st16_nt(p.q_out + row * p.q_ld + static_cast<int64_t>(h) * p.q_bstride + gcol,
+            make_uint4(pack_bf16x2(__uint_as_float(v[0]), __uint_as_float(v[1])),
+                       pack_bf16x2(__uint_as_float(v[2]), __uint_as_float(v[3])),
+                       pack_bf16x2(__uint_as_float(v[4]), __uint_as_float(v[5])),
+                       pack_bf16x2(__uint_as_float(v[6]), __uint_as_float(v[7]))));
+  }
+}
+
+// An up-projection tile of the merged launch that holds q^C columns: once
+// its q^C stores are complete, it bumps the counter of each head it covers.
+__device__ __forceinline__ void up_tile_signal(const GemmParams& up, const int b,
+                                               unsigned* ready) {
+  const int64_t n0 = static_cast<int64_t>(b) * kA6Cols;
+  if (n0 >= up.ND) return;  // q^R columns only
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's q^C stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t n1 = n0 + kA6Cols < up.ND ? n0 + kA6Cols : up.ND;
+    const int D = static_cast<int>(up.qc_D);
+    for (int h = static_cast<int>(n0 / D); h <= static_cast<int>((n1 - 1) / D); ++h)
+      __hip_atomic_fetch_add(ready + h * SYNC_STRIDE, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1706,6 +1842,42 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
 }
 
 // ---------------------------------------------------------------------------
+// Decode up projection and W^UK product in one launch (bf16, one 32-row
+// block, D <= 128): k_decode_tail<KS>.  Workgroups [0, up_tiles) are the up
+// projection's kA6Cols-column tiles (three streaming waves and a fourth
+// that joins the epilogue); q^C leaves with device-scope stores and the
+// tile then counts itself done for each head it covers (up_tile_signal).
+// The others are W^UK tiles (uk_tile_after_up), which load their W^UK
+// slices while the up projection streams and wait only for their head.
+// Measured at the DeepSeek-V3 decode shape: 20.2 us for the launch against
+// 15.0 + 5.7 us for two launches (step 35.9 vs 37.1 us); the up-projection
+// tiles and the W^UK loads together stream at about 5.9 TB/s, and the W^UK
+// tiles end 2.5 us after the last up-projection tile.  (Running the
+// down-projection finish as more workgroups of this launch, with the
+// up-projection tiles loading weight while they wait for c^Q, measured
+// 1 us slower: under the launch's load the finish took 6-7 us.)
+// ---------------------------------------------------------------------------
+struct DecodeTailParams {
+  GemmParams up, uk;
+  unsigned* ready;  // per head, SYNC_STRIDE words apart: up-projection tiles done
+  int up_tiles, uk_tiles;
+};
+
+template <int KS>
+__global__ __launch_bounds__(256) void k_decode_tail(DecodeTailParams p) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < p.up_tiles) {
+    skinny_tile<A_BF16, 1, 1, 3, 1, EPI_UQQR, 4, ALDS_NONE, A_LDS_STEPS, false, 1>(p.up, b, 0, 0);
+    up_tile_signal(p.up, b, p.ready);
+    return;
+  }
+  const int u = b - p.up_tiles;
+  const int h = u / p.uk_tiles, ct = u % p.uk_tiles;
+  uk_tile_after_up<KS>(p.uk, h, ct, p.ready + h * SYNC_STRIDE,
+                       up_tiles_of_head(h, static_cast<int>(p.up.qc_D)));
+}
+
+// ---------------------------------------------------------------------------
 // MlaPreprocessV2 first step (aclnnMlaPreprocessV2: x is processed by
 // RmsNormQuant before the W^DQKV product; formula block): per token,
 // codes = sat(rne((gamma * x / RMS(x) + bias) * scale)) in [-128, 127],
@@ -1919,7 +2091,6 @@ template <int MB>
 constexpr int a1_kw() { return MB >= 4 ? 2 : (MB == 2 ? 4 : 8); }
 template <int MB>
 constexpr int a6_kw() { return MB >= 4 ? 1 : 2; }
-constexpr int kA6Cols = 96;  // A6 tile: three waves across, one column block each
 template <int MB>
 constexpr int a8_nw() { return 4; }
 // A1 tiles are kA1Cols = 64 columns wide (plan.h): two column blocks, one
@@ -2172,6 +2343,13 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     f.sw_dkv = a->dequant_scale_w_dkv_kr;
   }
   if (pre != nullptr) f.qs_cq = pre->qs_cq;
+  // Merged decode tail: the down projection zeroes its handoff counters.
+  unsigned* ready = reinterpret_cast<unsigned*>(ws + pl.off_sync);
+  if (pl.merge_uk) {
+    g1.zero_words = ready;
+    g1.zero_count = static_cast<int>(a->N);
+    g6.qc_coherent = 1;
+  }
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
   const dim3 fin_block(static_cast<unsigned>(fin_threads(ntot)));
 
@@ -2225,13 +2403,32 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
-    switch (pl.mb) {
-      case 1: skinny_a6<1>(g6, quant, L6); break;
-      case 2: skinny_a6<2>(g6, quant, L6); break;
-      default: skinny_a6<4>(g6, quant, L6); break;
+    if (pl.merge_uk) {
+      DecodeTailParams u{};
+      u.up = g6;
+      u.uk = g8;
+      u.ready = ready;
+      u.up_tiles = static_cast<int>((g6.N0 + kA6Cols - 1) / kA6Cols);
+      u.uk_tiles = static_cast<int>((a->Hckv + UK_TILE_COLS - 1) / UK_TILE_COLS);
+      const dim3 grid(static_cast<unsigned>(u.up_tiles + nh * u.uk_tiles));
+      switch (a->D / 16) {
+        case 2: launch(L6, k_decode_tail<2>, grid, dim3(256), 0, u); break;
+        case 4: launch(L6, k_decode_tail<4>, grid, dim3(256), 0, u); break;
+        case 6: launch(L6, k_decode_tail<6>, grid, dim3(256), 0, u); break;
+        default: launch(L6, k_decode_tail<8>, grid, dim3(256), 0, u); break;
+      }
+      mark(MLA_PHASE_AFTER_UQQR);
+    } else {
+      switch (pl.mb) {
+        case 1: skinny_a6<1>(g6, quant, L6); break;
+        case 2: skinny_a6<2>(g6, quant, L6); break;
+        default: skinny_a6<4>(g6, quant, L6); break;
+      }
+      mark(MLA_PHASE_AFTER_UQQR);
     }
-    mark(MLA_PHASE_AFTER_UQQR);
-    if (qh) {
+    if (pl.merge_uk) {
+      // the W^UK product ran inside k_decode_tail
+    } else if (qh) {
       const dim3 grid(1, 1, static_cast<unsigned>(nh));
       if (a->Hckv <= 128)
         launch(L8, k_skinny<A_F32SPLIT, 1, 1, 4, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,

@@ -20,6 +20,9 @@ constexpr int FIN_MAXSPLIT = 8;
 constexpr int FIN_SPLIT_SMALL = 4;
 // Decode down-projection tile width: two 32-column blocks.
 constexpr int kA1Cols = 64;
+// Handoff counters of the merged decode launch: one per 256-byte line
+// (SYNC_STRIDE uint32 apart).
+constexpr int SYNC_STRIDE = 64;
 
 // Which kernel family runs, the split-K factor of the down projection and
 // the workspace carve-up.  A pure function of the arguments.
@@ -27,6 +30,8 @@ struct MlaPlan {
   bool skinny;        // decode-sized T: weight-streaming kernels
   bool gemm256;       // large T, bf16: 256x256-tile MFMA GEMMs
   bool fuse_uk;       // gemm256 with the W^UK product fused into A6's q^C tiles
+  bool merge_uk;      // skinny bf16, one row block: A6 and the W^UK product in
+                      // one launch (k_decode_tail), handing q^C over per head
   int mb;             // 32-row blocks held per wave (skinny only)
   int ksplit;         // down-projection split-K factor
   int64_t steps_per_split;
@@ -35,6 +40,8 @@ struct MlaPlan {
   size_t off_part, off_cq, off_cq_scale, off_qc;
   size_t off_qn;      // FULL_KV_INT8: q^N in fp32 before its per-head quant
   size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
+  size_t off_sync;    // merge_uk: N per-head handoff counters, one per
+                      // 256-byte line
   size_t off_prex8, off_presx;  // MlaPreprocessV2: RmsNormQuant codes of x
                                 // (T, He) int8 and their unit token scales
   int64_t rows;       // token rows padded to the plan's 32-row blocks

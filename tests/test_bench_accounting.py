@@ -93,6 +93,12 @@ def test_up_projection_bytes_match_the_workload_tensors():
               + c.T * c.N * c.Dr * 2)
     assert bench.uqqr_bytes(c) == expect == 76_029_952
     assert bench.uqqr_workspace_bytes(c) == c.T * c.Hcq * 2 + c.T * c.N * c.D * 2
+    # the W^UK product in the same launch adds W^UK and the query, and
+    # reads q^C back once per 128-column tile of each head's Hckv
+    assert bench.uk_bytes(c) == a["weight_uk"].nbytes + c.T * c.N * c.Hckv * 2 \
+        == 20_971_520
+    assert bench.uqqr_workspace_bytes(c, merged=True) == \
+        bench.uqqr_workspace_bytes(c) + 4 * c.T * c.N * c.D * 2
 
 
 def test_preprocess_bytes_match_the_workload_tensors():

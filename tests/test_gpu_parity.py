@@ -299,7 +299,8 @@ def test_mla_T0_and_no_slots():
 # decode-sized shapes beyond the small list: a ragged T = 21 (one partial
 # 32-row block), wider N / Hckv than one pass of 256 workgroups covers, and
 # two head-dim-128 shapes with partial tiles and batches
-DECODE_CASES = ["mla_ragged_t21", "mla_wide", "mla_dec_t13", "mla_dec_hckv96"]
+DECODE_CASES = ["mla_ragged_t21", "mla_wide", "mla_dec_t13", "mla_dec_hckv96",
+                "mla_dec_d96"]
 
 
 def _decode_case(key):

@@ -181,6 +181,11 @@ CONFIGS = {
                                 Hcq=160, N=3, D=128, Hckv=96, Dr=64,
                                 block_num=2, block_size=32, n_skip=1,
                                 seed=2013),
+    # head dim 96 (six 16-k steps per W^UK slice): each head's q^C is one
+    # whole 96-column up-projection tile, and Hckv is 1.25 W^UK column tiles
+    "mla_dec_d96": MlaConfig("mla_dec_d96_T17", B=17, S=1, He=256, Hcq=192,
+                             N=5, D=96, Hckv=160, Dr=32, block_num=2,
+                             block_size=16, n_skip=2, seed=2019),
     # full quantisation (int8 x and down-projection weights): a one-block
     # decode shape with bf16 caches, a two-block one with the int8 kv_cache
     # and int8 query, and a large-T shape on the tiled plan
