@@ -29,17 +29,17 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   // k-steps of the down projection: 16 k (bf16) or 32 k (int8 x)
   const int64_t steps = a->He / (xq ? 32 : 16);
   if (pl.gemm256) {
-    // Split the down projection over K so that its 128x256 tiles (two
-    // workgroups per CU) times the splits fill whole rounds of the 512
-    // workgroup slots best: minimise ceil(tiles * ks / 512) / ks over ks <= 4
-    // (more splits cost partial-sum traffic), with steps per split even
-    // (32-k pipeline stages).
-    const int64_t tiles = (T + G_TM_HALF - 1) / G_TM_HALF *
+    // Split the down projection over K so that its 256x256 tiles (one
+    // workgroup per CU) times the splits fill whole rounds of the 256 CUs
+    // best: minimise ceil(tiles * ks / 256) / ks over ks <= 4 (more splits
+    // cost partial-sum traffic), with steps per split even (32-k pipeline
+    // stages).
+    const int64_t tiles = (T + 255) / 256 *
                           ((a->Hcq + G_TN - 1) / G_TN + (a->Hckv + a->Dr + G_TN - 1) / G_TN);
     int64_t best = 1;
     double best_cost = 1e30;
     for (int64_t ks = 1; ks <= 4; ++ks) {
-      const double cost = static_cast<double>((tiles * ks + 511) / 512) / static_cast<double>(ks);
+      const double cost = static_cast<double>((tiles * ks + 255) / 256) / static_cast<double>(ks);
       if (cost < best_cost - 1e-9) {
         best_cost = cost;
         best = ks;

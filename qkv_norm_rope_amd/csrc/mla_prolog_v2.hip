@@ -1096,20 +1096,21 @@ __device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
 // bf16, registers 8h..8h+7 are then directly the token-side operand of a
 // 16-k step of the W^UK product -- in exactly the k order mla_pack_weight_uk
 // gives W^UK -- so q^C never leaves the registers.
-// Waves of a k_gemm workgroup: 2 x 2 of (TM/2) x 128, or for the fused
-// q^C + W^UK tiles 4 x 2 of 64 x 128 (two waves per SIMD: 128 accumulators
-// each, so one wave's MFMAs run while the other waits on LDS or a barrier).
-template <int EPI>
-constexpr int gemm_waves() { return EPI == EPI_QN ? 8 : 4; }
+// Waves of a k_gemm workgroup: 2 x 2 of 64 x 128 for 128-row tiles (two
+// workgroups per CU), 4 x 2 of 64 x 128 for 256-row tiles (one workgroup
+// per CU, two waves per SIMD: 128 accumulators each, so one wave's MFMAs
+// run while the other waits on LDS or a barrier).
+template <int TM>
+constexpr int gemm_waves() { return TM == 256 ? 8 : 4; }
 
 template <int EPI, int TM, int NBUF, int DH = 0>
-__global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
+__global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
   typedef Epilogue<A_BF16, EPI == EPI_QN ? EPI_UQQR : EPI> Epi;
   constexpr bool SWAP = EPI == EPI_QN;
   static_assert(!SWAP || (TM == 256 && DH == 128 && NBUF == 4),
                 "fused W^UK product: 256-row tiles, one 128-wide head per wave");
   static_assert(TM != 256 || NBUF == 4, "256-row tiles: the double-buffered pipeline");
-  constexpr int NWV = gemm_waves<EPI>();  // waves per workgroup
+  constexpr int NWV = gemm_waves<TM>();  // waves per workgroup
   constexpr int WR = NWV / 2;             // wave rows (two wave columns of 128)
   constexpr int TPW = TM / WR;            // tokens (rows) per wave
   constexpr int MA = TM / 32;   // A blocks per k-step
@@ -1376,10 +1377,10 @@ __global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_g
     // PB = 2 column blocks (32 columns each) of Hckv (MI m-blocks x PB
     // column blocks of accumulators: the rest of the AGPRs and the VGPRs
     // hold qc).  A pass's W^UK operands (2 heads x 8 k-steps x PB column
-    // blocks of 1 KB) are loaded into LDS by buffer->LDS loads one pass
-    // ahead, as [head*8 + k-step][lane] per column block: pass buffer b is
-    // stage b's arrays, sa<b> for the first column block and sb<b> for the
-    // second (16 KB each).
+    // blocks of 1 KB) are loaded into LDS by buffer->LDS loads two passes
+    // ahead, as [head*8 + k-step][lane] per column block: pass buffer b
+    // (0-2) is stage b's arrays, sa<b> for the first column block and sb<b>
+    // for the second (16 KB each).
     constexpr int PB = 2;
     constexpr int SPP = MI * 2 * PB;  // stores per wave per full pass
     const int KC2 = DH / 8;
@@ -1407,11 +1408,11 @@ __global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_g
       }
     };
     const int64_t head = head0 + wn;
-    // Output staging: a 4 KB slice per wave of stage buffers 2 and 3's A
-    // arrays (the passes use buffers 0 and 1; every load into LDS has
-    // landed).
-    static_assert(sizeof(sa2) == 4 * 4096, "staging: four waves per A array");
-    char* stg = reinterpret_cast<char*>(w < 4 ? &sa2[0][0][0] : &sa3[0][0][0]) + (w & 3) * 4096;
+    // Output staging: a 4 KB slice per wave of stage buffer 3's arrays
+    // (the passes use buffers 0-2; every load into LDS has landed).
+    static_assert(sizeof(sa3) == 4 * 4096 && sizeof(sb3) == 4 * 4096,
+                  "staging: four waves per array");
+    char* stg = reinterpret_cast<char*>(w < 4 ? &sa3[0][0][0] : &sb3[0][0][0]) + (w & 3) * 4096;
     const bool rows_in = m0 + TPW * wm + TPW - 1 < p.M;  // all of this wave's tokens are rows
     // Returns whether the pass issued exactly SPP stores (all in range).
     auto pass_uk = [&](auto bc, int pp) -> bool {
@@ -1467,34 +1468,59 @@ __global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_g
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // Each step: wait for this wave's loads of the pass -- only the previous
-    // pass's SPP stores were issued after them when that pass was full, so
-    // those stay in flight -- then a barrier (everybody's loads landed,
-    // everybody done with the other buffer), start the next pass's loads,
-    // compute and store.
-    auto wait_pass = [&](bool prev_full) {
-      if (prev_full)
-        vm_barrier<SPP>();
-      else
-        vm_barrier<0>();
+    using P2 = std::integral_constant<int, 2>;
+    // Three pass buffers: pass pp's W^UK loads are issued two passes ahead,
+    // so a pass's stores have two passes to complete before any wait needs
+    // them.  Before pass pp a wave waits until its loads of pass pp have
+    // landed: with in-order completion, until no more than the vector-memory
+    // operations it issued after those loads are in flight.  after[b] counts
+    // them for the pass in buffer b (a lower bound: a pass whose stores were
+    // not all issued counts none).  The barrier then covers every wave's
+    // loads, and every wave is done reading the buffer refilled next (pass
+    // pp - 1's).
+    constexpr int LPP = PB * KPW;  // W^UK loads per wave per pass
+    int after[3] = {0, 0, 0};
+    auto note = [&](int n) {
+      after[0] += n;
+      after[1] += n;
+      after[2] += n;
     };
-    issue_uk(P0{}, 0);
-    bool prev_full = false;
-    for (int pp = 0; pp < npass; pp += 2) {
-      wait_pass(prev_full);
-      if (pp + 1 < npass) issue_uk(P1{}, pp + 1);
-      prev_full = pass_uk(P0{}, pp);
+    auto issue_pass = [&](auto bc, int pp) {
+      if (pp >= npass) return;
+      note(LPP);
+      issue_uk(bc, pp);
+      after[decltype(bc)::value] = 0;
+    };
+    auto wait_loads = [&](int n) {  // n: a multiple of 4 (LPP and SPP are)
+      static_assert(LPP % 4 == 0 && SPP % 4 == 0, "wait counts");
+      if (n >= 20) vm_barrier<20>();
+      else if (n >= 16) vm_barrier<16>();
+      else if (n >= 12) vm_barrier<12>();
+      else if (n >= 8) vm_barrier<8>();
+      else if (n >= 4) vm_barrier<4>();
+      else vm_barrier<0>();
+    };
+    auto run_pass = [&](auto bc, auto nextbc, int pp) {
+      wait_loads(after[decltype(bc)::value]);
+      issue_pass(nextbc, pp + 2);
+      note(pass_uk(bc, pp) ? SPP : 0);
+    };
+    issue_pass(P0{}, 0);
+    issue_pass(P1{}, 1);
+    for (int pp = 0; pp < npass; pp += 3) {
+      run_pass(P0{}, P2{}, pp);
       if (pp + 1 >= npass) break;
-      wait_pass(prev_full);
-      if (pp + 2 < npass) issue_uk(P0{}, pp + 2);
-      prev_full = pass_uk(P1{}, pp + 1);
+      run_pass(P1{}, P0{}, pp + 1);
+      if (pp + 2 >= npass) break;
+      run_pass(P2{}, P1{}, pp + 2);
     }
     return;
   }
 
   // Epilogue.  Wave w stages 32-row pieces of its tile (32 x 128 fp32) in
   // two 8 KB halves (rows 0-15 and 16-31) of B stage buffer sb<w> (with
-  // three buffers, wave 3 uses sa0 and sa1), 128 words
+  // three buffers, wave 3 uses sa0 and sa1; with eight waves, waves 4-7 use
+  // the 16 KB A buffers sa<w-4>), 128 words
   // per row with 32-word halves swapped on every other 4-row group (so the
   // two lane halves of an accumulator write hit different banks).  Then
   // each lane takes 8 groups of 8 consecutive columns: 16 lanes cover one
@@ -1502,13 +1528,14 @@ __global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_g
   // (bf16).  RoPE partners lie in the same 32-column block, so in the same
   // row.
   static_assert(sizeof(sb0) >= 16384 && sizeof(sa0) >= 8192, "staging space");
+  static_assert(NWV == 4 || (NBUF == 4 && sizeof(sa0) >= 16384), "eight staging slices");
   uint32_t* se_lo;
   uint32_t* se_hi;
   switch (w) {
     case 0: se_lo = &sb0[0][0][0].x; se_hi = se_lo + 2048; break;
     case 1: se_lo = &sb1[0][0][0].x; se_hi = se_lo + 2048; break;
     case 2: se_lo = &sb2[0][0][0].x; se_hi = se_lo + 2048; break;
-    default:
+    case 3:
       if constexpr (NBUF == 4) {
         se_lo = &SB(std::integral_constant<int, 3>{})[0][0][0].x;
         se_hi = se_lo + 2048;
@@ -1516,6 +1543,17 @@ __global__ __launch_bounds__(64 * gemm_waves<EPI>(), TM == 256 ? 1 : 2) void k_g
         se_lo = &sa0[0][0][0].x;
         se_hi = &sa1[0][0][0].x;
       }
+      break;
+    case 4: se_lo = &sa0[0][0][0].x; se_hi = se_lo + 2048; break;
+    case 5: se_lo = &sa1[0][0][0].x; se_hi = se_lo + 2048; break;
+    case 6: se_lo = &sa2[0][0][0].x; se_hi = se_lo + 2048; break;
+    default:
+      if constexpr (NBUF == 4) {
+        se_lo = &SA(std::integral_constant<int, 3>{})[0][0][0].x;
+      } else {
+        se_lo = &sa2[0][0][0].x;  // not reached: three buffers run four waves
+      }
+      se_hi = se_lo + 2048;
       break;
   }
   auto sep = [&](int row, int col) -> uint32_t& {
@@ -2457,14 +2495,16 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     g1.A = ws + pl.off_xfrag;
     g1.a_frag = 1;
     g1.a_mbs = a->He * 64;
-    // A1 and A6's q^R columns: 128x256 tiles and three buffers, two
-    // workgroups per CU so one's epilogue stores overlap the other's main
-    // loop.  The fused q^C + W^UK tiles: 256x256, four buffers.
+    // A6's q^R columns: 128x256 tiles and three buffers, two workgroups
+    // per CU so one's epilogue stores overlap the other's main loop (256-row
+    // tiles measured the same).  A1 and the fused q^C + W^UK tiles: 256x256,
+    // eight waves, four buffers (A1 at T = 4096: 157 vs 167 us).
     const unsigned mt2 = static_cast<unsigned>((T + G_TM_HALF - 1) / G_TM_HALF);
     g1.ntiles0 = static_cast<int>((g1.N0 + G_TN - 1) / G_TN);
     const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + G_TN - 1) / G_TN);
-    launch(L1, k_gemm<EPI_PARTIAL, G_TM_HALF, 3>,
-           dim3(nt1, mt2, static_cast<unsigned>(pl.ksplit)), dim3(256), 0, g1);
+    launch(L1, k_gemm<EPI_PARTIAL, 256, 4>,
+           dim3(nt1, static_cast<unsigned>((T + 255) / 256), static_cast<unsigned>(pl.ksplit)),
+           dim3(64 * gemm_waves<256>()), 0, g1);
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
@@ -2490,7 +2530,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gq.q_bstride = g8.q_bstride;
       const unsigned mt = static_cast<unsigned>((T + 255) / 256);
       launch(L8, k_gemm<EPI_QN, 256, 4, 128>, dim3(static_cast<unsigned>(ND / G_TN), mt, 1),
-             dim3(64 * gemm_waves<EPI_QN>()), 0, gq);
+             dim3(64 * gemm_waves<256>()), 0, gq);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
       launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, dim3(nt6, mt2, 1), dim3(256), 0, g6);
