@@ -24,7 +24,7 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   const bool xq = a->quant_mode == MLA_QUANT_FULL_KV_BF16 || a->quant_mode == MLA_QUANT_FULL_KV_INT8;
   const int64_t ntot = a->Hcq + a->Hckv + a->Dr;
   pl.skinny = T <= 128;
-  pl.gemm256 = !pl.skinny && !quant;
+  pl.gemm256 = !pl.skinny;
   pl.mb = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
   // k-steps of the down projection: 16 k (bf16) or 32 k (int8 x)
   const int64_t steps = a->He / (xq ? 32 : 16);
@@ -70,7 +70,7 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   // Prefill fuses the W^UK product into the q^C tiles of A6 when a wave's
   // 128 q^C columns are exactly one head (D = 128) and the q^C columns end
   // on a tile boundary.
-  pl.fuse_uk = pl.gemm256 && a->D == 128 && (a->N * a->D) % G_TN == 0;
+  pl.fuse_uk = pl.gemm256 && !quant && a->D == 128 && (a->N * a->D) % G_TN == 0;
   // Decode with one row block in bf16 runs the up projection and the W^UK
   // product as one launch when a head's q^C and W^UK slices fit a wave's
   // registers (D <= 128).

@@ -57,6 +57,9 @@ struct GemmParams {
   int64_t N1;
   int64_t b_bstride;
   int64_t M, K;
+  int64_t KB;  // k_gemm: B's K when it is shorter than A's (EPI_UK over q^C
+               // hi | lo: A's k-step s pairs with B's k-step s mod KB-steps);
+               // 0: KB = K
   int ntiles0;
   int64_t steps_per_split;  // k-steps handled per blockIdx.y
   // EPI_PARTIAL: part[m][part_ld] of this launch's split (the skinny kernel
@@ -77,6 +80,8 @@ struct GemmParams {
   int64_t qc_mblocks;     // 32-row blocks per head (fragment layout)
   int qc_coherent;        // bf16 fragment q^C with device-scope stores, for a
                           // consumer in the same launch (k_decode_tail)
+  int qc_split;           // fragment q^C as bf16 hi and lo = bf16(v - hi):
+                          // per head 2*D k, hi in k-steps [0, D/16), lo after
   // Handoff words of the merged decode launch that this launch zeroes
   // first (workgroup 0), SYNC_STRIDE words apart; NULL: none.
   unsigned* zero_words;
@@ -210,13 +215,26 @@ struct Epilogue {
           const uint32_t gc = static_cast<uint32_t>(gcol), D = static_cast<uint32_t>(p.qc_D);
           const uint32_t head = gc / D, d = gc - head * D;
           const uint32_t mm = static_cast<uint32_t>(m);
+          const uint32_t hsteps = (D >> 4) * (p.qc_split ? 2u : 1u);  // k-steps per head
           const int64_t base =
-              ((static_cast<int64_t>(head) * p.qc_mblocks + (mm >> 5)) * (D >> 4) + (d >> 4)) * 512 +
+              ((static_cast<int64_t>(head) * p.qc_mblocks + (mm >> 5)) * hsteps + (d >> 4)) * 512 +
               (mm & 31) * 8 + ((d >> 3) & 1) * 4;  // slots 0-3 or 4-7
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int64_t off = base + hh * 32 * 8;  // lane half hh
-            if (p.qc_f32) {
+            if (p.qc_split) {
+              uint32_t hw[2], lw[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                const float a = v[4 * hh + 2 * e], b = v[4 * hh + 2 * e + 1];
+                const uint16_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+                hw[e] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
+                lw[e] = pack_bf16x2(a - bf16_to_f32(ha), b - bf16_to_f32(hb));
+              }
+              uint16_t* q = static_cast<uint16_t*>(p.qc_out);
+              st8(q + off, make_uint2(hw[0], hw[1]));
+              st8(q + off + static_cast<int64_t>(D >> 4) * 512, make_uint2(lw[0], lw[1]));
+            } else if (p.qc_f32) {
               st16(static_cast<float*>(p.qc_out) + off,
                    make_uint4(__float_as_uint(v[4 * hh]), __float_as_uint(v[4 * hh + 1]),
                               __float_as_uint(v[4 * hh + 2]), __float_as_uint(v[4 * hh + 3])));
@@ -803,239 +821,25 @@ __device__ __forceinline__ void up_tile_signal(const GemmParams& up, const int b
 }
 
 // ---------------------------------------------------------------------------
-// Tiled GEMM for large M: 128x128 output tile per 256-thread workgroup, 4
-// waves as 2x2 of 64x64 (2x2 MFMA 32x32 blocks each).  A stage holds 64 bytes
-// of K per row (32 bf16 / 64 int8 = two MFMA k-steps); stages are double
-// buffered in LDS with one barrier per stage.  The epilogue stages each wave's
-// 64x64 fp32 tile through LDS so every lane stores 8 consecutive columns.
-// ---------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128;
-constexpr int A_PITCH = 80;  // bytes per A row in LDS (64 + 16 pad)
-constexpr int A_STAGE = TBM * A_PITCH;          // 10240
-constexpr int B_STAGE = 4 * TBN * 16;            // 8192
-constexpr int EPI_PITCH = 68;                    // words per staged row
-constexpr int EPI_WAVE = 64 * EPI_PITCH * 4;     // 17408 bytes per wave
-constexpr int TILED_LDS = 4 * EPI_WAVE;          // 69632 >= 2*(2*A_STAGE+B_STAGE)
-
-template <int AK, int EPI>
-__global__ __launch_bounds__(256) void k_tiled(GemmParams p) {
-  typedef typename AccT<AK>::type Acc;
-  constexpr bool SPLIT = AK == A_F32SPLIT;
-  constexpr int NA = SPLIT ? 2 : 1;  // A tiles per stage (hi, lo)
-  constexpr int STAGE = NA * A_STAGE + B_STAGE;
-  static_assert(2 * STAGE <= TILED_LDS, "LDS budget");
-  __shared__ __attribute__((aligned(16))) char smem[TILED_LDS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int g = lane >> 5;
-  const int li = lane & 31;
-  const int z = blockIdx.z;
-
-  const uint4* B;
-  int64_t N, n0, ocol0;
-  if (static_cast<int>(blockIdx.x) < p.ntiles0) {
-    B = p.B0;
-    N = p.N0;
-    n0 = static_cast<int64_t>(blockIdx.x) * TBN;
-    ocol0 = 0;
-  } else {
-    B = p.B1;
-    N = p.N1;
-    n0 = static_cast<int64_t>(blockIdx.x - p.ntiles0) * TBN;
-    ocol0 = p.N0;
-  }
-  B += static_cast<int64_t>(z) * p.b_bstride;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * TBM;
-
-  constexpr int AEB = (AK == A_I8) ? 1 : (SPLIT ? 4 : 2);
-  const char* Abase = static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_bstride * AEB;
-  const int64_t a_row_bytes = p.lda * AEB;
-  constexpr int KPS = (AK == A_I8) ? 64 : 32;  // k per stage
-  const int64_t nstages = p.K / KPS;
-  const int64_t KC = p.K / ((AK == A_I8) ? 16 : 8);  // chunk rows per column
-
-  // Global -> register loads of one stage.  A: 128 rows x 64 B (bf16/int8)
-  // = 512 chunks of 16 B, 2 per thread; fp32 A: 128 rows x 128 B, 4 per
-  // thread.  B: 4 chunk-rows x 128 columns, 2 per thread.
-  constexpr int ACH = SPLIT ? 4 : 2;
-  uint4 ra[ACH], rb[2];
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int64_t st) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = SPLIT ? (c >> 3) : (c >> 2);
-      const int q = SPLIT ? (c & 7) : (c & 3);
-      const int64_t m = m0 + row;
-      const char* src = Abase + m * a_row_bytes + st * (SPLIT ? 128 : 64) + 16 * q;
-      ra[i] = m < p.M ? ld16(src) : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      // 4 column blocks x 4 chunk rows x 32 columns; each (block, row) run
-      // is 512 contiguous bytes of the N32-blocked weight.
-      const int c = tid + 256 * i;
-      const int nbl = c >> 7;
-      const int kc = (c >> 5) & 3;
-      const int j = c & 31;
-      const int64_t nb = n0 / 32 + nbl;
-      rb[i] = nb * 32 < N ? ld16(B + (nb * KC + st * 4 + kc) * 32 + j) : zero4;
-    }
-  };
-  auto swrite = [&](int buf) {
-    char* sa = smem + buf * STAGE;
-    char* sb = sa + NA * A_STAGE;
-    if constexpr (SPLIT) {
-#pragma unroll
-      for (int i = 0; i < ACH; ++i) {
-        const int c = tid + 256 * i;
-        const int row = c >> 3;
-        const int q = c & 7;  // 4 fp32 = k [4q, 4q+4)
-        const float f[4] = {__uint_as_float(ra[i].x), __uint_as_float(ra[i].y),
-                            __uint_as_float(ra[i].z), __uint_as_float(ra[i].w)};
-        uint16_t h[4];
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          h[e] = f32_to_bf16(f[e]);
-          r[e] = f[e] - bf16_to_f32(h[e]);
-        }
-        uint2 hv = make_uint2(static_cast<uint32_t>(h[0]) | (static_cast<uint32_t>(h[1]) << 16),
-                              static_cast<uint32_t>(h[2]) | (static_cast<uint32_t>(h[3]) << 16));
-        uint2 lv = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
-        *reinterpret_cast<uint2*>(sa + row * A_PITCH + 8 * q) = hv;
-        *reinterpret_cast<uint2*>(sa + A_STAGE + row * A_PITCH + 8 * q) = lv;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < ACH; ++i) {
-        const int c = tid + 256 * i;
-        *reinterpret_cast<uint4*>(sa + (c >> 2) * A_PITCH + 16 * (c & 3)) = ra[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i;
-      const int col = (c >> 7) * 32 + (c & 31);
-      *reinterpret_cast<uint4*>(sb + (((c >> 5) & 3) * TBN + col) * 16) = rb[i];
-    }
-  };
-
-  Acc acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = Acc{};
-
-  if (nstages > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-  for (int64_t st = 0; st < nstages; ++st) {
-    const int buf = static_cast<int>(st & 1);
-    if (st + 1 < nstages) gload(st + 1);
-    const char* sa = smem + buf * STAGE;
-    const char* sb = sa + NA * A_STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 af[2], afl[2], bfr[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = wm * 64 + mb * 32 + li;
-        if constexpr (EPI == EPI_UK) {
-          // packed W^UK k order: lane half g takes k offsets {4g..4g+3} and
-          // {8+4g..8+4g+3} of the 16-k step
-          auto ld = [&](const char* base) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(base + ks * 32 + 8 * g);
-            const uint2 hi = *reinterpret_cast<const uint2*>(base + ks * 32 + 16 + 8 * g);
-            return make_uint4(lo.x, lo.y, hi.x, hi.y);
-          };
-          af[mb] = ld(sa + row * A_PITCH);
-          if constexpr (SPLIT) afl[mb] = ld(sa + A_STAGE + row * A_PITCH);
-        } else {
-          af[mb] = *reinterpret_cast<const uint4*>(sa + row * A_PITCH + ks * 32 + 16 * g);
-          if constexpr (SPLIT)
-            afl[mb] = *reinterpret_cast<const uint4*>(sa + A_STAGE + row * A_PITCH + ks * 32 + 16 * g);
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int col = wn * 64 + nb * 32 + li;
-        bfr[nb] = *reinterpret_cast<const uint4*>(sb + ((ks * 2 + g) * TBN + col) * 16);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          mfma_step<AK>(acc[mb][nb], af[mb], bfr[nb]);
-          if constexpr (SPLIT) mfma_step<AK>(acc[mb][nb], afl[mb], bfr[nb]);
-        }
-    }
-    if (st + 1 < nstages) swrite(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue staging: this wave's 64x64 tile in its own LDS slice.
-  uint32_t* ew = reinterpret_cast<uint32_t*>(smem + wave * EPI_WAVE);
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int col = nb * 32 + li;
-        uint32_t bits;
-        if constexpr (AK == A_I8)
-          bits = static_cast<uint32_t>(acc[mb][nb][r]);
-        else
-          bits = __float_as_uint(acc[mb][nb][r]);
-        ew[row * EPI_PITCH + col] = bits;
-      }
-  __syncthreads();
-
-  for (int it = lane; it < 64 * 8; it += 64) {
-    const int row = it >> 3;
-    const int c0 = (it & 7) * 8;
-    const int64_t m = m0 + wm * 64 + row;
-    const int64_t gcol = n0 + wn * 64 + c0;
-    if (m >= p.M || gcol >= N) continue;
-    uint32_t raw[8], rawp[8];
-    const int poff = Epilogue<AK, EPI>::partner_offset(p, gcol);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      raw[e] = ew[row * EPI_PITCH + c0 + e];
-      rawp[e] = poff ? ew[row * EPI_PITCH + c0 + poff + e] : 0u;
-    }
-    Epilogue<AK, EPI>::apply(p, m, gcol, ocol0 + gcol, z, raw, rawp,
-                             Epilogue<AK, EPI>::prefetch(p, m, gcol));
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Large-M bf16 GEMM (prefill): one TM x 256 output tile per 256-thread
-// workgroup, 4 waves as 2x2 of (TM/2) x 128, each a (TM/64) x 4 grid of
-// 32x32 MFMA blocks (TM = 256: 256 fp32 accumulators per lane in AGPRs, one
-// workgroup per CU; TM = 128: 128, two workgroups per CU).  One stage covers
-// 32 k: for each of its two k-steps, TM/32 A blocks and 8 B blocks of 1 KB
-// each in MFMA operand (lane) order, so every LDS read is one conflict-free
-// ds_read_b128 per lane.  Stages are filled by direct buffer->LDS loads and
-// rotate through NBUF LDS buffers: the loads of the next NBUF-1 stages fly
-// during the MFMAs of the current one, and before reading a stage a wave
-// waits only for its own loads of it, then one barrier publishes all of
-// them.
+// Large-M GEMM (T > 128, every mode): one TM x 256 output tile per
+// workgroup, bf16 or int8 operands (16 or 32 k per 16-byte fragment), waves
+// as rows x 2 of 64 x 128, each a 2 x 4 grid of 32x32 MFMA blocks: 4 waves
+// for TM = 128 (two workgroups per CU), 8 waves for TM = 256 (one workgroup
+// per CU, two waves per SIMD).  One stage covers two k-steps: for each, TM/32
+// A blocks and 8 B blocks of 1 KB each in MFMA operand (lane) order, so
+// every LDS read is one conflict-free ds_read_b128 per lane.  Stages are
+// filled by direct buffer->LDS loads and rotate through NBUF LDS buffers:
+// the loads of the next stages fly during the MFMAs of the current one, and
+// before reading a stage a wave waits only for its own loads of it, then one
+// barrier publishes all of them.
 // ---------------------------------------------------------------------------
 // (G_TN = 256 columns, plan.h.)
-// 128-row tiles (three stage buffers, 72 KB of LDS, at most 181 VGPRs) let
-// two workgroups share a CU, so one's epilogue stores overlap the other's
-// main loop; the prefill q^R and down-projection GEMMs use them (14% and 4%
-// faster than 256-row tiles at T = 4096).  The fused q^C + W^UK tiles stay
-// 256 rows: each tile loads its two heads' W^UK, and 128-row tiles double
-// that traffic (437 vs 320 us).  (G_TM_HALF = 128, plan.h.)
+// 128-row tiles (three stage buffers, 72 KB of LDS) let two workgroups share
+// a CU, so one's epilogue stores overlap the other's main loop; the prefill
+// q^R GEMM and the quantised up projection and W^UK product use them.  The
+// down projection and the fused q^C + W^UK tiles use 256 rows: the fused
+// tiles load their two heads' W^UK per tile, and 128-row tiles double that
+// traffic (437 vs 320 us).  (G_TM_HALF = 128, plan.h.)
 
 // One wave's 16-byte-per-lane buffer -> LDS load (buffer_load_dwordx4 ...
 // lds): lane l's 16 bytes land at lds + 16*l.  Issued from inline assembly
@@ -1103,10 +907,13 @@ __device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
 template <int TM>
 constexpr int gemm_waves() { return TM == 256 ? 8 : 4; }
 
-template <int EPI, int TM, int NBUF, int DH = 0>
+template <int EPI, int TM, int NBUF, int DH = 0, int AK = A_BF16>
 __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
-  typedef Epilogue<A_BF16, EPI == EPI_QN ? EPI_UQQR : EPI> Epi;
+  typedef Epilogue<AK, EPI == EPI_QN ? EPI_UQQR : EPI> Epi;
+  typedef typename AccT<AK>::type Acc;
+  static_assert(AK == A_BF16 || AK == A_I8, "bf16 or int8 operands (16 or 32 k per 16 bytes)");
   constexpr bool SWAP = EPI == EPI_QN;
+  static_assert(!SWAP || AK == A_BF16, "the fused W^UK product takes bf16 q^C");
   static_assert(!SWAP || (TM == 256 && DH == 128 && NBUF == 4),
                 "fused W^UK product: 256-row tiles, one 128-wide head per wave");
   static_assert(TM != 256 || NBUF == 4, "256-row tiles: the double-buffered pipeline");
@@ -1169,8 +976,12 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   }
   B += static_cast<int64_t>(zb) * p.b_bstride;
   const int64_t m0 = static_cast<int64_t>(ty) * TM;
-  const int KC = static_cast<int>(p.K / 8);
-  const int nsteps = static_cast<int>(p.K / 16);
+  // 16-byte chunk rows per column of B, and MFMA k-steps (16 bf16 or 32
+  // int8 k) of A and of B
+  const int64_t KB = p.KB > 0 ? p.KB : p.K;
+  const int KC = static_cast<int>(KB / (AK == A_I8 ? 16 : 8));
+  const int nsteps = static_cast<int>(p.K / (AK == A_I8 ? 32 : 16));
+  const uint32_t bsteps = static_cast<uint32_t>(KB / (AK == A_I8 ? 32 : 16));
   int s_lo = 0, s_hi = nsteps;
   if constexpr (EPI == EPI_PARTIAL) {
     s_lo = z * static_cast<int>(p.steps_per_split);
@@ -1208,18 +1019,19 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint32_t s = static_cast<uint32_t>(s_lo + 2 * t + ks);
+      const uint32_t sb = EPI == EPI_UK ? s % bsteps : s;
 #pragma unroll
       for (int j = 0; j < AW; ++j) dma16(ra, va[j], s * 1024u, &SA(bufc)[ks][AW * w + j][0]);
 #pragma unroll
-      for (int j = 0; j < BW; ++j) dma16(rb, vb[j], s * 1024u, &SB(bufc)[ks][BW * w + j][0]);
+      for (int j = 0; j < BW; ++j) dma16(rb, vb[j], sb * 1024u, &SB(bufc)[ks][BW * w + j][0]);
     }
   };
 
-  f32x16_t acc[MI][4];
+  Acc acc[MI][4];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{};
 
   auto compute = [&](auto bufc) {
 #pragma unroll
@@ -1237,8 +1049,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b[j]), as_bf16x8(a[i]),
                                                                  acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[i]), as_bf16x8(b[j]),
-                                                                 acc[i][j], 0, 0, 0);
+            mfma_step<AK>(acc[i][j], a[i], b[j]);
         }
     }
   };
@@ -1286,8 +1097,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[j]), as_bf16x8(fa[i]),
                                                                  acc[i][j], 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]),
-                                                                 acc[i][j], 0, 0, 0);
+            mfma_step<AK>(acc[i][j], fa[i], fb[j]);
         }
     };
     // Stage t in buffer BUF = t % NBUF; on entry fa0/fb0 hold its k-step 0.
@@ -1561,7 +1371,8 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
     return base[(row & 15) * 128 + (col ^ (((row >> 2) & 1) << 5))];
   };
   // Only tiles holding q^R columns need the RoPE tables (uniform per tile).
-  const bool need_pre = EPI == EPI_UQQR && n0 + G_TN > p.ND;
+  // (int8 tiles also need every column's dequant scale and every token's)
+  const bool need_pre = EPI == EPI_UQQR && (AK == A_I8 || n0 + G_TN > p.ND);
   GemmParams pe = p;
   if constexpr (EPI == EPI_PARTIAL) pe.part += static_cast<int64_t>(z) * p.M * p.part_ld;
 #pragma unroll
@@ -1570,7 +1381,8 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        sep(8 * (r >> 2) + 4 * g + (r & 3), 32 * j + li) = __float_as_uint(acc[i][j][r]);
+        sep(8 * (r >> 2) + 4 * g + (r & 3), 32 * j + li) =
+            AK == A_I8 ? static_cast<uint32_t>(acc[i][j][r]) : __float_as_uint(acc[i][j][r]);
     // Rolled over 2 batches of 4 groups: the accumulators must stay
     // statically indexed, which needs the unrolled loop above to stay
     // small.  A batch issues its RoPE-table loads together.
@@ -2110,10 +1922,6 @@ void skinny(const GemmParams& p, dim3 grid, const Launch& L) {
   launch(L, k_skinny<AK, MB, NB, NW, KW, EPI>, grid, dim3(64 * NW * KW), 0, p);
 }
 
-template <int AK, int EPI>
-void tiled(const GemmParams& p, dim3 grid, const Launch& L) {
-  launch(L, k_tiled<AK, EPI>, grid, dim3(256), 0, p);
-}
 
 // Decode plan: three weight-streaming launches plus the down-projection
 // finish (launched between A1 and A6).  Many short per-wave weight runs keep
@@ -2484,27 +2292,33 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
         default: skinny_a8<4>(g8, nh, quant, L8); break;
       }
     }
-  } else if (pl.gemm256) {
-    // x into fragment layout first: the GEMM's A loads are then 1 KB
-    // contiguous per wave (row-major x costs 32 cache lines per load).
+  } else {
+    // Large T (pl.gemm256).  x into fragment layout first: the GEMM's A
+    // loads are then 1 KB contiguous per wave (row-major x costs 32 cache
+    // lines per load).  int8 x (full quantisation, MlaPreprocessV2's codes)
+    // moves as 16-bit pairs: a 32-byte k-step is 32 int8 k or 16 bf16 k.
+    const int64_t xk = xq ? a->He / 2 : a->He;  // row length in 16-bit units
     launch(L0, k_pack_a,
-           dim3(static_cast<unsigned>((a->He / 16 + PA_STEPS - 1) / PA_STEPS),
+           dim3(static_cast<unsigned>((xk / 16 + PA_STEPS - 1) / PA_STEPS),
                 static_cast<unsigned>(mblocks)),
-           dim3(256), 0, static_cast<const uint16_t*>(a->token_x),
-           reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, a->He);
+           dim3(256), 0, static_cast<const uint16_t*>(g1.A),
+           reinterpret_cast<uint4*>(ws + pl.off_xfrag), T, xk);
     g1.A = ws + pl.off_xfrag;
     g1.a_frag = 1;
-    g1.a_mbs = a->He * 64;
-    // A6's q^R columns: 128x256 tiles and three buffers, two workgroups
-    // per CU so one's epilogue stores overlap the other's main loop (256-row
-    // tiles measured the same).  A1 and the fused q^C + W^UK tiles: 256x256,
-    // eight waves, four buffers (A1 at T = 4096: 157 vs 167 us).
+    g1.a_mbs = xk * 64;
+    // A6's q^R columns (bf16) and the quantised A6 and W^UK product:
+    // 128x256 tiles and three buffers, two workgroups per CU so one's
+    // epilogue stores overlap the other's main loop (256-row tiles measured
+    // the same for q^R).  A1 and the fused q^C + W^UK tiles: 256x256, eight
+    // waves, four buffers (A1 at T = 4096: 157 vs 167 us).
     const unsigned mt2 = static_cast<unsigned>((T + G_TM_HALF - 1) / G_TM_HALF);
     g1.ntiles0 = static_cast<int>((g1.N0 + G_TN - 1) / G_TN);
     const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + G_TN - 1) / G_TN);
-    launch(L1, k_gemm<EPI_PARTIAL, 256, 4>,
-           dim3(nt1, static_cast<unsigned>((T + 255) / 256), static_cast<unsigned>(pl.ksplit)),
-           dim3(64 * gemm_waves<256>()), 0, g1);
+    const dim3 grid1(nt1, static_cast<unsigned>((T + 255) / 256), static_cast<unsigned>(pl.ksplit));
+    if (xq)
+      launch(L1, k_gemm<EPI_PARTIAL, 256, 4, 0, A_I8>, grid1, dim3(64 * gemm_waves<256>()), 0, g1);
+    else
+      launch(L1, k_gemm<EPI_PARTIAL, 256, 4>, grid1, dim3(64 * gemm_waves<256>()), 0, g1);
     mark(MLA_PHASE_AFTER_DOWN);
     finish();
     mark(MLA_PHASE_AFTER_NORM);
@@ -2533,35 +2347,26 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
              dim3(64 * gemm_waves<256>()), 0, gq);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
-      launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, dim3(nt6, mt2, 1), dim3(256), 0, g6);
+      if (quant) {
+        // int8 c^Q . int8 [W^UQ | W^QR]; q^C leaves as bf16 hi and lo
+        // fragments so that the W^UK product runs as one bf16 GEMM over
+        // K = 2D (q^C hi | lo against W^UK twice): the fp32 q^C of the
+        // quantised modes, to about 16 bits, as the decode kernels' hi + lo
+        // split keeps it.
+        g6.qc_f32 = 0;
+        g6.qc_split = 1;
+        launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3, 0, A_I8>, dim3(nt6, mt2, 1), dim3(256), 0, g6);
+        g8.K = 2 * a->D;
+        g8.KB = a->D;
+      } else {
+        launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, dim3(nt6, mt2, 1), dim3(256), 0, g6);
+      }
       mark(MLA_PHASE_AFTER_UQQR);
       const unsigned nt8 = static_cast<unsigned>((g8.N0 + G_TN - 1) / G_TN);
       launch(L8, k_gemm<EPI_UK, 128, 3>,
              dim3(nt8, static_cast<unsigned>((T + 127) / 128), static_cast<unsigned>(nh)),
              dim3(256), 0, g8);
     }
-  } else {
-    const unsigned mt = static_cast<unsigned>((T + TBM - 1) / TBM);
-    g1.ntiles0 = static_cast<int>((g1.N0 + TBN - 1) / TBN);
-    const unsigned nt1 = static_cast<unsigned>(g1.ntiles0 + (g1.N1 + TBN - 1) / TBN);
-    if (xq)
-      tiled<A_I8, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), L1);
-    else
-      tiled<A_BF16, EPI_PARTIAL>(g1, dim3(nt1, mt, 1), L1);
-    mark(MLA_PHASE_AFTER_DOWN);
-    finish();
-    mark(MLA_PHASE_AFTER_NORM);
-    const unsigned nt6 = static_cast<unsigned>((g6.N0 + TBN - 1) / TBN);
-    if (quant)
-      tiled<A_I8, EPI_UQQR>(g6, dim3(nt6, mt, 1), L6);
-    else
-      tiled<A_BF16, EPI_UQQR>(g6, dim3(nt6, mt, 1), L6);
-    mark(MLA_PHASE_AFTER_UQQR);
-    const unsigned nt8 = static_cast<unsigned>((g8.N0 + TBN - 1) / TBN);
-    if (quant)
-      tiled<A_F32SPLIT, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
-    else
-      tiled<A_BF16, EPI_UK>(g8, dim3(nt8, mt, static_cast<unsigned>(nh)), L8);
   }
   if (q8out && !qh) {
     const int64_t rows = T * a->N;

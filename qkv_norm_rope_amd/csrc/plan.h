@@ -28,7 +28,7 @@ constexpr int SYNC_STRIDE = 64;
 // the workspace carve-up.  A pure function of the arguments.
 struct MlaPlan {
   bool skinny;        // decode-sized T: weight-streaming kernels
-  bool gemm256;       // large T, bf16: 256x256-tile MFMA GEMMs
+  bool gemm256;       // large T (every mode): LDS-pipelined MFMA GEMMs
   bool fuse_uk;       // gemm256 with the W^UK product fused into A6's q^C tiles
   bool merge_uk;      // skinny bf16, one row block: A6 and the W^UK product in
                       // one launch (k_decode_tail), handing q^C over per head
