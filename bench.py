@@ -171,7 +171,7 @@ def qkv_bytes(c, n_valid):
 # source still hashes to what was profiled; otherwise null.
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                            "profiles", "mla_decode_up_projection_hbm_traffic.md")
+                            "profiles", "mla_decode_up_uk_hbm_traffic.md")
 KERNEL_SOURCES = ("qkv_norm_rope_amd/csrc/mla_prolog_v2.hip",
                   "qkv_norm_rope_amd/csrc/device_common.h",
                   "qkv_norm_rope_amd/csrc/mla_device.h")
