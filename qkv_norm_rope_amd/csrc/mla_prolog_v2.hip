@@ -342,10 +342,15 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   constexpr int PITCH = TN + 4;  // words per LDS row
   constexpr int NA = (AK == A_F32SPLIT) ? 2 : 1;  // 16-byte A loads per fragment
   __shared__ uint32_t lds[KW][MB * 32][PITCH];
-  // LDS-staged A (bf16, MB = 1), up to ACAP k-steps of this workgroup's
-  // split in fragment order: chunk (step s, lane) at (s - s_lo)*64 + lane.
-  static_assert(ALDS == ALDS_NONE || (MB == 1 && AK == A_BF16), "LDS-staged A: one bf16 row block");
-  __shared__ uint4 alds[ALDS != ALDS_NONE ? ACAP * 64 : 1];
+  // LDS-staged A, up to ACAP k-steps of this workgroup's split: row-major
+  // bf16 A (one row block), or fragment-layout bf16 or fp32-split A (MB row
+  // blocks).  Chunk n (of NA) of lane `lane`, k-step s, row block mb sits at
+  // ((mb*NA + n)*ACAP + s - s_lo)*64 + lane, so each wave's read of one
+  // operand chunk is 64 consecutive 16-byte words.
+  static_assert(ALDS == ALDS_NONE || (ALDS == ALDS_ROWMAJOR && MB == 1 && AK == A_BF16) ||
+                    (ALDS == ALDS_FRAG && AK != A_I8),
+                "LDS-staged A: one row-major bf16 row block, or bf16 / fp32 fragments");
+  __shared__ uint4 alds[ALDS != ALDS_NONE ? ACAP * 64 * NA * MB : 1];
 
   const int lane = threadIdx.x & 63;
   // Wave-level quantities live in SGPRs: the per-step load offsets below are
@@ -477,7 +482,11 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
     for (int u = 0; u < P; ++u) {
       const int s = (s0 + u) < s_last ? (s0 + u) : s_last;
       if constexpr (ALDS != ALDS_NONE) {
-        x.a[u][0][0] = alds[(s - s_lo) * 64 + lane];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int n = 0; n < NA; ++n)
+            x.a[u][mb][n] = alds[((mb * NA + n) * ACAP + (s - s_lo)) * 64 + lane];
       } else {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -524,26 +533,36 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   // hits) so the load sequence never depends on a branch.
   Batch X, Y;
   if constexpr (ALDS == ALDS_FRAG) if (cnt > 0) {  // cnt is uniform over the workgroup
-    // Fragment-layout A: the split's chunks are one contiguous run of
-    // 64*cnt 16-byte chunks, copied straight into LDS (cnt <= ACAP).
+    // Fragment-layout A: per row block the split's chunks are one
+    // contiguous run of 64*NA*cnt 16-byte chunks (cnt <= ACAP); chunk r of
+    // row block mb is lane (r / NA) % 64, part r % NA, k-step s_lo + r /
+    // (64*NA), and lands at its LDS slot.
     constexpr int NT = 64 * NW * KW;
-    constexpr int PER = (ACAP * 64 + NT - 1) / NT;
-    const int total = 64 * cnt;
-    const rsrc_t rx = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_zs +
-                                    static_cast<int64_t>(s_lo) * 1024,
-                                static_cast<uint32_t>(total) * 16u);
+    constexpr int PER = (ACAP * 64 * NA * MB + NT - 1) / NT;
+    const int run = 64 * NA * cnt;  // chunks per row block
+    const int total = MB * run;
+    const rsrc_t rx = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(z) * p.a_zs,
+                                static_cast<uint32_t>(MB * p.a_mbs));
     uint4 st[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       int c = static_cast<int>(threadIdx.x) + i * NT;
       c = c < total ? c : total - 1;
-      st[i] = bld16(rx, static_cast<uint32_t>(c) * 16u, 0u);
+      const int mb = c / run, r = c - mb * run;
+      st[i] = bld16(rx,
+                    static_cast<uint32_t>(mb * p.a_mbs) +
+                        (static_cast<uint32_t>(s_lo) * 64u * NA + static_cast<uint32_t>(r)) * 16u,
+                    0u);
     }
     load_b(X, w_lo);  // unconditional: a branch here would drain the staging loads
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = static_cast<int>(threadIdx.x) + i * NT;
-      if (c < total) alds[c] = st[i];
+      if (c < total) {
+        const int mb = c / run, r = c - mb * run;
+        const int ls = r / (64 * NA), rem = r - ls * 64 * NA;
+        alds[((mb * NA + rem % NA) * ACAP + ls) * 64 + rem / NA] = st[i];
+      }
     }
     lds_barrier();  // keeps the first weight batch in flight
     if (w_lo < w_hi) load_a(X, w_lo);
@@ -1980,8 +1999,13 @@ void skinny_a6(const GemmParams& g6, bool quant, const Launch& L) {
   else
     skinny<A_BF16, MB, 1, 3, a6_kw<MB>(), EPI_UQQR>(g6, dim3(nt, 1, 1), L);
 }
-// A8 stages a head's q^C (K = D <= 16 k-steps) in LDS once per workgroup.
+// A8 stages a head's q^C (K = D <= 16 k-steps) in LDS once per workgroup;
+// the one-workgroup-per-head query-quant variant stages fp32 q^C (<= 8
+// k-steps).  (Staging fp32 q^C in the four-wave quantised tiles below made
+// them slower, 5.4 -> 6.7 us at T = 64: the staging latency comes before
+// the first MFMA, and the lockstep waves' re-reads hit L1.)
 constexpr int A8_LDS_STEPS = 16;
+constexpr int A8_LDS_STEPS_F32 = 8;
 template <int MB>
 void skinny_a8(const GemmParams& g8, int nheads, bool quant, const Launch& L) {
   constexpr int NW = a8_nw<MB>();
@@ -2275,13 +2299,25 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     if (pl.merge_uk) {
       // the W^UK product ran inside k_decode_tail
     } else if (qh) {
+      // one workgroup per head; its fp32 q^C (D <= 128) staged in LDS once
+      // (16 waves re-reading it: 11.2 -> 9.9 us at the DeepSeek-V3 shape)
       const dim3 grid(1, 1, static_cast<unsigned>(nh));
-      if (a->Hckv <= 128)
+      const bool stage = a->D / 16 <= A8_LDS_STEPS_F32;
+      if (a->Hckv <= 128 && stage)
+        launch(L8, k_skinny<A_F32SPLIT, 1, 1, 4, 1, EPI_UK, 2, ALDS_FRAG, A8_LDS_STEPS_F32, true>,
+               grid, dim3(64 * 4), 0, g8);
+      else if (a->Hckv <= 128)
         launch(L8, k_skinny<A_F32SPLIT, 1, 1, 4, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,
                grid, dim3(64 * 4), 0, g8);
+      else if (a->Hckv <= 256 && stage)
+        launch(L8, k_skinny<A_F32SPLIT, 1, 1, 8, 1, EPI_UK, 2, ALDS_FRAG, A8_LDS_STEPS_F32, true>,
+               grid, dim3(64 * 8), 0, g8);
       else if (a->Hckv <= 256)
         launch(L8, k_skinny<A_F32SPLIT, 1, 1, 8, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,
                grid, dim3(64 * 8), 0, g8);
+      else if (stage)
+        launch(L8, k_skinny<A_F32SPLIT, 1, 1, 16, 1, EPI_UK, 2, ALDS_FRAG, A8_LDS_STEPS_F32, true>,
+               grid, dim3(64 * 16), 0, g8);
       else
         launch(L8, k_skinny<A_F32SPLIT, 1, 1, 16, 1, EPI_UK, 2, ALDS_NONE, A_LDS_STEPS, true>,
                grid, dim3(64 * 16), 0, g8);
