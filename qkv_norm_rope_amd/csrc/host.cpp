@@ -70,7 +70,9 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   // Prefill fuses the W^UK product into the q^C tiles of A6 when a wave's
   // 128 q^C columns are exactly one head (D = 128) and the q^C columns end
   // on a tile boundary.
-  pl.fuse_uk = pl.gemm256 && !quant && a->D == 128 && (a->N * a->D) % G_TN == 0;
+  // (FULL_KV_INT8 keeps the unfused path: its query quant needs q^N in fp32)
+  pl.fuse_uk = pl.gemm256 && a->quant_mode != MLA_QUANT_FULL_KV_INT8 && a->D == 128 &&
+               (a->N * a->D) % G_TN == 0;
   // Decode with one row block in bf16 runs the up projection and the W^UK
   // product as one launch when a head's q^C and W^UK slices fit a wave's
   // registers (D <= 128).

@@ -932,7 +932,6 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   typedef typename AccT<AK>::type Acc;
   static_assert(AK == A_BF16 || AK == A_I8, "bf16 or int8 operands (16 or 32 k per 16 bytes)");
   constexpr bool SWAP = EPI == EPI_QN;
-  static_assert(!SWAP || AK == A_BF16, "the fused W^UK product takes bf16 q^C");
   static_assert(!SWAP || (TM == 256 && DH == 128 && NBUF == 4),
                 "fused W^UK product: 256-row tiles, one 128-wide head per wave");
   static_assert(TM != 256 || NBUF == 4, "256-row tiles: the double-buffered pipeline");
@@ -1065,8 +1064,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(b[j]), as_bf16x8(a[i]),
-                                                                 acc[i][j], 0, 0, 0);
+            mfma_step<AK>(acc[i][j], b[j], a[i]);
           else
             mfma_step<AK>(acc[i][j], a[i], b[j]);
         }
@@ -1113,8 +1111,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[j]), as_bf16x8(fa[i]),
-                                                                 acc[i][j], 0, 0, 0);
+            mfma_step<AK>(acc[i][j], fb[j], fa[i]);
           else
             mfma_step<AK>(acc[i][j], fa[i], fb[j]);
         }
@@ -1190,18 +1187,63 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   vm_barrier<0>();
 
   if constexpr (EPI == EPI_QN) {
-    // q^C as bf16 operand fragments in registers: qc[i][k] = 16-k step k of
-    // the wave's 128 q^C columns (its head) for m-block i.
-    uint4 qc[MI][8];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
+    // q^C as bf16 operand fragments in registers: qc[0][i][k] = 16-k step k
+    // of the wave's 128 q^C columns (its head) for m-block i.  With int8
+    // operands the accumulators are integer sums, dequantised as the
+    // unfused epilogue does (sum * s_t * dq_c: the token's c^Q scale, the
+    // column's dequant scale, both staged in LDS) and carried as bf16 hi
+    // (qc[0]) and lo = bf16(q^C - hi) (qc[1]); the W^UK product then
+    // multiplies both, as the decode kernels' fp32-split operand does.
+    constexpr int NQ = AK == A_I8 ? 2 : 1;
+    uint4 qc[NQ][MI][8];
+    if constexpr (AK == A_I8) {
+      // stage buffer 3's A array (free until the passes' output staging)
+      float* scl = reinterpret_cast<float*>(&SA(C3{})[0][0][0]);
+      for (int t = threadIdx.x; t < TM + G_TN; t += 64 * NWV) {
+        float v = 0.f;
+        if (t < TM) {
+          if (m0 + t < p.M) v = gld(p.cq_scale + m0 + t);
+        } else {
+          v = gld(p.dq + n0 + (t - TM));  // the tile's columns are all q^C columns
+        }
+        scl[t] = v;
+      }
+      lds_barrier();
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const f32x16_t& c = acc[i][k >> 1];
-        const int o = 8 * (k & 1);
-        qc[i][k] = make_uint4(pack_bf16x2(c[o], c[o + 1]), pack_bf16x2(c[o + 2], c[o + 3]),
-                              pack_bf16x2(c[o + 4], c[o + 5]), pack_bf16x2(c[o + 6], c[o + 7]));
+        // registers 8(k&1) .. +7 of block k>>1: columns cb + 16(k&1) + {0..3, 8..11}
+        const int cb = TM + 32 * (4 * wn + (k >> 1)) + 4 * g + 16 * (k & 1);
+        const float4 d0 = *reinterpret_cast<const float4*>(scl + cb);
+        const float4 d1 = *reinterpret_cast<const float4*>(scl + cb + 8);
+        const float dq[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const float cs = scl[TPW * wm + 32 * i + li];
+          const int o = 8 * (k & 1);
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = static_cast<float>(acc[i][k >> 1][o + 2 * e]) * cs * dq[2 * e];
+            const float b = static_cast<float>(acc[i][k >> 1][o + 2 * e + 1]) * cs * dq[2 * e + 1];
+            const uint16_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+            hw[e] = static_cast<uint32_t>(ha) | (static_cast<uint32_t>(hb) << 16);
+            lw[e] = pack_bf16x2(a - bf16_to_f32(ha), b - bf16_to_f32(hb));
+          }
+          qc[0][i][k] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          qc[NQ - 1][i][k] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const Acc& c = acc[i][k >> 1];
+          const int o = 8 * (k & 1);
+          qc[0][i][k] = make_uint4(pack_bf16x2(c[o], c[o + 1]), pack_bf16x2(c[o + 2], c[o + 3]),
+                                   pack_bf16x2(c[o + 4], c[o + 5]), pack_bf16x2(c[o + 6], c[o + 7]));
+        }
+    }
     // The tile's two heads (wn = 0, 1) run the W^UK product over passes of
     // PB = 2 column blocks (32 columns each) of Hckv (MI m-blocks x PB
     // column blocks of accumulators: the rest of the AGPRs and the VGPRs
@@ -1256,11 +1298,13 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
 #pragma unroll
         for (int jb = 0; jb < PB; ++jb) wf[jb] = pbuf(bc, jb)[(wn * 8 + ks) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
-          for (int jb = 0; jb < PB; ++jb)
-            o[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wf[jb]), as_bf16x8(qc[i][ks]),
-                                                                o[i][jb], 0, 0, 0);
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int jb = 0; jb < PB; ++jb)
+              o[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(wf[jb]), as_bf16x8(qc[q][i][ks]), o[i][jb], 0, 0, 0);
       }
       // o[i][jb]: lane l holds token 32*(MI*wm+i) + l%32, registers r the
       // output columns 32*(PB*pp+jb) + 8(r/4) + 4g + r%4.  Transpose each
@@ -2363,11 +2407,15 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       // rope region at column 0 every column is a rope column).
       const int64_t ND = a->N * a->D;
       GemmParams gr = g6;
-      gr.B0 = wuqqr + (ND / 32) * (a->Hcq / 8) * 32;
+      gr.B0 = wuqqr + (ND / 32) * (a->Hcq / (quant ? 16 : 8)) * 32;
       gr.N0 = a->N * a->Dr;
       gr.ND = 0;
-      launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>,
-             dim3(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt2, 1), dim3(256), 0, gr);
+      if (quant) gr.dq = g6.dq + ND;  // the W^QR columns' dequant scales
+      const dim3 gridr(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt2, 1);
+      if (quant)
+        launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3, 0, A_I8>, gridr, dim3(256), 0, gr);
+      else
+        launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, gridr, dim3(256), 0, gr);
       mark(MLA_PHASE_AFTER_UQQR);
       // q^C tiles with the W^UK product in the epilogue.
       GemmParams gq = g6;
@@ -2378,9 +2426,11 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gq.q_out = g8.q_out;
       gq.q_ld = g8.q_ld;
       gq.q_bstride = g8.q_bstride;
-      const unsigned mt = static_cast<unsigned>((T + 255) / 256);
-      launch(L8, k_gemm<EPI_QN, 256, 4, 128>, dim3(static_cast<unsigned>(ND / G_TN), mt, 1),
-             dim3(64 * gemm_waves<256>()), 0, gq);
+      const dim3 gridq(static_cast<unsigned>(ND / G_TN), static_cast<unsigned>((T + 255) / 256), 1);
+      if (quant)
+        launch(L8, k_gemm<EPI_QN, 256, 4, 128, A_I8>, gridq, dim3(64 * gemm_waves<256>()), 0, gq);
+      else
+        launch(L8, k_gemm<EPI_QN, 256, 4, 128>, gridq, dim3(64 * gemm_waves<256>()), 0, gq);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
       if (quant) {

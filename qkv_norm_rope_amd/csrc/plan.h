@@ -30,6 +30,7 @@ struct MlaPlan {
   bool skinny;        // decode-sized T: weight-streaming kernels
   bool gemm256;       // large T (every mode): LDS-pipelined MFMA GEMMs
   bool fuse_uk;       // gemm256 with the W^UK product fused into A6's q^C tiles
+                      // (bf16, or int8 with q^C as bf16 hi + lo)
   bool merge_uk;      // skinny bf16, one row block: A6 and the W^UK product in
                       // one launch (k_decode_tail), handing q^C over per head
   int mb;             // 32-row blocks held per wave (skinny only)

@@ -175,13 +175,29 @@ def test_mla_parity_prefill_T4096():
     gh.announce(f"  ok (worst err/tol) {gh.check_mla(w, out, before, chunk=512)}")
 
 
-def test_mla_prefill_partial_quant_tiled_path():
-    # T > 128 takes the tiled kernels in the partial-quant scenario too.
+def test_mla_prefill_partial_quant_large_t_path():
+    # T > 128 takes the large-T GEMMs in the partial-quant scenario too
+    # (D = 64: the unfused int8 up projection and hi | lo W^UK product).
     cfg = get_config("mla_ragged_q").replace(B=3, S=67, block_num=8,
                                             block_size=32, n_skip=9,
                                             seed=2010, layout="BSH")
     w = make_workload(cfg)
-    gh.announce(f"mla tiled quant T={cfg.T}")
+    gh.announce(f"mla large-T quant T={cfg.T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev, bsh=True)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
+@pytest.mark.parametrize("mode", ["partial_kv_int8", "partial_kv_bf16",
+                                  "full_kv_bf16", "full_kv_int8"])
+def test_mla_large_t_quant_fused(mode):
+    # D = 128 with N*D a multiple of 256: the int8 q^C tiles carry the W^UK
+    # product in their epilogue (q^C as bf16 hi + lo in registers), except
+    # FULL_KV_INT8, whose query quant takes the unfused path.
+    w = make_workload(get_config("mla_fused_q").replace(quant_mode=mode))
+    gh.announce(f"mla fused quant {mode} T={w.cfg.T}")
     dev = gh.upload(w)
     before = _before(dev, ["kv_cache", "kr_cache"])
     out = gh.run_mla_gpu(w, dev, bsh=True)

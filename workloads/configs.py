@@ -215,6 +215,12 @@ CONFIGS = {
                                   He=256, Hcq=160, N=4, D=128, Hckv=224,
                                   Dr=64, block_num=4, block_size=128,
                                   n_skip=5, seed=2018, layout="BSH"),
+    # the same fused path in the quantised modes (int8 q^C tiles, q^C as
+    # bf16 hi + lo into W^UK): Hcq a multiple of 64, two heads per tile
+    "mla_fused_q": MlaConfig("mla_fused_q_T300", B=3, S=100, He=256, Hcq=192,
+                             N=4, D=128, Hckv=224, Dr=64, block_num=4,
+                             block_size=128, n_skip=5, seed=2020, layout="BSH",
+                             quant_mode="partial_kv_int8"),
     # prefill-sized T with no dimension a multiple of the 256x256 GEMM tile
     "mla_prefill_ragged": MlaConfig("mla_prefill_ragged_T300", B=3, S=100,
                                     He=512, Hcq=320, N=5, D=64, Hckv=96,
