@@ -2282,21 +2282,28 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   const Launch& L6 = Lk[MLA_KERNEL_UQQR];
   const Launch& L8 = Lk[MLA_KERNEL_UK];
 
+  // The large-T plan splits at most FIN_SPLIT_SMALL ways: its instances
+  // hold fewer partials per thread and keep more workgroups resident.
   auto finish = [&]() {
     const dim3 grid(static_cast<unsigned>(T));
-    if (qm == 0 && pl.ksplit <= FIN_SPLIT_SMALL)
-      launch(Lf, k_down_finish<0, FIN_SPLIT_SMALL>, grid, fin_block,
-             static_cast<uint32_t>(fin_smem), f);
-    else if (qm == 0)
-      launch(Lf, k_down_finish<0>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
-    else if (qm == 1)
-      launch(Lf, k_down_finish<1>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
-    else if (qm == 2)
-      launch(Lf, k_down_finish<2>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
-    else if (qm == 3)
-      launch(Lf, k_down_finish<3>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
-    else
-      launch(Lf, k_down_finish<4>, grid, fin_block, static_cast<uint32_t>(fin_smem), f);
+    const uint32_t sm = static_cast<uint32_t>(fin_smem);
+    if (pl.ksplit <= FIN_SPLIT_SMALL) {
+      switch (qm) {
+        case 0: launch(Lf, k_down_finish<0, FIN_SPLIT_SMALL>, grid, fin_block, sm, f); break;
+        case 1: launch(Lf, k_down_finish<1, FIN_SPLIT_SMALL>, grid, fin_block, sm, f); break;
+        case 2: launch(Lf, k_down_finish<2, FIN_SPLIT_SMALL>, grid, fin_block, sm, f); break;
+        case 3: launch(Lf, k_down_finish<3, FIN_SPLIT_SMALL>, grid, fin_block, sm, f); break;
+        default: launch(Lf, k_down_finish<4, FIN_SPLIT_SMALL>, grid, fin_block, sm, f); break;
+      }
+      return;
+    }
+    switch (qm) {
+      case 0: launch(Lf, k_down_finish<0>, grid, fin_block, sm, f); break;
+      case 1: launch(Lf, k_down_finish<1>, grid, fin_block, sm, f); break;
+      case 2: launch(Lf, k_down_finish<2>, grid, fin_block, sm, f); break;
+      case 3: launch(Lf, k_down_finish<3>, grid, fin_block, sm, f); break;
+      default: launch(Lf, k_down_finish<4>, grid, fin_block, sm, f); break;
+    }
   };
 
   const int nh = static_cast<int>(a->N);
