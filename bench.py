@@ -762,10 +762,10 @@ def main():
         pms, pk = pr["ms"], pr["kernel_ms"]
         fl = mla_flops(pc)
         # The prefill plan fuses q^C.W^UK into the q^C tiles of the up
-        # projection: the two launches after the norm phase (q^R tiles, then
-        # q^C tiles with the W^UK product) are one roofline unit.
+        # projection and runs the q^R tiles in the same launch: everything
+        # after the norm phase is one roofline unit (one launch, or two).
         upf = uqqr_flops(pc) + uk_flops(pc)
-        up_ms = pk[2] + pk[3]
+        up_ms = sum(k for k in pk[2:4] if k is not None)
         frac = fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
         out["prefill"] = {
             "workload": pc.name, "tokens_per_s": pc.T / (pms * 1e-3),
@@ -778,7 +778,7 @@ def main():
             "mfma_frac": frac, "target_mfma_frac": PREFILL_TARGET_FRAC,
             "gap_to_target": PREFILL_TARGET_FRAC - frac,
             "kernel_us": dict(zip(("down", "norm", "up_qr_rope",
-                                   "up_qc_uk"),
+                                   "up_qc_uk_qr"),
                                   [None if k is None else k * 1e3 for k in pk])),
             "phase_us": dict(zip(("down", "norm_cache", "up_qr_rope",
                                   "up_qc_uk"),

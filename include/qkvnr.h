@@ -256,8 +256,9 @@ typedef struct MlaPrologV2Args {
 } MlaPrologV2Args;
 
 /* The main kernels of one call, for kernel_events.  With the large-T plan
- * that fuses the W^UK product, MLA_KERNEL_UQQR is the q^R-column launch and
- * MLA_KERNEL_UK the q^C-column launch with the fused W^UK product.  With
+ * that fuses the W^UK product (D = 128), MLA_KERNEL_UK is one launch that
+ * runs the q^C columns with the fused W^UK product and the q^R columns, and
+ * MLA_KERNEL_UQQR is not launched.  With
  * the bf16 decode plan for T <= 32 and D <= 128, MLA_KERNEL_UQQR is one
  * launch that runs the up projection and the W^UK product, and
  * MLA_KERNEL_UK is not launched (mla_prolog_v2_kernels reports which). */

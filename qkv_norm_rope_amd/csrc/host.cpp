@@ -480,11 +480,13 @@ int mla_prolog_v2_kernels(const MlaPrologV2Args* args, uint32_t* mask) {
   if (rc != QKVNR_OK) return rc;
   // Every plan launches each of the main kernels once when there are
   // tokens, except that the merged decode launch runs the W^UK product
-  // inside the up projection's kernel.
+  // inside the up projection's kernel, and the fused large-T launch runs
+  // the q^R columns inside the W^UK one.
   if (args->B * args->S > 0) {
     *mask = (1u << MLA_KERNEL_COUNT) - 1u;
     const MlaPlan pl = make_mla_plan(args);
     if (pl.merge_uk) *mask &= ~(1u << MLA_KERNEL_UK);
+    if (pl.fuse_uk) *mask &= ~(1u << MLA_KERNEL_UQQR);
 
   }
   return QKVNR_OK;

@@ -895,9 +895,10 @@ __device__ __forceinline__ void vm_barrier() {
 // within a group), so the ~32 tiles an XCD runs at once share A and B tiles
 // in its L2.
 constexpr int G_GROUP = 4;
-__device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
+// l: the workgroup's linear index within this set of nx x ny tiles (its XCD
+// is l % 8 when the set starts at a multiple of 8 in the launch).
+__device__ __forceinline__ void gemm_tile(int nx, int ny, int l, int& tx, int& ty) {
   const int n = nx * ny;
-  int l = static_cast<int>(blockIdx.x) + nx * static_cast<int>(blockIdx.y);
   if (n % 8 == 0) l = (l % 8) * (n / 8) + l / 8;
   const int gsz = G_GROUP * nx;
   const int grp = l / gsz;
@@ -926,8 +927,14 @@ __device__ __forceinline__ void gemm_tile(int nx, int ny, int& tx, int& ty) {
 template <int TM>
 constexpr int gemm_waves() { return TM == 256 ? 8 : 4; }
 
-template <int EPI, int TM, int NBUF, int DH = 0, int AK = A_BF16>
-__global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
+// One tile (tx, ty) of batch / split z, run by the calling workgroup on the
+// stage arrays its kernel declares (k_gemm, k_up_fused).
+template <int EPI, int TM, int NBUF, int DH, int AK, int MA>
+__device__ __forceinline__ void gemm_tile_run(
+    const GemmParams& p, const int tx, const int ty, const int z, uint4 (&sa0)[2][MA][64],
+    uint4 (&sa1)[2][MA][64], uint4 (&sa2)[2][MA][64], uint4 (&sa3)[2][MA][64],
+    uint4 (&sb0)[2][8][64], uint4 (&sb1)[2][8][64], uint4 (&sb2)[2][8][64],
+    uint4 (&sb3)[2][8][64]) {
   typedef Epilogue<AK, EPI == EPI_QN ? EPI_UQQR : EPI> Epi;
   typedef typename AccT<AK>::type Acc;
   static_assert(AK == A_BF16 || AK == A_I8, "bf16 or int8 operands (16 or 32 k per 16 bytes)");
@@ -938,7 +945,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   constexpr int NWV = gemm_waves<TM>();  // waves per workgroup
   constexpr int WR = NWV / 2;             // wave rows (two wave columns of 128)
   constexpr int TPW = TM / WR;            // tokens (rows) per wave
-  constexpr int MA = TM / 32;   // A blocks per k-step
+  static_assert(MA == TM / 32, "A blocks per k-step");
   constexpr int MI = TPW / 32;  // m-blocks per wave
   constexpr int AW = MA / NWV;  // A blocks loaded per wave per k-step
   constexpr int BW = 8 / NWV;   // B blocks loaded per wave per k-step
@@ -946,13 +953,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   constexpr int LPW = 2 * (AW + BW);  // loads per wave per stage
   static_assert(TM == 256 || TM == 128, "tile height");
   static_assert(NBUF >= 3 && NBUF <= 4, "stage buffers");
-  // Stage t: A blocks in sa<t>, B blocks in sb<t>, per k-step.  (Separate
-  // arrays: with A and B in one array per stage the compiler drains the
-  // loads in flight before each stage's second k-step.  sa3/sb3 are
-  // referenced only with four buffers, so three-buffer instances do not
-  // allocate them.)
-  __shared__ uint4 sa0[2][MA][64], sa1[2][MA][64], sa2[2][MA][64], sa3[2][MA][64];
-  __shared__ uint4 sb0[2][8][64], sb1[2][8][64], sb2[2][8][64], sb3[2][8][64];
+  // Stage t: A blocks in sa<t>, B blocks in sb<t>, per k-step.
   auto SA = [&](auto bufc) -> uint4 (&)[2][MA][64] {
     constexpr int B = decltype(bufc)::value;
     static_assert(B < NBUF, "stage buffer");
@@ -974,10 +975,7 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wm = w >> 1, wn = w & 1;
   const int g = lane >> 5, li = lane & 31;
-  const int z = blockIdx.z;
   const int zb = EPI == EPI_PARTIAL ? 0 : z;  // batch index
-  int tx, ty;
-  gemm_tile(static_cast<int>(gridDim.x), static_cast<int>(gridDim.y), tx, ty);
 
   const uint4* B;
   int64_t N, n0, ocol0;
@@ -1478,6 +1476,45 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
         Epi::apply(pe, m, gcol, ocol0 + gcol, zb, raw, rawp, pre[u]);
       }
     }
+  }
+}
+
+template <int EPI, int TM, int NBUF, int DH = 0, int AK = A_BF16>
+__global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_gemm(GemmParams p) {
+  // Stage t: A blocks in sa<t>, B blocks in sb<t>, per k-step.  (Separate
+  // arrays: with A and B in one array per stage the compiler drains the
+  // loads in flight before each stage's second k-step.  Three-buffer
+  // instances never name sa3/sb3, so they do not allocate them.)
+  constexpr int MA = TM / 32;
+  __shared__ uint4 sa0[2][MA][64], sa1[2][MA][64], sa2[2][MA][64], sa3[2][MA][64];
+  __shared__ uint4 sb0[2][8][64], sb1[2][8][64], sb2[2][8][64], sb3[2][8][64];
+  int tx, ty;
+  gemm_tile(static_cast<int>(gridDim.x), static_cast<int>(gridDim.y),
+            static_cast<int>(blockIdx.x + gridDim.x * blockIdx.y), tx, ty);
+  const int z = static_cast<int>(blockIdx.z);
+  if constexpr (NBUF == 4)
+    gemm_tile_run<EPI, TM, NBUF, DH, AK, MA>(p, tx, ty, z, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
+  else  // (the fourth buffer is never touched)
+    gemm_tile_run<EPI, TM, NBUF, DH, AK, MA>(p, tx, ty, z, sa0, sa1, sa2, sa2, sb0, sb1, sb2, sb2);
+}
+
+// Prefill up projection in one launch (D = 128): workgroups [0, nq) are the
+// q^C tiles with the fused W^UK product (nqx x ny tiles), the rest the q^R
+// column tiles (nrx x ny), both 256 x 256 with eight waves on one set of
+// stage arrays.  The shorter q^R tiles come last and fill the final round.
+template <int AK>
+__global__ __launch_bounds__(64 * gemm_waves<256>(), 1) void k_up_fused(GemmParams pq, GemmParams pr,
+                                                                       int nqx, int nrx, int ny) {
+  __shared__ uint4 sa0[2][8][64], sa1[2][8][64], sa2[2][8][64], sa3[2][8][64];
+  __shared__ uint4 sb0[2][8][64], sb1[2][8][64], sb2[2][8][64], sb3[2][8][64];
+  const int b = static_cast<int>(blockIdx.x), nq = nqx * ny;
+  int tx, ty;
+  if (b < nq) {
+    gemm_tile(nqx, ny, b, tx, ty);
+    gemm_tile_run<EPI_QN, 256, 4, 128, AK, 8>(pq, tx, ty, 0, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
+  } else {
+    gemm_tile(nrx, ny, b - nq, tx, ty);
+    gemm_tile_run<EPI_UQQR, 256, 4, 0, AK, 8>(pr, tx, ty, 0, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
   }
 }
 
@@ -2410,21 +2447,16 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     finish();
     mark(MLA_PHASE_AFTER_NORM);
     if (pl.fuse_uk) {
-      // q^R: the W^QR columns alone (packed columns from N*D on; with the
-      // rope region at column 0 every column is a rope column).
+      // One launch: the q^C tiles with the W^UK product in their epilogue,
+      // then the q^R tiles.  q^R: the W^QR columns alone (packed columns
+      // from N*D on; with the rope region at column 0 every column is a
+      // rope column).
       const int64_t ND = a->N * a->D;
       GemmParams gr = g6;
       gr.B0 = wuqqr + (ND / 32) * (a->Hcq / (quant ? 16 : 8)) * 32;
       gr.N0 = a->N * a->Dr;
       gr.ND = 0;
       if (quant) gr.dq = g6.dq + ND;  // the W^QR columns' dequant scales
-      const dim3 gridr(static_cast<unsigned>((gr.N0 + G_TN - 1) / G_TN), mt2, 1);
-      if (quant)
-        launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3, 0, A_I8>, gridr, dim3(256), 0, gr);
-      else
-        launch(L6, k_gemm<EPI_UQQR, G_TM_HALF, 3>, gridr, dim3(256), 0, gr);
-      mark(MLA_PHASE_AFTER_UQQR);
-      // q^C tiles with the W^UK product in the epilogue.
       GemmParams gq = g6;
       gq.N0 = ND;
       gq.Buk = wuk;
@@ -2433,11 +2465,15 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       gq.q_out = g8.q_out;
       gq.q_ld = g8.q_ld;
       gq.q_bstride = g8.q_bstride;
-      const dim3 gridq(static_cast<unsigned>(ND / G_TN), static_cast<unsigned>((T + 255) / 256), 1);
+      const int nqx = static_cast<int>(ND / G_TN);
+      const int nrx = static_cast<int>((gr.N0 + G_TN - 1) / G_TN);
+      const int ny = static_cast<int>((T + 255) / 256);
+      const dim3 grid(static_cast<unsigned>((nqx + nrx) * ny));
       if (quant)
-        launch(L8, k_gemm<EPI_QN, 256, 4, 128, A_I8>, gridq, dim3(64 * gemm_waves<256>()), 0, gq);
+        launch(L8, k_up_fused<A_I8>, grid, dim3(64 * gemm_waves<256>()), 0, gq, gr, nqx, nrx, ny);
       else
-        launch(L8, k_gemm<EPI_QN, 256, 4, 128>, gridq, dim3(64 * gemm_waves<256>()), 0, gq);
+        launch(L8, k_up_fused<A_BF16>, grid, dim3(64 * gemm_waves<256>()), 0, gq, gr, nqx, nrx, ny);
+      mark(MLA_PHASE_AFTER_UQQR);
     } else {
       const unsigned nt6 = static_cast<unsigned>((g6.N0 + G_TN - 1) / G_TN);
       if (quant) {

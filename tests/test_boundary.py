@@ -132,11 +132,14 @@ def test_mla_valid_args_pass():
 def test_mla_kernels_mask():
     # every plan launches the four main kernels once when there are tokens,
     # except bf16 decode with one 32-row block (T <= 32), whose up
-    # projection launch also runs the W^UK product
+    # projection launch also runs the W^UK product, and above T = 128 with
+    # D = 128 (except FULL_KV_INT8), whose fused launch also runs q^R
     merged = ("down", "norm", "uqqr")
+    fused = ("down", "norm", "uk")
     for T in (1, 32, 33, 64, 128, 129, 4096):
         for q in ("none", "partial_kv_int8", "full_kv_int8"):
-            want = merged if (q == "none" and T <= 32) else qn.MLA_KERNELS
+            want = merged if (q == "none" and T <= 32) else (
+                fused if (T > 128 and q != "full_kv_int8") else qn.MLA_KERNELS)
             assert qn.mla_prolog_v2_kernels(mla_args(T=T, quant=q)) == want
     e = mla_args(T=0)
     assert qn.mla_prolog_v2_kernels(e) == ()
@@ -525,7 +528,9 @@ def test_mla_fuzzed_args_validate_size_and_plan_consistently():
             # all four kernels, or all but the W^UK launch (merged into the
             # up projection's for bf16 decode with D <= 128 and T <= 32)
             merged = q == "none" and 0 < T <= 32 and a.D <= 128
-            want = 0 if T == 0 else (7 if merged else 15)
+            fused = (T > 128 and q != "full_kv_int8" and a.D == 128
+                     and (a.N * a.D) % 256 == 0)
+            want = 0 if T == 0 else (7 if merged else (11 if fused else 15))
             assert (n.value > 0) == (T > 0) and m.value == want, (it, T, q)
 
 
