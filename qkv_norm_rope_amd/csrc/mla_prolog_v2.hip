@@ -24,6 +24,7 @@
 // column are one 16-byte chunk, which is exactly one lane's MFMA operand.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -1616,7 +1617,10 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
   __shared__ float2 red[FIN_MAX_THREADS / 64];
   const int64_t t = blockIdx.x;
   const int ntot = p.Hcq + p.Hckv + p.Dr;
-  const int nch = ntot / 8;
+  // With two workgroups per token (gridDim.y = 2), y = 0 takes the c^Q
+  // chunks and y = 1 the c^KV and k^R chunks: their norms are independent.
+  const int jlo = gridDim.y == 2 && blockIdx.y == 1 ? p.Hcq / 8 : 0;
+  const int nch = gridDim.y == 2 && blockIdx.y == 0 ? p.Hcq / 8 : ntot / 8;
   const int half = p.Dr >> 1;
   const int64_t slot = gld(p.index + t);
 
@@ -1641,11 +1645,11 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
   };
   // The first chunk's parameters load together with its partials; with one
   // round of chunks (the DeepSeek-V3 shapes) nothing is loaded later.
-  if (static_cast<int>(threadIdx.x) < nch) load_params(threadIdx.x);
+  if (jlo + static_cast<int>(threadIdx.x) < nch) load_params(jlo + threadIdx.x);
 
   // Pass 1: per chunk, sum the partials in split order into row[].
   float sq = 0.f, skv = 0.f, amax = 0.f;
-  for (int j = threadIdx.x; j < nch; j += blockDim.x) {
+  for (int j = jlo + threadIdx.x; j < nch; j += blockDim.x) {
     const int c0 = 8 * j;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float v[MAXS][8];
@@ -1692,9 +1696,9 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
   const bool write_cache = slot >= 0 && slot < p.slots;
 
   // Pass 2: outputs.
-  for (int j = threadIdx.x; j < nch; j += blockDim.x) {
+  for (int j = jlo + threadIdx.x; j < nch; j += blockDim.x) {
     const int c0 = 8 * j;
-    if (j != static_cast<int>(threadIdx.x)) load_params(j);
+    if (j != jlo + static_cast<int>(threadIdx.x)) load_params(j);
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = row[c0 + e];
@@ -1767,7 +1771,7 @@ __global__ __launch_bounds__(FIN_MAX_THREADS) void k_down_finish(FinishParams p)
       }
     }
   }
-  if (QM == 0) return;
+  if (QM == 0 || jlo > 0) return;  // (the c^Q quant below: the c^Q workgroup)
   if (QM == 4) {
     if (threadIdx.x == 0) gst(p.cq_scale + t, 1.0f);  // static quant: no per-token scale
     return;
@@ -2302,7 +2306,11 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     g6.qc_coherent = 1;
   }
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
-  const dim3 fin_block(static_cast<unsigned>(fin_threads(ntot)));
+  // Decode: two workgroups per token (c^Q; c^KV and k^R), sized for the
+  // larger part.
+  const int fin_y = pl.skinny ? 2 : 1;
+  const dim3 fin_block(static_cast<unsigned>(
+      fin_threads(pl.skinny ? std::max<int64_t>(a->Hcq, a->Hckv + a->Dr) : ntot)));
 
   // Launch contexts of the main kernels (optional per-kernel timing).
   Launch Lk[MLA_KERNEL_COUNT];
@@ -2322,7 +2330,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   // The large-T plan splits at most FIN_SPLIT_SMALL ways: its instances
   // hold fewer partials per thread and keep more workgroups resident.
   auto finish = [&]() {
-    const dim3 grid(static_cast<unsigned>(T));
+    const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(fin_y));
     const uint32_t sm = static_cast<uint32_t>(fin_smem);
     if (pl.ksplit <= FIN_SPLIT_SMALL) {
       switch (qm) {
