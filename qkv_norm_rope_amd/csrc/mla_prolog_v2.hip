@@ -2306,11 +2306,10 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
     g6.qc_coherent = 1;
   }
   const size_t fin_smem = static_cast<size_t>(ntot) * sizeof(float);
-  // Decode: two workgroups per token (c^Q; c^KV and k^R), sized for the
-  // larger part.
-  const int fin_y = pl.skinny ? 2 : 1;
-  const dim3 fin_block(static_cast<unsigned>(
-      fin_threads(pl.skinny ? std::max<int64_t>(a->Hcq, a->Hckv + a->Dr) : ntot)));
+  // Two workgroups per token (c^Q; c^KV and k^R), sized for the larger
+  // part.
+  const int fin_y = 2;
+  const dim3 fin_block(static_cast<unsigned>(fin_threads(std::max<int64_t>(a->Hcq, a->Hckv + a->Dr))));
 
   // Launch contexts of the main kernels (optional per-kernel timing).
   Launch Lk[MLA_KERNEL_COUNT];
