@@ -55,7 +55,8 @@ def _prepared(w, d):
 
 
 @pytest.mark.parametrize("key", [1, 3, "mla_mid_dsv3", "mla_full_kvint8",
-                                 "mla_full_kvint8_small_t"])
+                                 "mla_full_kvint8_small_t", "mla_fused_ragged",
+                                 "mla_fused_q"])
 def test_mla_graph_replays_match_eager(key):
     if key == "mla_full_kvint8_small_t":  # the query quantised in A8's epilogue
         w = make_workload(get_config("mla_full_kvint8").replace(B=21, n_skip=2))
