@@ -17,7 +17,7 @@ import torch
 
 from tests import gpu_helpers as gh
 from workloads import make_workload
-from workloads.configs import MlaConfig
+from workloads.configs import MlaConfig, PreConfig
 
 pytestmark = pytest.mark.gpu
 
@@ -83,3 +83,39 @@ def test_mla_fuzzed_shapes_match_oracle(cfg):
     out = gh.run_mla_gpu(w, dev, layout=layout, bsh=cfg.layout == "BSH")
     torch.cuda.synchronize()
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
+def _draw_pre_cases(n, seed=4343):
+    # MlaPreprocessV2 runs on the full-quantisation kernels: He and Hcq
+    # multiples of 64
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        D = int(rng.choice([32, 64, 128]))
+        Dr = int(rng.choice([16, 32, 64]))
+        N = int(rng.integers(1, 7))
+        if (N * D) % Dr:
+            continue
+        T = int(rng.choice([1, 7, 32, 40, 96, 130, 200]))
+        cases.append(PreConfig(
+            f"pfuzz{len(cases)}_T{T}_N{N}_D{D}_Dr{Dr}", B=1, S=T,
+            He=int(rng.choice([64, 128, 256])), Hcq=int(rng.choice([64, 128, 192])),
+            N=N, D=D, Hckv=int(16 * rng.integers(1, 13)), Dr=Dr,
+            block_num=(T + 40) // 32, block_size=32,
+            n_skip=int(rng.integers(0, min(2, T - 1) + 1)), seed=7000 + len(cases)))
+    return cases
+
+
+PRE_CASES = _draw_pre_cases(10)
+
+
+@pytest.mark.parametrize("cfg", PRE_CASES, ids=[c.name for c in PRE_CASES])
+def test_preprocess_fuzzed_shapes_match_oracle(cfg):
+    w = make_workload(cfg)
+    layout = "nd" if cfg.seed % 2 else "packed"
+    gh.announce(f"preprocess fuzz {cfg} layout={layout}")
+    dev = gh.upload(w)
+    before = {k: gh.raw_bits(dev[k]).copy() for k in ("kv_cache", "kr_cache")}
+    out = gh.run_preprocess_gpu(w, dev, layout=layout)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_preprocess(w, out, before)}")
