@@ -929,8 +929,10 @@ template <int TM>
 constexpr int gemm_waves() { return TM == 256 ? 8 : 4; }
 
 // One tile (tx, ty) of batch / split z, run by the calling workgroup on the
-// stage arrays its kernel declares (k_gemm, k_up_fused).
-template <int EPI, int TM, int NBUF, int DH, int AK, int MA>
+// stage arrays its kernel declares (k_gemm, k_up_fused).  NJ: the 32-column
+// blocks this wave computes of its 4 (fewer only where the rest lie past N:
+// a ragged last column tile; the wave still loads and waits like the others).
+template <int EPI, int TM, int NBUF, int DH, int AK, int MA, int NJ = 4>
 __device__ __forceinline__ void gemm_tile_run(
     const GemmParams& p, const int tx, const int ty, const int z, uint4 (&sa0)[2][MA][64],
     uint4 (&sa1)[2][MA][64], uint4 (&sa2)[2][MA][64], uint4 (&sa3)[2][MA][64],
@@ -940,6 +942,8 @@ __device__ __forceinline__ void gemm_tile_run(
   typedef typename AccT<AK>::type Acc;
   static_assert(AK == A_BF16 || AK == A_I8, "bf16 or int8 operands (16 or 32 k per 16 bytes)");
   constexpr bool SWAP = EPI == EPI_QN;
+  static_assert(NJ == 4 || (EPI == EPI_PARTIAL && NJ >= 0 && NJ < 4), "ragged tiles: partials only");
+  constexpr int NJA = NJ > 0 ? NJ : 1;  // accumulator blocks allocated
   static_assert(!SWAP || (TM == 256 && DH == 128 && NBUF == 4),
                 "fused W^UK product: 256-row tiles, one 128-wide head per wave");
   static_assert(TM != 256 || NBUF == 4, "256-row tiles: the double-buffered pipeline");
@@ -1044,24 +1048,24 @@ __device__ __forceinline__ void gemm_tile_run(
     }
   };
 
-  Acc acc[MI][4];
+  Acc acc[MI][NJA];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{};
+    for (int j = 0; j < NJA; ++j) acc[i][j] = Acc{};
 
   auto compute = [&](auto bufc) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint4 a[MI], b[4];
+      uint4 a[MI], b[NJA];
 #pragma unroll
       for (int i = 0; i < MI; ++i) a[i] = SA(bufc)[ks][MI * wm + i][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = SB(bufc)[ks][4 * wn + j][lane];
+      for (int j = 0; j < NJ; ++j) b[j] = SB(bufc)[ks][4 * wn + j][lane];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           if constexpr (SWAP)
             mfma_step<AK>(acc[i][j], b[j], a[i]);
           else
@@ -1102,13 +1106,13 @@ __device__ __forceinline__ void gemm_tile_run(
 #pragma unroll
       for (int i = 0; i < MI; ++i) fa[i] = SA(bufc)[ks][MI * wm + i][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = SB(bufc)[ks][4 * wn + j][lane];
+      for (int j = 0; j < NJ; ++j) fb[j] = SB(bufc)[ks][4 * wn + j][lane];
     };
     auto mm = [&](const uint4 (&fa)[MI], const uint4 (&fb)[4]) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           if constexpr (SWAP)
             mfma_step<AK>(acc[i][j], fb[j], fa[i]);
           else
@@ -1440,7 +1444,7 @@ __device__ __forceinline__ void gemm_tile_run(
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)  // (blocks past NJ lie past N: never stored)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         sep(8 * (r >> 2) + 4 * g + (r & 3), 32 * j + li) =
@@ -1493,10 +1497,24 @@ __global__ __launch_bounds__(64 * gemm_waves<TM>(), TM == 256 ? 1 : 2) void k_ge
   gemm_tile(static_cast<int>(gridDim.x), static_cast<int>(gridDim.y),
             static_cast<int>(blockIdx.x + gridDim.x * blockIdx.y), tx, ty);
   const int z = static_cast<int>(blockIdx.z);
-  if constexpr (NBUF == 4)
+  if constexpr (NBUF == 4 && EPI == EPI_PARTIAL) {
+    // A ragged last column tile (e.g. c^KV + k^R = 576 columns: 2.25 tiles):
+    // a wave whose 128 columns reach past N by 64 or more computes only
+    // the blocks before it (2 or none of its 4).  Same loads and barriers.
+    const int64_t n0 = static_cast<int64_t>(tx < p.ntiles0 ? tx : tx - p.ntiles0) * G_TN;
+    const int64_t valid = (tx < p.ntiles0 ? p.N0 : p.N1) - n0 -
+                          128 * (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) & 1);
+    if (valid > 64)
+      gemm_tile_run<EPI, TM, NBUF, DH, AK, MA>(p, tx, ty, z, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
+    else if (valid > 0)
+      gemm_tile_run<EPI, TM, NBUF, DH, AK, MA, 2>(p, tx, ty, z, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
+    else
+      gemm_tile_run<EPI, TM, NBUF, DH, AK, MA, 0>(p, tx, ty, z, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
+  } else if constexpr (NBUF == 4) {
     gemm_tile_run<EPI, TM, NBUF, DH, AK, MA>(p, tx, ty, z, sa0, sa1, sa2, sa3, sb0, sb1, sb2, sb3);
-  else  // (the fourth buffer is never touched)
+  } else {  // (the fourth buffer is never touched)
     gemm_tile_run<EPI, TM, NBUF, DH, AK, MA>(p, tx, ty, z, sa0, sa1, sa2, sa2, sb0, sb1, sb2, sb2);
+  }
 }
 
 // Prefill up projection in one launch (D = 128): workgroups [0, nq) are the
