@@ -342,16 +342,26 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   constexpr int TN = 32 * NB * NW;
   constexpr int PITCH = TN + 4;  // words per LDS row
   constexpr int NA = (AK == A_F32SPLIT) ? 2 : 1;  // 16-byte A loads per fragment
-  __shared__ uint32_t lds[KW][MB * 32][PITCH];
   // LDS-staged A, up to ACAP k-steps of this workgroup's split: row-major
-  // bf16 A (one row block), or fragment-layout bf16 or fp32-split A (MB row
-  // blocks).  Chunk n (of NA) of lane `lane`, k-step s, row block mb sits at
+  // bf16 A, or fragment-layout bf16 or fp32-split A (MB row blocks).  Chunk
+  // n (of NA) of lane `lane`, k-step s, row block mb sits at
   // ((mb*NA + n)*ACAP + s - s_lo)*64 + lane, so each wave's read of one
   // operand chunk is 64 consecutive 16-byte words.
-  static_assert(ALDS == ALDS_NONE || (ALDS == ALDS_ROWMAJOR && MB == 1 && AK == A_BF16) ||
+  static_assert(ALDS == ALDS_NONE || (ALDS == ALDS_ROWMAJOR && MB <= 2 && AK == A_BF16) ||
                     (ALDS == ALDS_FRAG && AK != A_I8),
-                "LDS-staged A: one row-major bf16 row block, or bf16 / fp32 fragments");
-  __shared__ uint4 alds[ALDS != ALDS_NONE ? ACAP * 64 * NA * MB : 1];
+                "LDS-staged A: row-major bf16 (one or two row blocks), or bf16 / fp32 fragments");
+  // The waves' partial tiles (summed over KW in the epilogue).  With two
+  // row-major row blocks staged, they share the staged A's memory (both
+  // together would exceed the CU's 160 KB): a barrier separates the main
+  // loop's last A read from the first partial-tile write.
+  constexpr bool ALIAS = ALDS == ALDS_ROWMAJOR && MB > 1;
+  constexpr int ALDS_CH = ALDS != ALDS_NONE ? ACAP * 64 * NA * MB : 1;
+  constexpr int TILE_CH = (KW * MB * 32 * PITCH + 3) / 4;
+  __shared__ uint4 alds[ALIAS && TILE_CH > ALDS_CH ? TILE_CH : ALDS_CH];
+  __shared__ uint32_t lds_own[ALIAS ? 1 : KW][ALIAS ? 1 : MB * 32][ALIAS ? 1 : PITCH];
+  typedef uint32_t TileLds[KW][MB * 32][PITCH];
+  TileLds& lds = *reinterpret_cast<TileLds*>(ALIAS ? static_cast<void*>(alds)
+                                                   : static_cast<void*>(lds_own));
 
   const int lane = threadIdx.x & 63;
   // Wave-level quantities live in SGPRs: the per-step load offsets below are
@@ -569,15 +579,15 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
     if (w_lo < w_hi) load_a(X, w_lo);
   }
   if constexpr (ALDS == ALDS_ROWMAJOR) if (cnt > 0) {
-    // Stage rows 0..31 of A over this split's k range [16*s_lo, 16*s_hi):
-    // thread c of the 64*cnt 16-byte chunks takes row c / (2*cnt), chunk
-    // c % (2*cnt), so each wave reads 1 KB of consecutive row bytes.  Rows
-    // past M repeat row M-1 (their products are never stored); surplus
-    // threads repeat the last chunk.  The loads are issued before the first
-    // weight batch, so both are in flight together.
+    // Stage rows 0..32*MB-1 of A over this split's k range [16*s_lo,
+    // 16*s_hi): thread c of the 64*cnt*MB 16-byte chunks takes row
+    // c / (2*cnt), chunk c % (2*cnt), so each wave reads 1 KB of consecutive
+    // row bytes.  Rows past M repeat row M-1 (their products are never
+    // stored); surplus threads repeat the last chunk.  The loads are issued
+    // before the first weight batch, so both are in flight together.
     constexpr int NT = 64 * NW * KW;
-    constexpr int PER = (A_LDS_STEPS * 64 + NT - 1) / NT;
-    const int total = 64 * cnt;
+    constexpr int PER = (ACAP * 64 * MB + NT - 1) / NT;
+    const int total = 64 * cnt * MB;
     const int per_row = 2 * cnt;
     // Buffer loads like the weight stream (loads of one kind complete in
     // order, so waiting for these does not drain the weight batch).
@@ -598,7 +608,7 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
       int c = static_cast<int>(threadIdx.x) + i * NT;
       c = c < total ? c : total - 1;
       const int row = c / per_row, q = c % per_row;
-      alds[(q >> 1) * 64 + (q & 1) * 32 + row] = st[i];
+      alds[((row >> 5) * ACAP + (q >> 1)) * 64 + (q & 1) * 32 + (row & 31)] = st[i];
     }
     lds_barrier();  // keeps the first weight batch in flight
     if (w_lo < w_hi) load_a(X, w_lo);
@@ -620,6 +630,7 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
 
   // Stage: 32x32 MFMA output, lane l / register r -> row 8*(r/4) + 4*(l/32)
   // + r%4, column l%32.
+  if constexpr (ALIAS) __syncthreads();
   if (active)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -2081,6 +2092,13 @@ void skinny_a1(const GemmParams& g1, const MlaPlan& pl, bool xq, const Launch& L
       // one column block per wave, two waves across, K over 8 waves
       launch(L, k_skinny<A_BF16, 1, 1, 2, KW, EPI_PARTIAL, 4, ALDS_ROWMAJOR>, grid,
              dim3(64 * 2 * KW), 0, g1);
+      return;
+    }
+  } else if constexpr (MB == 2) {
+    if (pl.steps_per_split <= A_LDS_STEPS) {
+      // the same shape over two row blocks (x split staged once: 128 KB)
+      launch(L, k_skinny<A_BF16, 2, 1, 2, 8, EPI_PARTIAL, 3, ALDS_ROWMAJOR>, grid,
+             dim3(64 * 2 * 8), 0, g1);
       return;
     }
   }
