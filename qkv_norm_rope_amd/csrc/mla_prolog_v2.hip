@@ -347,9 +347,10 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   // n (of NA) of lane `lane`, k-step s, row block mb sits at
   // ((mb*NA + n)*ACAP + s - s_lo)*64 + lane, so each wave's read of one
   // operand chunk is 64 consecutive 16-byte words.
-  static_assert(ALDS == ALDS_NONE || (ALDS == ALDS_ROWMAJOR && MB <= 2 && AK == A_BF16) ||
+  static_assert(ALDS == ALDS_NONE || (ALDS == ALDS_ROWMAJOR && MB <= 2 && AK != A_F32SPLIT) ||
                     (ALDS == ALDS_FRAG && AK != A_I8),
-                "LDS-staged A: row-major bf16 (one or two row blocks), or bf16 / fp32 fragments");
+                "LDS-staged A: row-major bf16 or int8 (one or two row blocks), or bf16 / fp32 "
+                "fragments");
   // The waves' partial tiles (summed over KW in the epilogue).  With two
   // row-major row blocks staged, they share the staged A's memory (both
   // together would exceed the CU's 160 KB): a barrier separates the main
@@ -374,19 +375,14 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
   const int li = lane & 31;
   const int z = bz;
 
-  const uint4* B;
-  int64_t N, n0, ocol0;
-  if (bx < p.ntiles0) {
-    B = p.B0;
-    N = p.N0;
-    n0 = static_cast<int64_t>(bx) * TN;
-    ocol0 = 0;
-  } else {
-    B = p.B1;
-    N = p.N1;
-    n0 = static_cast<int64_t>(bx - p.ntiles0) * TN;
-    ocol0 = p.N0;
-  }
+  // (the weight pointer is chosen arithmetically: a branch over the two
+  // kernel-argument pointers has been lowered to a private-memory table)
+  const bool second = bx >= p.ntiles0;
+  const uint4* B = reinterpret_cast<const uint4*>(
+      second ? reinterpret_cast<uintptr_t>(p.B1) : reinterpret_cast<uintptr_t>(p.B0));
+  const int64_t N = second ? p.N1 : p.N0;
+  const int64_t n0 = static_cast<int64_t>(second ? bx - p.ntiles0 : bx) * TN;
+  const int64_t ocol0 = second ? p.N0 : 0;
   B += static_cast<int64_t>(z) * p.b_bstride;
   const int KC = static_cast<int>(p.K / G);  // 16-byte chunk rows per column
 
@@ -488,7 +484,12 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
       }
     }
   };
+  // Row-major staged A is read from LDS where each MFMA uses it (so a batch
+  // holds only weight chunks and can cover a wave's whole k range); the
+  // other staged forms are read a batch ahead like the global ones.
+  constexpr bool A_AT_USE = ALDS == ALDS_ROWMAJOR;
   auto load_a = [&](Batch& x, int s0) {
+    if constexpr (A_AT_USE) return;
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       const int s = (s0 + u) < s_last ? (s0 + u) : s_last;
@@ -512,12 +513,18 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
     load_b(x, s0);
     load_a(x, s0);
   };
-  auto compute = [&](const Batch& x, int count) {
+  auto compute = [&](const Batch& x, int s0, int count) {
 #pragma unroll
     for (int u = 0; u < P; ++u) {
       if (u >= count) break;  // wave-uniform; only MFMAs are skipped
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (A_AT_USE) {
+          const uint4 av = alds[(mb * ACAP + (s0 + u - s_lo)) * 64 + lane];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) mfma_step<AK>(acc[mb][b], av, x.b[u][b]);
+          continue;
+        }
         if constexpr (AK == A_F32SPLIT) {
           uint4 hi, lo;
           const uint4 r0 = x.a[u][mb][0], r1 = x.a[u][mb][1];
@@ -591,8 +598,9 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
     const int per_row = 2 * cnt;
     // Buffer loads like the weight stream (loads of one kind complete in
     // order, so waiting for these does not drain the weight batch).
+    // (a k-step is 32 bytes of a row: 16 bf16 or 32 int8 k)
     const rsrc_t rx = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(s_lo) * 32,
-                                static_cast<uint32_t>(p.M * p.lda * 2 - s_lo * 32));
+                                static_cast<uint32_t>(p.M * p.lda * AEB - s_lo * 32));
     uint4 st[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -600,7 +608,7 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
       c = c < total ? c : total - 1;
       int m = c / per_row;
       m = m < p.M ? m : static_cast<int>(p.M) - 1;
-      st[i] = bld16(rx, static_cast<uint32_t>(m * p.lda * 2 + (c % per_row) * 16), 0u);
+      st[i] = bld16(rx, static_cast<uint32_t>(m * p.lda * AEB + (c % per_row) * 16), 0u);
     }
     load_b(X, w_lo);  // unconditional: a branch here would drain the staging loads
 #pragma unroll
@@ -613,16 +621,20 @@ __device__ __forceinline__ void skinny_tile(const GemmParams& p, const int bx, c
     lds_barrier();  // keeps the first weight batch in flight
     if (w_lo < w_hi) load_a(X, w_lo);
   }
+  // A batch as deep as a wave's whole k range (row-major staged A, at most
+  // ACAP steps over KW waves) is loaded once, with no re-read prefetch.
+  constexpr bool ONE_BATCH = A_AT_USE && P * KW >= ACAP;
   if (active && w_lo < w_hi) {
     int s = w_lo;
     if constexpr (ALDS == ALDS_NONE) load(X, s);
-    for (;;) {
+    if constexpr (ONE_BATCH) compute(X, s, w_hi - s);
+    else for (;;) {
       load(Y, s + P < w_hi ? s + P : s);
-      compute(X, w_hi - s);
+      compute(X, s, w_hi - s);
       s += P;
       if (s >= w_hi) break;
       load(X, s + P < w_hi ? s + P : s);
-      compute(Y, w_hi - s);
+      compute(Y, s, w_hi - s);
       s += P;
       if (s >= w_hi) break;
     }
@@ -2077,27 +2089,36 @@ constexpr int a8_nw() { return 4; }
 
 // A1 reads x row-major: with one 32-row block each workgroup stages its
 // split of x in LDS (fragment order), otherwise lanes load rows directly.
+constexpr int A1_I8_LDS_STEPS = 32;
 template <int MB>
 void skinny_a1(const GemmParams& g1, const MlaPlan& pl, bool xq, const Launch& L) {
   const dim3 grid(static_cast<unsigned>(g1.ntiles0 + (g1.N1 + kA1Cols - 1) / kA1Cols),
                   static_cast<unsigned>(pl.ksplit), 1);
   constexpr int KW = a1_kw<MB>();
   if (xq) {
-    // full quantisation: int8 x . int8 weights (32-k steps), int32 sums
+    // full quantisation: int8 x . int8 weights (32-k steps), int32 sums;
+    // staged like the bf16 x below (a split of at most 32 steps: 4 per wave)
+    if constexpr (MB <= 2) {
+      if (pl.steps_per_split <= A1_I8_LDS_STEPS) {
+        launch(L, k_skinny<A_I8, MB, 1, 2, 8, EPI_PARTIAL, 4, ALDS_ROWMAJOR, A1_I8_LDS_STEPS>,
+               grid, dim3(64 * 2 * 8), 0, g1);
+        return;
+      }
+    }
     skinny<A_I8, MB, 2, 1, KW, EPI_PARTIAL>(g1, grid, L);
     return;
   }
   if constexpr (MB == 1) {
     if (pl.steps_per_split <= A_LDS_STEPS) {
       // one column block per wave, two waves across, K over 8 waves
-      launch(L, k_skinny<A_BF16, 1, 1, 2, KW, EPI_PARTIAL, 4, ALDS_ROWMAJOR>, grid,
+      launch(L, k_skinny<A_BF16, 1, 1, 2, KW, EPI_PARTIAL, 8, ALDS_ROWMAJOR>, grid,
              dim3(64 * 2 * KW), 0, g1);
       return;
     }
   } else if constexpr (MB == 2) {
     if (pl.steps_per_split <= A_LDS_STEPS) {
       // the same shape over two row blocks (x split staged once: 128 KB)
-      launch(L, k_skinny<A_BF16, 2, 1, 2, 8, EPI_PARTIAL, 3, ALDS_ROWMAJOR>, grid,
+      launch(L, k_skinny<A_BF16, 2, 1, 2, 8, EPI_PARTIAL, 8, ALDS_ROWMAJOR>, grid,
              dim3(64 * 2 * 8), 0, g1);
       return;
     }
