@@ -77,6 +77,10 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   // product as one launch when a head's q^C and W^UK slices fit a wave's
   // registers (D <= 128).
   pl.merge_uk = pl.skinny && pl.mb == 1 && !quant && a->D <= 128;
+  // FULL_KV_INT8 decode with one row block quantises the query in the W^UK
+  // product's epilogue when a head's Hckv fits one tile of at most 16 waves;
+  // otherwise q^N goes out in fp32 for a separate quant kernel.
+  pl.qh = pl.skinny && pl.mb == 1 && a->quant_mode == MLA_QUANT_FULL_KV_INT8 && a->Hckv <= 512;
   size_t off = 0;
   if (a->weight_layout == MLA_WEIGHT_ND) {
     // packed copies: columns padded to whole 32-column blocks
@@ -100,7 +104,7 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   pl.off_qc = off;
   off += align256(static_cast<size_t>(pl.rows * a->N * a->D) * (quant ? 4 : 2));
   pl.off_qn = off;
-  if (a->quant_mode == MLA_QUANT_FULL_KV_INT8)
+  if (a->quant_mode == MLA_QUANT_FULL_KV_INT8 && !pl.qh)
     off += align256(static_cast<size_t>(T * a->N * a->Hckv) * sizeof(float));
   pl.off_xfrag = off;
   if (pl.gemm256) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);

@@ -2309,8 +2309,9 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   g8.q_bstride = a->Hckv;
   // FULL_KV_INT8: one workgroup per head quantises the query in its
   // epilogue when a head's Hckv fits one tile of at most 16 waves and T fits
-  // one row block; otherwise q^N goes out in fp32 for k_quant_query.
-  const bool qh = q8out && pl.skinny && pl.mb == 1 && a->Hckv <= 512;
+  // one row block (the plan's qh); otherwise q^N goes out in fp32 for
+  // k_quant_query.
+  const bool qh = pl.qh;
   if (q8out && !qh) g8.q_f32 = reinterpret_cast<float*>(ws + pl.off_qn);
   if (qh) {
     g8.q8_out = static_cast<int8_t*>(a->query);

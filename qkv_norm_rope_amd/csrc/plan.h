@@ -33,13 +33,16 @@ struct MlaPlan {
                       // (bf16, or int8 with q^C as bf16 hi + lo)
   bool merge_uk;      // skinny bf16, one row block: A6 and the W^UK product in
                       // one launch (k_decode_tail), handing q^C over per head
+  bool qh;            // FULL_KV_INT8 decode, one row block, Hckv <= 512: the
+                      // query quant runs in the W^UK product's epilogue
   int mb;             // 32-row blocks held per wave (skinny only)
   int ksplit;         // down-projection split-K factor
   int64_t steps_per_split;
   // workspace offsets (bytes) and total size
   size_t off_wdq, off_wdkvkr, off_wuqqr, off_wuk;  // packed weights (ND layout only)
   size_t off_part, off_cq, off_cq_scale, off_qc;
-  size_t off_qn;      // FULL_KV_INT8: q^N in fp32 before its per-head quant
+  size_t off_qn;      // FULL_KV_INT8 without qh: q^N in fp32 before its
+                      // per-head quant
   size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
   size_t off_sync;    // merge_uk: N per-head handoff counters, one per
                       // 256-byte line
