@@ -190,5 +190,9 @@ __device__ __forceinline__ void bst8_dev(rsrc_t r, uint32_t voff, uint2 v) {
   const u32x2_t w = {v.x, v.y};
   __builtin_amdgcn_raw_buffer_store_b64(w, r, static_cast<int>(voff), 0, kDeviceScope);
 }
+__device__ __forceinline__ void bst16_dev(rsrc_t r, uint32_t voff, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, static_cast<int>(voff), 0, kDeviceScope);
+}
 
 }  // namespace qkvnr

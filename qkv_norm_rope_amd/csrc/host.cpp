@@ -77,6 +77,13 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   // product as one launch when a head's q^C and W^UK slices fit a wave's
   // registers (D <= 128).
   pl.merge_uk = pl.skinny && pl.mb == 1 && !quant && a->D <= 128;
+  // The quantised scenarios with a bf16 query (T <= 64) when their up
+  // projection runs on 32-column tiles (fewer than 128 of the 96-column
+  // ones: few heads) and a head's q^C is whole 32-column k-steps (D a
+  // multiple of 32 up to 128).
+  pl.merge_uk_q = pl.skinny && pl.mb <= 2 && quant &&
+                  a->quant_mode != MLA_QUANT_FULL_KV_INT8 && a->D % 32 == 0 && a->D <= 128 &&
+                  (a->N * (a->D + a->Dr) + 95) / 96 < 128;
   // FULL_KV_INT8 decode with one row block quantises the query in the W^UK
   // product's epilogue when a head's Hckv fits one tile of at most 16 waves;
   // otherwise q^N goes out in fp32 for a separate quant kernel.
@@ -109,7 +116,7 @@ MlaPlan make_mla_plan(const MlaPrologV2Args* a) {
   pl.off_xfrag = off;
   if (pl.gemm256) off += align256(static_cast<size_t>(pl.rows * a->He) * 2);
   pl.off_sync = off;
-  if (pl.merge_uk) off += static_cast<size_t>(a->N) * SYNC_STRIDE * 4;
+  if (pl.merge_uk || pl.merge_uk_q) off += static_cast<size_t>(a->N) * SYNC_STRIDE * 4;
   pl.total = T > 0 ? off : 0;
   return pl;
 }
@@ -489,7 +496,7 @@ int mla_prolog_v2_kernels(const MlaPrologV2Args* args, uint32_t* mask) {
   if (args->B * args->S > 0) {
     *mask = (1u << MLA_KERNEL_COUNT) - 1u;
     const MlaPlan pl = make_mla_plan(args);
-    if (pl.merge_uk) *mask &= ~(1u << MLA_KERNEL_UK);
+    if (pl.merge_uk || pl.merge_uk_q) *mask &= ~(1u << MLA_KERNEL_UK);
     if (pl.fuse_uk) *mask &= ~(1u << MLA_KERNEL_UQQR);
 
   }

@@ -79,8 +79,9 @@ struct GemmParams {
   int qc_frag;            // write q^C in per-head fragment layout
   int64_t qc_D;           // head dim D (fragment layout)
   int64_t qc_mblocks;     // 32-row blocks per head (fragment layout)
-  int qc_coherent;        // bf16 fragment q^C with device-scope stores, for a
-                          // consumer in the same launch (k_decode_tail)
+  int qc_coherent;        // fragment q^C (bf16 or fp32) with device-scope
+                          // stores, for a consumer in the same launch
+                          // (k_decode_tail, k_decode_tail_q)
   int qc_split;           // fragment q^C as bf16 hi and lo = bf16(v - hi):
                           // per head 2*D k, hi in k-steps [0, D/16), lo after
   // Handoff words of the merged decode launch that this launch zeroes
@@ -236,9 +237,12 @@ struct Epilogue {
               st8(q + off, make_uint2(hw[0], hw[1]));
               st8(q + off + static_cast<int64_t>(D >> 4) * 512, make_uint2(lw[0], lw[1]));
             } else if (p.qc_f32) {
-              st16(static_cast<float*>(p.qc_out) + off,
-                   make_uint4(__float_as_uint(v[4 * hh]), __float_as_uint(v[4 * hh + 1]),
-                              __float_as_uint(v[4 * hh + 2]), __float_as_uint(v[4 * hh + 3])));
+              const uint4 f = make_uint4(__float_as_uint(v[4 * hh]), __float_as_uint(v[4 * hh + 1]),
+                                         __float_as_uint(v[4 * hh + 2]), __float_as_uint(v[4 * hh + 3]));
+              if (p.qc_coherent)  // (decode q^C, < 2^31 bytes: one resource)
+                bst16_dev(make_rsrc(p.qc_out, 0x7fffffffu), static_cast<uint32_t>(off) * 4u, f);
+              else
+                st16(static_cast<float*>(p.qc_out) + off, f);
             } else if (p.qc_coherent) {
               // decode q^C (< 2^31 bytes): one resource over the buffer
               bst8_dev(make_rsrc(p.qc_out, 0x7fffffffu), static_cast<uint32_t>(off) * 2u,
@@ -774,8 +778,8 @@ constexpr int kA6Cols = 96;  // decode A6 tile: three waves across, one column b
 
 // Up-projection tiles of kA6Cols columns that cover head h's q^C columns
 // [h*D, (h+1)*D): the count its W^UK tiles wait for.
-__device__ __forceinline__ unsigned up_tiles_of_head(int h, int D) {
-  return static_cast<unsigned>(((h + 1) * D - 1) / kA6Cols - (h * D) / kA6Cols + 1);
+__device__ __forceinline__ unsigned up_tiles_of_head(int h, int D, int tw = kA6Cols) {
+  return static_cast<unsigned>(((h + 1) * D - 1) / tw - (h * D) / tw + 1);
 }
 
 template <int KS>
@@ -849,13 +853,13 @@ __device__ __forceinline__ void uk_tile_after_up(const GemmParams& p, const int 
 // An up-projection tile of the merged launch that holds q^C columns: once
 // its q^C stores are complete, it bumps the counter of each head it covers.
 __device__ __forceinline__ void up_tile_signal(const GemmParams& up, const int b,
-                                               unsigned* ready) {
-  const int64_t n0 = static_cast<int64_t>(b) * kA6Cols;
+                                               unsigned* ready, const int tw = kA6Cols) {
+  const int64_t n0 = static_cast<int64_t>(b) * tw;
   if (n0 >= up.ND) return;  // q^R columns only
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's q^C stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int64_t n1 = n0 + kA6Cols < up.ND ? n0 + kA6Cols : up.ND;
+    const int64_t n1 = n0 + tw < up.ND ? n0 + tw : up.ND;
     const int D = static_cast<int>(up.qc_D);
     for (int h = static_cast<int>(n0 / D); h <= static_cast<int>((n1 - 1) / D); ++h)
       __hip_atomic_fetch_add(ready + h * SYNC_STRIDE, 1u, __ATOMIC_RELAXED,
@@ -1872,6 +1876,123 @@ __global__ __launch_bounds__(256) void k_decode_tail(DecodeTailParams p) {
                        up_tiles_of_head(h, static_cast<int>(p.up.qc_D)));
 }
 
+// W^UK tile of the quantised merged decode launch: as uk_tile_after_up, with
+// q^C in fp32 (fragment layout, 32 bytes per lane and k-step: the dequantised
+// int8 up projection) split into bf16 hi + lo = bf16(q^C - hi) for two MFMAs
+// per k-step, and MB 32-row blocks of tokens.  The head's q^C is staged in
+// LDS once; the same LDS then stages the output tile for whole-row stores.
+template <int KS, int MB>
+__device__ __forceinline__ void uk_tile_f32_after_up(const GemmParams& p, const int h,
+                                                     const int ct, const unsigned* ready,
+                                                     const unsigned need) {
+  static_assert(KS <= UK_MAX_STEPS, "the W^UK slice is held in registers");
+  constexpr int OPITCH = UK_TILE_COLS + 4;
+  constexpr int QC_CH = MB * KS * 128;                // 16-byte chunks of q^C
+  constexpr int OUT_CH = (MB * 32 * OPITCH + 3) / 4;  // 16-byte chunks of the output stage
+  __shared__ uint4 area[QC_CH > OUT_CH ? QC_CH : OUT_CH];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int li = lane & 31, g = lane >> 5;
+  const int KC = static_cast<int>(p.K / 8);  // 16-byte chunk rows per column block
+  const int64_t nblk = (p.N0 + 31) / 32;
+  int64_t nb = static_cast<int64_t>(ct) * (UK_TILE_COLS / 32) + wave;
+  nb = nb < nblk ? nb : nblk - 1;  // clamped blocks are computed, never stored
+  const rsrc_t rb = make_rsrc(p.B0 + static_cast<int64_t>(h) * p.b_bstride + nb * KC * 32,
+                              static_cast<uint32_t>(KC) * 512u);
+  const uint32_t vl = static_cast<uint32_t>(lane) * 16u;
+  uint4 w[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) w[s] = bld16_nt(rb, vl, static_cast<uint32_t>(s) * 1024u);
+
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need &&
+           ++n < SYNC_SPIN_LIMIT)
+      __builtin_amdgcn_s_sleep(4);
+  }
+  __syncthreads();
+
+  // Head h's fp32 q^C: row block mb, k-step s is 64 lanes x 32 bytes at
+  // (mb * KS + s) * 2 KB; copied as is.
+  const rsrc_t ra = make_rsrc(static_cast<const char*>(p.A) + static_cast<int64_t>(h) * p.a_zs,
+                              static_cast<uint32_t>(QC_CH) * 16u);
+  constexpr int PER = (QC_CH + 255) / 256;
+  uint4 q[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;
+    q[i] = bld16_dev(ra, static_cast<uint32_t>(c < QC_CH ? c : QC_CH - 1) * 16u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;
+    if (c < QC_CH) area[c] = q[i];
+  }
+  __syncthreads();
+  f32x16_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16_t{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint4 r0 = area[((mb * KS + s) * 64 + lane) * 2];
+      const uint4 r1 = area[((mb * KS + s) * 64 + lane) * 2 + 1];
+      uint4 hi, lo;
+      split8(make_float4(__uint_as_float(r0.x), __uint_as_float(r0.y), __uint_as_float(r0.z),
+                         __uint_as_float(r0.w)),
+             make_float4(__uint_as_float(r1.x), __uint_as_float(r1.y), __uint_as_float(r1.z),
+                         __uint_as_float(r1.w)),
+             hi, lo);
+      mfma_step<A_BF16>(acc[mb], hi, w[s]);
+      mfma_step<A_BF16>(acc[mb], lo, w[s]);
+    }
+  __syncthreads();  // every wave is done with the staged q^C
+
+  // MB 32x32 blocks -> LDS (row 32*mb + 8*(r/4) + 4*g + r%4, column
+  // 32*wave + li), then each thread stores 8 consecutive columns of a row.
+  uint32_t* stage = reinterpret_cast<uint32_t*>(area);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      stage[(32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)) * OPITCH + wave * 32 + li] =
+          __float_as_uint(acc[mb][r]);
+  __syncthreads();
+  for (int it = threadIdx.x; it < MB * 32 * (UK_TILE_COLS / 8); it += 256) {
+    const int row = it / (UK_TILE_COLS / 8);
+    const int c0 = (it % (UK_TILE_COLS / 8)) * 8;
+    const int64_t gcol = static_cast<int64_t>(ct) * UK_TILE_COLS + c0;
+    if (row >= p.M || gcol >= p.N0) continue;
+    const uint32_t* v = &stage[row * OPITCH + c0];
+    st16_nt(p.q_out + row * p.q_ld + static_cast<int64_t>(h) * p.q_bstride + gcol,
+            make_uint4(pack_bf16x2(__uint_as_float(v[0]), __uint_as_float(v[1])),
+                       pack_bf16x2(__uint_as_float(v[2]), __uint_as_float(v[3])),
+                       pack_bf16x2(__uint_as_float(v[4]), __uint_as_float(v[5])),
+                       pack_bf16x2(__uint_as_float(v[6]), __uint_as_float(v[7]))));
+  }
+}
+
+// Quantised decode (int8 c^Q and W^UQ_QR, bf16 query; T <= 32 * MB, D <=
+// 128): the up projection's 32-column tiles (K over four waves) and the W^UK
+// product in one launch, handed over per head as in k_decode_tail.  The up
+// tiles write fp32 q^C with device-scope stores; the W^UK tiles wait for the
+// D/32 tiles that cover their head.
+constexpr int kA6ColsQ = 32;
+template <int KS, int MB>
+__global__ __launch_bounds__(256) void k_decode_tail_q(DecodeTailParams p) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < p.up_tiles) {
+    skinny_tile<A_I8, MB, 1, 1, 4, EPI_UQQR>(p.up, b, 0, 0);
+    up_tile_signal(p.up, b, p.ready, kA6ColsQ);
+    return;
+  }
+  const int u = b - p.up_tiles;
+  const int h = u / p.uk_tiles, ct = u % p.uk_tiles;
+  uk_tile_f32_after_up<KS, MB>(p.uk, h, ct, p.ready + h * SYNC_STRIDE,
+                               up_tiles_of_head(h, static_cast<int>(p.up.qc_D), kA6ColsQ));
+}
+
 // ---------------------------------------------------------------------------
 // MlaPreprocessV2 first step (aclnnMlaPreprocessV2: x is processed by
 // RmsNormQuant before the W^DQKV product; formula block): per token,
@@ -2358,7 +2479,7 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
   if (pre != nullptr) f.qs_cq = pre->qs_cq;
   // Merged decode tail: the down projection zeroes its handoff counters.
   unsigned* ready = reinterpret_cast<unsigned*>(ws + pl.off_sync);
-  if (pl.merge_uk) {
+  if (pl.merge_uk || pl.merge_uk_q) {
     g1.zero_words = ready;
     g1.zero_count = static_cast<int>(a->N);
     g6.qc_coherent = 1;
@@ -2441,6 +2562,32 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
         default: launch(L6, k_decode_tail<8>, grid, dim3(256), 0, u); break;
       }
       mark(MLA_PHASE_AFTER_UQQR);
+    } else if (pl.merge_uk_q) {
+      DecodeTailParams u{};
+      u.up = g6;
+      u.uk = g8;
+      u.ready = ready;
+      u.up_tiles = static_cast<int>((g6.N0 + kA6ColsQ - 1) / kA6ColsQ);
+      u.uk_tiles = static_cast<int>((a->Hckv + UK_TILE_COLS - 1) / UK_TILE_COLS);
+      const dim3 grid(static_cast<unsigned>(u.up_tiles + nh * u.uk_tiles));
+      // (D a multiple of 32, at most 128: 2, 4, 6 or 8 k-steps)
+      const int ks = static_cast<int>(a->D / 16);
+      if (pl.mb == 1) {
+        switch (ks) {
+          case 2: launch(L6, k_decode_tail_q<2, 1>, grid, dim3(256), 0, u); break;
+          case 4: launch(L6, k_decode_tail_q<4, 1>, grid, dim3(256), 0, u); break;
+          case 6: launch(L6, k_decode_tail_q<6, 1>, grid, dim3(256), 0, u); break;
+          default: launch(L6, k_decode_tail_q<8, 1>, grid, dim3(256), 0, u); break;
+        }
+      } else {
+        switch (ks) {
+          case 2: launch(L6, k_decode_tail_q<2, 2>, grid, dim3(256), 0, u); break;
+          case 4: launch(L6, k_decode_tail_q<4, 2>, grid, dim3(256), 0, u); break;
+          case 6: launch(L6, k_decode_tail_q<6, 2>, grid, dim3(256), 0, u); break;
+          default: launch(L6, k_decode_tail_q<8, 2>, grid, dim3(256), 0, u); break;
+        }
+      }
+      mark(MLA_PHASE_AFTER_UQQR);
     } else {
       switch (pl.mb) {
         case 1: skinny_a6<1>(g6, quant, L6); break;
@@ -2449,8 +2596,8 @@ int launch_mla_prolog_v2(const MlaPrologV2Args* a, const MlaPlan& pl, void* work
       }
       mark(MLA_PHASE_AFTER_UQQR);
     }
-    if (pl.merge_uk) {
-      // the W^UK product ran inside k_decode_tail
+    if (pl.merge_uk || pl.merge_uk_q) {
+      // the W^UK product ran inside k_decode_tail(_q)
     } else if (qh) {
       // one workgroup per head; its fp32 q^C (D <= 128) staged in LDS once
       // (16 waves re-reading it: 11.2 -> 9.9 us at the DeepSeek-V3 shape)

@@ -33,6 +33,9 @@ struct MlaPlan {
                       // (bf16, or int8 with q^C as bf16 hi + lo)
   bool merge_uk;      // skinny bf16, one row block: A6 and the W^UK product in
                       // one launch (k_decode_tail), handing q^C over per head
+  bool merge_uk_q;    // skinny quantised with a bf16 query, at most two row
+                      // blocks, few up-projection columns: the same in one
+                      // launch with fp32 q^C (k_decode_tail_q)
   bool qh;            // FULL_KV_INT8 decode, one row block, Hckv <= 512: the
                       // query quant runs in the W^UK product's epilogue
   int mb;             // 32-row blocks held per wave (skinny only)
@@ -44,7 +47,7 @@ struct MlaPlan {
   size_t off_qn;      // FULL_KV_INT8 without qh: q^N in fp32 before its
                       // per-head quant
   size_t off_xfrag;   // token_x in fragment layout (256-tile plan)
-  size_t off_sync;    // merge_uk: N per-head handoff counters, one per
+  size_t off_sync;    // merge_uk(_q): N per-head handoff counters, one per
                       // 256-byte line
   size_t off_prex8, off_presx;  // MlaPreprocessV2: RmsNormQuant codes of x
                                 // (T, He) int8 and their unit token scales

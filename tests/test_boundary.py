@@ -141,6 +141,13 @@ def test_mla_kernels_mask():
             want = merged if (q == "none" and T <= 32) else (
                 fused if (T > 128 and q != "full_kv_int8") else qn.MLA_KERNELS)
             assert qn.mla_prolog_v2_kernels(mla_args(T=T, quant=q)) == want
+    # with 32 heads the quantised modes with a bf16 query merge the W^UK
+    # product into the up projection's launch up to T = 64 (two row blocks)
+    for T in (1, 32, 33, 64, 65, 129):
+        for q in ("partial_kv_bf16", "partial_kv_int8", "full_kv_bf16", "full_kv_int8"):
+            want = merged if (T <= 64 and q != "full_kv_int8") else (
+                fused if (T > 128 and q != "full_kv_int8") else qn.MLA_KERNELS)
+            assert qn.mla_prolog_v2_kernels(mla_args(T=T, quant=q, N=32)) == want, (T, q)
     e = mla_args(T=0)
     assert qn.mla_prolog_v2_kernels(e) == ()
     bad = mla_args()
@@ -526,8 +533,13 @@ def test_mla_fuzzed_args_validate_size_and_plan_consistently():
         else:
             T = a.B * a.S
             # all four kernels, or all but the W^UK launch (merged into the
-            # up projection's for bf16 decode with D <= 128 and T <= 32)
-            merged = q == "none" and 0 < T <= 32 and a.D <= 128
+            # up projection's for bf16 decode with D <= 128 and T <= 32, and
+            # for the quantised modes with a bf16 query, T <= 64, D <= 128
+            # and fewer than 128 of the 96-column up-projection tiles)
+            merged = ((q == "none" and 0 < T <= 32 and a.D <= 128) or
+                      (q in ("partial_kv_bf16", "partial_kv_int8", "full_kv_bf16")
+                       and 0 < T <= 64 and a.D <= 128
+                       and (a.N * (a.D + a.Dr) + 95) // 96 < 128))
             fused = (T > 128 and q != "full_kv_int8" and a.D == 128
                      and (a.N * a.D) % 256 == 0)
             want = 0 if T == 0 else (7 if merged else (11 if fused else 15))
