@@ -259,9 +259,12 @@ typedef struct MlaPrologV2Args {
  * that fuses the W^UK product (D = 128), MLA_KERNEL_UK is one launch that
  * runs the q^C columns with the fused W^UK product and the q^R columns, and
  * MLA_KERNEL_UQQR is not launched.  With
- * the bf16 decode plan for T <= 32 and D <= 128, MLA_KERNEL_UQQR is one
- * launch that runs the up projection and the W^UK product, and
- * MLA_KERNEL_UK is not launched (mla_prolog_v2_kernels reports which). */
+ * the bf16 decode plan for T <= 32 and D <= 128, and with the quantised
+ * decode plans that write a bf16 query for T <= 64 when the up projection
+ * has fewer than 128 x 96 columns (D a multiple of 32 up to 128),
+ * MLA_KERNEL_UQQR is one launch that runs the up projection and the W^UK
+ * product, and MLA_KERNEL_UK is not launched (mla_prolog_v2_kernels
+ * reports which). */
 enum {
   MLA_KERNEL_DOWN = 0,  /* x . [W^DQ | W^DKV_KR] */
   MLA_KERNEL_NORM = 1,  /* RmsNorms, c^Q quant, RoPE k^R, cache scatter */
