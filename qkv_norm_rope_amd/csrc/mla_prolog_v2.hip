@@ -2193,8 +2193,8 @@ void skinny(const GemmParams& p, dim3 grid, const Launch& L) {
 // finish (launched between A1 and A6).  Many short per-wave weight runs keep
 // the most bytes in flight.  A1: 64-column tiles with the K range split over
 // ksplit workgroups and, inside one, over 8 waves (fewer when more 32-row
-// blocks fill the registers); with one row block, x is staged in LDS and two
-// waves across take one column block each.  A6: 96-column tiles, three waves
+// blocks fill the registers); with one or two row blocks, x is staged in LDS
+// and two waves across take one column block each.  A6: 96-column tiles, three waves
 // across with one column block each (256 tiles for the DeepSeek-V3 shape:
 // one per CU); with one row block each wave streams the whole K in batches
 // of 4 k-steps, otherwise K is split over waves.  A8: 4 waves on different
@@ -2208,8 +2208,9 @@ constexpr int a8_nw() { return 4; }
 // A1 tiles are kA1Cols = 64 columns wide (plan.h): two column blocks, one
 // per wave across when x is staged in LDS, both in each wave otherwise.
 
-// A1 reads x row-major: with one 32-row block each workgroup stages its
-// split of x in LDS (fragment order), otherwise lanes load rows directly.
+// A1 reads x row-major: with one or two 32-row blocks each workgroup stages
+// its split of x in LDS (fragment order; bf16 x up to 64 k-steps, int8 x up
+// to A1_I8_LDS_STEPS), otherwise lanes load rows directly.
 constexpr int A1_I8_LDS_STEPS = 32;
 template <int MB>
 void skinny_a1(const GemmParams& g1, const MlaPlan& pl, bool xq, const Launch& L) {
