@@ -240,6 +240,25 @@ def test_mla_full_quant_query_in_epilogue(Hckv, T):
     gh.announce(f"  ok {gh.check_mla(w, out, before)}")
 
 
+@pytest.mark.parametrize("mode,D,Dr,T", [("partial_kv_int8", 64, 32, 33),
+                                         ("partial_kv_bf16", 96, 64, 64),
+                                         ("full_kv_bf16", 32, 16, 1),
+                                         ("partial_kv_int8", 128, 64, 17)])
+def test_mla_quant_merged_decode_launch(mode, D, Dr, T):
+    """The quantised decode plans with a bf16 query and few heads run the up
+    projection and the W^UK product as one launch (fp32 q^C handed over per
+    head): one and two 32-row blocks, ragged T, D = 32 to 128."""
+    cfg = get_config(3).replace(He=512, Hcq=256, N=8, D=D, Dr=Dr, Hckv=256, B=T,
+                                quant_mode=mode, seed=2060 + D + T)
+    w = make_workload(cfg)
+    gh.announce(f"mla {w.cfg.name} {mode} D={D} Dr={Dr} T={T}")
+    dev = gh.upload(w)
+    before = _before(dev, ["kv_cache", "kr_cache"])
+    out = gh.run_mla_gpu(w, dev)
+    torch.cuda.synchronize()
+    gh.announce(f"  ok {gh.check_mla(w, out, before)}")
+
+
 @pytest.mark.parametrize("mode,T", [("full_kv_int8", 32), ("full_kv_bf16", 64),
                                     ("full_kv_bf16", 32), ("full_kv_int8", 64),
                                     ("partial_kv_bf16", 64),
